@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed NR-MMDiT hot path on one MI355X.
+
+One step = one training forward over one synthetic pack, all on the GPU:
+pack ids -> gather per-sample tensors -> RF noising -> timestep conditioning
+-> token embedding -> one dual-stream block -> final layer -> RF loss.
+Default workload: the 256^2-stage pack, 16 samples x (16x16 latent grid +
+128 text tokens), hidden 3072, 24 x 128 heads, MLP 12288, bf16.
+
+Prints ONE JSON line.  `value` is whole-step token throughput (image + text
+tokens per second); the line also carries the block's TFLOP/s against the
+bf16 MFMA peak, the roofline of the dominant kernel (timed live with hipEvents
+over the timed region) and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed MMDiT block tokens/s + TFLOP/s (% bf16 peak); ms per 4-step 1024² pack"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def kernel_work(wl):
+    """Algorithmic work per launch of each tagged kernel of one step."""
+    d = wl.dims
+    H, M = d.hidden, d.mlp
+    n = sum(f * h * w + t for h, w, f, t in wl.samples)
+    n_tgt = sum(h * w for h, w, _, _ in wl.samples)
+    att = sum((f * h * w + t) ** 2 for h, w, f, t in wl.samples)
+    es = 2 if wl.dtype == "bf16" else 4
+    return {
+        "qkv_proj": ("mfma", 2.0 * n * H * 3 * H),
+        "out_proj_gated": ("mfma", 2.0 * n * H * H),
+        "mlp_up_gelu": ("mfma", 2.0 * n * H * M),
+        "mlp_down_gated": ("mfma", 2.0 * n * M * H),
+        "attn_mfma_kernel": ("mfma", 4.0 * H * att),
+        # one launch per stream: read x, write y (bytes); averaged over the two streams
+        "rms_modulate_kernel": ("hbm", 2.0 * es * H * n / 2),
+        "qk_norm_rope_kernel": ("hbm", 4.0 * es * H * n / 2),
+        "final_out": ("mfma", 2.0 * n_tgt * H * d.c_lat),
+    }
+
+
+def step_flops(wl):
+    from resolution_image_gen_amd.configs import block_flops
+
+    d = wl.dims
+    H = d.hidden
+    B = len(wl.samples)
+    n_img = sum(f * h * w for h, w, f, _ in wl.samples)
+    n_txt = sum(t for *_, t in wl.samples)
+    n_tgt = sum(h * w for h, w, _, _ in wl.samples)
+    blk = block_flops(d, wl.samples)[0] * wl.depth
+    wrap = 2.0 * (n_img * d.c_lat * H + n_txt * d.d_txt * H + n_tgt * H * d.c_lat
+                  + B * (d.t_dim * H + H * H + 12 * H * H * wl.depth + 2 * H * H))
+    return blk, wrap
+
+
+def cpu_baseline(wl, W, inputs, n_samples):
+    """The oracle (float64 numpy) on the first n_samples samples of the pack."""
+    import numpy as np
+
+    from oracle import flow as OF
+    from oracle import pack as OP
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    samples = list(wl.samples[:n_samples])
+    ref = OP.pack(samples)
+    ni, nt = ref["cu_img"][-1], ref["cu_txt"][-1]
+    Wd = {k: np.asarray(v, np.float64) for k, v in W.np_wrap.items()}
+    Wd["blocks"] = [{s: {k: np.asarray(v, np.float64) for k, v in nb[s].items()} for s in nb}
+                    for nb in W.np_blocks]
+    z, eps, tau, t = inputs["z"][:ni], inputs["eps"][:ni], inputs["tau"][:nt], inputs["t"][:n_samples]
+    t0 = time.perf_counter()
+    zt = OF.make_xt(z, eps, t, ref)
+    v = OF.velocity_model(zt, tau, t, Wd, ref, wl.dims.heads)
+    OF.loss(v, z, eps, ref)
+    dt = time.perf_counter() - t0
+    tokens = ni + nt
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_samples} of {len(wl.samples)} samples ({tokens} tokens), same step, float64 numpy, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pack256_bf16")
+    ap.add_argument("--cpu-samples", type=int, default=2, help="samples of the pack the CPU oracle runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(packs are independent; see the sharding notes of the design).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import runner as R
+
+    wl = CF.WORKLOADS[args.workload]
+    if wl.steps:
+        raise SystemExit("sampler workloads are timed by bench_sampler in this file's --workload list; "
+                         "use a training-forward workload")
+    torch.cuda.set_device(0)
+    W = R.Weights(wl)
+    inputs = R.training_inputs(wl)
+    tf = R.TrainForward(wl, W, inputs)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        tf.run()
+    torch.cuda.synchronize()
+
+    # timed region (hipEvents on the launch stream bracket the whole region)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        tf.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernels = B.timing_report()
+    B.timing_enable(False)
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
+    blk, wrap = step_flops(wl)
+    tflops = (blk + wrap) / (ms_step * 1e-3) / 1e12
+    work = kernel_work(wl)
+    # dominant kernel: largest total time among kernels with a known algorithmic work
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
+    kind, per_launch = work[dom]
+    avg_ms = kernels[dom][0] / kernels[dom][1]
+    if kind == "mfma":
+        achieved = per_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+
+    table = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] / args.steps}
+             for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][0])}
+    if args.kernels:
+        for k, v in table.items():
+            extra = ""
+            if k in work:
+                kd, wk = work[k]
+                per = v["ms_per_step"] / v["launches_per_step"] * 1e-3
+                extra = (f"  {wk / per / 1e12:8.1f} TFLOP/s" if kd == "mfma" else f"  {wk / per / 1e9:8.1f} GB/s")
+            print(f"{k:48s} {v['ms_per_step'] * 1e3:10.1f} us/step  x{v['launches_per_step']:.0f}{extra}",
+                  file=sys.stderr)
+
+    out = {
+        "metric": METRIC,
+        "value": round(n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded N(0,1) latents, noise and text features; random-init N(0,0.02) weights",
+        "config": {"workload": f"{wl.name}: {wl.note}", "tokens_per_step": n_tokens,
+                   "samples": len(wl.samples), "hidden": wl.dims.hidden, "heads": wl.dims.heads,
+                   "head_dim": wl.dims.head_dim, "mlp": wl.dims.mlp, "blocks": wl.depth},
+        "tflops": round(tflops, 1),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "block_tflop_per_step": round(blk / 1e12, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, W, inputs, args.cpu_samples)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,627 @@
+// C ABI of libmmdit: argument validation, workspace layout and the launch
+// sequence of the block, the conditioning and the rectified-flow wrapper.
+#include <map>
+#include <string>
+#include <vector>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace mmdit {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+mmdit_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MMDIT_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return MMDIT_E_HIP;
+}
+
+static bool sync_mode() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_SYNC");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// ------------------------------------------------------- kernel timing
+// While enabled, MMDIT_LAUNCH records an event before each launch and
+// launch_check one after it; the report sums the elapsed times per kernel
+// name.  Single-threaded use; not for use under stream capture.
+namespace {
+struct TimingRec {
+  const char* name;
+  int a, b;
+};
+bool g_timing = false;
+std::vector<hipEvent_t> g_events;
+size_t g_used = 0;
+int g_pending = -1;
+std::vector<TimingRec> g_recs;
+
+int next_event() {
+  if (g_used == g_events.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_events.push_back(e);
+  }
+  return (int)g_used++;
+}
+}  // namespace
+
+void timing_begin(hipStream_t s) {
+  if (!g_timing) return;
+  g_pending = next_event();
+  if (g_pending >= 0) hipEventRecord(g_events[g_pending], s);
+}
+
+mmdit_status launch_check(const char* kernel, hipStream_t s) {
+  MMDIT_TRY(hip_check(hipGetLastError(), kernel));
+  if (g_timing && g_pending >= 0) {
+    int e = next_event();
+    if (e >= 0) {
+      hipEventRecord(g_events[e], s);
+      g_recs.push_back({kernel, g_pending, e});
+    }
+    g_pending = -1;
+  }
+  if (sync_mode()) MMDIT_TRY(hip_check(hipStreamSynchronize(s), kernel));
+  return MMDIT_OK;
+}
+
+// implemented next to their kernels
+mmdit_status plan_impl(const mmdit_sample*, int32_t, int64_t, int64_t, int32_t*, int64_t*, int64_t*, int32_t*);
+mmdit_status pack_impl(const mmdit_sample*, int32_t, mmdit_pack_t*, hipStream_t);
+mmdit_status gather_impl(const mmdit_pack_t*, int32_t, const void* const*, int32_t, mmdit_dtype, void*, hipStream_t);
+mmdit_status make_xt_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const float*, void*, hipStream_t);
+mmdit_status loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, void*, size_t, hipStream_t);
+mmdit_status euler_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, int32_t, int32_t, float, float, float, float*, void*, hipStream_t);
+mmdit_status pack_latent_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const float*, int32_t, int32_t, void*, hipStream_t);
+mmdit_status rms_modulate_impl(mmdit_dtype, int64_t, int32_t, const void*, const int32_t*, const int32_t*, const float*, int64_t, int64_t, int64_t, void*, float, hipStream_t);
+mmdit_status qk_norm_rope_impl(mmdit_dtype, int64_t, int32_t, int32_t, void*, const int32_t*, const float*, const float*, float, float, hipStream_t);
+mmdit_status temb_impl(mmdit_dtype, int32_t, int32_t, const float*, void*, hipStream_t);
+mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, hipStream_t);
+
+namespace {
+
+size_t esize(mmdit_dtype d) { return d == MMDIT_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mmdit_status check_dims(const mmdit_dims* d, const char* who) {
+  if (!d) {
+    set_error("%s: dims is NULL", who);
+    return MMDIT_E_INVALID;
+  }
+  if (d->dtype != MMDIT_F32 && d->dtype != MMDIT_BF16) {
+    set_error("%s: unknown dtype %d", who, (int)d->dtype);
+    return MMDIT_E_INVALID;
+  }
+  if (d->heads <= 0 || d->hidden != d->heads * d->head_dim || d->mlp <= 0 || d->c_lat <= 0 ||
+      d->d_txt <= 0 || d->t_dim <= 0 || !(d->eps > 0.f) || !(d->rope_theta > 0.f)) {
+    set_error("%s: inconsistent dims (hidden=%d heads=%d head_dim=%d mlp=%d c_lat=%d d_txt=%d t_dim=%d)",
+              who, d->hidden, d->heads, d->head_dim, d->mlp, d->c_lat, d->d_txt, d->t_dim);
+    return MMDIT_E_INVALID;
+  }
+  if ((d->head_dim != 64 && d->head_dim != 128) || d->hidden % 64 || d->mlp % 64 || d->c_lat % 64 ||
+      d->d_txt % 64 || d->t_dim % 16 || d->hidden > 8192) {
+    set_error("%s: unsupported dims (head_dim in {64,128}; hidden, mlp, c_lat, d_txt multiples of 64, "
+              "hidden <= 8192; t_dim multiple of 16)", who);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  return MMDIT_OK;
+}
+
+mmdit_status check_pack(const mmdit_pack_t* pk, const char* who) {
+  if (!pk || pk->B < 0 || pk->B > MMDIT_MAX_SAMPLES || pk->h_cu_img[pk->B] != pk->n_img ||
+      pk->h_cu_txt[pk->B] != pk->n_txt || pk->h_cu_tgt[pk->B] != pk->n_tgt) {
+    set_error("%s: pack is invalid or was not built by mmdit_pack", who);
+    return MMDIT_E_INVALID;
+  }
+  if (!pk->cu_txt || !pk->cu_img || (pk->n_img > 0 && (!pk->seg_img || !pk->pos_img || !pk->tgt_row)) ||
+      (pk->n_txt > 0 && !pk->seg_txt)) {
+    set_error("%s: a device array of the pack is NULL", who);
+    return MMDIT_E_INVALID;
+  }
+  return MMDIT_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// scalar-read arrays (timesteps) only need their element alignment
+mmdit_status need4(const void* p, const char* who, const char* name) {
+  if (!p) {
+    set_error("%s: %s is NULL", who, name);
+    return MMDIT_E_INVALID;
+  }
+  if ((uintptr_t)p & 3) {
+    set_error("%s: %s is not 4-byte aligned", who, name);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  return MMDIT_OK;
+}
+
+mmdit_status need(const void* p, const char* who, const char* name) {
+  if (!p) {
+    set_error("%s: %s is NULL", who, name);
+    return MMDIT_E_INVALID;
+  }
+  if (!aligned16(p)) {
+    set_error("%s: %s is not 16-byte aligned", who, name);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  return MMDIT_OK;
+}
+
+struct Layout {
+  size_t mod_img, mod_txt, h, qkv, o, u, end;
+};
+
+Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  const size_t es = esize(d->dtype);
+  const size_t N = (size_t)(pk->n_img + pk->n_txt);
+  const size_t H = d->hidden;
+  Layout L;
+  size_t o = 0;
+  L.mod_img = o; o = align256(o + (size_t)pk->B * 6 * H * 4);
+  L.mod_txt = o; o = align256(o + (size_t)pk->B * 6 * H * 4);
+  L.h = o;       o = align256(o + N * H * es);
+  L.qkv = o;     o = align256(o + N * 3 * H * es);
+  L.o = o;       o = align256(o + N * H * es);
+  L.u = o;       o = align256(o + N * (size_t)d->mlp * es);
+  L.end = o;
+  return L;
+}
+
+size_t final_ws(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  return align256((size_t)pk->B * 2 * d->hidden * 4) + align256((size_t)pk->n_tgt * d->hidden * esize(d->dtype));
+}
+
+LinearArgs mk(int64_t M, int32_t N, int32_t K, const void* A, const void* W, void* Y, int epi) {
+  LinearArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = K;
+  a.W = W;
+  a.Y = Y;
+  a.ldy = N;
+  a.epilogue = epi;
+  return a;
+}
+
+mmdit_status check_stream_w(const mmdit_stream_w& w, const char* who) {
+  MMDIT_TRY(need(w.w_mod, who, "w_mod"));
+  MMDIT_TRY(need(w.w_qkv, who, "w_qkv"));
+  MMDIT_TRY(need(w.g_q, who, "g_q"));
+  MMDIT_TRY(need(w.g_k, who, "g_k"));
+  MMDIT_TRY(need(w.w_o, who, "w_o"));
+  MMDIT_TRY(need(w.w_up, who, "w_up"));
+  MMDIT_TRY(need(w.w_down, who, "w_down"));
+  return MMDIT_OK;
+}
+
+}  // namespace
+}  // namespace mmdit
+
+using namespace mmdit;
+
+extern "C" {
+
+const char* mmdit_last_error(void) { return g_err; }
+
+mmdit_status mmdit_timing_enable(int32_t on) {
+  g_timing = on != 0;
+  g_used = 0;
+  g_pending = -1;
+  g_recs.clear();
+  return MMDIT_OK;
+}
+
+int32_t mmdit_timing_report(int32_t max_entries, char* names, double* total_ms, int64_t* count) {
+  if (hip_check(hipDeviceSynchronize(), "mmdit_timing_report") != MMDIT_OK) return -1;
+  std::map<std::string, std::pair<double, int64_t>> agg;
+  std::vector<std::string> order;
+  for (const TimingRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_events[r.a], g_events[r.b]) != hipSuccess) continue;
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      order.push_back(r.name);
+      agg[r.name] = {ms, 1};
+    } else {
+      it->second.first += ms;
+      it->second.second += 1;
+    }
+  }
+  int32_t n = 0;
+  for (const std::string& k : order) {
+    if (n >= max_entries) break;
+    if (names) {
+      strncpy(names + 64 * n, k.c_str(), 63);
+      names[64 * n + 63] = 0;
+    }
+    if (total_ms) total_ms[n] = agg[k].first;
+    if (count) count[n] = agg[k].second;
+    ++n;
+  }
+  return n;
+}
+const char* mmdit_version(void) { return "mmdit-gfx950 0.1"; }
+
+mmdit_status mmdit_pack_plan(const mmdit_sample* s, int32_t n, int64_t img_budget, int64_t joint_budget,
+                             int32_t* n_taken, int64_t* n_img, int64_t* n_txt, int32_t* max_joint) {
+  return plan_impl(s, n, img_budget, joint_budget, n_taken, n_img, n_txt, max_joint);
+}
+
+mmdit_status mmdit_pack(const mmdit_sample* s, int32_t n, mmdit_pack_t* io, mmdit_stream stream) {
+  return pack_impl(s, n, io, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_pack_gather(const mmdit_pack_t* pk, int32_t which, const void* const* src,
+                               int32_t width, mmdit_dtype dt, void* dst, mmdit_stream stream) {
+  MMDIT_TRY(check_pack(pk, "mmdit_pack_gather"));
+  return gather_impl(pk, which, src, width, dt, dst, (hipStream_t)stream);
+}
+
+size_t mmdit_workspace_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  if (check_dims(d, "mmdit_workspace_size") != MMDIT_OK || check_pack(pk, "mmdit_workspace_size") != MMDIT_OK)
+    return 0;
+  size_t w = block_layout(d, pk).end;
+  size_t f = final_ws(d, pk);
+  size_t l = align256((size_t)pk->n_tgt * 4 + 4);
+  size_t c = align256((size_t)pk->B * (d->t_dim + d->hidden) * esize(d->dtype) + 256);
+  if (f > w) w = f;
+  if (l > w) w = l;
+  if (c > w) w = c;
+  return w;
+}
+
+int32_t mmdit_workspace_layout(const mmdit_dims* d, const mmdit_pack_t* pk, size_t* out) {
+  if (!out || check_dims(d, "mmdit_workspace_layout") != MMDIT_OK ||
+      check_pack(pk, "mmdit_workspace_layout") != MMDIT_OK)
+    return 0;
+  Layout L = block_layout(d, pk);
+  out[0] = L.mod_img;
+  out[1] = L.mod_txt;
+  out[2] = L.h;
+  out[3] = L.qkv;
+  out[4] = L.o;
+  out[5] = L.u;
+  return 6;
+}
+
+mmdit_status mmdit_cond(const mmdit_dims* d, const void* w_t1, const void* w_t2, const float* t, int32_t B,
+                        void* c, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_cond";
+  MMDIT_TRY(check_dims(d, who));
+  if (B < 0) {
+    set_error("%s: B=%d", who, B);
+    return MMDIT_E_INVALID;
+  }
+  if (B == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w_t1, who, "w_t1"));
+  MMDIT_TRY(need(w_t2, who, "w_t2"));
+  MMDIT_TRY(need4(t, who, "t"));
+  MMDIT_TRY(need(c, who, "c"));
+  const size_t es = esize(d->dtype);
+  const size_t emb_b = align256((size_t)B * d->t_dim * es);
+  const size_t need_b = emb_b + (size_t)B * d->hidden * es;
+  if (!ws || ws_bytes < need_b) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, need_b, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  void* emb = w;
+  void* h1 = w + emb_b;
+  MMDIT_TRY(temb_impl(d->dtype, B, d->t_dim, t, emb, s));
+  LinearArgs a = mk(B, d->hidden, d->t_dim, emb, w_t1, h1, MMDIT_EPI_STORE);
+  a.tag = "cond_mlp1";
+  MMDIT_TRY(linear(d->dtype, &a, 1, s));
+  LinearArgs b = mk(B, d->hidden, d->hidden, h1, w_t2, c, MMDIT_EPI_STORE);
+  b.a_silu = 1;
+  b.tag = "cond_mlp2";
+  return linear(d->dtype, &b, 1, s);
+}
+
+mmdit_status mmdit_modulation(const mmdit_dims* d, const void* w, int32_t chunks, int32_t B, const void* c,
+                              float* mod, mmdit_stream stream) {
+  const char* who = "mmdit_modulation";
+  MMDIT_TRY(check_dims(d, who));
+  if (chunks <= 0 || B < 0) {
+    set_error("%s: chunks=%d B=%d", who, chunks, B);
+    return MMDIT_E_INVALID;
+  }
+  if (B == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w, who, "w"));
+  MMDIT_TRY(need(c, who, "c"));
+  MMDIT_TRY(need(mod, who, "mod"));
+  LinearArgs a = mk(B, chunks * d->hidden, d->hidden, c, w, mod, MMDIT_EPI_STORE_F32);
+  a.a_silu = 1;
+  return linear(d->dtype, &a, 1, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_embed(const mmdit_dims* d, const void* w_in, const void* w_txt, const mmdit_pack_t* pk,
+                         const void* zt, const void* tau, void* x_img, void* x_txt, mmdit_stream stream) {
+  const char* who = "mmdit_embed";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  LinearArgs a[2];
+  int n = 0;
+  if (pk->n_img > 0) {
+    MMDIT_TRY(need(w_in, who, "w_in"));
+    MMDIT_TRY(need(zt, who, "zt"));
+    MMDIT_TRY(need(x_img, who, "x_img"));
+    a[n++] = mk(pk->n_img, d->hidden, d->c_lat, zt, w_in, x_img, MMDIT_EPI_STORE);
+  }
+  if (pk->n_txt > 0) {
+    MMDIT_TRY(need(w_txt, who, "w_txt"));
+    MMDIT_TRY(need(tau, who, "tau"));
+    MMDIT_TRY(need(x_txt, who, "x_txt"));
+    a[n++] = mk(pk->n_txt, d->hidden, d->d_txt, tau, w_txt, x_txt, MMDIT_EPI_STORE);
+  }
+  if (n == 0) return MMDIT_OK;
+  a[0].tag = "embed";
+  // group the two streams only when they can share a kernel configuration
+  if (n == 2 && (d->c_lat % 64 != 0)) {
+    MMDIT_TRY(linear(d->dtype, &a[0], 1, (hipStream_t)stream));
+    return linear(d->dtype, &a[1], 1, (hipStream_t)stream);
+  }
+  return linear(d->dtype, a, n, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_rms_modulate(const mmdit_dims* d, int64_t n_rows, const void* x, const int32_t* row_map,
+                                const int32_t* seg, const float* mod, int64_t mod_stride, int64_t shift_off,
+                                int64_t scale_off, void* y, mmdit_stream stream) {
+  const char* who = "mmdit_rms_modulate";
+  MMDIT_TRY(check_dims(d, who));
+  if (n_rows < 0 || mod_stride < 0 || shift_off < 0 || scale_off < 0 ||
+      (mod_stride > 0 && (shift_off + d->hidden > mod_stride || scale_off + d->hidden > mod_stride)) ||
+      (shift_off | scale_off | mod_stride) % 4) {
+    set_error("%s: bad sizes (n_rows=%lld mod_stride=%lld shift_off=%lld scale_off=%lld)", who,
+              (long long)n_rows, (long long)mod_stride, (long long)shift_off, (long long)scale_off);
+    return MMDIT_E_INVALID;
+  }
+  if (n_rows == 0) return MMDIT_OK;
+  MMDIT_TRY(need(x, who, "x"));
+  MMDIT_TRY(need(seg, who, "seg"));
+  MMDIT_TRY(need(mod, who, "mod"));
+  MMDIT_TRY(need(y, who, "y"));
+  return rms_modulate_impl(d->dtype, n_rows, d->hidden, x, row_map, seg, mod, mod_stride, shift_off, scale_off,
+                           y, d->eps, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_qk_norm_rope(const mmdit_dims* d, int64_t n_rows, void* qkv, const int32_t* pos,
+                                const float* g_q, const float* g_k, mmdit_stream stream) {
+  const char* who = "mmdit_qk_norm_rope";
+  MMDIT_TRY(check_dims(d, who));
+  if (n_rows < 0) {
+    set_error("%s: n_rows < 0", who);
+    return MMDIT_E_INVALID;
+  }
+  if (n_rows == 0) return MMDIT_OK;
+  MMDIT_TRY(need(qkv, who, "qkv"));
+  MMDIT_TRY(need(g_q, who, "g_q"));
+  MMDIT_TRY(need(g_k, who, "g_k"));
+  return qk_norm_rope_impl(d->dtype, n_rows, d->heads, d->head_dim, qkv, pos, g_q, g_k, d->rope_theta, d->eps,
+                           (hipStream_t)stream);
+}
+
+mmdit_status mmdit_attention(const mmdit_dims* d, const mmdit_pack_t* pk, const void* qkv_img,
+                             const void* qkv_txt, void* o_img, void* o_txt, mmdit_stream stream) {
+  const char* who = "mmdit_attention";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  if (pk->n_img > 0) {
+    MMDIT_TRY(need(qkv_img, who, "qkv_img"));
+    MMDIT_TRY(need(o_img, who, "o_img"));
+  }
+  if (pk->n_txt > 0) {
+    MMDIT_TRY(need(qkv_txt, who, "qkv_txt"));
+    MMDIT_TRY(need(o_txt, who, "o_txt"));
+  }
+  return attention_impl(d->dtype, pk, d->heads, d->head_dim, qkv_img, qkv_txt, o_img, o_txt,
+                        (hipStream_t)stream);
+}
+
+mmdit_status mmdit_linear(mmdit_dtype dt, int64_t M, int32_t N, int32_t K, const void* A, const void* W,
+                          void* Y, int32_t epilogue, const float* gate, int64_t gate_stride,
+                          const int32_t* seg, int32_t a_silu, mmdit_stream stream) {
+  const char* who = "mmdit_linear";
+  if (dt != MMDIT_F32 && dt != MMDIT_BF16) {
+    set_error("%s: unknown dtype", who);
+    return MMDIT_E_INVALID;
+  }
+  if (epilogue < MMDIT_EPI_STORE || epilogue > MMDIT_EPI_GATED_RES || M < 0 || N <= 0 || K <= 0) {
+    set_error("%s: bad arguments (M=%lld N=%d K=%d epilogue=%d)", who, (long long)M, N, K, epilogue);
+    return MMDIT_E_INVALID;
+  }
+  if (M == 0) return MMDIT_OK;
+  MMDIT_TRY(need(A, who, "A"));
+  MMDIT_TRY(need(W, who, "W"));
+  MMDIT_TRY(need(Y, who, "Y"));
+  if (epilogue == MMDIT_EPI_GATED_RES) {
+    MMDIT_TRY(need(gate, who, "gate"));
+    MMDIT_TRY(need(seg, who, "seg"));
+    if (gate_stride < N) {
+      set_error("%s: gate_stride %lld < N %d", who, (long long)gate_stride, N);
+      return MMDIT_E_INVALID;
+    }
+  }
+  LinearArgs a = mk(M, N, K, A, W, Y, epilogue);
+  a.gate = gate;
+  a.gate_stride = gate_stride;
+  a.seg = seg;
+  a.a_silu = a_silu ? 1 : 0;
+  return linear(dt, &a, 1, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                             void* x_img, void* x_txt, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_block_fwd";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  if (!w) {
+    set_error("%s: weights are NULL", who);
+    return MMDIT_E_INVALID;
+  }
+  if (pk->B == 0) return MMDIT_OK;
+  MMDIT_TRY(check_stream_w(w->img, who));
+  MMDIT_TRY(check_stream_w(w->txt, who));
+  MMDIT_TRY(need(c, who, "c"));
+  if (pk->n_img > 0) MMDIT_TRY(need(x_img, who, "x_img"));
+  if (pk->n_txt > 0) MMDIT_TRY(need(x_txt, who, "x_txt"));
+  const Layout L = block_layout(d, pk);
+  if (!ws || ws_bytes < L.end) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, L.end, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  MMDIT_TRY(need(ws, who, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  const mmdit_dtype dt = d->dtype;
+  const size_t es = esize(dt);
+  const int32_t H = d->hidden;
+  const int64_t ni = pk->n_img, nt = pk->n_txt;
+  char* base = static_cast<char*>(ws);
+  float* mod_i = reinterpret_cast<float*>(base + L.mod_img);
+  float* mod_t = reinterpret_cast<float*>(base + L.mod_txt);
+  char* h = base + L.h;
+  char* qkv = base + L.qkv;
+  char* o = base + L.o;
+  char* u = base + L.u;
+  char* h_t = h + ni * H * es;
+  char* qkv_t = qkv + ni * 3 * H * es;
+  char* o_t = o + ni * H * es;
+  char* u_t = u + ni * (int64_t)d->mlp * es;
+
+  // adaLN vectors of both streams: mod = W_mod SiLU(c)
+  {
+    LinearArgs a[2] = {mk(pk->B, 6 * H, H, c, w->img.w_mod, mod_i, MMDIT_EPI_STORE_F32),
+                       mk(pk->B, 6 * H, H, c, w->txt.w_mod, mod_t, MMDIT_EPI_STORE_F32)};
+    a[0].a_silu = a[1].a_silu = 1;
+    a[0].tag = "adaln_mod";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // h = rms(x)(1 + scale1) + shift1
+  MMDIT_TRY(rms_modulate_impl(dt, ni, H, x_img, nullptr, pk->seg_img, mod_i, 6 * H, 0, H, h, d->eps, s));
+  MMDIT_TRY(rms_modulate_impl(dt, nt, H, x_txt, nullptr, pk->seg_txt, mod_t, 6 * H, 0, H, h_t, d->eps, s));
+  // qkv = h W_qkv^T
+  {
+    LinearArgs a[2] = {mk(ni, 3 * H, H, h, w->img.w_qkv, qkv, MMDIT_EPI_STORE),
+                       mk(nt, 3 * H, H, h_t, w->txt.w_qkv, qkv_t, MMDIT_EPI_STORE)};
+    a[0].tag = "qkv_proj";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
+  MMDIT_TRY(qk_norm_rope_impl(dt, ni, d->heads, d->head_dim, qkv, pk->pos_img, w->img.g_q, w->img.g_k,
+                              d->rope_theta, d->eps, s));
+  MMDIT_TRY(qk_norm_rope_impl(dt, nt, d->heads, d->head_dim, qkv_t, nullptr, w->txt.g_q, w->txt.g_k,
+                              d->rope_theta, d->eps, s));
+  // o = block-diagonal joint attention
+  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, s));
+  // x += gate1 * (o W_o^T)
+  {
+    LinearArgs a[2] = {mk(ni, H, H, o, w->img.w_o, x_img, MMDIT_EPI_GATED_RES),
+                       mk(nt, H, H, o_t, w->txt.w_o, x_txt, MMDIT_EPI_GATED_RES)};
+    a[0].gate = mod_i + 2 * H;
+    a[1].gate = mod_t + 2 * H;
+    a[0].gate_stride = a[1].gate_stride = 6 * H;
+    a[0].seg = pk->seg_img;
+    a[1].seg = pk->seg_txt;
+    a[0].tag = "out_proj_gated";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // h = rms(x)(1 + scale2) + shift2
+  MMDIT_TRY(rms_modulate_impl(dt, ni, H, x_img, nullptr, pk->seg_img, mod_i, 6 * H, 3 * H, 4 * H, h, d->eps, s));
+  MMDIT_TRY(rms_modulate_impl(dt, nt, H, x_txt, nullptr, pk->seg_txt, mod_t, 6 * H, 3 * H, 4 * H, h_t, d->eps, s));
+  // u = GELU(h W_up^T)
+  {
+    LinearArgs a[2] = {mk(ni, d->mlp, H, h, w->img.w_up, u, MMDIT_EPI_GELU),
+                       mk(nt, d->mlp, H, h_t, w->txt.w_up, u_t, MMDIT_EPI_GELU)};
+    a[0].tag = "mlp_up_gelu";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // x += gate2 * (u W_down^T)
+  {
+    LinearArgs a[2] = {mk(ni, H, d->mlp, u, w->img.w_down, x_img, MMDIT_EPI_GATED_RES),
+                       mk(nt, H, d->mlp, u_t, w->txt.w_down, x_txt, MMDIT_EPI_GATED_RES)};
+    a[0].gate = mod_i + 5 * H;
+    a[1].gate = mod_t + 5 * H;
+    a[0].gate_stride = a[1].gate_stride = 6 * H;
+    a[0].seg = pk->seg_img;
+    a[1].seg = pk->seg_txt;
+    a[0].tag = "mlp_down_gated";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  return MMDIT_OK;
+}
+
+mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,
+                         const void* c, const void* x_img, void* v, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_final";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w_fmod, who, "w_fmod"));
+  MMDIT_TRY(need(w_out, who, "w_out"));
+  MMDIT_TRY(need(c, who, "c"));
+  MMDIT_TRY(need(x_img, who, "x_img"));
+  MMDIT_TRY(need(v, who, "v"));
+  const size_t need_b = final_ws(d, pk);
+  if (!ws || ws_bytes < need_b) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, need_b, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  MMDIT_TRY(need(ws, who, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t H = d->hidden;
+  float* modf = static_cast<float*>(ws);
+  void* hf = static_cast<char*>(ws) + align256((size_t)pk->B * 2 * H * 4);
+  LinearArgs a = mk(pk->B, 2 * H, H, c, w_fmod, modf, MMDIT_EPI_STORE_F32);
+  a.a_silu = 1;
+  a.tag = "final_mod";
+  MMDIT_TRY(linear(d->dtype, &a, 1, s));
+  MMDIT_TRY(rms_modulate_impl(d->dtype, pk->n_tgt, H, x_img, pk->tgt_row, pk->seg_img, modf, 2 * H, 0, H, hf,
+                              d->eps, s));
+  LinearArgs b = mk(pk->n_tgt, d->c_lat, H, hf, w_out, v, MMDIT_EPI_STORE);
+  b.tag = "final_out";
+  return linear(d->dtype, &b, 1, s);
+}
+
+mmdit_status rf_make_xt(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* z, const void* eps,
+                        const float* t, void* zt, mmdit_stream stream) {
+  return make_xt_impl(pk, dt, C, z, eps, t, zt, (hipStream_t)stream);
+}
+
+mmdit_status rf_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                     const void* eps, float* sse, float* loss, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  return loss_impl(pk, dt, C, v, z, eps, sse, loss, ws, ws_bytes, (hipStream_t)stream);
+}
+
+mmdit_status rf_euler_step(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, int32_t cond_b,
+                           int32_t uncond_b, float guidance, float t_cur, float t_next, float* z, void* zt_next,
+                           mmdit_stream stream) {
+  return euler_impl(pk, dt, C, v, cond_b, uncond_b, guidance, t_cur, t_next, z, zt_next, (hipStream_t)stream);
+}
+
+mmdit_status rf_pack_latent(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const float* z, int32_t b0,
+                            int32_t b1, void* zt, mmdit_stream stream) {
+  return pack_latent_impl(pk, dt, C, z, b0, b1, zt, (hipStream_t)stream);
+}
+
+}  // extern "C"

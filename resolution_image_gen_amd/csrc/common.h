@@ -1,0 +1,115 @@
+// Shared device/host helpers of the HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/mmdit.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace mmdit {
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+mmdit_status hip_check(hipError_t e, const char* what);
+// Checks the launch just made (and synchronises the stream when MMDIT_SYNC=1).
+mmdit_status launch_check(const char* kernel, hipStream_t s);
+
+// Every kernel launch goes through MMDIT_LAUNCH followed by launch_check(name, stream):
+// when kernel timing is enabled the pair brackets the launch with hipEvents.
+void timing_begin(hipStream_t s);
+#define MMDIT_LAUNCH(kernel, grid, block, shm, stream, ...)                 \
+  do {                                                                      \
+    ::mmdit::timing_begin(stream);                                          \
+    hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);      \
+  } while (0)
+
+#define MMDIT_TRY(expr)                         \
+  do {                                          \
+    mmdit_status _st = (expr);                  \
+    if (_st != MMDIT_OK) return _st;            \
+  } while (0)
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// 8-element vector load/store in either storage type, widened to float.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  __device__ __forceinline__ static void load(const bf16* p, float* v) {
+    bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+  }
+  __device__ __forceinline__ static void store(bf16* p, const float* v) {
+    bf16x8 x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = x;
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void load(const float* p, float* v) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  __device__ __forceinline__ static void store(float* p, const float* v) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
+  }
+};
+
+// --------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// Exact (erf) GELU.
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------ internal API
+// Dense linear y = op(A) W^T: A [M, K] (row stride lda), W [N, K], fp32 accumulation.
+struct LinearArgs {
+  int64_t M;
+  int32_t N, K;
+  const void* A;
+  int64_t lda;
+  const void* W;
+  void* Y;                 // [M, N] (row stride ldy) output or in/out residual
+  int64_t ldy;
+  int32_t epilogue;        // mmdit_epilogue
+  int32_t a_silu;          // apply SiLU to A elements on load
+  const float* gate;       // gated residual: gate[seg[m] * gate_stride + n]
+  int64_t gate_stride;
+  const int32_t* seg;      // [M] sample of each row (gated residual)
+  const char* tag;         // kernel-timing name of the launch (NULL: generic name)
+};
+mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
+
+}  // namespace mmdit

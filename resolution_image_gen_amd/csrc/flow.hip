@@ -1,0 +1,290 @@
+// Rectified-flow wrapper kernels: noising, loss, CFG combine + Euler step.
+//
+// hyper.ai 2607.19064, 方法 (and blog close-reading 2.2(2), same equation):
+// z_t = (1 - t) z + t eps and the matching loss || v - (z - eps) ||^2.  Editing
+// scores the target latent only.  Sampling integrates the velocity ODE from
+// noise to data (blog close-reading, 5); packed CFG combines the cond and
+// uncond predictions of one packed forward (hyper.ai 2607.19064, 实验).
+// All are HBM-bound streaming kernels over [rows, C] with 16-byte accesses.
+#include "common.h"
+
+namespace mmdit {
+
+namespace {
+
+int grid_for(int64_t work, int threads) {
+  int64_t g = cdiv(work, threads);
+  if (g < 1) g = 1;
+  if (g > 1 << 20) g = 1 << 20;
+  return (int)g;
+}
+
+// One thread per 8 channels of an image row.
+template <typename T>
+__global__ void make_xt_kernel(int64_t n_img, int32_t C, const T* __restrict__ z,
+                               const T* __restrict__ eps, const float* __restrict__ t,
+                               const int32_t* __restrict__ seg, const int32_t* __restrict__ pos,
+                               T* __restrict__ zt) {
+  const int32_t upr = C >> 3;
+  const int64_t n_units = n_img * upr;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = u / upr;
+    const int64_t off = row * C + (u - row * upr) * 8;
+    float zv[8];
+    Vec8<T>::load(z + off, zv);
+    if (pos[3 * row] == 0) {  // frame 0: target rows are noised
+      const float tb = t[seg[row]];
+      float ev[8];
+      Vec8<T>::load(eps + off, ev);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zv[i] = (1.0f - tb) * zv[i] + tb * ev[i];
+    }
+    Vec8<T>::store(zt + off, zv);
+  }
+}
+
+// Per-target-row sum of squared residuals; 16 lanes per row, 8 channels per lane-step.
+template <typename T>
+__global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v,
+                               const T* __restrict__ z, const T* __restrict__ eps,
+                               const int32_t* __restrict__ tgt_row, float* __restrict__ row_sse) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  float acc = 0.f;
+  if (row < n_tgt) {
+    const int64_t src = tgt_row[row];
+    for (int c8 = lane16; c8 < (C >> 3); c8 += 16) {
+      float vv[8], zv[8], ev[8];
+      Vec8<T>::load(v + row * C + c8 * 8, vv);
+      Vec8<T>::load(z + src * C + c8 * 8, zv);
+      Vec8<T>::load(eps + src * C + c8 * 8, ev);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float d = vv[i] - (zv[i] - ev[i]);
+        acc += d * d;
+      }
+    }
+  }
+  acc = group_sum(acc, 16);
+  if (row < n_tgt && lane16 == 0) row_sse[row] = acc;
+}
+
+// One block: per-sample sums in a fixed order, then the mean loss.
+__global__ void __launch_bounds__(256) loss_finalize_kernel(int32_t B, int32_t C,
+                                                            const int32_t* __restrict__ cu_tgt,
+                                                            const float* __restrict__ row_sse,
+                                                            float* __restrict__ sse,
+                                                            float* __restrict__ loss) {
+  __shared__ float red[256];
+  float total = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const int32_t r0 = cu_tgt[b], r1 = cu_tgt[b + 1];
+    float acc = 0.f;
+    for (int32_t r = r0 + threadIdx.x; r < r1; r += 256) acc += row_sse[r];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      sse[b] = red[0];
+      total += red[0] / ((float)(r1 - r0) * (float)C);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = B > 0 ? total / (float)B : 0.f;
+}
+
+// z (float32 [n, C]) += dt * (v_u + g (v_c - v_u)); optionally writes z into two target row ranges.
+template <typename T>
+__global__ void euler_kernel(int64_t n, int32_t C, const T* __restrict__ v_c,
+                             const T* __restrict__ v_u, float g, float dt, float* __restrict__ z,
+                             T* __restrict__ zt_a, T* __restrict__ zt_b) {
+  const int64_t n_units = n * (C >> 3);
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t off = u * 8;
+    float vc[8], zz[8];
+    Vec8<T>::load(v_c + off, vc);
+    Vec8<float>::load(z + off, zz);
+    if (v_u) {
+      float vu[8];
+      Vec8<T>::load(v_u + off, vu);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zz[i] += dt * (vu[i] + g * (vc[i] - vu[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zz[i] += dt * vc[i];
+    }
+    Vec8<float>::store(z + off, zz);
+    if (zt_a) Vec8<T>::store(zt_a + off, zz);
+    if (zt_b) Vec8<T>::store(zt_b + off, zz);
+  }
+}
+
+template <typename T>
+__global__ void pack_latent_kernel(int64_t n, int32_t C, const float* __restrict__ z,
+                                   T* __restrict__ zt_a, T* __restrict__ zt_b) {
+  const int64_t n_units = n * (C >> 3);
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    float zz[8];
+    Vec8<float>::load(z + u * 8, zz);
+    Vec8<T>::store(zt_a + u * 8, zz);
+    if (zt_b) Vec8<T>::store(zt_b + u * 8, zz);
+  }
+}
+
+mmdit_status check_pack(const mmdit_pack_t* pk, const char* who) {
+  if (!pk || pk->B < 0 || pk->B > MMDIT_MAX_SAMPLES || pk->n_img < 0 || pk->n_txt < 0 ||
+      pk->n_tgt < 0 || pk->h_cu_img[pk->B] != pk->n_img || pk->h_cu_txt[pk->B] != pk->n_txt ||
+      pk->h_cu_tgt[pk->B] != pk->n_tgt) {
+    set_error("%s: pack is invalid or was not built by mmdit_pack", who);
+    return MMDIT_E_INVALID;
+  }
+  return MMDIT_OK;
+}
+
+mmdit_status check_c(int32_t C, const char* who) {
+  if (C <= 0 || C % 8) {
+    set_error("%s: C=%d must be a positive multiple of 8", who, C);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  return MMDIT_OK;
+}
+
+}  // namespace
+
+mmdit_status make_xt_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* z,
+                          const void* eps, const float* t, void* zt, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_make_xt"));
+  MMDIT_TRY(check_c(C, "rf_make_xt"));
+  if (pk->n_img == 0) return MMDIT_OK;
+  if (!z || !eps || !t || !zt || !pk->seg_img || !pk->pos_img) {
+    set_error("rf_make_xt: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  int g = grid_for(pk->n_img * (C / 8), 256);
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(make_xt_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_img, C,
+                       (const bf16*)z, (const bf16*)eps, t, pk->seg_img, pk->pos_img, (bf16*)zt);
+  else
+    MMDIT_LAUNCH(make_xt_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_img, C,
+                       (const float*)z, (const float*)eps, t, pk->seg_img, pk->pos_img, (float*)zt);
+  return launch_check("make_xt_kernel", s);
+}
+
+mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v,
+                       const void* z, const void* eps, float* sse, float* loss, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_loss"));
+  MMDIT_TRY(check_c(C, "rf_loss"));
+  if (!sse && pk->B > 0) {
+    set_error("rf_loss: sse is NULL");
+    return MMDIT_E_INVALID;
+  }
+  if (!loss || (pk->n_tgt > 0 && (!v || !z || !eps || !pk->tgt_row))) {
+    set_error("rf_loss: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  if (!ws || ws_bytes < (size_t)pk->n_tgt * 4 + 4) {
+    set_error("rf_loss: workspace needs %zu bytes, got %zu", (size_t)pk->n_tgt * 4 + 4, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  float* row_sse = static_cast<float*>(ws);
+  if (pk->n_tgt > 0) {
+    int g = grid_for(pk->n_tgt * 16, 256);
+    if (dt == MMDIT_BF16)
+      MMDIT_LAUNCH(row_sse_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_tgt, C,
+                         (const bf16*)v, (const bf16*)z, (const bf16*)eps, pk->tgt_row, row_sse);
+    else
+      MMDIT_LAUNCH(row_sse_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_tgt, C,
+                         (const float*)v, (const float*)z, (const float*)eps, pk->tgt_row, row_sse);
+    MMDIT_TRY(launch_check("row_sse_kernel", s));
+  }
+  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(256), 0, s, pk->B, C, pk->cu_tgt, row_sse,
+                     sse, loss);
+  return launch_check("loss_finalize_kernel", s);
+}
+
+static mmdit_status check_target_sample(const mmdit_pack_t* pk, int32_t b, const char* who) {
+  if (b < 0 || b >= pk->B) {
+    set_error("%s: sample index %d out of range [0, %d)", who, b, pk->B);
+    return MMDIT_E_INVALID;
+  }
+  return MMDIT_OK;
+}
+
+mmdit_status euler_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v,
+                        int32_t cb, int32_t ub, float g, float t_cur, float t_next, float* z,
+                        void* zt_next, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_euler_step"));
+  MMDIT_TRY(check_c(C, "rf_euler_step"));
+  MMDIT_TRY(check_target_sample(pk, cb, "rf_euler_step"));
+  const int64_t n = pk->h_cu_tgt[cb + 1] - pk->h_cu_tgt[cb];
+  if (ub >= 0) {
+    MMDIT_TRY(check_target_sample(pk, ub, "rf_euler_step"));
+    if (pk->h_cu_tgt[ub + 1] - pk->h_cu_tgt[ub] != n) {
+      set_error("rf_euler_step: cond and uncond samples have different target sizes");
+      return MMDIT_E_INVALID;
+    }
+  }
+  if (!v || !z) {
+    set_error("rf_euler_step: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  const size_t es = dt == MMDIT_BF16 ? 2 : 4;
+  const char* vb = static_cast<const char*>(v);
+  const void* vc = vb + (size_t)pk->h_cu_tgt[cb] * C * es;
+  const void* vu = ub >= 0 ? vb + (size_t)pk->h_cu_tgt[ub] * C * es : nullptr;
+  // target rows of sample b are the first h*w image rows of the sample
+  char* ztb = static_cast<char*>(zt_next);
+  void* za = zt_next ? ztb + (size_t)pk->h_cu_img[cb] * C * es : nullptr;
+  void* zb = (zt_next && ub >= 0) ? ztb + (size_t)pk->h_cu_img[ub] * C * es : nullptr;
+  const float dtv = t_cur - t_next;
+  if (n == 0) return MMDIT_OK;
+  int gr = grid_for(n * (C / 8), 256);
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(euler_kernel<bf16>, dim3(gr), dim3(256), 0, s, n, C, (const bf16*)vc,
+                       (const bf16*)vu, g, dtv, z, (bf16*)za, (bf16*)zb);
+  else
+    MMDIT_LAUNCH(euler_kernel<float>, dim3(gr), dim3(256), 0, s, n, C, (const float*)vc,
+                       (const float*)vu, g, dtv, z, (float*)za, (float*)zb);
+  return launch_check("euler_kernel", s);
+}
+
+mmdit_status pack_latent_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const float* z,
+                              int32_t b0, int32_t b1, void* zt, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_pack_latent"));
+  MMDIT_TRY(check_c(C, "rf_pack_latent"));
+  MMDIT_TRY(check_target_sample(pk, b0, "rf_pack_latent"));
+  const int64_t n = pk->h_cu_tgt[b0 + 1] - pk->h_cu_tgt[b0];
+  if (b1 >= 0) {
+    MMDIT_TRY(check_target_sample(pk, b1, "rf_pack_latent"));
+    if (pk->h_cu_tgt[b1 + 1] - pk->h_cu_tgt[b1] != n) {
+      set_error("rf_pack_latent: samples have different target sizes");
+      return MMDIT_E_INVALID;
+    }
+  }
+  if (!z || !zt) {
+    set_error("rf_pack_latent: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  const size_t es = dt == MMDIT_BF16 ? 2 : 4;
+  char* ztb = static_cast<char*>(zt);
+  void* za = ztb + (size_t)pk->h_cu_img[b0] * C * es;
+  void* zb = b1 >= 0 ? ztb + (size_t)pk->h_cu_img[b1] * C * es : nullptr;
+  if (n == 0) return MMDIT_OK;
+  int gr = grid_for(n * (C / 8), 256);
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(pack_latent_kernel<bf16>, dim3(gr), dim3(256), 0, s, n, C, z, (bf16*)za,
+                       (bf16*)zb);
+  else
+    MMDIT_LAUNCH(pack_latent_kernel<float>, dim3(gr), dim3(256), 0, s, n, C, z, (float*)za,
+                       (float*)zb);
+  return launch_check("pack_latent_kernel", s);
+}
+
+}  // namespace mmdit

@@ -1,0 +1,425 @@
+// Dense linears of the block: Y = op(A) W^T with fused epilogues (store,
+// float32 store, exact GELU, gated residual x += gate[seg] * y).
+//
+// The gating and residual chain is fused into the producing GEMM (blog
+// close-reading 2.2(3): norm, RoPE, gating and residual chains are fused so
+// intermediates stay on chip).  Three kernels:
+//   gemm_mfma_kernel   bf16, MFMA 32x32x16, LDS double buffer, grouped over
+//                      up to two problems (image and text streams) per launch
+//   gemm_skinny_kernel bf16, M <= 16 (adaLN modulation, conditioning MLP):
+//                      weight-streaming MFMA 16x16x32 with split-K over waves
+//   gemm_simt_kernel   float32 (and any shape the MFMA kernels reject)
+#include "common.h"
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+namespace mmdit {
+
+namespace {
+
+struct GemmProb {
+  const void* A;
+  const void* W;
+  void* Y;
+  const float* gate;
+  const int32_t* seg;
+  int64_t lda, ldy, gate_stride, M;
+  int32_t N, K;
+  int32_t tiles_n;
+  int32_t tile_begin;
+};
+
+struct GemmBatch {
+  GemmProb p[2];
+  int32_t nprob;
+  const char* tag;
+};
+
+__device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
+  if (bt.nprob > 1 && tile >= bt.p[1].tile_begin) {
+    tile -= bt.p[1].tile_begin;
+    return bt.p[1];
+  }
+  return bt.p[0];
+}
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_store(const GemmProb& P, int64_t m, int n, float acc) {
+  if constexpr (EPI == MMDIT_EPI_STORE_F32) {
+    static_cast<float*>(P.Y)[m * P.ldy + n] = acc;
+  } else if constexpr (EPI == MMDIT_EPI_STORE) {
+    static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(acc);
+  } else if constexpr (EPI == MMDIT_EPI_GELU) {
+    static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(gelu_f(acc));
+  } else {
+    T* y = static_cast<T*>(P.Y) + m * P.ldy + n;
+    const float g = P.gate[(int64_t)P.seg[m] * P.gate_stride + n];
+    *y = from_f<T>(to_f(*y) + g * acc);
+  }
+}
+
+// ------------------------------------------------------------------ SIMT
+template <typename T, int EPI, bool SILU>
+__global__ void __launch_bounds__(256) gemm_simt_kernel(GemmBatch bt) {
+  int tile = blockIdx.x;
+  const GemmProb& P = pick(bt, tile);
+  const int64_t m0 = (int64_t)(tile / P.tiles_n) * 64;
+  const int n0 = (tile % P.tiles_n) * 64;
+  __shared__ float As[16][68], Ws[16][68];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const T* A = static_cast<const T*>(P.A);
+  const T* W = static_cast<const T*>(P.W);
+  float acc[4][4] = {};
+  const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;
+  for (int k0 = 0; k0 < P.K; k0 += 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + lk + e;
+      const int64_t m = m0 + lr;
+      float a = (m < P.M && k < P.K) ? to_f(A[m * P.lda + k]) : 0.f;
+      if (SILU) a = silu_f(a);
+      As[lk + e][lr] = a;
+      const int n = n0 + lr;
+      Ws[lk + e][lr] = (n < P.N && k < P.K) ? to_f(W[(int64_t)n * P.K + k]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty * 4 + i];
+        w[i] = Ws[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty * 4 + i;
+    if (m >= P.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < P.N) epi_store<T, EPI>(P, m, n, acc[i][j]);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 silu8(bf16x8 x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)silu_f((float)x[i]);
+  return r;
+}
+
+// ---------------------------------------------------------------- skinny
+// One block per 16 output columns; 4 waves split K into 4 contiguous ranges;
+// fixed-order reduction of the 4 partial tiles through LDS.
+template <int EPI, bool SILU>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmBatch bt) {
+  int tile = blockIdx.x;
+  const GemmProb& P = pick(bt, tile);
+  const int n0 = tile * 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kq = P.K >> 2;
+  const int kbeg = wave * kq;
+  const int r16 = lane & 15, kofs = (lane >> 4) * 8;
+  const bf16* A = static_cast<const bf16*>(P.A) + (int64_t)r16 * P.lda + kofs;
+  const bf16* W = static_cast<const bf16*>(P.W) + (int64_t)(n0 + r16) * P.K + kofs;
+  const bool arow = r16 < P.M;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nit = kq >> 5;
+  for (int it = 0; it < nit; ++it) {
+    const int k = kbeg + it * 32;
+    bf16x8 b = *reinterpret_cast<const bf16x8*>(W + k);
+    bf16x8 a = {};
+    if (arow) {
+      a = *reinterpret_cast<const bf16x8*>(A + k);
+      if (SILU) a = silu8(a);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  __shared__ f32x4 red[4][64];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += red[w][lane];
+    // D[i][j]: j = lane % 16 (output column), i = 4 * (lane / 16) + v (row)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * (lane >> 4) + v;
+      if (m < P.M) epi_store<bf16, EPI>(P, m, n0 + r16, s[v]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MFMA
+// Tile BM x BN x 64, WM x WN waves, each wave (BM/WM) x (BN/WN) built from
+// 32x32 MFMA tiles.  LDS rows are 64 bf16 = 8 chunks of 16 B, chunk c of
+// row r stored at c ^ swz(r) to keep the 16-B fragment reads conflict-free.
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
+  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile / thread mismatch");
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  bf16* As = smem;                    // [2][BM*BK]
+  bf16* Bs = smem + 2 * BM * BK;      // [2][BN*BK]
+
+  int tile = blockIdx.x;
+  const GemmProb& P = pick(bt, tile);
+  const int64_t m0 = (int64_t)(tile / P.tiles_n) * BM;
+  const int n0 = (tile % P.tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const bf16* A = static_cast<const bf16*>(P.A);
+  const bf16* W = static_cast<const bf16*>(P.W);
+
+  u32x4 ra[ACH], rb[BCH];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
+      const int64_t m = m0 + row;
+      if (m < P.M)
+        ra[c] = *reinterpret_cast<const u32x4*>(A + m * P.lda + k0 + kc * 8);
+      else
+        ra[c] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
+      rb[c] = *reinterpret_cast<const u32x4*>(W + (int64_t)(n0 + row) * P.K + k0 + kc * 8);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
+      u32x4 v = ra[c];
+      if (SILU) {
+        bf16x8 x = silu8(*reinterpret_cast<bf16x8*>(&v));
+        v = *reinterpret_cast<u32x4*>(&x);
+      }
+      *reinterpret_cast<u32x4*>(As + buf * BM * BK + row * BK + ((kc ^ swz8(row)) << 3)) = v;
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
+      *reinterpret_cast<u32x4*>(Bs + buf * BN * BK + row * BK + ((kc ^ swz8(row)) << 3)) = rb[c];
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = P.K / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  const int l32 = lane & 31, g = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) load((kt + 1) * BK);
+    const bf16* as = As + buf * BM * BK;
+    const bf16* bs = Bs + buf * BN * BK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[TM], bfr[TN];
+      const int ch = kk * 2 + g;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + l32;
+        af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + ((ch ^ swz8(r)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + l32;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * BK + ((ch ^ swz8(r)) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) store(buf ^ 1);
+    __syncthreads();
+  }
+  // D[i][j] of a 32x32 tile: j = lane % 32, i = 8 * (v / 4) + 4 * (lane / 32) + v % 4
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (m >= P.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) epi_store<bf16, EPI>(P, m, n0 + wn * TN * 32 + j * 32 + l32, acc[i][j][v]);
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU>
+mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    bt.p[i].tiles_n = bt.p[i].N / BN;
+    bt.p[i].tile_begin = tiles;
+    tiles += (int)(cdiv(bt.p[i].M, BM) * bt.p[i].tiles_n);
+  }
+  if (tiles == 0) return MMDIT_OK;
+  const size_t lds = 2 * (BM + BN) * 64 * sizeof(bf16);
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                        "hipFuncSetAttribute(gemm_mfma_kernel)"));
+    attr_set = true;
+  }
+  MMDIT_LAUNCH(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, bt);
+  static char name[64];
+  if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s>", BM, BN, WM, WN, EPI, SILU ? ",silu" : "");
+  return launch_check(bt.tag ? bt.tag : name, s);
+}
+
+template <int EPI, bool SILU>
+mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
+  bool n128 = true;
+  int64_t big_tiles = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    n128 = n128 && (bt.p[i].N % 128 == 0);
+    big_tiles += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 128);
+  }
+  if (!n128) return launch_mfma_cfg<128, 64, 2, 2, EPI, SILU>(bt, s);
+  if (big_tiles >= 512) return launch_mfma_cfg<256, 128, 2, 2, EPI, SILU>(bt, s);
+  return launch_mfma_cfg<128, 128, 2, 2, EPI, SILU>(bt, s);
+}
+
+template <int EPI, bool SILU>
+mmdit_status launch_skinny(GemmBatch& bt, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    bt.p[i].tiles_n = bt.p[i].N / 16;
+    bt.p[i].tile_begin = tiles;
+    tiles += bt.p[i].tiles_n;
+  }
+  if (tiles == 0) return MMDIT_OK;
+  MMDIT_LAUNCH((gemm_skinny_kernel<EPI, SILU>), dim3(tiles), dim3(256), 0, s, bt);
+  static char name[64];
+  if (!name[0]) snprintf(name, sizeof(name), "gemm_skinny_kernel<epi%d%s>", EPI, SILU ? ",silu" : "");
+  return launch_check(bt.tag ? bt.tag : name, s);
+}
+
+template <typename T, int EPI, bool SILU>
+mmdit_status launch_simt(GemmBatch& bt, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    bt.p[i].tiles_n = (int)cdiv(bt.p[i].N, 64);
+    bt.p[i].tile_begin = tiles;
+    tiles += (int)(cdiv(bt.p[i].M, 64) * bt.p[i].tiles_n);
+  }
+  if (tiles == 0) return MMDIT_OK;
+  MMDIT_LAUNCH((gemm_simt_kernel<T, EPI, SILU>), dim3(tiles), dim3(256), 0, s, bt);
+  return launch_check(bt.tag ? bt.tag : "gemm_simt_kernel", s);
+}
+
+enum class Path { SIMT, SKINNY, MFMA };
+
+template <int EPI, bool SILU>
+mmdit_status dispatch(mmdit_dtype dt, Path path, GemmBatch& bt, hipStream_t s) {
+  if (dt == MMDIT_F32) return launch_simt<float, EPI, SILU>(bt, s);
+  switch (path) {
+    case Path::SKINNY: return launch_skinny<EPI, SILU>(bt, s);
+    case Path::MFMA: return launch_mfma<EPI, SILU>(bt, s);
+    default: return launch_simt<bf16, EPI, SILU>(bt, s);
+  }
+}
+
+bool force_simt() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_GEMM");
+    v = (e && strcmp(e, "simt") == 0) ? 1 : 0;
+  }
+  return v == 1;
+}
+
+}  // namespace
+
+mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t s) {
+  if (nprob < 1 || nprob > 2) {
+    set_error("linear: nprob=%d", nprob);
+    return MMDIT_E_INVALID;
+  }
+  GemmBatch bt;
+  memset(&bt, 0, sizeof(bt));
+  int n = 0;
+  const int epi = pa[0].epilogue, silu = pa[0].a_silu;
+  bool skinny = true, mfma = true;
+  for (int i = 0; i < nprob; ++i) {
+    const LinearArgs& a = pa[i];
+    if (a.epilogue != epi || a.a_silu != silu) {
+      set_error("linear: grouped problems must share the epilogue");
+      return MMDIT_E_INVALID;
+    }
+    if (a.M < 0 || a.N <= 0 || a.K <= 0 || a.lda < a.K || a.ldy < a.N) {
+      set_error("linear: bad shape M=%lld N=%d K=%d lda=%lld ldy=%lld", (long long)a.M, a.N, a.K,
+                (long long)a.lda, (long long)a.ldy);
+      return MMDIT_E_INVALID;
+    }
+    if (a.M == 0) continue;
+    if (!a.A || !a.W || !a.Y || (epi == MMDIT_EPI_GATED_RES && (!a.gate || !a.seg))) {
+      set_error("linear: NULL pointer");
+      return MMDIT_E_INVALID;
+    }
+    GemmProb& p = bt.p[n++];
+    p.A = a.A;
+    p.W = a.W;
+    p.Y = a.Y;
+    p.gate = a.gate;
+    p.seg = a.seg;
+    p.lda = a.lda;
+    p.ldy = a.ldy;
+    p.gate_stride = a.gate_stride;
+    p.M = a.M;
+    p.N = a.N;
+    p.K = a.K;
+    skinny = skinny && a.M <= 16 && a.K % 128 == 0 && a.N % 16 == 0 && a.lda % 8 == 0;
+    mfma = mfma && a.K % 64 == 0 && a.N % 64 == 0 && a.lda % 8 == 0;
+  }
+  bt.nprob = n;
+  bt.tag = pa[0].tag;
+  if (n == 0) return MMDIT_OK;
+  Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
+  switch (epi * 2 + (silu ? 1 : 0)) {
+    case MMDIT_EPI_STORE * 2: return dispatch<MMDIT_EPI_STORE, false>(dt, path, bt, s);
+    case MMDIT_EPI_STORE * 2 + 1: return dispatch<MMDIT_EPI_STORE, true>(dt, path, bt, s);
+    case MMDIT_EPI_STORE_F32 * 2: return dispatch<MMDIT_EPI_STORE_F32, false>(dt, path, bt, s);
+    case MMDIT_EPI_STORE_F32 * 2 + 1: return dispatch<MMDIT_EPI_STORE_F32, true>(dt, path, bt, s);
+    case MMDIT_EPI_GELU * 2: return dispatch<MMDIT_EPI_GELU, false>(dt, path, bt, s);
+    case MMDIT_EPI_GATED_RES * 2: return dispatch<MMDIT_EPI_GATED_RES, false>(dt, path, bt, s);
+    default:
+      set_error("linear: unsupported epilogue %d (a_silu=%d)", epi, silu);
+      return MMDIT_E_UNSUPPORTED;
+  }
+}
+
+}  // namespace mmdit

@@ -1,0 +1,202 @@
+"""Whole-path drivers over the C ABI: the training forward with the RF loss
+and the packed-CFG Euler sampler.  Marshalling and buffer ownership only:
+every arithmetic step is a libmmdit kernel launch on the given stream.
+"""
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synthetic as S
+
+
+def _dev(a, dtype, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+
+class Weights:
+    """Device weights of a workload: wrapper matrices + `depth` blocks."""
+
+    def __init__(self, wl, device="cuda", recipe="default", depth=None, source="numpy", seed_blocks=None):
+        self.wl = wl
+        self.dims = B.Dims(wl.dims, wl.dtype)
+        dt = self.dims.torch_dtype
+        depth = wl.depth if depth is None else depth
+        self.np_wrap = S.wrapper_weights(wl.dims, wl.dtype, wl.name, recipe) if source == "numpy" else None
+        if source == "numpy":
+            self.wrap = {k: _dev(v, dt, device) for k, v in self.np_wrap.items()}
+        else:
+            self.wrap = _torch_wrap(wl, dt, device)
+        self.np_blocks = []
+        self.blocks = []
+        for i in range(depth):
+            blk = seed_blocks[i] if seed_blocks is not None else i
+            if source == "numpy":
+                nb = S.block_weights(wl.dims, wl.dtype, wl.name, blk, recipe)
+                self.np_blocks.append(nb)
+                tb = {s: {k: _dev(v, torch.float32 if k in ("g_q", "g_k") else dt, device)
+                          for k, v in nb[s].items()} for s in nb}
+            else:
+                tb = _torch_block(wl, dt, device, blk)
+            self.blocks.append(tb)
+        self.bw = [B.block_weights(tb) for tb in self.blocks]
+
+
+def _torch_gen(device, *key):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([0] + S._key(*key)).generate_state(1)[0]))
+    return g
+
+
+def _torch_normal(shape, std, dt, device, *key):
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, std, generator=_torch_gen(device, *key))
+    return t.to(dt)
+
+
+def _torch_wrap(wl, dt, device):
+    d = wl.dims
+    H = d.hidden
+    k = (wl.name, "torch", "wrap")
+    return {"w_t1": _torch_normal((H, d.t_dim), 0.02, dt, device, *k, "w_t1"),
+            "w_t2": _torch_normal((H, H), 0.02, dt, device, *k, "w_t2"),
+            "w_in": _torch_normal((H, d.c_lat), 0.02, dt, device, *k, "w_in"),
+            "w_txt": _torch_normal((H, d.d_txt), 0.02, dt, device, *k, "w_txt"),
+            "w_fmod": _torch_normal((2 * H, H), 0.02, dt, device, *k, "w_fmod"),
+            "w_out": _torch_normal((d.c_lat, H), 0.02, dt, device, *k, "w_out")}
+
+
+def _torch_block(wl, dt, device, blk):
+    """Device-side seeded weights for deep stacks (same distributions as the
+    numpy recipe, drawn by torch's generator on the GPU for speed)."""
+    d = wl.dims
+    H, M = d.hidden, d.mlp
+    out = {}
+    for s in ("img", "txt"):
+        k = (wl.name, "torch", "block", blk, s)
+        out[s] = {"w_mod": _torch_normal((6 * H, H), 0.02, dt, device, *k, "w_mod"),
+                  "w_qkv": _torch_normal((3 * H, H), 0.02, dt, device, *k, "w_qkv"),
+                  "g_q": torch.ones(d.head_dim, dtype=torch.float32, device=device),
+                  "g_k": torch.ones(d.head_dim, dtype=torch.float32, device=device),
+                  "w_o": _torch_normal((H, H), 0.02, dt, device, *k, "w_o"),
+                  "w_up": _torch_normal((M, H), 0.02, dt, device, *k, "w_up"),
+                  "w_down": _torch_normal((H, M), 0.02, dt, device, *k, "w_down")}
+    return out
+
+
+def training_inputs(wl, samples=None):
+    """Packed synthetic inputs (numpy): z, eps [n_img, C]; tau [n_txt, d_txt]; t [B]."""
+    samples = wl.samples if samples is None else samples
+    d = wl.dims
+    n_img = sum(f * h * w for h, w, f, _ in samples)
+    n_txt = sum(t for *_, t in samples)
+    return {"z": S.latents(n_img, d.c_lat, wl.dtype, wl.name, "z"),
+            "eps": S.latents(n_img, d.c_lat, wl.dtype, wl.name, "eps"),
+            "tau": S.text(n_txt, d.d_txt, wl.dtype, wl.name, "tau"),
+            "t": S.timesteps(len(samples), wl.name)}
+
+
+class TrainForward:
+    """One training forward over a pack: gather per-sample tensors, noise,
+    condition, embed, run the blocks, final layer and RF loss."""
+
+    def __init__(self, wl, W, inputs, device="cuda", samples=None, img_budget=None):
+        self.wl, self.W = wl, W
+        self.samples = list(wl.samples if samples is None else samples)
+        budget = wl.img_budget if img_budget is None else img_budget
+        n_taken = B.pack_plan(self.samples, budget)[0]
+        if n_taken != len(self.samples):
+            raise ValueError(f"workload does not fit one pack ({n_taken} of {len(self.samples)})")
+        d = wl.dims
+        self.dims = W.dims
+        dt = self.dims.torch_dtype
+        self.device = device
+        self.pk = B.pack(self.samples, device)
+        pk = self.pk
+        cu_img, cu_txt = pk.host("h_cu_img"), pk.host("h_cu_txt")
+        z = _dev(inputs["z"], dt, device)
+        eps = _dev(inputs["eps"], dt, device)
+        tau = _dev(inputs["tau"], dt, device)
+        # per-sample tensors: the path starts from separate samples and packs them
+        self.z_s = [z[cu_img[b]:cu_img[b + 1]].clone() for b in range(pk.B)]
+        self.eps_s = [eps[cu_img[b]:cu_img[b + 1]].clone() for b in range(pk.B)]
+        self.tau_s = [tau[cu_txt[b]:cu_txt[b + 1]].clone() for b in range(pk.B)]
+        self.t = torch.from_numpy(inputs["t"]).to(device)
+        e = dict(dtype=dt, device=device)
+        ni, nt, ng = max(pk.n_img, 1), max(pk.n_txt, 1), max(pk.n_tgt, 1)
+        self.z = torch.empty(ni, d.c_lat, **e)
+        self.eps = torch.empty(ni, d.c_lat, **e)
+        self.tau = torch.empty(nt, d.d_txt, **e)
+        self.zt = torch.empty(ni, d.c_lat, **e)
+        self.c = torch.empty(pk.B, d.hidden, **e)
+        self.x_img = torch.empty(ni, d.hidden, **e)
+        self.x_txt = torch.empty(nt, d.hidden, **e)
+        self.v = torch.empty(ng, d.c_lat, **e)
+        self.sse = torch.empty(max(pk.B, 1), dtype=torch.float32, device=device)
+        self.loss = torch.empty(1, dtype=torch.float32, device=device)
+        self.ws = torch.empty(B.workspace_size(self.dims, pk), dtype=torch.uint8, device=device)
+
+    def run(self, stream=None, repack=True):
+        W, pk, dm = self.W, self.pk, self.dims
+        if repack:
+            pk = self._repack(stream)
+        B.pack_gather(pk, 0, self.z_s, self.z, stream)
+        B.pack_gather(pk, 0, self.eps_s, self.eps, stream)
+        B.pack_gather(pk, 1, self.tau_s, self.tau, stream)
+        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, stream)
+        B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.c, self.ws, stream)
+        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
+        for bw in W.bw:
+            B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
+        B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
+        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, stream)
+
+    def _repack(self, stream):
+        # rebuild the ids of the pack in place (same buffers, same samples)
+        pk = self.pk
+        B._ck(B._lib.mmdit_pack(B._samples(self.samples), len(self.samples), pk.ref, B._stream(stream)))
+        return pk
+
+
+class Sampler:
+    """Packed-CFG Euler sampler: one pack [cond, uncond] of the same grid,
+    `steps` forwards through the block stack, CFG combine + Euler per step."""
+
+    def __init__(self, wl, W, eps, tau_c, tau_u, device="cuda", guidance=None, schedule=None):
+        self.wl, self.W = wl, W
+        d = wl.dims
+        self.dims = W.dims
+        dt = self.dims.torch_dtype
+        h, w = wl.samples[0][0], wl.samples[0][1]
+        self.samples = [(h, w, 1, len(tau_c)), (h, w, 1, len(tau_u))]
+        self.pk = B.pack(self.samples, device)
+        self.g = float(wl.guidance if guidance is None else guidance)
+        self.schedule = list(wl.schedule if schedule is None else schedule)
+        e = dict(dtype=dt, device=device)
+        self.eps = torch.from_numpy(np.ascontiguousarray(eps, np.float32)).to(device)
+        self.z = torch.empty_like(self.eps)
+        self.tau = torch.cat([_dev(tau_c, dt, device), _dev(tau_u, dt, device)])
+        n = self.pk.n_img
+        self.zt = torch.empty(n, d.c_lat, **e)
+        self.c = torch.empty(2, d.hidden, **e)
+        self.x_img = torch.empty(n, d.hidden, **e)
+        self.x_txt = torch.empty(self.pk.n_txt, d.hidden, **e)
+        self.v = torch.empty(self.pk.n_tgt, d.c_lat, **e)
+        self.tsched = torch.tensor([[t, t] for t in self.schedule[:-1]], dtype=torch.float32, device=device)
+        self.ws = torch.empty(B.workspace_size(self.dims, self.pk), dtype=torch.uint8, device=device)
+
+    def run(self, stream=None, on_step=None):
+        W, pk, dm = self.W, self.pk, self.dims
+        self.z.copy_(self.eps)               # z_1 = eps
+        B.rf_pack_latent(pk, self.z, 0, 1, self.zt, stream)
+        for i in range(len(self.schedule) - 1):
+            B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i], self.c, self.ws, stream)
+            B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
+            for bw in W.bw:
+                B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
+            B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
+            if on_step is not None:
+                on_step(i, self)
+            B.rf_euler_step(pk, self.v, 0, 1, self.g, self.schedule[i], self.schedule[i + 1], self.z,
+                            self.zt, stream)
+        return self.z

@@ -1,0 +1,168 @@
+"""Host-only checks of the C ABI (no GPU): exports, struct layout, the host
+planner against the oracle, and argument validation that fails before any
+launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from oracle import pack as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmdit.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from resolution_image_gen_amd import binding
+
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:mmdit|rf)_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = declared_functions()
+    assert len(names) >= 20, names
+    for n in names:
+        assert hasattr(B._lib, n), f"{n} declared in mmdit.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T ((?:mmdit|rf)_\w+)", out))
+    assert set(names) <= exported
+    assert B._lib.mmdit_version().decode().startswith("mmdit")
+
+
+LAYOUT_PROBE = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "mmdit.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("mmdit_pack_t %zu\nmmdit_dims %zu\nmmdit_sample %zu\nmmdit_block_w %zu\n", sizeof(mmdit_pack_t),
+         sizeof(mmdit_dims), sizeof(mmdit_sample), sizeof(mmdit_block_w));
+  F(mmdit_pack_t, n_img) F(mmdit_pack_t, cu_txt) F(mmdit_pack_t, tgt_row) F(mmdit_pack_t, h_cu_txt)
+  F(mmdit_pack_t, h_cu_img) F(mmdit_pack_t, h_cu_tgt) F(mmdit_pack_t, h_frames)
+  F(mmdit_dims, rope_theta) F(mmdit_dims, dtype) F(mmdit_block_w, txt)
+  return 0;
+}
+"""
+
+
+def test_struct_layout_matches_binding(B):
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "probe.c"), os.path.join(d, "probe")
+        open(src, "w").write(LAYOUT_PROBE)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    c = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+    c = {k: int(v) for k, v in c.items()}
+    assert c["mmdit_pack_t"] == ctypes.sizeof(B._PackT)
+    assert c["mmdit_dims"] == ctypes.sizeof(B._DimsT)
+    assert c["mmdit_sample"] == ctypes.sizeof(B._Sample)
+    assert c["mmdit_block_w"] == ctypes.sizeof(B._BlockW)
+    for f in ("n_img", "cu_txt", "tgt_row", "h_cu_txt", "h_cu_img", "h_cu_tgt", "h_frames"):
+        assert c[f"mmdit_pack_t.{f}"] == getattr(B._PackT, f).offset, f
+    assert c["mmdit_dims.rope_theta"] == B._DimsT.rope_theta.offset
+    assert c["mmdit_dims.dtype"] == B._DimsT.dtype.offset
+    assert c["mmdit_block_w.txt"] == B._BlockW.txt.offset
+
+
+def test_host_plan_matches_oracle_random(B):
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        n = int(rng.integers(0, 12))
+        s = [(int(rng.integers(1, 40)), int(rng.integers(1, 40)), int(rng.integers(1, 3)), int(rng.integers(0, 300)))
+             for _ in range(n)]
+        budget = int(rng.integers(1, 6000))
+        joint = int(rng.choice([0, int(rng.integers(1, 8000))]))
+        try:
+            want = OP.plan(s, budget, joint)
+        except OP.BudgetError:
+            with pytest.raises(B.MmditError) as e:
+                B.pack_plan(s, budget, joint)
+            assert e.value.status == -2
+            continue
+        assert B.pack_plan(s, budget, joint) == want, (s, budget, joint)
+
+
+def test_plan_caps_at_max_samples(B):
+    assert B.pack_plan([(1, 1, 1, 0)] * 300, 10 ** 6)[0] == B.MAX_SAMPLES
+
+
+def _fake_pack(B, samples):
+    """A host-consistent pack struct with placeholder device pointers, for
+    validation paths that return before any launch."""
+    pk = B._PackT()
+    ref = OP.pack(samples)
+    pk.B = len(samples)
+    pk.max_joint = ref["max_joint"]
+    pk.n_img, pk.n_txt, pk.n_tgt = int(ref["cu_img"][-1]), int(ref["cu_txt"][-1]), int(ref["cu_tgt"][-1])
+    for i in range(pk.B + 1):
+        pk.h_cu_img[i], pk.h_cu_txt[i], pk.h_cu_tgt[i] = (int(ref["cu_img"][i]), int(ref["cu_txt"][i]),
+                                                         int(ref["cu_tgt"][i]))
+    fake = 1 << 20
+    for f in ("cu_txt", "cu_img", "cu_joint", "cu_tgt", "tgt_len", "seg_img", "seg_txt", "pos_img", "tgt_row"):
+        setattr(pk, f, fake)
+    return pk
+
+
+def _dims(B, **kw):
+    from resolution_image_gen_amd import configs as CF
+
+    d = dict(CF.B4.__dict__)
+    d.update(kw)
+    return B._DimsT(d["hidden"], d["heads"], d["head_dim"], d["mlp"], d["c_lat"], d["d_txt"], d["t_dim"],
+                    d["rope_theta"], d["eps"], 1)
+
+
+def test_validation_errors_before_launch(B):
+    lib = B._lib
+    pk = _fake_pack(B, [(16, 16, 1, 128), (8, 8, 2, 3)])
+    P = ctypes.byref(pk)
+    ok = ctypes.byref(_dims(B))
+    fake = ctypes.c_void_p(1 << 20)
+    w = B._BlockW(B._StreamW(*([1 << 20] * 7)), B._StreamW(*([1 << 20] * 7)))
+    # head_dim outside {64, 128}
+    assert lib.mmdit_block_fwd(ctypes.byref(_dims(B, heads=32, head_dim=96)), ctypes.byref(w), P, fake, fake,
+                               fake, fake, 1 << 40, None) == -3
+    # hidden != heads * head_dim
+    assert lib.mmdit_block_fwd(ctypes.byref(_dims(B, heads=20)), ctypes.byref(w), P, fake, fake, fake, fake,
+                               1 << 40, None) == -1
+    # workspace too small
+    need = lib.mmdit_workspace_size(ok, P)
+    assert need > 0
+    assert lib.mmdit_block_fwd(ok, ctypes.byref(w), P, fake, fake, fake, fake, need - 1, None) == -4
+    assert b"workspace" in lib.mmdit_last_error()
+    # NULL weight
+    w2 = B._BlockW(B._StreamW(*([1 << 20] * 7)), B._StreamW(*([1 << 20] * 6 + [0])))
+    assert lib.mmdit_block_fwd(ok, ctypes.byref(w2), P, fake, fake, fake, fake, need, None) == -1
+    # misaligned pointer
+    assert lib.mmdit_block_fwd(ok, ctypes.byref(w), P, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, need,
+                               None) == -3
+    # pack whose host mirror is inconsistent
+    bad = _fake_pack(B, [(4, 4, 1, 1)])
+    bad.n_img = 99
+    assert lib.mmdit_block_fwd(ok, ctypes.byref(w), ctypes.byref(bad), fake, fake, fake, fake, need, None) == -1
+    # rf wrapper
+    assert lib.rf_euler_step(P, 1, 128, fake, 0, 5, ctypes.c_float(4.0), ctypes.c_float(1.0),
+                             ctypes.c_float(0.75), fake, None, None) == -1
+    assert lib.rf_euler_step(P, 1, 128, fake, 0, 1, ctypes.c_float(4.0), ctypes.c_float(1.0),
+                             ctypes.c_float(0.75), fake, None, None) == -1    # different target sizes
+    assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, fake, 16, None) == -4
+    assert lib.rf_make_xt(P, 1, 12, fake, fake, fake, fake, None) == -3        # C % 8
+    # linear shape errors
+    assert lib.mmdit_linear(1, -1, 64, 64, fake, fake, fake, 0, None, 0, None, 0, None) == -1
+    assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, None, 0, None, 0, None) == -1
+    # pack: too many samples
+    arr = (B._Sample * 300)(*[B._Sample(1, 1, 1, 0)] * 300)
+    assert lib.mmdit_pack(arr, 300, ctypes.byref(B._PackT()), None) == -1
+    assert lib.mmdit_workspace_size(ctypes.byref(_dims(B, head_dim=96, heads=32)), P) == 0
