@@ -70,31 +70,32 @@ __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
   if (row < n_tgt && lane16 == 0) row_sse[row] = acc;
 }
 
-// One block: per-sample sums in a fixed order, then the mean loss.
-__global__ void __launch_bounds__(256) loss_finalize_kernel(int32_t B, int32_t C,
-                                                            const int32_t* __restrict__ cu_tgt,
-                                                            const float* __restrict__ row_sse,
-                                                            float* __restrict__ sse,
-                                                            float* __restrict__ loss) {
-  __shared__ float red[256];
-  float total = 0.f;
-  for (int b = 0; b < B; ++b) {
+// One block of 16 waves: wave w sums the rows of samples w, w+16, ... in a
+// fixed order; then one thread forms the mean loss over samples in order.
+__global__ void __launch_bounds__(1024) loss_finalize_kernel(int32_t B, int32_t C,
+                                                             const int32_t* __restrict__ cu_tgt,
+                                                             const float* __restrict__ row_sse,
+                                                             float* __restrict__ sse,
+                                                             float* __restrict__ loss) {
+  __shared__ float sh[MMDIT_MAX_SAMPLES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int b = wave; b < B; b += 16) {
     const int32_t r0 = cu_tgt[b], r1 = cu_tgt[b + 1];
     float acc = 0.f;
-    for (int32_t r = r0 + threadIdx.x; r < r1; r += 256) acc += row_sse[r];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-      __syncthreads();
+    for (int32_t r = r0 + lane; r < r1; r += 64) acc += row_sse[r];
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      sse[b] = acc;
+      sh[b] = acc;
     }
-    if (threadIdx.x == 0) {
-      sse[b] = red[0];
-      total += red[0] / ((float)(r1 - r0) * (float)C);
-    }
-    __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = B > 0 ? total / (float)B : 0.f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float total = 0.f;
+    for (int b = 0; b < B; ++b)
+      total += sh[b] / ((float)(cu_tgt[b + 1] - cu_tgt[b]) * (float)C);
+    loss[0] = B > 0 ? total / (float)B : 0.f;
+  }
 }
 
 // z (float32 [n, C]) += dt * (v_u + g (v_c - v_u)); optionally writes z into two target row ranges.
@@ -204,7 +205,7 @@ mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const 
                          (const float*)v, (const float*)z, (const float*)eps, pk->tgt_row, row_sse);
     MMDIT_TRY(launch_check("row_sse_kernel", s));
   }
-  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(256), 0, s, pk->B, C, pk->cu_tgt, row_sse,
+  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse,
                      sse, loss);
   return launch_check("loss_finalize_kernel", s);
 }

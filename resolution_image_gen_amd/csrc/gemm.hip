@@ -136,7 +136,24 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmBatch bt) {
   const bool arow = r16 < P.M;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int nit = kq >> 5;
-  for (int it = 0; it < nit; ++it) {
+  int it = 0;
+  // four independent 16-B weight loads in flight per lane before the MFMAs
+  for (; it + 4 <= nit; it += 4) {
+    bf16x8 b[4], a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b[u] = *reinterpret_cast<const bf16x8*>(W + kbeg + (it + u) * 32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = bf16x8{};
+      if (arow) a[u] = *reinterpret_cast<const bf16x8*>(A + kbeg + (it + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (SILU) a[u] = silu8(a[u]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+    }
+  }
+  for (; it < nit; ++it) {
     const int k = kbeg + it * 32;
     bf16x8 b = *reinterpret_cast<const bf16x8*>(W + k);
     bf16x8 a = {};
@@ -164,18 +181,29 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmBatch bt) {
 
 // ------------------------------------------------------------------ MFMA
 // Tile BM x BN x 64, WM x WN waves, each wave (BM/WM) x (BN/WN) built from
-// 32x32 MFMA tiles.  LDS rows are 64 bf16 = 8 chunks of 16 B, chunk c of
-// row r stored at c ^ swz(r) to keep the 16-B fragment reads conflict-free.
+// 32x32x16 MFMA tiles.  Operands go global -> LDS directly
+// (global_load_lds_dwordx4: each wave instruction fills 1 KB = 8 rows of 64
+// bf16), double-buffered with one barrier per 64-deep k step.  LDS rows are
+// 8 chunks of 16 B; chunk c of row r sits at position c ^ swz8(r), which the
+// loads realise by choosing each lane's global chunk, so the 16-B fragment
+// reads of the MFMA operands are free of bank conflicts.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
+}
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int BK = 64;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
-  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile / thread mismatch");
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  constexpr int ABLK = BM / 8, BBLK = BN / 8;       // 1-KB blocks (8 rows) per stage
+  static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile / wave mismatch");
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
   bf16* As = smem;                    // [2][BM*BK]
   bf16* Bs = smem + 2 * BM * BK;      // [2][BN*BK]
 
@@ -188,39 +216,30 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   const bf16* A = static_cast<const bf16*>(P.A);
   const bf16* W = static_cast<const bf16*>(P.W);
 
-  u32x4 ra[ACH], rb[BCH];
-  auto load = [&](int k0) {
+  // per-lane source of each 1-KB block this wave fills: row r8 = lane / 8 of
+  // the block, LDS chunk position p = lane % 8 holds global chunk p ^ swz8(row)
+  const int r8 = lane >> 3, p8 = lane & 7;
+  const bf16* asrc[ABLK / NW];
+  const bf16* bsrc[BBLK / NW];
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
-      const int64_t m = m0 + row;
-      if (m < P.M)
-        ra[c] = *reinterpret_cast<const u32x4*>(A + m * P.lda + k0 + kc * 8);
-      else
-        ra[c] = u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < ABLK / NW; ++i) {
+    const int row = (wave + i * NW) * 8 + r8;
+    int64_t m = m0 + row;
+    if (m >= P.M) m = P.M - 1;        // rows past M load a valid row; never stored
+    asrc[i] = A + m * P.lda + ((p8 ^ swz8(row)) << 3);
+  }
 #pragma unroll
-    for (int c = 0; c < BCH; ++c) {
-      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
-      rb[c] = *reinterpret_cast<const u32x4*>(W + (int64_t)(n0 + row) * P.K + k0 + kc * 8);
-    }
-  };
-  auto store = [&](int buf) {
+  for (int i = 0; i < BBLK / NW; ++i) {
+    const int row = (wave + i * NW) * 8 + r8;
+    bsrc[i] = W + (int64_t)(n0 + row) * P.K + ((p8 ^ swz8(row)) << 3);
+  }
+  auto issue = [&](int k0, int buf) {
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
-      u32x4 v = ra[c];
-      if (SILU) {
-        bf16x8 x = silu8(*reinterpret_cast<bf16x8*>(&v));
-        v = *reinterpret_cast<u32x4*>(&x);
-      }
-      *reinterpret_cast<u32x4*>(As + buf * BM * BK + row * BK + ((kc ^ swz8(row)) << 3)) = v;
-    }
+    for (int i = 0; i < ABLK / NW; ++i)
+      load_lds16(asrc[i] + k0, As + buf * BM * BK + (wave + i * NW) * 512);
 #pragma unroll
-    for (int c = 0; c < BCH; ++c) {
-      const int q = tid + c * NT, row = q >> 3, kc = q & 7;
-      *reinterpret_cast<u32x4*>(Bs + buf * BN * BK + row * BK + ((kc ^ swz8(row)) << 3)) = rb[c];
-    }
+    for (int i = 0; i < BBLK / NW; ++i)
+      load_lds16(bsrc[i] + k0, Bs + buf * BN * BK + (wave + i * NW) * 512);
   };
 
   f32x16 acc[TM][TN];
@@ -232,13 +251,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int KT = P.K / BK;
-  load(0);
-  store(0);
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const int l32 = lane & 31, g = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) load((kt + 1) * BK);
+    if (kt + 1 < KT) issue((kt + 1) * BK, buf ^ 1);
     const bf16* as = As + buf * BM * BK;
     const bf16* bs = Bs + buf * BN * BK;
 #pragma unroll
@@ -249,6 +268,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       for (int i = 0; i < TM; ++i) {
         const int r = wm * TM * 32 + i * 32 + l32;
         af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + ((ch ^ swz8(r)) << 3));
+        if (SILU) af[i] = silu8(af[i]);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -261,7 +281,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) store(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   // D[i][j] of a 32x32 tile: j = lane % 32, i = 8 * (v / 4) + 4 * (lane / 32) + v % 4
@@ -300,17 +320,47 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   return launch_check(bt.tag ? bt.tag : name, s);
 }
 
+int tile_override() {
+  static int v = -2;
+  if (v == -2) {
+    const char* e = getenv("MMDIT_GEMM_TILE");
+    v = e ? atoi(e) : -1;
+  }
+  return v;
+}
+
 template <int EPI, bool SILU>
 mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
-  bool n128 = true;
-  int64_t big_tiles = 0;
+  bool n256 = true, n128 = true;
+  int64_t t256 = 0, t128 = 0;
   for (int i = 0; i < bt.nprob; ++i) {
+    n256 = n256 && (bt.p[i].N % 256 == 0);
     n128 = n128 && (bt.p[i].N % 128 == 0);
-    big_tiles += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 128);
+    t256 += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 256);
+    t128 += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 128);
   }
-  if (!n128) return launch_mfma_cfg<128, 64, 2, 2, EPI, SILU>(bt, s);
-  if (big_tiles >= 512) return launch_mfma_cfg<256, 128, 2, 2, EPI, SILU>(bt, s);
-  return launch_mfma_cfg<128, 128, 2, 2, EPI, SILU>(bt, s);
+  int cfg = tile_override();
+  bool thin = true;
+  for (int i = 0; i < bt.nprob; ++i) thin = thin && bt.p[i].N <= 256 && bt.p[i].N % 128 == 0 && bt.p[i].K >= 1024;
+  if (cfg < 0) {
+    // measured on MI355X: the 8-wave 256x256 tile wins once it fills two rounds
+    // of 256 CUs; below that the 128x128 tile (two per CU) quantizes better
+    if (thin) cfg = 6;
+    else if (!n128) cfg = 0;
+    else if (n256 && t256 >= 512) cfg = 3;
+    else cfg = 1;
+  }
+  if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
+  if (cfg >= 1 && !n128) cfg = 0;
+  switch (cfg) {
+    case 6: return launch_mfma_cfg<32, 128, 1, 4, EPI, SILU>(bt, s);
+    case 5: return launch_mfma_cfg<256, 128, 2, 2, EPI, SILU>(bt, s);
+    case 4: return launch_mfma_cfg<256, 256, 2, 2, EPI, SILU>(bt, s);
+    case 3: return launch_mfma_cfg<256, 256, 2, 4, EPI, SILU>(bt, s);
+    case 2: return launch_mfma_cfg<256, 128, 2, 4, EPI, SILU>(bt, s);
+    case 1: return launch_mfma_cfg<128, 128, 2, 2, EPI, SILU>(bt, s);
+    default: return launch_mfma_cfg<128, 64, 2, 2, EPI, SILU>(bt, s);
+  }
 }
 
 template <int EPI, bool SILU>

@@ -120,6 +120,8 @@ LINEAR_CASES = [
     ("f32", 5, 1536, 256, 1, True),
     ("bf16", 1000, 384, 256, 0, False),       # MFMA 128x128, ragged M
     ("bf16", 4096, 4096, 128, 0, False),      # MFMA 256x128
+    ("bf16", 4000, 8192, 128, 2, False),      # MFMA 256x256, ragged M, GELU
+    ("bf16", 300, 512, 128, 1, True),         # MFMA with SiLU on A (M > 16), float32 out
     ("bf16", 515, 320, 192, 2, False),        # MFMA 128x64 (N % 128 != 0), GELU
     ("bf16", 700, 256, 512, 3, False),        # gated residual
     ("bf16", 5, 1024, 512, 1, True),          # skinny, float32 out, SiLU on A
