@@ -227,10 +227,13 @@ mmdit_status mmdit_qk_norm_rope(const mmdit_dims* dims, int64_t n_rows, void* qk
 /* Block-diagonal joint attention ([blog] 2.2(2): attention confined to each
  * sample of the pack; [blog] 5 "MMDiT": joint over text and image).  Reads
  * q, k, v from qkv_txt [n_txt, 3H] and qkv_img [n_img, 3H]; writes
- * o_txt [n_txt, H] and o_img [n_img, H]. */
+ * o_txt [n_txt, H] and o_img [n_img, H].  The bfloat16 path stages V
+ * transposed per head in ws (at least mmdit_attention_workspace_size bytes;
+ * the float32 path needs none and ws may be NULL). */
+size_t mmdit_attention_workspace_size(const mmdit_dims* dims, const mmdit_pack_t* pack);
 mmdit_status mmdit_attention(const mmdit_dims* dims, const mmdit_pack_t* pack,
                              const void* qkv_img, const void* qkv_txt, void* o_img, void* o_txt,
-                             mmdit_stream stream);
+                             void* ws, size_t ws_bytes, mmdit_stream stream);
 
 typedef enum {
   MMDIT_EPI_STORE = 0,        /* Y = A W^T in the model dtype */

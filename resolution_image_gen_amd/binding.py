@@ -82,7 +82,8 @@ def _load():
         "mmdit_block_fwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "mmdit_rms_modulate": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
         "mmdit_qk_norm_rope": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _vp]),
-        "mmdit_attention": (_i32, [D, P, _vp, _vp, _vp, _vp, _vp]),
+        "mmdit_attention": (_i32, [D, P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_attention_workspace_size": (_sz, [D, P]),
         "mmdit_linear": (_i32, [_i32, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _vp]),
         "mmdit_final": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_make_xt": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -270,9 +271,15 @@ def qk_norm_rope(dims, qkv, pos, g_q, g_k, stream=None):
                                 _p(g_k), _stream(stream)))
 
 
-def attention(dims, pk, qkv_img, qkv_txt, o_img, o_txt, stream=None):
+def attention(dims, pk, qkv_img, qkv_txt, o_img, o_txt, ws=None, stream=None):
+    """Joint attention; allocates the V^T staging buffer when ws is not given."""
+    if ws is None:
+        import torch
+
+        n = int(_lib.mmdit_attention_workspace_size(ctypes.byref(dims.c), pk.ref))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=qkv_img.device)
     _ck(_lib.mmdit_attention(ctypes.byref(dims.c), pk.ref, _p(qkv_img), _p(qkv_txt), _p(o_img),
-                             _p(o_txt), _stream(stream)))
+                             _p(o_txt), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def linear(A, W, Y, epilogue=EPI_STORE, gate=None, gate_stride=0, seg=None, a_silu=False, stream=None):

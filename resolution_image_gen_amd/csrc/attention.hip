@@ -113,23 +113,80 @@ __global__ void __launch_bounds__(256) attn_simt_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------- MFMA
-template <int D>
-__device__ __forceinline__ int kswz(int key) {
-  // K rows are D bf16 = D/8 chunks of 16 B; chunk c of key r stored at c ^ kswz(r)
-  if constexpr (D == 128) return key & 15;
-  else return (key ^ (key >> 3)) & 7;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
+// Start of sample b in the 64-padded joint axis of the V^T buffer.
+__device__ __forceinline__ int32_t padded_start(const AttnArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  int32_t acc = 0;
+  for (int i = lane; i < b; i += 64) {
+    const int32_t L = (a.cu_txt[i + 1] - a.cu_txt[i]) + (a.cu_img[i + 1] - a.cu_img[i]);
+    acc += (L + 63) & ~63;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  return acc;
+}
+
+// V^T[head][d][padded joint token] (bf16) from the v columns of the QKV
+// buffers; tokens past the end of a sample are written as zeros.
 template <int D>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) v_transpose_kernel(AttnArgs a, bf16* __restrict__ vt, int32_t njp) {
+  __shared__ bf16 t[64][D + 2];
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.cu_txt[b], i0 = a.cu_img[b];
+  const int32_t Tb = a.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.cu_img[b + 1] - i0;
+  const int32_t kv0 = blockIdx.x * 64;
+  if (kv0 >= L) return;
+  const int32_t pstart = padded_start(a, b);
+  constexpr int DCH = D / 8;
+  for (int q = threadIdx.x; q < 64 * DCH; q += 256) {
+    const int r = q / DCH, c = q % DCH;
+    bf16x8 v = {};
+    if (kv0 + r < L) v = *reinterpret_cast<const bf16x8*>(joint_row<bf16>(a, kv0 + r, Tb, t0, i0) + 2 * a.H + head * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[r][c * 8 + e] = v[e];
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < D * 8; q += 256) {
+    const int d = q >> 3, c = q & 7;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[c * 8 + e][d];
+    *reinterpret_cast<bf16x8*>(vt + ((int64_t)head * D + d) * njp + pstart + kv0 + c * 8) = v;
+  }
+}
+
+// K rows are D bf16 = D/8 chunks of 16 B; chunk c of key row r sits at c ^ ksw(r).
+template <int D>
+__device__ __forceinline__ int ksw(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r ^ (r >> 3)) & 7;
+}
+// V^T rows are 64 keys = 8 chunks of 16 B; chunk c of row d sits at c ^ vsw(d).
+__device__ __forceinline__ int vsw(int d) { return (d >> 1) & 7; }
+
+// S^T row i of a 32-key tile is loaded from key row perm(i), which swaps bits 2
+// and 3: then the 8 probabilities a lane holds for each 16-key PV step are 8
+// consecutive keys, so the matching V^T operand is one 16-byte LDS read.
+__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf16* __restrict__ vt, int32_t njp) {
   constexpr int BKV = 64;
-  constexpr int DCH = D / 8;             // 16-B chunks per K/V row
-  constexpr int KPT = BKV * DCH / 256;   // keys staged per thread (consecutive)
-  constexpr int VLD = BKV + 4;           // padded row of V^T in LDS (bf16)
   constexpr int DT = D / 32;             // 32-wide d tiles of O^T
   constexpr int QS = D / 16;             // 16-deep k steps of S^T
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BKV * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VLD];
+  constexpr int KROWS = 512 / D;         // K rows per 1-KB block
+  constexpr int KB = BKV / KROWS / 4;    // K blocks per wave per tile
+  constexpr int VB = D / 8 / 4;          // V^T blocks (8 rows) per wave per tile
+  constexpr int STAGE = 2 * BKV * D;     // bf16 elements per stage (K then V^T)
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
 
   const int b = blockIdx.z, head = blockIdx.y;
   const int32_t t0 = a.cu_txt[b], i0 = a.cu_img[b];
@@ -137,10 +194,10 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   const int32_t L = Tb + a.cu_img[b + 1] - i0;
   const int32_t qbase = blockIdx.x * 128;
   if (qbase >= L) return;
+  const int32_t pstart = padded_start(a, b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // this lane's query (column of S^T and O^T)
   const int32_t jq = qbase + wave * 32 + l32;
   bf16x8 qf[QS];
   if (jq < L) {
@@ -151,6 +208,30 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < QS; ++s) qf[s] = bf16x8{};
   }
+
+  // per-lane sources of the 1-KB blocks this wave fills
+  const int kr = lane / (D / 8), kp = lane % (D / 8);     // row in block, chunk position
+  const bf16* vsrc[VB];
+#pragma unroll
+  for (int i = 0; i < VB; ++i) {
+    const int d = (wave + 4 * i) * 8 + (lane >> 3);
+    vsrc[i] = vt + ((int64_t)head * D + d) * njp + pstart + (((lane & 7) ^ vsw(d)) << 3);
+  }
+  auto issue = [&](int32_t kv0, int st) {
+    bf16* ks = smem + st * STAGE;
+    bf16* vs = ks + BKV * D;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int blk = wave + 4 * i;
+      const int r = blk * KROWS + kr;
+      int32_t key = kv0 + r;
+      if (key >= L) key = L - 1;            // masked in the scores
+      load_lds16(joint_row<bf16>(a, key, Tb, t0, i0) + a.H + head * D + ((kp ^ ksw<D>(r)) << 3), ks + blk * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < VB; ++i) load_lds16(vsrc[i] + kv0, vs + (wave + 4 * i) * 512);
+  };
+
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -158,98 +239,84 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  // staging map: chunk ch of keys kg*KPT .. kg*KPT + KPT-1
-  const int ch = tid % DCH, kg = tid / DCH;
-  for (int32_t kv0 = 0; kv0 < L; kv0 += BKV) {
-    bf16x8 kr[KPT], vr[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int32_t key = kv0 + kg * KPT + i;
-      if (key < L) {
-        const bf16* p = joint_row<bf16>(a, key, Tb, t0, i0) + head * D + ch * 8;
-        kr[i] = *reinterpret_cast<const bf16x8*>(p + a.H);
-        vr[i] = *reinterpret_cast<const bf16x8*>(p + 2 * a.H);
-      } else {
-        kr[i] = bf16x8{};
-        vr[i] = bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int r = kg * KPT + i;
-      *reinterpret_cast<bf16x8*>(Ks + r * D + ((ch ^ kswz<D>(r)) << 3)) = kr[i];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KPT == 4) {
-        bf16x4 t = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
-        *reinterpret_cast<bf16x4*>(Vt + (ch * 8 + e) * VLD + kg * 4) = t;
-      } else {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) Vt[(ch * 8 + e) * VLD + kg * KPT + i] = vr[i][e];
-      }
-    }
-    __syncthreads();
-
-    // S^T[key][query] for two 32-key tiles
-    f32x16 st[2];
+  const int ntile = (L + BKV - 1) / BKV;
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int prow = (l32 & 16) | kperm(l32 & 15);
+  for (int it = 0; it < ntile; ++it) {
+    const int st = it & 1;
+    const int32_t kv0 = it * BKV;
+    if (it + 1 < ntile) issue(kv0 + BKV, st ^ 1);
+    const bf16* ks = smem + st * STAGE;
+    const bf16* vs = ks + BKV * D;
+    f32x16 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st[kt][v] = 0.f;
-      const int r = kt * 32 + l32;
+      for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
+      const int r = kt * 32 + prow;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + r * D + (((s * 2 + g) ^ kswz<D>(r)) << 3));
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kt], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + r * D + (((s * 2 + g) ^ ksw<D>(r)) << 3));
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kt], 0, 0, 0);
       }
     }
-    // online softmax over this lane's 32 keys (+ the other half's 32 via one exchange)
+    // register v of tile kt holds key kv0 + 32 kt + 16 (v / 8) + 8 g + v % 8;
+    // only the last tile of a sample has keys past its end to mask
     float mx = -INFINITY;
+    if (kv0 + BKV <= L) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int32_t key = kv0 + kt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        const float x = key < L ? st[kt][v] * a.scale_log2 : -INFINITY;
-        st[kt][v] = x;
-        mx = fmaxf(mx, x);
-      }
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int32_t key = kv0 + kt * 32 + 16 * (v >> 3) + 8 * g + (v & 7);
+          if (key >= L) sc[kt][v] = -INFINITY;
+          mx = fmaxf(mx, sc[kt][v]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float corr = exp2f(m - mn);
+    // softmax in the log2 domain: p = 2^(s * log2(e)/sqrt(d) - m)
+    const float mn = fmaxf(m, mx * a.scale_log2);
+    const float corr = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(st[kt][v] - mn);
-        st[kt][v] = p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], a.scale_log2, -mn));
+        sc[kt][v] = p;
         ps += p;
       }
     lsum = lsum * corr + ps;
+    if (__any(corr != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[t][v] *= corr;
-    // O^T[d][query] += V^T[d][keys] P^T[keys][query], 16 keys per step.  Lane
-    // supplies keys {16ks + 4g + 0..3, 16ks + 8 + 4g + 0..3}: the P registers
-    // 8*(ks%2) .. +7 of tile ks/2, and the matching V^T entries.
+        for (int v = 0; v < 16; ++v) oacc[t][v] *= corr;
+    }
+    // O^T[d][query] += V^T[d][keys] P^T[keys][query]; step ks covers keys
+    // 16 ks .. 16 ks + 15, this lane's 8 of them being 16 ks + 8 g + 0..7
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
       bf16x8 pf;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pf[u] = (bf16)st[ks >> 1][8 * (ks & 1) + u];
+      for (int u = 0; u < 8; ++u) pf[u] = (bf16)sc[ks2 >> 1][8 * (ks2 & 1) + u];
+      const int c = 2 * ks2 + g;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const bf16* vp = Vt + (t * 32 + l32) * VLD + ks * 16 + 4 * g;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vp);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vp + 8);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int d = t * 32 + l32;
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + d * BKV + ((c ^ vsw(d)) << 3));
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
       }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   lsum += __shfl_xor(lsum, 32, 64);
@@ -270,9 +337,18 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
 
 }  // namespace
 
+int64_t attention_vt_elems(const mmdit_pack_t* pk, int32_t H) {
+  int64_t njp = 0;
+  for (int b = 0; b < pk->B; ++b) {
+    const int64_t L = (pk->h_cu_txt[b + 1] - pk->h_cu_txt[b]) + (pk->h_cu_img[b + 1] - pk->h_cu_img[b]);
+    njp += (L + 63) & ~(int64_t)63;
+  }
+  return njp * H;
+}
+
 mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t heads, int32_t D,
                             const void* qkv_img, const void* qkv_txt, void* o_img, void* o_txt,
-                            hipStream_t s) {
+                            void* ws, size_t ws_bytes, hipStream_t s) {
   if (pk->B == 0 || pk->max_joint == 0) return MMDIT_OK;
   AttnArgs a;
   a.qkv_img = qkv_img;
@@ -285,11 +361,43 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
   a.H = heads * D;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   if (dt == MMDIT_BF16) {
-    dim3 grid((unsigned)cdiv(pk->max_joint, 128), heads, pk->B);
+    const int64_t vt_elems = attention_vt_elems(pk, a.H);
+    if (!ws || ws_bytes < (size_t)vt_elems * 2) {
+      set_error("mmdit_attention: workspace needs %zu bytes, got %zu", (size_t)vt_elems * 2, ws_bytes);
+      return MMDIT_E_WORKSPACE;
+    }
+    if (vt_elems / a.H > INT32_MAX) {
+      set_error("mmdit_attention: padded pack too long");
+      return MMDIT_E_UNSUPPORTED;
+    }
+    const int32_t njp = (int32_t)(vt_elems / a.H);
+    bf16* vt = static_cast<bf16*>(ws);
+    dim3 tgrid((unsigned)cdiv(pk->max_joint, 64), heads, pk->B);
     if (D == 128)
-      MMDIT_LAUNCH(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a);
+      MMDIT_LAUNCH(v_transpose_kernel<128>, tgrid, dim3(256), 0, s, a, vt, njp);
     else
-      MMDIT_LAUNCH(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a);
+      MMDIT_LAUNCH(v_transpose_kernel<64>, tgrid, dim3(256), 0, s, a, vt, njp);
+    MMDIT_TRY(launch_check("v_transpose_kernel", s));
+    dim3 grid((unsigned)cdiv(pk->max_joint, 128), heads, pk->B);
+    const size_t lds = 2 * 2 * 64 * D * sizeof(bf16);
+    static bool attr[2] = {false, false};
+    if (D == 128) {
+      if (!attr[1]) {
+        MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_mfma_kernel<128>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                            "hipFuncSetAttribute(attn_mfma_kernel)"));
+        attr[1] = true;
+      }
+      MMDIT_LAUNCH(attn_mfma_kernel<128>, grid, dim3(256), lds, s, a, vt, njp);
+    } else {
+      if (!attr[0]) {
+        MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_mfma_kernel<64>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                            "hipFuncSetAttribute(attn_mfma_kernel)"));
+        attr[0] = true;
+      }
+      MMDIT_LAUNCH(attn_mfma_kernel<64>, grid, dim3(256), lds, s, a, vt, njp);
+    }
     return launch_check("attn_mfma_kernel", s);
   }
   dim3 grid((unsigned)cdiv(pk->max_joint, 64), heads, pk->B);

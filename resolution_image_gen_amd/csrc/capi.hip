@@ -93,7 +93,8 @@ mmdit_status pack_latent_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const f
 mmdit_status rms_modulate_impl(mmdit_dtype, int64_t, int32_t, const void*, const int32_t*, const int32_t*, const float*, int64_t, int64_t, int64_t, void*, float, hipStream_t);
 mmdit_status qk_norm_rope_impl(mmdit_dtype, int64_t, int32_t, int32_t, void*, const int32_t*, const float*, const float*, float, float, hipStream_t);
 mmdit_status temb_impl(mmdit_dtype, int32_t, int32_t, const float*, void*, hipStream_t);
-mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, hipStream_t);
+mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, void*, size_t, hipStream_t);
+int64_t attention_vt_elems(const mmdit_pack_t*, int32_t);
 
 namespace {
 
@@ -166,7 +167,7 @@ mmdit_status need(const void* p, const char* who, const char* name) {
 }
 
 struct Layout {
-  size_t mod_img, mod_txt, h, qkv, o, u, end;
+  size_t mod_img, mod_txt, h, qkv, o, u, vt, end;
 };
 
 Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -181,6 +182,7 @@ Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   L.qkv = o;     o = align256(o + N * 3 * H * es);
   L.o = o;       o = align256(o + N * H * es);
   L.u = o;       o = align256(o + N * (size_t)d->mlp * es);
+  L.vt = o;      o = align256(o + (size_t)attention_vt_elems(pk, d->hidden) * es);
   L.end = o;
   return L;
 }
@@ -422,8 +424,16 @@ mmdit_status mmdit_qk_norm_rope(const mmdit_dims* d, int64_t n_rows, void* qkv, 
                            (hipStream_t)stream);
 }
 
+size_t mmdit_attention_workspace_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  if (check_dims(d, "mmdit_attention_workspace_size") != MMDIT_OK ||
+      check_pack(pk, "mmdit_attention_workspace_size") != MMDIT_OK)
+    return 0;
+  return d->dtype == MMDIT_BF16 ? (size_t)attention_vt_elems(pk, d->hidden) * 2 : 0;
+}
+
 mmdit_status mmdit_attention(const mmdit_dims* d, const mmdit_pack_t* pk, const void* qkv_img,
-                             const void* qkv_txt, void* o_img, void* o_txt, mmdit_stream stream) {
+                             const void* qkv_txt, void* o_img, void* o_txt, void* ws, size_t ws_bytes,
+                             mmdit_stream stream) {
   const char* who = "mmdit_attention";
   MMDIT_TRY(check_dims(d, who));
   MMDIT_TRY(check_pack(pk, who));
@@ -435,7 +445,8 @@ mmdit_status mmdit_attention(const mmdit_dims* d, const mmdit_pack_t* pk, const 
     MMDIT_TRY(need(qkv_txt, who, "qkv_txt"));
     MMDIT_TRY(need(o_txt, who, "o_txt"));
   }
-  return attention_impl(d->dtype, pk, d->heads, d->head_dim, qkv_img, qkv_txt, o_img, o_txt,
+  if (d->dtype == MMDIT_BF16) MMDIT_TRY(need(ws, who, "ws"));
+  return attention_impl(d->dtype, pk, d->heads, d->head_dim, qkv_img, qkv_txt, o_img, o_txt, ws, ws_bytes,
                         (hipStream_t)stream);
 }
 
@@ -533,7 +544,7 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   MMDIT_TRY(qk_norm_rope_impl(dt, nt, d->heads, d->head_dim, qkv_t, nullptr, w->txt.g_q, w->txt.g_k,
                               d->rope_theta, d->eps, s));
   // o = block-diagonal joint attention
-  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, s));
+  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s));
   // x += gate1 * (o W_o^T)
   {
     LinearArgs a[2] = {mk(ni, H, H, o, w->img.w_o, x_img, MMDIT_EPI_GATED_RES),
