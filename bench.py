@@ -63,8 +63,17 @@ def step_flops(wl):
     return blk, wrap
 
 
-def cpu_baseline(wl, W, inputs, n_samples):
-    """The oracle (float64 numpy) on the first n_samples samples of the pack."""
+class _NumpyWeights:
+    """Host copies of the weights for the CPU oracle (the device copies can be freed)."""
+
+    def __init__(self, W):
+        self.np_wrap = W.np_wrap
+        self.np_blocks = W.np_blocks
+
+
+def cpu_baseline(wl, W, inputs, n_samples, min_seconds=10.0):
+    """The oracle (float64 numpy) on the first n_samples samples of the pack,
+    repeated until at least min_seconds of CPU work have been timed."""
     import numpy as np
 
     from oracle import flow as OF
@@ -83,15 +92,56 @@ def cpu_baseline(wl, W, inputs, n_samples):
     Wd["blocks"] = [{s: {k: np.asarray(v, np.float64) for k, v in nb[s].items()} for s in nb}
                     for nb in W.np_blocks]
     z, eps, tau, t = inputs["z"][:ni], inputs["eps"][:ni], inputs["tau"][:nt], inputs["t"][:n_samples]
-    t0 = time.perf_counter()
-    zt = OF.make_xt(z, eps, t, ref)
-    v = OF.velocity_model(zt, tau, t, Wd, ref, wl.dims.heads)
-    OF.loss(v, z, eps, ref)
-    dt = time.perf_counter() - t0
-    tokens = ni + nt
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_samples} of {len(wl.samples)} samples ({tokens} tokens), same step, float64 numpy, "
-                      f"{dt:.1f} s wall"}
+    runs, dt = 0, 0.0
+    while runs == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        zt = OF.make_xt(z, eps, t, ref)
+        v = OF.velocity_model(zt, tau, t, Wd, ref, wl.dims.heads)
+        OF.loss(v, z, eps, ref)
+        dt += time.perf_counter() - t0
+        runs += 1
+    tokens = (ni + nt) * runs
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_samples} of {len(wl.samples)} samples ({ni + nt} tokens) of the same step "
+                      f"(noise, cond, embed, block, final, loss), float64 numpy, {runs} runs, {dt:.1f} s"}
+
+
+def bench_sampler(steps, warmup):
+    """ms per 4-step packed-CFG pack: cond + uncond (64x64 grid + 256 text
+    tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0."""
+    import torch
+
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import runner as R
+    from resolution_image_gen_amd import synthetic as S
+
+    wl = CF.WORKLOADS["sampler1024_cfg_bf16"]
+    d = wl.dims
+    W = R.Weights(wl, source="torch")            # 28 blocks drawn on the GPU (19 GB bf16)
+    h, w, _, T = wl.samples[0]
+    eps = S.normal((h * w, d.c_lat), 1.0, "bf16", wl.name, "eps")
+    tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
+    tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    for _ in range(warmup):
+        sm.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sm.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(sm.z).all()
+    from resolution_image_gen_amd.configs import block_flops
+
+    blk = block_flops(d, sm.samples)[0] * wl.depth * (len(wl.schedule) - 1)
+    n = sum(hh * ww * f + t for hh, ww, f, t in sm.samples)
+    return {"workload": f"{wl.name}: {wl.note}", "ms_per_4step_pack": round(ms, 2), "packs_timed": steps,
+            "block_tokens_per_s": round(n * wl.depth * (len(wl.schedule) - 1) / (ms * 1e-3), 1),
+            "block_tflops": round(blk / (ms * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
 def main():
@@ -100,13 +150,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="pack256_bf16")
-    ap.add_argument("--cpu-samples", type=int, default=2, help="samples of the pack the CPU oracle runs")
+    ap.add_argument("--cpu-samples", type=int, default=16, help="samples of the pack the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
+    ap.add_argument("--sampler-packs", type=int, default=0,
+                    help="also time N packs of the 4-step packed-CFG sampler (28 blocks) and report them "
+                         "under 'sampler' (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(packs are independent; see the sharding notes of the design).", file=sys.stderr)
+        print("bench.py measures one GPU only: packs are independent, so more GPUs would each take "
+              "their own pack with no exchange in the forward pass; no multi-GPU path is built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -117,10 +171,11 @@ def main():
 
     wl = CF.WORKLOADS[args.workload]
     if wl.steps:
-        raise SystemExit("sampler workloads are timed by bench_sampler in this file's --workload list; "
-                         "use a training-forward workload")
+        raise SystemExit("the sampler workload is timed with --sampler-packs N next to a training-forward "
+                         "workload")
     torch.cuda.set_device(0)
     W = R.Weights(wl)
+    W_np = _NumpyWeights(W)
     inputs = R.training_inputs(wl)
     tf = R.TrainForward(wl, W, inputs)
     stream = torch.cuda.current_stream()
@@ -197,8 +252,12 @@ def main():
         "roofline": roof,
         "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
     }
+    if args.sampler_packs > 0:
+        del tf, W
+        torch.cuda.empty_cache()
+        out["sampler"] = bench_sampler(args.sampler_packs, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, W, inputs, args.cpu_samples)
+        out["cpu_baseline"] = cpu_baseline(wl, W_np, inputs, args.cpu_samples)
     print(json.dumps(out), flush=True)
 
 

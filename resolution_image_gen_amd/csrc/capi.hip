@@ -577,6 +577,7 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].seg = pk->seg_img;
     a[1].seg = pk->seg_txt;
     a[0].tag = "mlp_down_gated";
+    a[0].site = 1;
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   return MMDIT_OK;

@@ -109,6 +109,7 @@ struct LinearArgs {
   int64_t gate_stride;
   const int32_t* seg;      // [M] sample of each row (gated residual)
   const char* tag;         // kernel-timing name of the launch (NULL: generic name)
+  int32_t site;            // 1: MLP down projection (own kernel instantiation for profiling)
 };
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 

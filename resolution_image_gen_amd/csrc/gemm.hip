@@ -35,6 +35,7 @@ struct GemmBatch {
   GemmProb p[2];
   int32_t nprob;
   const char* tag;
+  int32_t site;
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -196,7 +197,9 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU>
+// SITE only separates the MLP down projection's instantiation from the output
+// projection's (same epilogue) so profiles can tell the two apart.
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int NW = WM * WN;
   constexpr int BK = 64;
@@ -296,7 +299,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU>
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0>
 mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   int tiles = 0;
   for (int i = 0; i < bt.nprob; ++i) {
@@ -306,7 +309,7 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   }
   if (tiles == 0) return MMDIT_OK;
   const size_t lds = 2 * (BM + BN) * 64 * sizeof(bf16);
-  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU>;
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE>;
   static bool attr_set = false;
   if (!attr_set) {
     MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern,
@@ -316,7 +319,9 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   }
   MMDIT_LAUNCH(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, bt);
   static char name[64];
-  if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s>", BM, BN, WM, WN, EPI, SILU ? ",silu" : "");
+  if (!name[0])
+    snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s>", BM, BN, WM, WN, EPI, SILU ? ",silu" : "",
+             SITE ? ",down" : "");
   return launch_check(bt.tag ? bt.tag : name, s);
 }
 
@@ -352,6 +357,17 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   }
   if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
   if (cfg >= 1 && !n128) cfg = 0;
+  if constexpr (EPI == MMDIT_EPI_GATED_RES && !SILU) {
+    if (bt.site == 1) switch (cfg) {
+      case 6: return launch_mfma_cfg<32, 128, 1, 4, EPI, SILU, 1>(bt, s);
+      case 5: return launch_mfma_cfg<256, 128, 2, 2, EPI, SILU, 1>(bt, s);
+      case 4: return launch_mfma_cfg<256, 256, 2, 2, EPI, SILU, 1>(bt, s);
+      case 3: return launch_mfma_cfg<256, 256, 2, 4, EPI, SILU, 1>(bt, s);
+      case 2: return launch_mfma_cfg<256, 128, 2, 4, EPI, SILU, 1>(bt, s);
+      case 1: return launch_mfma_cfg<128, 128, 2, 2, EPI, SILU, 1>(bt, s);
+      default: return launch_mfma_cfg<128, 64, 2, 2, EPI, SILU, 1>(bt, s);
+    }
+  }
   switch (cfg) {
     case 6: return launch_mfma_cfg<32, 128, 1, 4, EPI, SILU>(bt, s);
     case 5: return launch_mfma_cfg<256, 128, 2, 2, EPI, SILU>(bt, s);
@@ -457,6 +473,7 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   }
   bt.nprob = n;
   bt.tag = pa[0].tag;
+  bt.site = pa[0].site;
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
   switch (epi * 2 + (silu ? 1 : 0)) {
