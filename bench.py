@@ -153,6 +153,9 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=16, help="samples of the pack the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
+                         "scale the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--sampler-packs", type=int, default=0,
                     help="also time N packs of the 4-step packed-CFG sampler (28 blocks) and report them "
                          "under 'sampler' (0: skip)")
@@ -164,6 +167,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_mib": args.copy_calibration_mib, "launches": 3}))
+        return
 
     from resolution_image_gen_amd import binding as B
     from resolution_image_gen_amd import configs as CF

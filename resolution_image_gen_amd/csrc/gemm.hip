@@ -36,6 +36,7 @@ struct GemmBatch {
   int32_t nprob;
   const char* tag;
   int32_t site;
+  int32_t xcd_remap;   // renumber tiles per XCD (off when grouped problems differ in K)
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -193,57 +194,93 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
+__device__ __forceinline__ int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber so that each XCD receives one contiguous range of tiles.
+__device__ __forceinline__ int xcd_tile(int hw, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int xcd = hw & 7, local = hw >> 3;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Tiles ordered in groups of 8 tile-rows, down the rows first: the tiles an
+// XCD runs together share a few A row-blocks and a few W column-blocks.
+__device__ __forceinline__ void grouped_tile(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = tile / per_group;
+  const int first = group * GM;
+  const int gsize = min(tiles_m - first, GM);
+  const int r = tile - group * per_group;
+  tm = first + r % gsize;
+  tn = r / gsize;
+}
+
 __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
 // SITE only separates the MLP down projection's instantiation from the output
 // projection's (same epilogue) so profiles can tell the two apart.
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0>
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int NW = WM * WN;
-  constexpr int BK = 64;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  constexpr int ABLK = BM / 8, BBLK = BN / 8;       // 1-KB blocks (8 rows) per stage
+  constexpr int CPR = BK / 8;            // 16-B chunks per LDS row
+  constexpr int RPB = 64 / CPR;          // rows per 1-KB block (one wave instruction)
+  constexpr int ABLK = BM / RPB, BBLK = BN / RPB;
   static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile / wave mismatch");
+  constexpr int LPS = ABLK / NW + BBLK / NW;   // direct loads per stage per wave
   extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
-  bf16* As = smem;                    // [2][BM*BK]
-  bf16* Bs = smem + 2 * BM * BK;      // [2][BN*BK]
+  bf16* As = smem;                    // [NS][BM*BK]
+  bf16* Bs = smem + NS * BM * BK;     // [NS][BN*BK]
 
-  int tile = blockIdx.x;
+  int tile = bt.xcd_remap ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const GemmProb& P = pick(bt, tile);
-  const int64_t m0 = (int64_t)(tile / P.tiles_n) * BM;
-  const int n0 = (tile % P.tiles_n) * BN;
+  int tm, tn;
+  grouped_tile(tile, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const bf16* A = static_cast<const bf16*>(P.A);
   const bf16* W = static_cast<const bf16*>(P.W);
+  auto swz = [](int r) { return CPR == 8 ? swz8(r) : ((r >> 2) & 3); };
 
-  // per-lane source of each 1-KB block this wave fills: row r8 = lane / 8 of
-  // the block, LDS chunk position p = lane % 8 holds global chunk p ^ swz8(row)
-  const int r8 = lane >> 3, p8 = lane & 7;
+  // per-lane source of each 1-KB block this wave fills: row rr = lane / CPR of
+  // the block, LDS chunk position p = lane % CPR holds global chunk p ^ swz(row)
+  const int rr = lane / CPR, pp = lane % CPR;
   const bf16* asrc[ABLK / NW];
   const bf16* bsrc[BBLK / NW];
 #pragma unroll
   for (int i = 0; i < ABLK / NW; ++i) {
-    const int row = (wave + i * NW) * 8 + r8;
+    const int row = (wave + i * NW) * RPB + rr;
     int64_t m = m0 + row;
     if (m >= P.M) m = P.M - 1;        // rows past M load a valid row; never stored
-    asrc[i] = A + m * P.lda + ((p8 ^ swz8(row)) << 3);
+    asrc[i] = A + m * P.lda + ((pp ^ swz(row)) << 3);
   }
 #pragma unroll
   for (int i = 0; i < BBLK / NW; ++i) {
-    const int row = (wave + i * NW) * 8 + r8;
-    bsrc[i] = W + (int64_t)(n0 + row) * P.K + ((p8 ^ swz8(row)) << 3);
+    const int row = (wave + i * NW) * RPB + rr;
+    bsrc[i] = W + (int64_t)(n0 + row) * P.K + ((pp ^ swz(row)) << 3);
   }
-  auto issue = [&](int k0, int buf) {
+  auto issue = [&](int kt) {
+    const int st = kt % NS, k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < ABLK / NW; ++i)
-      load_lds16(asrc[i] + k0, As + buf * BM * BK + (wave + i * NW) * 512);
+      load_lds16(asrc[i] + k0, As + st * BM * BK + (wave + i * NW) * 512);
 #pragma unroll
     for (int i = 0; i < BBLK / NW; ++i)
-      load_lds16(bsrc[i] + k0, Bs + buf * BN * BK + (wave + i * NW) * 512);
+      load_lds16(bsrc[i] + k0, Bs + st * BN * BK + (wave + i * NW) * 512);
   };
+  // wait until at most c stages of this wave's loads are still in flight
+  auto wait_stages = [&](int c) {
+    if (c <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (c == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LPS) : "memory");
+  };
+  static_assert(NS <= 4 && 2 * LPS < 64, "vmcnt range");
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -253,16 +290,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // NS-stage ring: stage kt + NS - 1 is requested while stage kt is consumed
   const int KT = P.K / BK;
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KT) issue(s);
+  wait_stages(min(NS - 1, KT) - 1);
   __syncthreads();
   const int l32 = lane & 31, g = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) issue((kt + 1) * BK, buf ^ 1);
-    const bf16* as = As + buf * BM * BK;
-    const bf16* bs = Bs + buf * BN * BK;
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const bf16* as = As + (kt % NS) * BM * BK;
+    const bf16* bs = Bs + (kt % NS) * BN * BK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[TM], bfr[TN];
@@ -270,13 +309,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * TM * 32 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + ((ch ^ swz8(r)) << 3));
+        af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + ((ch ^ swz(r)) << 3));
         if (SILU) af[i] = silu8(af[i]);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * TN * 32 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * BK + ((ch ^ swz8(r)) << 3));
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + r * BK + ((ch ^ swz(r)) << 3));
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -284,7 +323,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stage kt + 1 must have landed (for every wave) before the next step
+    wait_stages(min(KT - 1, kt + NS - 1) - kt - 1);
     __syncthreads();
   }
   // D[i][j] of a 32x32 tile: j = lane % 32, i = 8 * (v / 4) + 4 * (lane / 32) + v % 4
@@ -299,7 +339,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0>
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
 mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   int tiles = 0;
   for (int i = 0; i < bt.nprob; ++i) {
@@ -308,8 +348,8 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
     tiles += (int)(cdiv(bt.p[i].M, BM) * bt.p[i].tiles_n);
   }
   if (tiles == 0) return MMDIT_OK;
-  const size_t lds = 2 * (BM + BN) * 64 * sizeof(bf16);
-  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE>;
+  const size_t lds = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
+  auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
     MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern,
@@ -318,10 +358,10 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
     attr_set = true;
   }
   MMDIT_LAUNCH(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, bt);
-  static char name[64];
+  static char name[80];
   if (!name[0])
-    snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s>", BM, BN, WM, WN, EPI, SILU ? ",silu" : "",
-             SITE ? ",down" : "");
+    snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s,bk%d,s%d>", BM, BN, WM, WN, EPI,
+             SILU ? ",silu" : "", SITE ? ",down" : "", BK, NS);
   return launch_check(bt.tag ? bt.tag : name, s);
 }
 
@@ -474,6 +514,7 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.nprob = n;
   bt.tag = pa[0].tag;
   bt.site = pa[0].site;
+  bt.xcd_remap = (n < 2 || bt.p[0].K == bt.p[1].K) ? 1 : 0;
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
   switch (epi * 2 + (silu ? 1 : 0)) {
