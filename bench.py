@@ -41,9 +41,10 @@ def kernel_work(wl):
         "mlp_up_gelu": ("mfma", 2.0 * n * H * M),
         "mlp_down_gated": ("mfma", 2.0 * n * M * H),
         "attn_mfma_kernel": ("mfma", 4.0 * H * att),
-        # one launch per stream: read x, write y (bytes); averaged over the two streams
-        "rms_modulate_kernel": ("hbm", 2.0 * es * H * n / 2),
-        "qk_norm_rope_kernel": ("hbm", 4.0 * es * H * n / 2),
+        # read x, write y: two launches over all N rows + one over the target rows, averaged
+        "rms_modulate_kernel": ("hbm", (2 * (2.0 * es * H * n) + 2.0 * es * H * n_tgt) / 3),
+        # read and write q and k of every row, one launch
+        "qk_norm_rope_kernel": ("hbm", 4.0 * es * H * n),
         "final_out": ("mfma", 2.0 * n_tgt * H * d.c_lat),
     }
 

@@ -365,17 +365,18 @@ mmdit_status mmdit_embed(const mmdit_dims* d, const void* w_in, const void* w_tx
   MMDIT_TRY(check_pack(pk, who));
   LinearArgs a[2];
   int n = 0;
-  if (pk->n_img > 0) {
-    MMDIT_TRY(need(w_in, who, "w_in"));
-    MMDIT_TRY(need(zt, who, "zt"));
-    MMDIT_TRY(need(x_img, who, "x_img"));
-    a[n++] = mk(pk->n_img, d->hidden, d->c_lat, zt, w_in, x_img, MMDIT_EPI_STORE);
-  }
+  // the text problem (K = d_txt) goes first: its long-K tiles are scheduled before the short image ones
   if (pk->n_txt > 0) {
     MMDIT_TRY(need(w_txt, who, "w_txt"));
     MMDIT_TRY(need(tau, who, "tau"));
     MMDIT_TRY(need(x_txt, who, "x_txt"));
     a[n++] = mk(pk->n_txt, d->hidden, d->d_txt, tau, w_txt, x_txt, MMDIT_EPI_STORE);
+  }
+  if (pk->n_img > 0) {
+    MMDIT_TRY(need(w_in, who, "w_in"));
+    MMDIT_TRY(need(zt, who, "zt"));
+    MMDIT_TRY(need(x_img, who, "x_img"));
+    a[n++] = mk(pk->n_img, d->hidden, d->c_lat, zt, w_in, x_img, MMDIT_EPI_STORE);
   }
   if (n == 0) return MMDIT_OK;
   a[0].tag = "embed";
@@ -528,9 +529,12 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].tag = "adaln_mod";
     MMDIT_TRY(linear(dt, a, 2, s));
   }
-  // h = rms(x)(1 + scale1) + shift1
-  MMDIT_TRY(rms_modulate_impl(dt, ni, H, x_img, nullptr, pk->seg_img, mod_i, 6 * H, 0, H, h, d->eps, s));
-  MMDIT_TRY(rms_modulate_impl(dt, nt, H, x_txt, nullptr, pk->seg_txt, mod_t, 6 * H, 0, H, h_t, d->eps, s));
+  // h = rms(x)(1 + scale1) + shift1   (both streams, one launch)
+  {
+    RmsArgs r[2] = {{x_img, nullptr, pk->seg_img, mod_i, h, ni, 6 * H, 0, H},
+                    {x_txt, nullptr, pk->seg_txt, mod_t, h_t, nt, 6 * H, 0, H}};
+    MMDIT_TRY(rms_modulate2_impl(dt, H, d->eps, r, 2, s));
+  }
   // qkv = h W_qkv^T
   {
     LinearArgs a[2] = {mk(ni, 3 * H, H, h, w->img.w_qkv, qkv, MMDIT_EPI_STORE),
@@ -539,10 +543,10 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
-  MMDIT_TRY(qk_norm_rope_impl(dt, ni, d->heads, d->head_dim, qkv, pk->pos_img, w->img.g_q, w->img.g_k,
-                              d->rope_theta, d->eps, s));
-  MMDIT_TRY(qk_norm_rope_impl(dt, nt, d->heads, d->head_dim, qkv_t, nullptr, w->txt.g_q, w->txt.g_k,
-                              d->rope_theta, d->eps, s));
+  {
+    QkArgs q[2] = {{qkv, pk->pos_img, w->img.g_q, w->img.g_k, ni}, {qkv_t, nullptr, w->txt.g_q, w->txt.g_k, nt}};
+    MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_theta, d->eps, q, 2, s));
+  }
   // o = block-diagonal joint attention
   MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s));
   // x += gate1 * (o W_o^T)
@@ -558,8 +562,11 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // h = rms(x)(1 + scale2) + shift2
-  MMDIT_TRY(rms_modulate_impl(dt, ni, H, x_img, nullptr, pk->seg_img, mod_i, 6 * H, 3 * H, 4 * H, h, d->eps, s));
-  MMDIT_TRY(rms_modulate_impl(dt, nt, H, x_txt, nullptr, pk->seg_txt, mod_t, 6 * H, 3 * H, 4 * H, h_t, d->eps, s));
+  {
+    RmsArgs r[2] = {{x_img, nullptr, pk->seg_img, mod_i, h, ni, 6 * H, 3 * H, 4 * H},
+                    {x_txt, nullptr, pk->seg_txt, mod_t, h_t, nt, 6 * H, 3 * H, 4 * H}};
+    MMDIT_TRY(rms_modulate2_impl(dt, H, d->eps, r, 2, s));
+  }
   // u = GELU(h W_up^T)
   {
     LinearArgs a[2] = {mk(ni, d->mlp, H, h, w->img.w_up, u, MMDIT_EPI_GELU),

@@ -113,4 +113,26 @@ struct LinearArgs {
 };
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 
+// RMSNorm + adaLN modulate of up to two row sets in one launch.
+struct RmsArgs {
+  const void* x;
+  const int32_t* row_map;
+  const int32_t* seg;
+  const float* mod;
+  void* y;
+  int64_t n_rows, mod_stride, shift_off, scale_off;
+};
+mmdit_status rms_modulate2_impl(mmdit_dtype dt, int32_t H, float eps, const RmsArgs* a, int n, hipStream_t s);
+
+// QK-RMSNorm + RoPE of up to two row sets in one launch.
+struct QkArgs {
+  void* qkv;
+  const int32_t* pos;
+  const float* g_q;
+  const float* g_k;
+  int64_t n_rows;
+};
+mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkArgs* a,
+                                int n, hipStream_t s);
+
 }  // namespace mmdit

@@ -7,6 +7,7 @@
 #include "common.h"
 
 #include <math.h>
+#include <string.h>
 
 namespace mmdit {
 
@@ -14,16 +15,34 @@ namespace {
 
 // ------------------------------------------------ RMSNorm + adaLN modulate
 // y[i] = x[src] / sqrt(mean(x[src]^2) + eps) * (1 + scale[s]) + shift[s],
-// src = row_map ? row_map[i] : i, s = seg[src].  NCH = 8-element chunks per lane.
+// src = row_map ? row_map[i] : i, s = seg[src].  NCH = 8-element chunks per
+// lane.  Up to two problems (image and text streams) share one launch.
+struct RmsProb {
+  const void* x;
+  const int32_t* row_map;
+  const int32_t* seg;
+  const float* mod;
+  void* y;
+  int64_t n_rows, mod_stride, shift_off, scale_off;
+};
+struct RmsBatch {
+  RmsProb p[2];
+  int64_t split;   // rows of problem 0
+  int32_t H;
+  float eps;
+};
+
 template <typename T, int NCH>
-__global__ void __launch_bounds__(256) rms_modulate_kernel(
-    int64_t n_rows, int32_t H, const T* __restrict__ x, const int32_t* __restrict__ row_map,
-    const int32_t* __restrict__ seg, const float* __restrict__ mod, int64_t mod_stride,
-    int64_t shift_off, int64_t scale_off, T* __restrict__ y, float eps) {
+__global__ void __launch_bounds__(256) rms_modulate_kernel(RmsBatch bt) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= n_rows) return;
-  const int64_t src = row_map ? (int64_t)row_map[i] : i;
+  int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const RmsProb& P = i < bt.split ? bt.p[0] : bt.p[1];
+  if (i >= bt.split) i -= bt.split;
+  if (i >= P.n_rows) return;
+  const int H = bt.H;
+  const T* x = static_cast<const T*>(P.x);
+  T* y = static_cast<T*>(P.y);
+  const int64_t src = P.row_map ? (int64_t)P.row_map[i] : i;
   const int nch = H >> 3;
   float v[NCH][8];
   float ss = 0.f;
@@ -37,10 +56,10 @@ __global__ void __launch_bounds__(256) rms_modulate_kernel(
     }
   }
   ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  const float* mrow = mod + (int64_t)seg[src] * mod_stride;
-  const float* shift = mrow + shift_off;
-  const float* scale = mrow + scale_off;
+  const float r = 1.0f / sqrtf(ss / (float)H + bt.eps);
+  const float* mrow = P.mod + (int64_t)P.seg[src] * P.mod_stride;
+  const float* shift = mrow + P.shift_off;
+  const float* scale = mrow + P.scale_off;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = lane + 64 * j;
@@ -56,23 +75,19 @@ __global__ void __launch_bounds__(256) rms_modulate_kernel(
 }
 
 template <typename T>
-mmdit_status launch_rms(int64_t n, int32_t H, const void* x, const int32_t* map, const int32_t* seg,
-                        const float* mod, int64_t ms, int64_t so, int64_t co, void* y, float eps,
-                        hipStream_t s) {
-  dim3 g((unsigned)cdiv(n, 4)), b(256);
-  const T* xp = static_cast<const T*>(x);
-  T* yp = static_cast<T*>(y);
-  const int nch = H / 8;
+mmdit_status launch_rms(const RmsBatch& bt, int64_t total, hipStream_t s) {
+  dim3 g((unsigned)cdiv(total, 4)), b(256);
+  const int nch = bt.H / 8;
   if (nch <= 64)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 1>), g, b, 0, s, n, H, xp, map, seg, mod, ms, so, co, yp, eps);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 1>), g, b, 0, s, bt);
   else if (nch <= 128)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 2>), g, b, 0, s, n, H, xp, map, seg, mod, ms, so, co, yp, eps);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 2>), g, b, 0, s, bt);
   else if (nch <= 256)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 4>), g, b, 0, s, n, H, xp, map, seg, mod, ms, so, co, yp, eps);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 4>), g, b, 0, s, bt);
   else if (nch <= 384)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 6>), g, b, 0, s, n, H, xp, map, seg, mod, ms, so, co, yp, eps);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 6>), g, b, 0, s, bt);
   else
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 16>), g, b, 0, s, n, H, xp, map, seg, mod, ms, so, co, yp, eps);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 16>), g, b, 0, s, bt);
   return launch_check("rms_modulate_kernel", s);
 }
 
@@ -84,18 +99,31 @@ struct RopeTab {
   int32_t axis[64];    // 0 frame, 1 row, 2 col
 };
 
+struct QkProb {
+  void* qkv;
+  const int32_t* pos;   // NULL: no rotation (text rows)
+  const float* g_q;
+  const float* g_k;
+  int64_t n_rows;
+};
+struct QkBatch {
+  QkProb p[2];
+  int64_t split;
+  int32_t heads;
+  float eps;
+};
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256) qk_norm_rope_kernel(int64_t n_rows, int32_t heads,
-                                                           T* __restrict__ qkv,
-                                                           const int32_t* __restrict__ pos,
-                                                           const float* __restrict__ g_q,
-                                                           const float* __restrict__ g_k,
-                                                           RopeTab tab, float eps) {
+__global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkBatch bt, RopeTab tab) {
   constexpr int LPH = D / 8;      // lanes per head vector
   constexpr int HPS = 64 / LPH;   // head vectors per wave step
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const QkProb& P = row < bt.split ? bt.p[0] : bt.p[1];
+  if (row >= bt.split) row -= bt.split;
+  if (row >= P.n_rows) return;
+  const int heads = bt.heads;
+  const int32_t* pos = P.pos;
   const int sub = lane % LPH;
   const int hv0 = lane / LPH;
   float cs[4], sn[4];
@@ -109,10 +137,10 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(int64_t n_rows, int32
     }
   }
   float gq[8], gk[8];
-  Vec8<float>::load(g_q + sub * 8, gq);
-  Vec8<float>::load(g_k + sub * 8, gk);
+  Vec8<float>::load(P.g_q + sub * 8, gq);
+  Vec8<float>::load(P.g_k + sub * 8, gk);
   const int64_t H3 = 3 * (int64_t)heads * D;
-  T* base = qkv + row * H3 + sub * 8;
+  T* base = static_cast<T*>(P.qkv) + row * H3 + sub * 8;
   for (int hv = hv0; hv < 2 * heads; hv += HPS) {
     float v[8];
     Vec8<T>::load(base + hv * D, v);
@@ -120,7 +148,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(int64_t n_rows, int32
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     ss = group_sum(ss, LPH);
-    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    const float r = 1.0f / sqrtf(ss / (float)D + bt.eps);
     const float* g = hv < heads ? gq : gk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * r * g[e];
@@ -137,13 +165,12 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(int64_t n_rows, int32
 }
 
 template <typename T>
-mmdit_status launch_qk(int64_t n, int32_t heads, int32_t D, void* qkv, const int32_t* pos,
-                       const float* gq, const float* gk, const RopeTab& tab, float eps, hipStream_t s) {
-  dim3 g((unsigned)cdiv(n, 4)), b(256);
+mmdit_status launch_qk(const QkBatch& bt, int64_t total, int32_t D, const RopeTab& tab, hipStream_t s) {
+  dim3 g((unsigned)cdiv(total, 4)), b(256);
   if (D == 128)
-    MMDIT_LAUNCH((qk_norm_rope_kernel<T, 128>), g, b, 0, s, n, heads, (T*)qkv, pos, gq, gk, tab, eps);
+    MMDIT_LAUNCH((qk_norm_rope_kernel<T, 128>), g, b, 0, s, bt, tab);
   else
-    MMDIT_LAUNCH((qk_norm_rope_kernel<T, 64>), g, b, 0, s, n, heads, (T*)qkv, pos, gq, gk, tab, eps);
+    MMDIT_LAUNCH((qk_norm_rope_kernel<T, 64>), g, b, 0, s, bt, tab);
   return launch_check("qk_norm_rope_kernel", s);
 }
 
@@ -163,41 +190,86 @@ __global__ void temb_kernel(int32_t B, int32_t half, const float* __restrict__ t
 
 }  // namespace
 
-mmdit_status rms_modulate_impl(mmdit_dtype dt, int64_t n, int32_t H, const void* x,
-                               const int32_t* map, const int32_t* seg, const float* mod,
-                               int64_t ms, int64_t so, int64_t co, void* y, float eps, hipStream_t s) {
-  if (n == 0) return MMDIT_OK;
+mmdit_status rms_modulate2_impl(mmdit_dtype dt, int32_t H, float eps, const RmsArgs* a, int n, hipStream_t s) {
   if (H % 8 || H > 8192 || H <= 0) {
     set_error("rms_modulate: hidden=%d must be a multiple of 8 and <= 8192", H);
     return MMDIT_E_UNSUPPORTED;
   }
-  return dt == MMDIT_BF16 ? launch_rms<bf16>(n, H, x, map, seg, mod, ms, so, co, y, eps, s)
-                          : launch_rms<float>(n, H, x, map, seg, mod, ms, so, co, y, eps, s);
+  RmsBatch bt;
+  memset(&bt, 0, sizeof(bt));
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    if (a[i].n_rows == 0) continue;
+    RmsProb& p = bt.p[k++];
+    p.x = a[i].x;
+    p.row_map = a[i].row_map;
+    p.seg = a[i].seg;
+    p.mod = a[i].mod;
+    p.y = a[i].y;
+    p.n_rows = a[i].n_rows;
+    p.mod_stride = a[i].mod_stride;
+    p.shift_off = a[i].shift_off;
+    p.scale_off = a[i].scale_off;
+  }
+  if (k == 0) return MMDIT_OK;
+  bt.split = bt.p[0].n_rows;
+  bt.H = H;
+  bt.eps = eps;
+  const int64_t total = bt.p[0].n_rows + (k > 1 ? bt.p[1].n_rows : 0);
+  return dt == MMDIT_BF16 ? launch_rms<bf16>(bt, total, s) : launch_rms<float>(bt, total, s);
 }
 
-mmdit_status qk_norm_rope_impl(mmdit_dtype dt, int64_t n, int32_t heads, int32_t D, void* qkv,
-                               const int32_t* pos, const float* gq, const float* gk, float theta,
-                               float eps, hipStream_t s) {
-  if (n == 0) return MMDIT_OK;
+mmdit_status rms_modulate_impl(mmdit_dtype dt, int64_t n, int32_t H, const void* x,
+                               const int32_t* map, const int32_t* seg, const float* mod,
+                               int64_t ms, int64_t so, int64_t co, void* y, float eps, hipStream_t s) {
+  RmsArgs a = {x, map, seg, mod, y, n, ms, so, co};
+  return rms_modulate2_impl(dt, H, eps, &a, 1, s);
+}
+
+mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps,
+                                const QkArgs* a, int n, hipStream_t s) {
   if (D != 64 && D != 128) {
     set_error("qk_norm_rope: head_dim=%d unsupported (64 or 128)", D);
     return MMDIT_E_UNSUPPORTED;
   }
+  QkBatch bt;
+  memset(&bt, 0, sizeof(bt));
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    if (a[i].n_rows == 0) continue;
+    QkProb& p = bt.p[k++];
+    p.qkv = a[i].qkv;
+    p.pos = a[i].pos;
+    p.g_q = a[i].g_q;
+    p.g_k = a[i].g_k;
+    p.n_rows = a[i].n_rows;
+  }
+  if (k == 0) return MMDIT_OK;
+  bt.split = bt.p[0].n_rows;
+  bt.heads = heads;
+  bt.eps = eps;
   // bands (frame, row, col) = (D/4, 3D/8, 3D/8) dims = (D/8, 3D/16, 3D/16) pairs
   RopeTab tab;
   const int widths[3] = {D / 4, 3 * D / 8, 3 * D / 8};
   int p = 0;
-  for (int a = 0; a < 3; ++a)
-    for (int j = 0; j < widths[a] / 2; ++j, ++p) {
-      tab.axis[p] = a;
-      tab.inv_freq[p] = (float)pow((double)theta, -2.0 * j / (double)widths[a]);
+  for (int ax = 0; ax < 3; ++ax)
+    for (int j = 0; j < widths[ax] / 2; ++j, ++p) {
+      tab.axis[p] = ax;
+      tab.inv_freq[p] = (float)pow((double)theta, -2.0 * j / (double)widths[ax]);
     }
   for (; p < 64; ++p) {
     tab.axis[p] = 0;
     tab.inv_freq[p] = 0.f;
   }
-  return dt == MMDIT_BF16 ? launch_qk<bf16>(n, heads, D, qkv, pos, gq, gk, tab, eps, s)
-                          : launch_qk<float>(n, heads, D, qkv, pos, gq, gk, tab, eps, s);
+  const int64_t total = bt.p[0].n_rows + (k > 1 ? bt.p[1].n_rows : 0);
+  return dt == MMDIT_BF16 ? launch_qk<bf16>(bt, total, D, tab, s) : launch_qk<float>(bt, total, D, tab, s);
+}
+
+mmdit_status qk_norm_rope_impl(mmdit_dtype dt, int64_t n, int32_t heads, int32_t D, void* qkv,
+                               const int32_t* pos, const float* gq, const float* gk, float theta,
+                               float eps, hipStream_t s) {
+  QkArgs a = {qkv, pos, gq, gk, n};
+  return qk_norm_rope2_impl(dt, heads, D, theta, eps, &a, 1, s);
 }
 
 mmdit_status temb_impl(mmdit_dtype dt, int32_t B, int32_t t_dim, const float* t, void* emb,
