@@ -124,13 +124,14 @@ def bench_sampler(steps, warmup):
     tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
     tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
     sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    sm.capture()                              # one pack = one HIP graph (~1,600 launches)
     for _ in range(warmup):
-        sm.run()
+        sm.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        sm.run()
+        sm.replay()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps

@@ -65,7 +65,7 @@ int next_event() {
 void timing_begin(hipStream_t s) {
   if (!g_timing) return;
   g_pending = next_event();
-  if (g_pending >= 0) hipEventRecord(g_events[g_pending], s);
+  if (g_pending >= 0) (void)hipEventRecord(g_events[g_pending], s);
 }
 
 mmdit_status launch_check(const char* kernel, hipStream_t s) {
@@ -73,7 +73,7 @@ mmdit_status launch_check(const char* kernel, hipStream_t s) {
   if (g_timing && g_pending >= 0) {
     int e = next_event();
     if (e >= 0) {
-      hipEventRecord(g_events[e], s);
+      (void)hipEventRecord(g_events[e], s);
       g_recs.push_back({kernel, g_pending, e});
     }
     g_pending = -1;
@@ -187,8 +187,10 @@ Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   return L;
 }
 
+// final layer: adaLN vectors, modulated target rows, split-K partials (up to 8)
 size_t final_ws(const mmdit_dims* d, const mmdit_pack_t* pk) {
-  return align256((size_t)pk->B * 2 * d->hidden * 4) + align256((size_t)pk->n_tgt * d->hidden * esize(d->dtype));
+  return align256((size_t)pk->B * 2 * d->hidden * 4) + align256((size_t)pk->n_tgt * d->hidden * esize(d->dtype)) +
+         align256((size_t)8 * pk->n_tgt * d->c_lat * 4);
 }
 
 LinearArgs mk(int64_t M, int32_t N, int32_t K, const void* A, const void* W, void* Y, int epi) {
@@ -619,6 +621,8 @@ mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_
                               d->eps, s));
   LinearArgs b = mk(pk->n_tgt, d->c_lat, H, hf, w_out, v, MMDIT_EPI_STORE);
   b.tag = "final_out";
+  b.partial = reinterpret_cast<float*>(static_cast<char*>(hf) + align256((size_t)pk->n_tgt * H * esize(d->dtype)));
+  b.partial_elems = (int64_t)8 * pk->n_tgt * d->c_lat;
   return linear(d->dtype, &b, 1, s);
 }
 

@@ -110,6 +110,8 @@ struct LinearArgs {
   const int32_t* seg;      // [M] sample of each row (gated residual)
   const char* tag;         // kernel-timing name of the launch (NULL: generic name)
   int32_t site;            // 1: MLP down projection (own kernel instantiation for profiling)
+  float* partial;          // optional float32 workspace for split-K (single problem)
+  int64_t partial_elems;
 };
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 

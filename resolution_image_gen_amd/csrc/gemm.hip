@@ -37,6 +37,9 @@ struct GemmBatch {
   const char* tag;
   int32_t site;
   int32_t xcd_remap;   // renumber tiles per XCD (off when grouped problems differ in K)
+  int32_t splitk;      // > 1: blockIdx.y takes 1/splitk of K and writes float32 partials
+  float* partial;      // [splitk][M][N] (single problem)
+  int64_t partial_elems;
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -265,14 +268,14 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     const int row = (wave + i * NW) * RPB + rr;
     bsrc[i] = W + (int64_t)(n0 + row) * P.K + ((pp ^ swz(row)) << 3);
   }
-  auto issue = [&](int kt) {
-    const int st = kt % NS, k0 = kt * BK;
+  auto issue = [&](int kt, int kbase) {
+    const int st = kt % NS, ke = (kbase + kt) * BK;
 #pragma unroll
     for (int i = 0; i < ABLK / NW; ++i)
-      load_lds16(asrc[i] + k0, As + st * BM * BK + (wave + i * NW) * 512);
+      load_lds16(asrc[i] + ke, As + st * BM * BK + (wave + i * NW) * 512);
 #pragma unroll
     for (int i = 0; i < BBLK / NW; ++i)
-      load_lds16(bsrc[i] + k0, Bs + st * BN * BK + (wave + i * NW) * 512);
+      load_lds16(bsrc[i] + ke, Bs + st * BN * BK + (wave + i * NW) * 512);
   };
   // wait until at most c stages of this wave's loads are still in flight
   auto wait_stages = [&](int c) {
@@ -291,15 +294,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // NS-stage ring: stage kt + NS - 1 is requested while stage kt is consumed
-  const int KT = P.K / BK;
+  // this block's k steps [k0, k0 + KT) (all of K unless split-K)
+  const int KTall = P.K / BK;
+  const int KT = KTall / bt.splitk;
+  const int k0 = blockIdx.y * KT;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < KT) issue(s);
+    if (s < KT) issue(s, k0);
   wait_stages(min(NS - 1, KT) - 1);
   __syncthreads();
   const int l32 = lane & 31, g = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, k0);
     const bf16* as = As + (kt % NS) * BM * BK;
     const bf16* bs = Bs + (kt % NS) * BN * BK;
 #pragma unroll
@@ -335,8 +341,26 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       if (m >= P.M) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) epi_store<bf16, EPI>(P, m, n0 + wn * TN * 32 + j * 32 + l32, acc[i][j][v]);
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * TN * 32 + j * 32 + l32;
+        if (bt.splitk > 1)
+          bt.partial[((int64_t)blockIdx.y * P.M + m) * P.N + n] = acc[i][j][v];
+        else
+          epi_store<bf16, EPI>(P, m, n, acc[i][j][v]);
+      }
     }
+}
+
+// Sums the split-K partials in a fixed order and applies the epilogue.
+template <int EPI>
+__global__ void splitk_reduce_kernel(GemmBatch bt) {
+  const GemmProb& P = bt.p[0];
+  const int64_t total = P.M * P.N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < bt.splitk; ++s) acc += bt.partial[s * total + i];
+    epi_store<bf16, EPI>(P, i / P.N, (int)(i % P.N), acc);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
@@ -357,12 +381,20 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  MMDIT_LAUNCH(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, bt);
+  MMDIT_LAUNCH(kern, dim3(tiles, bt.splitk), dim3(WM * WN * 64), lds, s, bt);
   static char name[80];
   if (!name[0])
     snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s,bk%d,s%d>", BM, BN, WM, WN, EPI,
              SILU ? ",silu" : "", SITE ? ",down" : "", BK, NS);
-  return launch_check(bt.tag ? bt.tag : name, s);
+  MMDIT_TRY(launch_check(bt.tag ? bt.tag : name, s));
+  if (bt.splitk > 1) {
+    const int64_t total = bt.p[0].M * bt.p[0].N;
+    const int64_t nb = cdiv(total, 256);
+    const int blocks = (int)(nb < 4096 ? nb : 4096);
+    MMDIT_LAUNCH(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, bt);
+    MMDIT_TRY(launch_check("splitk_reduce_kernel", s));
+  }
+  return MMDIT_OK;
 }
 
 int tile_override() {
@@ -377,12 +409,11 @@ int tile_override() {
 template <int EPI, bool SILU>
 mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   bool n256 = true, n128 = true;
-  int64_t t256 = 0, t128 = 0;
+  int64_t t256 = 0;
   for (int i = 0; i < bt.nprob; ++i) {
     n256 = n256 && (bt.p[i].N % 256 == 0);
     n128 = n128 && (bt.p[i].N % 128 == 0);
     t256 += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 256);
-    t128 += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 128);
   }
   int cfg = tile_override();
   bool thin = true;
@@ -407,6 +438,15 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
       case 1: return launch_mfma_cfg<128, 128, 2, 2, EPI, SILU, 1>(bt, s);
       default: return launch_mfma_cfg<128, 64, 2, 2, EPI, SILU, 1>(bt, s);
     }
+  }
+  if (cfg == 6 && bt.partial && bt.nprob == 1) {
+    // too few thin tiles to fill the chip: split K (deterministic, fixed-order sum)
+    const int tiles = (int)cdiv(bt.p[0].M, 32) * (bt.p[0].N / 128);
+    const int KT = bt.p[0].K / 64;
+    int sk = 1;
+    for (int c = 2; c <= 8; ++c)
+      if (KT % c == 0 && tiles * c <= 1024 && (int64_t)c * bt.p[0].M * bt.p[0].N <= bt.partial_elems) sk = c;
+    bt.splitk = sk;
   }
   switch (cfg) {
     case 6: return launch_mfma_cfg<32, 128, 1, 4, EPI, SILU>(bt, s);
@@ -515,6 +555,9 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.tag = pa[0].tag;
   bt.site = pa[0].site;
   bt.xcd_remap = (n < 2 || bt.p[0].K == bt.p[1].K) ? 1 : 0;
+  bt.splitk = 1;
+  bt.partial = pa[0].partial;
+  bt.partial_elems = pa[0].partial_elems;
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
   switch (epi * 2 + (silu ? 1 : 0)) {

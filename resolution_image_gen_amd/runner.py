@@ -185,6 +185,23 @@ class Sampler:
         self.tsched = torch.tensor([[t, t] for t in self.schedule[:-1]], dtype=torch.float32, device=device)
         self.ws = torch.empty(B.workspace_size(self.dims, self.pk), dtype=torch.uint8, device=device)
 
+    def capture(self):
+        """Record one whole pack (every launch of the 4 steps) as a HIP graph.
+
+        The library allocates nothing and records no memset, so the graph
+        replays the same launches on the same buffers."""
+        self.run()                           # first call sets kernel attributes
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        torch.cuda.synchronize()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()
+        return self.z
+
     def run(self, stream=None, on_step=None):
         W, pk, dm = self.W, self.pk, self.dims
         self.z.copy_(self.eps)               # z_1 = eps

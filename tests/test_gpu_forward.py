@@ -141,3 +141,29 @@ def test_packed_cfg_equals_two_pass_on_gpu():
     # the per-row work is independent of the pack, so the results agree to the last bit
     assert torch.equal(vp[:n], vc), (vp[:n].float() - vc.float()).abs().max()
     assert torch.equal(vp[n:], vu)
+
+
+def test_sampler_graph_replays_match_eager():
+    """A whole 4-step pack recorded as a HIP graph replays to the eager result,
+    every time, with eager work and synchronisations in between."""
+    from resolution_image_gen_amd import runner as R
+
+    wl = _small_sampler_wl("bf16", depth=2)
+    W = R.Weights(wl, recipe="stress")
+    h, w = wl.samples[0][:2]
+    eps = S.normal((h * w, wl.dims.c_lat), 1.0, "bf16", wl.name, "eps")
+    tau_c = S.text(24, wl.dims.d_txt, "bf16", wl.name, "tau_c")
+    tau_u = S.text(24, wl.dims.d_txt, "bf16", wl.name, "tau_u")
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    sm.run()
+    torch.cuda.synchronize()
+    eager = sm.z.clone()
+    sm.capture()
+    for i in range(4):
+        sm.z.zero_()
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        torch.cuda.synchronize()
+        sm.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sm.z, eager), f"replay {i} differs"
+        del junk
