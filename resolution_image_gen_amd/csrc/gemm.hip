@@ -11,6 +11,9 @@
 //   gemm_simt_kernel   float32 (and any shape the MFMA kernels reject)
 #include "common.h"
 
+#include <map>
+#include <string>
+
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -40,6 +43,10 @@ struct GemmBatch {
   int32_t splitk;      // > 1: blockIdx.y takes 1/splitk of K and writes float32 partials
   float* partial;      // [splitk][M][N] (single problem)
   int64_t partial_elems;
+  void* sk_ws;
+  size_t sk_ws_bytes;
+  int32_t tail_begin;  // > 0: blocks from here on compute K chunks of tiles tail_begin.. (last-round fill)
+  int32_t tail_chunks;
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -224,10 +231,13 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
-// SITE only separates the MLP down projection's instantiation from the output
-// projection's (same epilogue) so profiles can tell the two apart.
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
+// acc[TM][TN] += A[m0:m0+BM, K-steps kt0 .. kt0+nkt) W[n0:n0+BN, ...]^T for one
+// tile.  Operands go global -> LDS directly (global_load_lds_dwordx4: one wave
+// instruction fills 1 KB), NS-stage ring with one barrier per BK-deep step.
+// Ends with a barrier, so the caller may reuse the LDS right away.
+template <int BM, int BN, int WM, int WN, bool SILU, int BK, int NS>
+__device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, int kt0, int nkt, bf16* smem,
+                                         f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   constexpr int CPR = BK / 8;            // 16-B chunks per LDS row
@@ -235,16 +245,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int ABLK = BM / RPB, BBLK = BN / RPB;
   static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile / wave mismatch");
   constexpr int LPS = ABLK / NW + BBLK / NW;   // direct loads per stage per wave
-  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+  static_assert(NS <= 4 && 2 * LPS < 64, "vmcnt range");
   bf16* As = smem;                    // [NS][BM*BK]
   bf16* Bs = smem + NS * BM * BK;     // [NS][BN*BK]
-
-  int tile = bt.xcd_remap ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-  const GemmProb& P = pick(bt, tile);
-  int tm, tn;
-  grouped_tile(tile, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const bf16* A = static_cast<const bf16*>(P.A);
@@ -268,8 +271,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     const int row = (wave + i * NW) * RPB + rr;
     bsrc[i] = W + (int64_t)(n0 + row) * P.K + ((pp ^ swz(row)) << 3);
   }
-  auto issue = [&](int kt, int kbase) {
-    const int st = kt % NS, ke = (kbase + kt) * BK;
+  auto issue = [&](int kt) {
+    const int st = kt % NS, ke = (kt0 + kt) * BK;
 #pragma unroll
     for (int i = 0; i < ABLK / NW; ++i)
       load_lds16(asrc[i] + ke, As + st * BM * BK + (wave + i * NW) * 512);
@@ -283,29 +286,15 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     else if (c == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPS) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LPS) : "memory");
   };
-  static_assert(NS <= 4 && 2 * LPS < 64, "vmcnt range");
 
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // NS-stage ring: stage kt + NS - 1 is requested while stage kt is consumed
-  // this block's k steps [k0, k0 + KT) (all of K unless split-K)
-  const int KTall = P.K / BK;
-  const int KT = KTall / bt.splitk;
-  const int k0 = blockIdx.y * KT;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < KT) issue(s, k0);
-  wait_stages(min(NS - 1, KT) - 1);
+    if (s < nkt) issue(s);
+  wait_stages(min(NS - 1, nkt) - 1);
   __syncthreads();
   const int l32 = lane & 31, g = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NS - 1 < KT) issue(kt + NS - 1, k0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + NS - 1 < nkt) issue(kt + NS - 1);
     const bf16* as = As + (kt % NS) * BM * BK;
     const bf16* bs = Bs + (kt % NS) * BN * BK;
 #pragma unroll
@@ -330,10 +319,19 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     // stage kt + 1 must have landed (for every wave) before the next step
-    wait_stages(min(KT - 1, kt + NS - 1) - kt - 1);
+    wait_stages(min(nkt - 1, kt + NS - 1) - kt - 1);
     __syncthreads();
   }
-  // D[i][j] of a 32x32 tile: j = lane % 32, i = 8 * (v / 4) + 4 * (lane / 32) + v % 4
+}
+
+// Epilogue of one tile.  D[i][j] of a 32x32 MFMA tile: j = lane % 32,
+// i = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void store_tile(const GemmProb& P, int64_t m0, int n0,
+                                           const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], float* partial) {
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN, l32 = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -343,12 +341,90 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * TN * 32 + j * 32 + l32;
-        if (bt.splitk > 1)
-          bt.partial[((int64_t)blockIdx.y * P.M + m) * P.N + n] = acc[i][j][v];
+        if (partial)
+          partial[m * P.N + n] = acc[i][j][v];
         else
           epi_store<bf16, EPI>(P, m, n, acc[i][j][v]);
       }
     }
+}
+
+// SITE only separates the MLP down projection's instantiation from the output
+// projection's (same epilogue) so profiles can tell the two apart.
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+  int tile, chunk = -1;
+  if (bt.tail_begin > 0 && (int)blockIdx.x >= bt.tail_begin) {
+    const int u = blockIdx.x - bt.tail_begin;
+    tile = bt.tail_begin + u / bt.tail_chunks;
+    chunk = u % bt.tail_chunks;
+  } else {
+    const int full = bt.tail_begin > 0 ? bt.tail_begin : (int)gridDim.x;
+    tile = bt.xcd_remap ? xcd_tile(blockIdx.x, full) : (int)blockIdx.x;
+  }
+  const int gtile = tile;
+  const GemmProb& P = pick(bt, tile);
+  int tm, tn;
+  grouped_tile(tile, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (chunk >= 0) {
+    // last-round fill: K chunk `chunk` of this tile, float32 partial in thread order
+    const int KT = P.K / BK / bt.tail_chunks;
+    mma_tile<BM, BN, WM, WN, SILU, BK, NS>(P, m0, n0, chunk * KT, KT, smem, acc);
+    float* dst = bt.partial + ((int64_t)(gtile - bt.tail_begin) * bt.tail_chunks + chunk) * (BM * BN);
+    constexpr int NT = WM * WN * 64;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[((i * TN + j) * 16 + v) * NT + threadIdx.x] = acc[i][j][v];
+    return;
+  }
+  // this block's k steps (all of K unless split-K)
+  const int KT = P.K / BK / bt.splitk;
+  mma_tile<BM, BN, WM, WN, SILU, BK, NS>(P, m0, n0, blockIdx.y * KT, KT, smem, acc);
+  store_tile<BM, BN, WM, WN, EPI>(P, m0, n0, acc,
+                                  bt.splitk > 1 ? bt.partial + (int64_t)blockIdx.y * P.M * P.N : nullptr);
+}
+
+// Sums the K-chunk partials of the last-round tiles in chunk order and applies
+// the epilogue.  64 blocks of 256 threads per 256x256 tile; each thread
+// handles the 4 values the MFMA thread (of 512) at index t holds, t = this
+// thread's index within the 512-thread tile layout (see the producer).
+template <int EPI>
+__global__ void __launch_bounds__(256) tail_reduce_kernel(GemmBatch bt) {
+  constexpr int TM = 4, TN = 2, WN = 4, NT = 512;
+  const int local = blockIdx.x / 64;                 // tail tile
+  const int part = blockIdx.x % 64;
+  int tile = bt.tail_begin + local;
+  const GemmProb& P = pick(bt, tile);
+  int tm, tn;
+  grouped_tile(tile, (int)cdiv_d(P.M, 256), P.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256;
+  const int n0 = tn * 256;
+  const float* src = bt.partial + (int64_t)local * bt.tail_chunks * (256 * 256);
+  // element e of the thread-order layout: e = ((i * TN + j) * 16 + v) * NT + t
+  for (int e = part * 256 + threadIdx.x; e < 256 * 256; e += 64 * 256) {
+    const int t = e % NT, r = e / NT;
+    const int v = r % 16, ij = r / 16, j = ij % TN, i = ij / TN;
+    const int lane = t & 63, wave = t >> 6, wm = wave / WN, wn = wave % WN;
+    const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int n = n0 + wn * TN * 32 + j * 32 + (lane & 31);
+    float acc = 0.f;
+    for (int c = 0; c < bt.tail_chunks; ++c) acc += src[(int64_t)c * (256 * 256) + e];
+    if (m < P.M) epi_store<bf16, EPI>(P, m, n, acc);
+  }
 }
 
 // Sums the split-K partials in a fixed order and applies the epilogue.
@@ -406,6 +482,78 @@ int tile_override() {
   return v;
 }
 
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = -1;
+  }
+  return n;
+}
+
+// "<tag>.reduce": the tail reduction is timed under its GEMM's tag.
+const char* reduce_tag(const char* tag) {
+  static std::map<std::string, std::string> names;
+  if (!tag) return "tail_reduce_kernel";
+  auto it = names.find(tag);
+  if (it == names.end()) it = names.emplace(tag, std::string(tag) + ".reduce").first;
+  return it->second.c_str();
+}
+
+bool tailsplit_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_TAILSPLIT");
+    v = e ? atoi(e) : 1;
+  }
+  return v != 0;
+}
+
+// Last-round fill: when the 256x256 tiles leave the last round of CUs mostly
+// idle, the tiles of that round are split into S K-chunks (fixed split points)
+// whose float32 partials a second kernel sums in chunk order.
+template <int EPI, int SITE>
+mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
+  const int KT = bt.p[0].K / 64;
+  const int rounds = tiles / nb;
+  const int tail = tiles - rounds * nb;
+  int S = 1;
+  for (int c = 2; c <= 16; ++c)
+    if (KT % c == 0 && tail * c <= nb) S = c;
+  bt.tail_begin = rounds * nb;
+  bt.tail_chunks = S;
+  bt.partial = static_cast<float*>(bt.sk_ws);
+  const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16);
+  auto kern = gemm_mfma_kernel<256, 256, 2, 4, EPI, false, SITE>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                        "hipFuncSetAttribute(gemm_mfma_kernel)"));
+    attr_set = true;
+  }
+  MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(512), lds, s, bt);
+  static char name[80];
+  if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,4,epi%d%s,tailsplit>", EPI, SITE ? ",down" : "");
+  MMDIT_TRY(launch_check(bt.tag ? bt.tag : name, s));
+  MMDIT_LAUNCH(tail_reduce_kernel<EPI>, dim3(tail * 64), dim3(256), 0, s, bt);
+  return launch_check(reduce_tag(bt.tag), s);
+}
+
+// Worth it when the tiles fill at least one round and the last round is at
+// most half occupied (so every tail tile can take two or more CUs).
+bool want_tailsplit(const GemmBatch& bt, int64_t t256, bool n256, int& nb) {
+  nb = cu_count();
+  if (!tailsplit_enabled() || !bt.sk_ws || bt.sk_ws_bytes < sk_workspace_bytes() || !n256 || nb <= 0 ||
+      nb > kTailMaxBlocks)
+    return false;
+  for (int i = 1; i < bt.nprob; ++i)
+    if (bt.p[i].K != bt.p[0].K) return false;
+  const int64_t tail = t256 % nb;
+  return t256 >= nb && tail > 0 && tail * 2 <= nb && (bt.p[0].K / 64) % 2 == 0;
+}
+
 template <int EPI, bool SILU>
 mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   bool n256 = true, n128 = true;
@@ -425,6 +573,19 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
     else if (!n128) cfg = 0;
     else if (n256 && t256 >= 512) cfg = 3;
     else cfg = 1;
+  }
+  if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
+    int nb = 0;
+    if (tile_override() < 0 && want_tailsplit(bt, t256, n256, nb)) {
+      int tiles = 0;
+      for (int i = 0; i < bt.nprob; ++i) {
+        bt.p[i].tiles_n = bt.p[i].N / 256;
+        bt.p[i].tile_begin = tiles;
+        tiles += (int)(cdiv(bt.p[i].M, 256) * bt.p[i].tiles_n);
+      }
+      if (EPI == MMDIT_EPI_GATED_RES && bt.site == 1) return launch_tailsplit<EPI, 1>(bt, tiles, nb, s);
+      return launch_tailsplit<EPI, 0>(bt, tiles, nb, s);
+    }
   }
   if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
   if (cfg >= 1 && !n128) cfg = 0;
@@ -558,6 +719,10 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.splitk = 1;
   bt.partial = pa[0].partial;
   bt.partial_elems = pa[0].partial_elems;
+  bt.sk_ws = pa[0].sk_ws;
+  bt.sk_ws_bytes = pa[0].sk_ws_bytes;
+  bt.tail_begin = 0;
+  bt.tail_chunks = 1;
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
   switch (epi * 2 + (silu ? 1 : 0)) {

@@ -177,3 +177,33 @@ def test_block_full_size_sampled_rows(B, name):
                      want["x_out_img"] - x_img[i0 + irows], TOL[dtype])
         assert_close(f"delta_txt[b={b}]", got_t[t0 + trows] - x_txt[t0 + trows],
                      want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype])
+
+
+def test_block_last_round_split_ragged_tail():
+    """A pack whose four GEMMs span a few full rounds of 256x256 tiles on a
+    256-CU device and end in a short last round: those tiles are computed as
+    K chunks and summed by a second kernel.  The text rows (1218 of them) end
+    in a ragged tile that falls in that last round; every text row of the last
+    two samples and sampled image rows are checked."""
+    from resolution_image_gen_amd import binding as B
+
+    d = CF.Dims(hidden=1024, heads=8, head_dim=128, mlp=4096, c_lat=64, d_txt=1024)
+    dtype = "bf16"
+    samples = [(16, 24, 1, 29)] * 42
+    print("last-round split, 42 x (384 + 29) rows, hidden 1024", flush=True)
+    ref, nb, x_img, x_txt, c = _inputs(d, dtype, samples, "tailsplit", "stress")
+    _, _, xi, xt, _ = _run_block(B, d, dtype, samples, nb, x_img, x_txt, c)
+    got_i, got_t = to_np(xi), to_np(xt)
+    nbf = f64_block(nb)
+    rng = np.random.default_rng(1)
+    for b in (40, 41):
+        Ii = ref["cu_img"][b + 1] - ref["cu_img"][b]
+        Tt = ref["cu_txt"][b + 1] - ref["cu_txt"][b]
+        irows = np.unique(rng.integers(0, Ii, 16))
+        trows = np.arange(Tt)
+        want = OB.block_forward_rows(x_img, x_txt, c, nbf, ref, d.heads, b, irows, trows)
+        i0, t0 = ref["cu_img"][b], ref["cu_txt"][b]
+        assert_close(f"delta_img[b={b}]", got_i[i0 + irows] - x_img[i0 + irows],
+                     want["x_out_img"] - x_img[i0 + irows], TOL[dtype])
+        assert_close(f"delta_txt[b={b}]", got_t[t0 + trows] - x_txt[t0 + trows],
+                     want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype])
