@@ -231,13 +231,6 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
-    red = dom + ".reduce"
-    if red in kernels:
-        # the GEMM's last-round K chunks are summed by a second, small kernel:
-        # the whole operation's rate counts both launches
-        op_ms = avg_ms + kernels[red][0] / kernels[dom][1]
-        roof["reduce_us"] = round((op_ms - avg_ms) * 1e3, 2)
-        roof["frac_with_reduce"] = round(per_launch / (op_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
 
     table = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] / args.steps}
              for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][0])}

@@ -167,7 +167,7 @@ mmdit_status need(const void* p, const char* who, const char* name) {
 }
 
 struct Layout {
-  size_t mod_img, mod_txt, h, qkv, o, u, vt, sk, end;
+  size_t mod_img, mod_txt, h, qkv, o, u, vt, end;
 };
 
 Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -183,7 +183,6 @@ Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   L.o = o;       o = align256(o + N * H * es);
   L.u = o;       o = align256(o + N * (size_t)d->mlp * es);
   L.vt = o;      o = align256(o + (size_t)attention_vt_elems(pk, d->hidden) * es);
-  L.sk = o;      o = align256(o + (d->dtype == MMDIT_BF16 ? sk_workspace_bytes() : 0));
   L.end = o;
   return L;
 }
@@ -543,8 +542,6 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     LinearArgs a[2] = {mk(ni, 3 * H, H, h, w->img.w_qkv, qkv, MMDIT_EPI_STORE),
                        mk(nt, 3 * H, H, h_t, w->txt.w_qkv, qkv_t, MMDIT_EPI_STORE)};
     a[0].tag = "qkv_proj";
-    a[0].sk_ws = base + L.sk;
-    a[0].sk_ws_bytes = L.end - L.sk;
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
@@ -553,7 +550,7 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_theta, d->eps, q, 2, s));
   }
   // o = block-diagonal joint attention
-  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.sk - L.vt, s));
+  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s));
   // x += gate1 * (o W_o^T)
   {
     LinearArgs a[2] = {mk(ni, H, H, o, w->img.w_o, x_img, MMDIT_EPI_GATED_RES),
@@ -564,8 +561,6 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].seg = pk->seg_img;
     a[1].seg = pk->seg_txt;
     a[0].tag = "out_proj_gated";
-    a[0].sk_ws = base + L.sk;
-    a[0].sk_ws_bytes = L.end - L.sk;
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // h = rms(x)(1 + scale2) + shift2
@@ -579,8 +574,6 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     LinearArgs a[2] = {mk(ni, d->mlp, H, h, w->img.w_up, u, MMDIT_EPI_GELU),
                        mk(nt, d->mlp, H, h_t, w->txt.w_up, u_t, MMDIT_EPI_GELU)};
     a[0].tag = "mlp_up_gelu";
-    a[0].sk_ws = base + L.sk;
-    a[0].sk_ws_bytes = L.end - L.sk;
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // x += gate2 * (u W_down^T)
@@ -593,8 +586,6 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].seg = pk->seg_img;
     a[1].seg = pk->seg_txt;
     a[0].tag = "mlp_down_gated";
-    a[0].sk_ws = base + L.sk;
-    a[0].sk_ws_bytes = L.end - L.sk;
     a[0].site = 1;
     MMDIT_TRY(linear(dt, a, 2, s));
   }

@@ -112,13 +112,7 @@ struct LinearArgs {
   int32_t site;            // 1: MLP down projection (own kernel instantiation for profiling)
   float* partial;          // optional float32 workspace for split-K (single problem)
   int64_t partial_elems;
-  void* sk_ws;             // optional workspace for the last-round K split (sk_workspace_bytes())
-  size_t sk_ws_bytes;
 };
-// Workspace for the last-round split of grouped GEMMs: up to one 256x256
-// float32 partial tile per CU (kTailMaxBlocks CUs at most).
-constexpr int kTailMaxBlocks = 320;
-inline size_t sk_workspace_bytes() { return (size_t)kTailMaxBlocks * (256 * 256 * 4) + 256; }
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 
 // RMSNorm + adaLN modulate of up to two row sets in one launch.

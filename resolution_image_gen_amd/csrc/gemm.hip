@@ -11,9 +11,6 @@
 //   gemm_simt_kernel   float32 (and any shape the MFMA kernels reject)
 #include "common.h"
 
-#include <map>
-#include <string>
-
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -43,10 +40,8 @@ struct GemmBatch {
   int32_t splitk;      // > 1: blockIdx.y takes 1/splitk of K and writes float32 partials
   float* partial;      // [splitk][M][N] (single problem)
   int64_t partial_elems;
-  void* sk_ws;
-  size_t sk_ws_bytes;
-  int32_t tail_begin;  // > 0: blocks from here on compute K chunks of tiles tail_begin.. (last-round fill)
-  int32_t tail_chunks;
+  int32_t tail_begin;   // > 0: blocks from here on share the tiles tail_begin.. (last-round fill)
+  int32_t tail_chunks;  // blocks (sub-tiles) per last-round tile: 2, 4 or 8
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -377,54 +372,42 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (chunk >= 0) {
-    // last-round fill: K chunk `chunk` of this tile, float32 partial in thread order
-    const int KT = P.K / BK / bt.tail_chunks;
-    mma_tile<BM, BN, WM, WN, SILU, BK, NS>(P, m0, n0, chunk * KT, KT, smem, acc);
-    float* dst = bt.partial + ((int64_t)(gtile - bt.tail_begin) * bt.tail_chunks + chunk) * (BM * BN);
-    constexpr int NT = WM * WN * 64;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[((i * TN + j) * 16 + v) * NT + threadIdx.x] = acc[i][j][v];
-    return;
+  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 4) {
+    if (chunk >= 0) {
+      // last-round fill by sub-tiles: each block takes a 256x128, 128x128 or
+      // 64x128 part of the tile over the whole K (same per-element k order as
+      // a full tile, so the result does not depend on which round a row is in).
+      // The two smaller ones run a 4-stage ring in the same 128 KB of LDS.
+      static_assert(NS * (BM + BN) * BK >= 4 * (128 + 128) * BK, "LDS of the sub-tile ring");
+      const int KT = P.K / BK;
+      if (bt.tail_chunks == 2) {
+        f32x16 a2[4][1];
+        for (int v = 0; v < 16; ++v) a2[0][0][v] = a2[1][0][v] = a2[2][0][v] = a2[3][0][v] = 0.f;
+        mma_tile<256, 128, 2, 4, SILU, BK, NS>(P, m0, n0 + chunk * 128, 0, KT, smem, a2);
+        store_tile<256, 128, 2, 4, EPI>(P, m0, n0 + chunk * 128, a2, nullptr);
+      } else if (bt.tail_chunks == 4) {
+        const int64_t sm0 = m0 + (chunk >> 1) * 128;
+        if (sm0 >= P.M) return;
+        f32x16 a4[2][1];
+        for (int v = 0; v < 16; ++v) a4[0][0][v] = a4[1][0][v] = 0.f;
+        mma_tile<128, 128, 2, 4, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a4);
+        store_tile<128, 128, 2, 4, EPI>(P, sm0, n0 + (chunk & 1) * 128, a4, nullptr);
+      } else {
+        const int64_t sm0 = m0 + (chunk >> 1) * 64;
+        if (sm0 >= P.M) return;
+        f32x16 a8[1][1];
+        for (int v = 0; v < 16; ++v) a8[0][0][v] = 0.f;
+        mma_tile<64, 128, 2, 4, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a8);
+        store_tile<64, 128, 2, 4, EPI>(P, sm0, n0 + (chunk & 1) * 128, a8, nullptr);
+      }
+      return;
+    }
   }
   // this block's k steps (all of K unless split-K)
   const int KT = P.K / BK / bt.splitk;
   mma_tile<BM, BN, WM, WN, SILU, BK, NS>(P, m0, n0, blockIdx.y * KT, KT, smem, acc);
   store_tile<BM, BN, WM, WN, EPI>(P, m0, n0, acc,
                                   bt.splitk > 1 ? bt.partial + (int64_t)blockIdx.y * P.M * P.N : nullptr);
-}
-
-// Sums the K-chunk partials of the last-round tiles in chunk order and applies
-// the epilogue.  64 blocks of 256 threads per 256x256 tile; each thread
-// handles the 4 values the MFMA thread (of 512) at index t holds, t = this
-// thread's index within the 512-thread tile layout (see the producer).
-template <int EPI>
-__global__ void __launch_bounds__(256) tail_reduce_kernel(GemmBatch bt) {
-  constexpr int TM = 4, TN = 2, WN = 4, NT = 512;
-  const int local = blockIdx.x / 64;                 // tail tile
-  const int part = blockIdx.x % 64;
-  int tile = bt.tail_begin + local;
-  const GemmProb& P = pick(bt, tile);
-  int tm, tn;
-  grouped_tile(tile, (int)cdiv_d(P.M, 256), P.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 256;
-  const int n0 = tn * 256;
-  const float* src = bt.partial + (int64_t)local * bt.tail_chunks * (256 * 256);
-  // element e of the thread-order layout: e = ((i * TN + j) * 16 + v) * NT + t
-  for (int e = part * 256 + threadIdx.x; e < 256 * 256; e += 64 * 256) {
-    const int t = e % NT, r = e / NT;
-    const int v = r % 16, ij = r / 16, j = ij % TN, i = ij / TN;
-    const int lane = t & 63, wave = t >> 6, wm = wave / WN, wn = wave % WN;
-    const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    const int n = n0 + wn * TN * 32 + j * 32 + (lane & 31);
-    float acc = 0.f;
-    for (int c = 0; c < bt.tail_chunks; ++c) acc += src[(int64_t)c * (256 * 256) + e];
-    if (m < P.M) epi_store<bf16, EPI>(P, m, n, acc);
-  }
 }
 
 // Sums the split-K partials in a fixed order and applies the epilogue.
@@ -493,15 +476,7 @@ int cu_count() {
   return n;
 }
 
-// "<tag>.reduce": the tail reduction is timed under its GEMM's tag.
-const char* reduce_tag(const char* tag) {
-  static std::map<std::string, std::string> names;
-  if (!tag) return "tail_reduce_kernel";
-  auto it = names.find(tag);
-  if (it == names.end()) it = names.emplace(tag, std::string(tag) + ".reduce").first;
-  return it->second.c_str();
-}
-
+// env MMDIT_TAILSPLIT=0 turns the last-round sub-tiling off
 bool tailsplit_enabled() {
   static int v = -1;
   if (v < 0) {
@@ -511,20 +486,18 @@ bool tailsplit_enabled() {
   return v != 0;
 }
 
-// Last-round fill: when the 256x256 tiles leave the last round of CUs mostly
-// idle, the tiles of that round are split into S K-chunks (fixed split points)
-// whose float32 partials a second kernel sums in chunk order.
+// Last-round fill: when the 256x256 tiles leave the last round of CUs at
+// most half busy, each tile of that round is shared by S = 2, 4 or 8 blocks,
+// each computing a sub-tile over the whole K.
 template <int EPI, int SITE>
 mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
-  const int KT = bt.p[0].K / 64;
   const int rounds = tiles / nb;
   const int tail = tiles - rounds * nb;
   int S = 1;
-  for (int c = 2; c <= 16; ++c)
-    if (KT % c == 0 && tail * c <= nb) S = c;
+  for (int c = 2; c <= 8; c *= 2)
+    if (tail * c <= nb) S = c;
   bt.tail_begin = rounds * nb;
   bt.tail_chunks = S;
-  bt.partial = static_cast<float*>(bt.sk_ws);
   const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16);
   auto kern = gemm_mfma_kernel<256, 256, 2, 4, EPI, false, SITE>;
   static bool attr_set = false;
@@ -536,22 +509,16 @@ mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(512), lds, s, bt);
   static char name[80];
   if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,4,epi%d%s,tailsplit>", EPI, SITE ? ",down" : "");
-  MMDIT_TRY(launch_check(bt.tag ? bt.tag : name, s));
-  MMDIT_LAUNCH(tail_reduce_kernel<EPI>, dim3(tail * 64), dim3(256), 0, s, bt);
-  return launch_check(reduce_tag(bt.tag), s);
+  return launch_check(bt.tag ? bt.tag : name, s);
 }
 
-// Worth it when the tiles fill at least one round and the last round is at
-// most half occupied (so every tail tile can take two or more CUs).
-bool want_tailsplit(const GemmBatch& bt, int64_t t256, bool n256, int& nb) {
+// Worth it when the 256x256 tiles fill at least one round of CUs and the last
+// round is at most half occupied.
+bool want_tailsplit(int64_t t256, bool n256, int& nb) {
   nb = cu_count();
-  if (!tailsplit_enabled() || !bt.sk_ws || bt.sk_ws_bytes < sk_workspace_bytes() || !n256 || nb <= 0 ||
-      nb > kTailMaxBlocks)
-    return false;
-  for (int i = 1; i < bt.nprob; ++i)
-    if (bt.p[i].K != bt.p[0].K) return false;
+  if (!tailsplit_enabled() || !n256 || nb <= 0) return false;
   const int64_t tail = t256 % nb;
-  return t256 >= nb && tail > 0 && tail * 2 <= nb && (bt.p[0].K / 64) % 2 == 0;
+  return t256 >= nb && tail > 0 && tail * 2 <= nb;
 }
 
 template <int EPI, bool SILU>
@@ -576,7 +543,7 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   }
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
     int nb = 0;
-    if (tile_override() < 0 && want_tailsplit(bt, t256, n256, nb)) {
+    if (tile_override() < 0 && want_tailsplit(t256, n256, nb)) {
       int tiles = 0;
       for (int i = 0; i < bt.nprob; ++i) {
         bt.p[i].tiles_n = bt.p[i].N / 256;
@@ -719,8 +686,6 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.splitk = 1;
   bt.partial = pa[0].partial;
   bt.partial_elems = pa[0].partial_elems;
-  bt.sk_ws = pa[0].sk_ws;
-  bt.sk_ws_bytes = pa[0].sk_ws_bytes;
   bt.tail_begin = 0;
   bt.tail_chunks = 1;
   if (n == 0) return MMDIT_OK;

@@ -207,3 +207,29 @@ def test_block_last_round_split_ragged_tail():
                      want["x_out_img"] - x_img[i0 + irows], TOL[dtype])
         assert_close(f"delta_txt[b={b}]", got_t[t0 + trows] - x_txt[t0 + trows],
                      want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype])
+
+
+def test_block_sample_order_invariant_with_last_round_split():
+    """Shapes like the test above's (last-round sub-tiles on a 256-CU device):
+    reversing the samples moves rows between full tiles and shared last-round
+    tiles, and every row must still come out bitwise the same."""
+    from resolution_image_gen_amd import binding as B
+
+    d = CF.Dims(hidden=1024, heads=8, head_dim=128, mlp=4096, c_lat=64, d_txt=1024)
+    dtype = "bf16"
+    samples = [(16, 24, 1, 29)] * 40 + [(8, 8, 1, 7), (20, 20, 1, 300)]
+    print("sample order, 42 samples, hidden 1024", flush=True)
+    ref, nb, x_img, x_txt, c = _inputs(d, dtype, samples, "tailperm", "stress")
+    _, _, xi1, xt1, _ = _run_block(B, d, dtype, samples, nb, x_img, x_txt, c)
+    perm = list(range(len(samples)))[::-1]
+    cu_i, cu_t = ref["cu_img"], ref["cu_txt"]
+
+    def cat(a, cu):
+        return np.concatenate([a[cu[p]:cu[p + 1]] for p in perm])
+
+    _, _, xi2, xt2, _ = _run_block(B, d, dtype, [samples[p] for p in perm], nb, cat(x_img, cu_i),
+                                   cat(x_txt, cu_t), c[perm])
+    a, b = xi1.cpu(), xi2.cpu()
+    assert torch.equal(torch.cat([a[cu_i[p]:cu_i[p + 1]] for p in perm]), b), "image rows differ after permuting"
+    a, b = xt1.cpu(), xt2.cpu()
+    assert torch.equal(torch.cat([a[cu_t[p]:cu_t[p + 1]] for p in perm]), b[:cu_t[-1]]), "text rows differ"
