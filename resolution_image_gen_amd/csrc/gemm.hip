@@ -319,6 +319,157 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
   }
 }
 
+// 256x256 tile on 4 waves (2x2, 128x128 each, accumulators in AGPRs) with an
+// explicitly pipelined schedule.  Per BK=64 step a wave issues 64 MFMAs in
+// four k-slices of 16; the fragments of slice kk+1 are read from LDS while
+// the MFMAs of slice kk issue, each slice starting with MFMAs so its reads
+// have a whole slice to land.  The next stage's 16 direct-to-LDS loads issue
+// between the first slice's MFMAs; the stage switch (own loads landed, then a
+// barrier) sits after the first quarter of the last slice, so the next
+// stage's first fragments are read while the rest of that slice issues.
+// The order of the MFMAs on each accumulator is the same as mma_tile's.
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One BK=64 step of mma_tile_pipe.  NEXT: a next stage exists (switch to it
+// at the end of this step); ISSUE: the stage after that exists (its loads
+// issue right after the switch, into the buffer this step just finished).
+template <bool NEXT, bool ISSUE>
+__device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
+                                          const uint32_t (&offb)[8], int kt, bf16* smem, const lds_char* lsm,
+                                          const uint32_t (&aoff)[4], const uint32_t (&boff)[4],
+                                          bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4], f32x16 (&acc)[4][4]) {
+  constexpr int BM = 256, BK = 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int st = kt & 1;
+  // slice kk of stage s into fragment buffer buf (odd row blocks use the
+  // offset of slice kk ^ 2: their swizzle differs in bit 2)
+  auto read_slice = [&](int s, int kk, int buf) {
+    const uint32_t so = s * BM * BK * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[buf][j] = *reinterpret_cast<const lds_bf16x8*>(lsm + boff[(j & 1) ? (kk ^ 2) : kk] + so + j * 4096);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[buf][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? (kk ^ 2) : kk] + so + i * 4096);
+  };
+  auto mma_rows = [&](int buf, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  // slices 0..2: MFMAs on one fragment buffer while the next slice is read
+  // into the other; each slice starts with MFMAs
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    read_slice(st, kk + 1, (kk + 1) & 1);
+    mma_rows(kk & 1, 0, 4);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // slice 3: a quarter of its MFMAs, the stage switch, then the loads of the
+  // stage after next and the next stage's slice 0 while the rest issue
+  mma_rows(1, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NEXT) {
+    // vmcnt(0) lgkmcnt(0): this wave's loads of the next stage have landed
+    // and its reads of stage st are done; after the barrier the same holds
+    // for every wave, so stage st's buffer may be refilled
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ISSUE) {
+      const char* ab = reinterpret_cast<const char*>(atile + (kt + 2) * BK);
+      const char* bb = reinterpret_cast<const char*>(btile + (kt + 2) * BK);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        load_lds16(ab + offa[i], smem + st * BM * BK + (wave + i * 4) * 512);
+        load_lds16(bb + offb[i], smem + 2 * BM * BK + st * BM * BK + (wave + i * 4) * 512);
+      }
+    }
+    read_slice(st ^ 1, 0, 0);
+  }
+  mma_rows(1, 1, 4);
+  if constexpr (NEXT) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc += A[m0:m0+256, :] W[n0:n0+256, :]^T over the whole K (K % 64 == 0).
+// 256 threads; smem holds two stages of both operands (128 KB).  Ends with a
+// barrier, so the caller may reuse the LDS right away.
+__device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int n0, bf16* smem,
+                                              f32x16 (&acc)[4][4]) {
+  constexpr int BM = 256, BK = 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rr = lane >> 3, pp = lane & 7;
+  const int row0 = wave * 8 + rr;
+  const bf16* atile = static_cast<const bf16*>(P.A) + m0 * P.lda;
+  const bf16* btile = static_cast<const bf16*>(P.W) + (int64_t)n0 * P.K;
+  // per-lane byte offsets of the 8 one-KB blocks this wave fills per operand
+  // and stage (rows past M load row M-1; never stored)
+  uint32_t offa[8], offb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = row0 + i * 32;
+    const int64_t m = (m0 + row < P.M) ? row : P.M - 1 - m0;
+    offa[i] = (uint32_t)((m * P.lda + ((pp ^ swz8(row)) << 3)) * 2);
+    offb[i] = (uint32_t)(((int64_t)row * P.K + ((pp ^ swz8(row)) << 3)) * 2);
+  }
+  const lds_char* lsm = (const lds_char*)(smem);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int ra = wm * 128 + l32, rb = wn * 128 + l32;
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    aoff[kk] = ra * 128 + (((kk * 2 + g) ^ swz8(ra)) << 4);
+    boff[kk] = 2 * BM * BK * 2 + rb * 128 + (((kk * 2 + g) ^ swz8(rb)) << 4);
+  }
+  bf16x8 fa[2][4], fb[2][4];
+  const int KT = P.K / BK;
+  auto issue = [&](int k) {
+    const int s2 = k & 1;
+    const char* ab = reinterpret_cast<const char*>(atile + k * BK);
+    const char* bb = reinterpret_cast<const char*>(btile + k * BK);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      load_lds16(ab + offa[i], smem + s2 * BM * BK + (wave + i * 4) * 512);
+      load_lds16(bb + offb[i], smem + 2 * BM * BK + s2 * BM * BK + (wave + i * 4) * 512);
+    }
+  };
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (KT > 1) issue(1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    fb[0][j] = *reinterpret_cast<const lds_bf16x8*>(lsm + boff[(j & 1) ? 2 : 0] + j * 4096);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
+  for (int kt = 0; kt < KT - 2; ++kt)
+    pipe_step<true, true>(atile, btile, offa, offb, kt, smem, lsm, aoff, boff, fa, fb, acc);
+  if (KT > 1) pipe_step<true, false>(atile, btile, offa, offb, KT - 2, smem, lsm, aoff, boff, fa, fb, acc);
+  pipe_step<false, false>(atile, btile, offa, offb, KT - 1, smem, lsm, aoff, boff, fa, fb, acc);
+  __syncthreads();
+}
+
 // Epilogue of one tile.  D[i][j] of a 32x32 MFMA tile: j = lane % 32,
 // i = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -372,36 +523,48 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 4) {
+  if constexpr (BM == 256 && BN == 256 && WM == 2 && (WN == 4 || WN == 2)) {
     if (chunk >= 0) {
       // last-round fill by sub-tiles: each block takes a 256x128, 128x128 or
       // 64x128 part of the tile over the whole K (same per-element k order as
       // a full tile, so the result does not depend on which round a row is in).
       // The two smaller ones run a 4-stage ring in the same 128 KB of LDS.
       static_assert(NS * (BM + BN) * BK >= 4 * (128 + 128) * BK, "LDS of the sub-tile ring");
+      constexpr int T2 = 128 / WN / 32;   // 128-wide sub-tiles: MFMA columns per wave
       const int KT = P.K / BK;
       if (bt.tail_chunks == 2) {
-        f32x16 a2[4][1];
-        for (int v = 0; v < 16; ++v) a2[0][0][v] = a2[1][0][v] = a2[2][0][v] = a2[3][0][v] = 0.f;
-        mma_tile<256, 128, 2, 4, SILU, BK, NS>(P, m0, n0 + chunk * 128, 0, KT, smem, a2);
-        store_tile<256, 128, 2, 4, EPI>(P, m0, n0 + chunk * 128, a2, nullptr);
+        f32x16 a2[4][T2];
+        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < T2; ++j)
+            for (int v = 0; v < 16; ++v) a2[i][j][v] = 0.f;
+        mma_tile<256, 128, WM, WN, SILU, BK, NS>(P, m0, n0 + chunk * 128, 0, KT, smem, a2);
+        store_tile<256, 128, WM, WN, EPI>(P, m0, n0 + chunk * 128, a2, nullptr);
       } else if (bt.tail_chunks == 4) {
         const int64_t sm0 = m0 + (chunk >> 1) * 128;
         if (sm0 >= P.M) return;
-        f32x16 a4[2][1];
-        for (int v = 0; v < 16; ++v) a4[0][0][v] = a4[1][0][v] = 0.f;
-        mma_tile<128, 128, 2, 4, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a4);
-        store_tile<128, 128, 2, 4, EPI>(P, sm0, n0 + (chunk & 1) * 128, a4, nullptr);
+        f32x16 a4[2][T2];
+        for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < T2; ++j)
+            for (int v = 0; v < 16; ++v) a4[i][j][v] = 0.f;
+        mma_tile<128, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a4);
+        store_tile<128, 128, WM, WN, EPI>(P, sm0, n0 + (chunk & 1) * 128, a4, nullptr);
       } else {
         const int64_t sm0 = m0 + (chunk >> 1) * 64;
         if (sm0 >= P.M) return;
-        f32x16 a8[1][1];
-        for (int v = 0; v < 16; ++v) a8[0][0][v] = 0.f;
-        mma_tile<64, 128, 2, 4, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a8);
-        store_tile<64, 128, 2, 4, EPI>(P, sm0, n0 + (chunk & 1) * 128, a8, nullptr);
+        f32x16 a8[1][T2];
+        for (int j = 0; j < T2; ++j)
+          for (int v = 0; v < 16; ++v) a8[0][j][v] = 0.f;
+        mma_tile<64, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a8);
+        store_tile<64, 128, WM, WN, EPI>(P, sm0, n0 + (chunk & 1) * 128, a8, nullptr);
       }
       return;
     }
+  }
+  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2) {
+    // whole K, explicitly pipelined 4-wave mainloop (no split-K on this shape)
+    mma_tile_pipe(P, m0, n0, smem, acc);
+    store_tile<BM, BN, WM, WN, EPI>(P, m0, n0, acc, nullptr);
+    return;
   }
   // this block's k steps (all of K unless split-K)
   const int KT = P.K / BK / bt.splitk;
@@ -476,6 +639,20 @@ int cu_count() {
   return n;
 }
 
+// The 256x256 tile: 4 = 4 waves with the pipelined mainloop, 3 = 8 waves
+// with the plain ring.  Measured on MI355X at the block's shapes, the 4-wave
+// tile wins for the gated-residual projections (N = hidden) and the 8-wave
+// tile for the wide QKV and MLP-up outputs.  env MMDIT_GEMM_BIG=3|4 forces one.
+int big_tile_cfg(int epi) {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_GEMM_BIG");
+    v = e ? atoi(e) : 0;
+  }
+  if (v == 3 || v == 4) return v;
+  return epi == MMDIT_EPI_GATED_RES ? 4 : 3;
+}
+
 // env MMDIT_TAILSPLIT=0 turns the last-round sub-tiling off
 bool tailsplit_enabled() {
   static int v = -1;
@@ -489,7 +666,7 @@ bool tailsplit_enabled() {
 // Last-round fill: when the 256x256 tiles leave the last round of CUs at
 // most half busy, each tile of that round is shared by S = 2, 4 or 8 blocks,
 // each computing a sub-tile over the whole K.
-template <int EPI, int SITE>
+template <int EPI, int SITE, int WN>
 mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   const int rounds = tiles / nb;
   const int tail = tiles - rounds * nb;
@@ -499,16 +676,16 @@ mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   bt.tail_begin = rounds * nb;
   bt.tail_chunks = S;
   const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16);
-  auto kern = gemm_mfma_kernel<256, 256, 2, 4, EPI, false, SITE>;
+  auto kern = gemm_mfma_kernel<256, 256, 2, WN, EPI, false, SITE>;
   static bool attr_set = false;
   if (!attr_set) {
     MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(512), lds, s, bt);
+  MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(2 * WN * 64), lds, s, bt);
   static char name[80];
-  if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,4,epi%d%s,tailsplit>", EPI, SITE ? ",down" : "");
+  if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,%d,epi%d%s,tailsplit>", WN, EPI, SITE ? ",down" : "");
   return launch_check(bt.tag ? bt.tag : name, s);
 }
 
@@ -538,7 +715,7 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
     // of 256 CUs; below that the 128x128 tile (two per CU) quantizes better
     if (thin) cfg = 6;
     else if (!n128) cfg = 0;
-    else if (n256 && t256 >= 512) cfg = 3;
+    else if (n256 && t256 >= 512) cfg = big_tile_cfg(EPI);
     else cfg = 1;
   }
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
@@ -550,8 +727,10 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
         bt.p[i].tile_begin = tiles;
         tiles += (int)(cdiv(bt.p[i].M, 256) * bt.p[i].tiles_n);
       }
-      if (EPI == MMDIT_EPI_GATED_RES && bt.site == 1) return launch_tailsplit<EPI, 1>(bt, tiles, nb, s);
-      return launch_tailsplit<EPI, 0>(bt, tiles, nb, s);
+      const bool w4 = big_tile_cfg(EPI) == 4;
+      if (EPI == MMDIT_EPI_GATED_RES && bt.site == 1)
+        return w4 ? launch_tailsplit<EPI, 1, 2>(bt, tiles, nb, s) : launch_tailsplit<EPI, 1, 4>(bt, tiles, nb, s);
+      return w4 ? launch_tailsplit<EPI, 0, 2>(bt, tiles, nb, s) : launch_tailsplit<EPI, 0, 4>(bt, tiles, nb, s);
     }
   }
   if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
