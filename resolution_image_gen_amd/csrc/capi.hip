@@ -367,7 +367,6 @@ mmdit_status mmdit_embed(const mmdit_dims* d, const void* w_in, const void* w_tx
   MMDIT_TRY(check_pack(pk, who));
   LinearArgs a[2];
   int n = 0;
-  // the text problem (K = d_txt) goes first: its long-K tiles are scheduled before the short image ones
   if (pk->n_txt > 0) {
     MMDIT_TRY(need(w_txt, who, "w_txt"));
     MMDIT_TRY(need(tau, who, "tau"));
@@ -381,13 +380,13 @@ mmdit_status mmdit_embed(const mmdit_dims* d, const void* w_in, const void* w_tx
     a[n++] = mk(pk->n_img, d->hidden, d->c_lat, zt, w_in, x_img, MMDIT_EPI_STORE);
   }
   if (n == 0) return MMDIT_OK;
-  a[0].tag = "embed";
-  // group the two streams only when they can share a kernel configuration
-  if (n == 2 && (d->c_lat % 64 != 0)) {
-    MMDIT_TRY(linear(d->dtype, &a[0], 1, (hipStream_t)stream));
-    return linear(d->dtype, &a[1], 1, (hipStream_t)stream);
+  // two launches: the long-K text GEMM and the short-K (epilogue-bound) image
+  // GEMM each get their own tile configuration
+  for (int i = 0; i < n; ++i) {
+    a[i].tag = a[i].K == d->c_lat && a[i].Y == x_img ? "embed_img" : "embed_txt";
+    MMDIT_TRY(linear(d->dtype, &a[i], 1, (hipStream_t)stream));
   }
-  return linear(d->dtype, a, n, (hipStream_t)stream);
+  return MMDIT_OK;
 }
 
 mmdit_status mmdit_rms_modulate(const mmdit_dims* d, int64_t n_rows, const void* x, const int32_t* row_map,

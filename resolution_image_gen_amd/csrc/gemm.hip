@@ -1,12 +1,15 @@
 // Dense linears of the block: Y = op(A) W^T with fused epilogues (store,
-// float32 store, exact GELU, gated residual x += gate[seg] * y).
+// float32 store, erf-form GELU, gated residual x += gate[seg] * y).
 //
 // The gating and residual chain is fused into the producing GEMM (blog
 // close-reading 2.2(3): norm, RoPE, gating and residual chains are fused so
 // intermediates stay on chip).  Three kernels:
 //   gemm_mfma_kernel   bf16, MFMA 32x32x16, LDS double buffer, grouped over
-//                      up to two problems (image and text streams) per launch
-//   gemm_skinny_kernel bf16, M <= 16 (adaLN modulation, conditioning MLP):
+//                      up to two problems (image and text streams) per launch;
+//                      the 256x256 tile runs 4 waves on an explicitly
+//                      pipelined mainloop (mma_tile_pipe)
+//   gemm_skinny_kernel bf16, M <= 16, K % 256 == 0 (adaLN modulation,
+//                      conditioning MLP):
 //                      weight-streaming MFMA 16x16x32 with split-K over waves
 //   gemm_simt_kernel   float32 (and any shape the MFMA kernels reject)
 #include "common.h"
@@ -127,61 +130,74 @@ __device__ __forceinline__ bf16x8 silu8(bf16x8 x) {
 }
 
 // ---------------------------------------------------------------- skinny
-// One block per 16 output columns; 4 waves split K into 4 contiguous ranges;
-// fixed-order reduction of the 4 partial tiles through LDS.
-template <int EPI, bool SILU>
-__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmBatch bt) {
+// One block per 16 * NG output columns (NG MFMA column groups sharing each A
+// fragment, so A is read once per 16 * NG weight rows); 8 waves split K into
+// 8 contiguous ranges (K % 256 == 0), each keeping U A loads and U * NG
+// weight loads (16 B each) in flight before its MFMAs; fixed-order reduction
+// of the 8 partial tiles through LDS.  NG = 4 for wide outputs, NG = 1 when
+// that would leave too few blocks to fill the chip.
+template <int EPI, bool SILU, int NG>
+__global__ void __launch_bounds__(512) gemm_skinny_kernel(GemmBatch bt) {
+  constexpr int U = NG == 1 ? 8 : 4;
   int tile = blockIdx.x;
   const GemmProb& P = pick(bt, tile);
-  const int n0 = tile * 16;
+  const int n0 = tile * 16 * NG;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kq = P.K >> 2;
+  const int kq = P.K >> 3;
   const int kbeg = wave * kq;
   const int r16 = lane & 15, kofs = (lane >> 4) * 8;
-  const bf16* A = static_cast<const bf16*>(P.A) + (int64_t)r16 * P.lda + kofs;
-  const bf16* W = static_cast<const bf16*>(P.W) + (int64_t)(n0 + r16) * P.K + kofs;
+  const bf16* A = static_cast<const bf16*>(P.A) + (int64_t)r16 * P.lda + kofs + kbeg;
+  const bf16* W = static_cast<const bf16*>(P.W) + (int64_t)(n0 + r16) * P.K + kofs + kbeg;
+  const int64_t gstride = (int64_t)16 * P.K;   // next column group's weight rows
   const bool arow = r16 < P.M;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nit = kq >> 5;
   int it = 0;
-  // four independent 16-B weight loads in flight per lane before the MFMAs
-  for (; it + 4 <= nit; it += 4) {
-    bf16x8 b[4], a[4];
+  for (; it + U <= nit; it += U) {
+    bf16x8 b[U][NG], a[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) b[u] = *reinterpret_cast<const bf16x8*>(W + kbeg + (it + u) * 32);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int g = 0; g < NG; ++g) b[u][g] = *reinterpret_cast<const bf16x8*>(W + g * gstride + (it + u) * 32);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       a[u] = bf16x8{};
-      if (arow) a[u] = *reinterpret_cast<const bf16x8*>(A + kbeg + (it + u) * 32);
+      if (arow) a[u] = *reinterpret_cast<const bf16x8*>(A + (it + u) * 32);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (SILU) a[u] = silu8(a[u]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][g], acc[g], 0, 0, 0);
     }
   }
   for (; it < nit; ++it) {
-    const int k = kbeg + it * 32;
-    bf16x8 b = *reinterpret_cast<const bf16x8*>(W + k);
     bf16x8 a = {};
     if (arow) {
-      a = *reinterpret_cast<const bf16x8*>(A + k);
+      a = *reinterpret_cast<const bf16x8*>(A + it * 32);
       if (SILU) a = silu8(a);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-  }
-  __shared__ f32x4 red[4][64];
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    f32x4 s = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s += red[w][lane];
+    for (int g = 0; g < NG; ++g) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(W + g * gstride + it * 32);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[g], 0, 0, 0);
+    }
+  }
+  __shared__ f32x4 red[8][NG][64];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) red[wave][g][lane] = acc[g];
+  __syncthreads();
+  for (int g = wave; g < NG; g += 8) {
+    f32x4 s = red[0][g][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) s += red[w][g][lane];
     // D[i][j]: j = lane % 16 (output column), i = 4 * (lane / 16) + v (row)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * (lane >> 4) + v;
-      if (m < P.M) epi_store<bf16, EPI>(P, m, n0 + r16, s[v]);
+      if (m < P.M) epi_store<bf16, EPI>(P, m, n0 + g * 16 + r16, s[v]);
     }
   }
 }
@@ -639,18 +655,16 @@ int cu_count() {
   return n;
 }
 
-// The 256x256 tile: 4 = 4 waves with the pipelined mainloop, 3 = 8 waves
-// with the plain ring.  Measured on MI355X at the block's shapes, the 4-wave
-// tile wins for the gated-residual projections (N = hidden) and the 8-wave
-// tile for the wide QKV and MLP-up outputs.  env MMDIT_GEMM_BIG=3|4 forces one.
-int big_tile_cfg(int epi) {
+// The 256x256 tile: 4 = 4 waves with the pipelined mainloop (default; it
+// measured ahead of or level with the 8-wave tile at every block shape),
+// 3 = 8 waves with the plain ring (env MMDIT_GEMM_BIG=3).
+int big_tile_cfg(int /*epi*/) {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("MMDIT_GEMM_BIG");
-    v = e ? atoi(e) : 0;
+    v = (e && atoi(e) == 3) ? 3 : 4;
   }
-  if (v == 3 || v == 4) return v;
-  return epi == MMDIT_EPI_GATED_RES ? 4 : 3;
+  return v;
 }
 
 // env MMDIT_TAILSPLIT=0 turns the last-round sub-tiling off
@@ -702,7 +716,9 @@ template <int EPI, bool SILU>
 mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   bool n256 = true, n128 = true;
   int64_t t256 = 0;
+  int kmax = 0;
   for (int i = 0; i < bt.nprob; ++i) {
+    kmax = bt.p[i].K > kmax ? bt.p[i].K : kmax;
     n256 = n256 && (bt.p[i].N % 256 == 0);
     n128 = n128 && (bt.p[i].N % 128 == 0);
     t256 += cdiv(bt.p[i].M, 256) * (bt.p[i].N / 256);
@@ -711,11 +727,12 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   bool thin = true;
   for (int i = 0; i < bt.nprob; ++i) thin = thin && bt.p[i].N <= 256 && bt.p[i].N % 128 == 0 && bt.p[i].K >= 1024;
   if (cfg < 0) {
-    // measured on MI355X: the 8-wave 256x256 tile wins once it fills two rounds
-    // of 256 CUs; below that the 128x128 tile (two per CU) quantizes better
+    // measured on MI355X: the 256x256 tile wins once it fills two rounds of
+    // 256 CUs, and for short K (where the epilogue dominates) at any count;
+    // otherwise the 128x128 tile (two per CU) quantizes better
     if (thin) cfg = 6;
     else if (!n128) cfg = 0;
-    else if (n256 && t256 >= 512) cfg = big_tile_cfg(EPI);
+    else if (n256 && (t256 >= 512 || kmax <= 256)) cfg = big_tile_cfg(EPI);
     else cfg = 1;
   }
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
@@ -768,14 +785,24 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
 
 template <int EPI, bool SILU>
 mmdit_status launch_skinny(GemmBatch& bt, hipStream_t s) {
+  int64_t ncols = 0;
+  bool n64 = true;
+  for (int i = 0; i < bt.nprob; ++i) {
+    ncols += bt.p[i].N;
+    n64 = n64 && bt.p[i].N % 64 == 0;
+  }
+  const int ng = (n64 && ncols >= 32768) ? 4 : 1;
   int tiles = 0;
   for (int i = 0; i < bt.nprob; ++i) {
-    bt.p[i].tiles_n = bt.p[i].N / 16;
+    bt.p[i].tiles_n = bt.p[i].N / (16 * ng);
     bt.p[i].tile_begin = tiles;
     tiles += bt.p[i].tiles_n;
   }
   if (tiles == 0) return MMDIT_OK;
-  MMDIT_LAUNCH((gemm_skinny_kernel<EPI, SILU>), dim3(tiles), dim3(256), 0, s, bt);
+  if (ng == 4)
+    MMDIT_LAUNCH((gemm_skinny_kernel<EPI, SILU, 4>), dim3(tiles), dim3(512), 0, s, bt);
+  else
+    MMDIT_LAUNCH((gemm_skinny_kernel<EPI, SILU, 1>), dim3(tiles), dim3(512), 0, s, bt);
   static char name[64];
   if (!name[0]) snprintf(name, sizeof(name), "gemm_skinny_kernel<epi%d%s>", EPI, SILU ? ",silu" : "");
   return launch_check(bt.tag ? bt.tag : name, s);
@@ -855,7 +882,7 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
-    skinny = skinny && a.M <= 16 && a.K % 128 == 0 && a.N % 16 == 0 && a.lda % 8 == 0;
+    skinny = skinny && a.M <= 16 && a.K % 256 == 0 && a.N % 16 == 0 && a.lda % 8 == 0;
     mfma = mfma && a.K % 64 == 0 && a.N % 64 == 0 && a.lda % 8 == 0;
   }
   bt.nprob = n;
