@@ -27,23 +27,50 @@ struct RmsProb {
 };
 struct RmsBatch {
   RmsProb p[2];
-  int64_t split;   // rows of problem 0
+  int64_t split;     // rows of problem 0
+  int64_t bsplit;    // blocks of problem 0 (= ceil(split / 8))
   int32_t H;
   float eps;
 };
 
+// A block of 8 waves handles 8 consecutive rows of one problem, one row per
+// wave.  The (1 + scale) and shift vectors of the block's first sample are
+// staged once in LDS (float32, 2 * H) and shared by the waves whose row
+// belongs to that sample (rows are grouped by sample, so that is nearly
+// always all 8); a row of another sample reads its vectors from memory.  This
+// cuts the float32 modulation traffic from 8 H bytes per row to H bytes.
+constexpr int kRmsRows = 8;
+
 template <typename T, int NCH>
-__global__ void __launch_bounds__(256) rms_modulate_kernel(RmsBatch bt) {
-  const int lane = threadIdx.x & 63;
-  int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const RmsProb& P = i < bt.split ? bt.p[0] : bt.p[1];
-  if (i >= bt.split) i -= bt.split;
-  if (i >= P.n_rows) return;
+__global__ void __launch_bounds__(64 * kRmsRows) rms_modulate_kernel(RmsBatch bt) {
+  extern __shared__ float mods[];   // [2][H]: 1 + scale, shift
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t blk = blockIdx.x;
+  const bool second = blk >= bt.bsplit;
+  const RmsProb& P = second ? bt.p[1] : bt.p[0];
+  if (second) blk -= bt.bsplit;
+  const int64_t r0 = blk * kRmsRows;
   const int H = bt.H;
+  const int nch = H >> 3;
+  const int64_t src0 = P.row_map ? (int64_t)P.row_map[r0] : r0;
+  const int seg0 = P.seg[src0];
+  {
+    const float* mrow = P.mod + (int64_t)seg0 * P.mod_stride;
+    for (int c = threadIdx.x; c < H / 4; c += 64 * kRmsRows) {
+      f32x4 sc = *reinterpret_cast<const f32x4*>(mrow + P.scale_off + c * 4);
+      f32x4 sh = *reinterpret_cast<const f32x4*>(mrow + P.shift_off + c * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = 1.0f + sc[e];
+      *reinterpret_cast<f32x4*>(mods + c * 4) = sc;
+      *reinterpret_cast<f32x4*>(mods + H + c * 4) = sh;
+    }
+  }
+  __syncthreads();
+  const int64_t i = r0 + wave;
+  if (i >= P.n_rows) return;
   const T* x = static_cast<const T*>(P.x);
   T* y = static_cast<T*>(P.y);
   const int64_t src = P.row_map ? (int64_t)P.row_map[i] : i;
-  const int nch = H >> 3;
   float v[NCH][8];
   float ss = 0.f;
 #pragma unroll
@@ -57,37 +84,46 @@ __global__ void __launch_bounds__(256) rms_modulate_kernel(RmsBatch bt) {
   }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)H + bt.eps);
-  const float* mrow = P.mod + (int64_t)P.seg[src] * P.mod_stride;
-  const float* shift = mrow + P.shift_off;
-  const float* scale = mrow + P.scale_off;
+  const int sg = P.seg[src];
+  const float* mrow = P.mod + (int64_t)sg * P.mod_stride;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = lane + 64 * j;
     if (c < nch) {
-      float sh[8], sc[8], o[8];
-      Vec8<float>::load(shift + c * 8, sh);
-      Vec8<float>::load(scale + c * 8, sc);
+      float sc1[8], sh[8], o[8];
+      if (sg == seg0) {
+        Vec8<float>::load(mods + c * 8, sc1);
+        Vec8<float>::load(mods + H + c * 8, sh);
+      } else {
+        Vec8<float>::load(mrow + P.shift_off + c * 8, sh);
+        Vec8<float>::load(mrow + P.scale_off + c * 8, sc1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = v[j][e] * r * (1.0f + sc[e]) + sh[e];
+        for (int e = 0; e < 8; ++e) sc1[e] = 1.0f + sc1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[j][e] * r * sc1[e] + sh[e];
       Vec8<T>::store(y + i * H + c * 8, o);
     }
   }
 }
 
 template <typename T>
-mmdit_status launch_rms(const RmsBatch& bt, int64_t total, hipStream_t s) {
-  dim3 g((unsigned)cdiv(total, 4)), b(256);
+mmdit_status launch_rms(RmsBatch& bt, int64_t total, hipStream_t s) {
+  bt.bsplit = cdiv(bt.split, kRmsRows);
+  const int64_t blocks = bt.bsplit + cdiv(total - bt.split, kRmsRows);
+  dim3 g((unsigned)blocks), b(64 * kRmsRows);
+  const size_t shm = (size_t)2 * bt.H * sizeof(float);
   const int nch = bt.H / 8;
   if (nch <= 64)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 1>), g, b, 0, s, bt);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 1>), g, b, shm, s, bt);
   else if (nch <= 128)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 2>), g, b, 0, s, bt);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 2>), g, b, shm, s, bt);
   else if (nch <= 256)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 4>), g, b, 0, s, bt);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 4>), g, b, shm, s, bt);
   else if (nch <= 384)
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 6>), g, b, 0, s, bt);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 6>), g, b, shm, s, bt);
   else
-    MMDIT_LAUNCH((rms_modulate_kernel<T, 16>), g, b, 0, s, bt);
+    MMDIT_LAUNCH((rms_modulate_kernel<T, 16>), g, b, shm, s, bt);
   return launch_check("rms_modulate_kernel", s);
 }
 
