@@ -49,6 +49,36 @@ def kernel_work(wl):
     }
 
 
+# HBM bytes per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# scaled by a plain copy's counter reading (profiles/traffic.json); valid only
+# while the kernel's sources are unchanged since the counters were taken.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("resolution_image_gen_amd/csrc/gemm.hip", "resolution_image_gen_amd/csrc/common.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(tag, workload):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != tag or rec.get("workload") != workload:
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def step_flops(wl):
     from resolution_image_gen_amd.configs import block_flops
 
@@ -231,6 +261,7 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+    roof["traffic"] = measured_traffic(dom, wl.name)
 
     table = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] / args.steps}
              for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][0])}
