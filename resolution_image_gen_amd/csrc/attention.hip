@@ -217,19 +217,28 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
     const int d = (wave + 4 * i) * 8 + (lane >> 3);
     vsrc[i] = vt + ((int64_t)head * D + d) * njp + pstart + (((lane & 7) ^ vsw(d)) << 3);
   }
+  // K row of joint key j: text row t0 + j for j < Tb, image row i0 + j - Tb
+  // after it; both bases are offset so that base + j * 3H addresses key j
+  // (byte offsets fit 32 bits: checked on the host).  The chunk swizzle of
+  // this lane's K rows does not depend on the tile.
+  const uint32_t rowb = 3u * (uint32_t)a.H * 2u;
+  const char* ktxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.qkv_txt) + (int64_t)t0 * 3 * a.H + a.H + head * D);
+  const char* kimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.qkv_img) + ((int64_t)i0 - Tb) * 3 * a.H + a.H + head * D);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kswc[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) kswc[i] = ((kp ^ ksw<D>((wave + 4 * i) * KROWS + kr)) << 4);
   auto issue = [&](int32_t kv0, int st) {
     bf16* ks = smem + st * STAGE;
     bf16* vs = ks + BKV * D;
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int blk = wave + 4 * i;
-      const int r = blk * KROWS + kr;
-      int32_t key = kv0 + r;
-      if (key >= L) key = L - 1;            // masked in the scores
-      load_lds16(joint_row<bf16>(a, key, Tb, t0, i0) + a.H + head * D + ((kp ^ ksw<D>(r)) << 3), ks + blk * 512);
+      const int blk = wu + 4 * i;
+      const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);   // keys past L are masked in the scores
+      load_lds16((key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]), ks + blk * 512);
     }
 #pragma unroll
-    for (int i = 0; i < VB; ++i) load_lds16(vsrc[i] + kv0, vs + (wave + 4 * i) * 512);
+    for (int i = 0; i < VB; ++i) load_lds16(vsrc[i] + kv0, vs + (wu + 4 * i) * 512);
   };
 
   f32x16 oacc[DT];
@@ -366,8 +375,8 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
       set_error("mmdit_attention: workspace needs %zu bytes, got %zu", (size_t)vt_elems * 2, ws_bytes);
       return MMDIT_E_WORKSPACE;
     }
-    if (vt_elems / a.H > INT32_MAX) {
-      set_error("mmdit_attention: padded pack too long");
+    if (vt_elems / a.H > INT32_MAX || (double)pk->max_joint * 3.0 * a.H * 2.0 >= 2147483648.0) {
+      set_error("mmdit_attention: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31)");
       return MMDIT_E_UNSUPPORTED;
     }
     const int32_t njp = (int32_t)(vt_elems / a.H);

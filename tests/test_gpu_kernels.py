@@ -33,6 +33,10 @@ CASES = {
     "ragged_bf16_d128": (CF.B4, "bf16", [(16, 16, 1, 128), (9, 13, 1, 77), (5, 3, 2, 0), (1, 1, 1, 1)]),
     "ragged_bf16_d64": (CF.Dims(hidden=512, heads=8, head_dim=64, mlp=2048, c_lat=64, d_txt=512), "bf16",
                         [(11, 7, 2, 19), (4, 4, 1, 64), (1, 2, 1, 0)]),
+    # long samples: many 64-key tiles per query block, ragged last tiles
+    "long_bf16_d128": (CF.B4, "bf16", [(48, 50, 1, 37), (40, 52, 1, 100), (3, 5, 1, 7)]),
+    "long_bf16_d64": (CF.Dims(hidden=512, heads=8, head_dim=64, mlp=2048, c_lat=64, d_txt=512), "bf16",
+                      [(50, 44, 1, 19), (21, 30, 2, 33)]),
 }
 
 
