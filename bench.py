@@ -8,9 +8,13 @@ Default workload: the 256^2-stage pack, 16 samples x (16x16 latent grid +
 128 text tokens), hidden 3072, 24 x 128 heads, MLP 12288, bf16.
 
 Prints ONE JSON line.  `value` is whole-step token throughput (image + text
-tokens per second); the line also carries the block's TFLOP/s against the
-bf16 MFMA peak, the roofline of the dominant kernel (timed live with hipEvents
-over the timed region) and the CPU oracle timed on a bounded sample.
+tokens per second) over K eagerly launched steps bracketed by hipEvents;
+`graph_ms_per_step` is the same step replayed from a HIP graph.  A second pass
+of K steps brackets every launch with hipEvents on its stream (that would add
+~9% to the step if done in the first pass): it gives the per-kernel table and
+the roofline of the dominant kernel.  The line also carries the block's
+TFLOP/s against the bf16 MFMA peak and the CPU oracle timed on a bounded
+sample.
 """
 
 import argparse
@@ -185,6 +189,7 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=16, help="samples of the pack the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -230,7 +235,6 @@ def main():
 
     # timed region (hipEvents on the launch stream bracket the whole region)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    B.timing_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
@@ -239,9 +243,31 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # the same step replayed from a HIP graph (launch overhead removed)
+    graph_ms = None
+    if not args.no_graph:
+        tf.capture()
+        for _ in range(2):
+            tf.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            tf.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        del tf.graph
+
+    # per-kernel times: every launch bracketed by hipEvents on its stream
+    B.timing_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        tf.run()
+    torch.cuda.synchronize()
     kernels = B.timing_report()
     B.timing_enable(False)
-    ms_step = e0.elapsed_time(e1) / args.steps
 
     n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
     blk, wrap = step_flops(wl)
@@ -295,6 +321,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "block_tflop_per_step": round(blk / 1e12, 4),
         "wall_s_timed": round(wall, 3),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "roofline": roof,
         "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
     }

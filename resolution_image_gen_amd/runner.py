@@ -151,6 +151,20 @@ class TrainForward:
         B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
         B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, stream)
 
+    def capture(self):
+        """Record one whole training forward (every launch) as a HIP graph."""
+        self.run()                           # first call sets kernel attributes
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        torch.cuda.synchronize()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()
+        return self.loss
+
     def _repack(self, stream):
         # rebuild the ids of the pack in place (same buffers, same samples)
         pk = self.pk
