@@ -511,6 +511,67 @@ __device__ __forceinline__ void store_tile(const GemmProb& P, int64_t m0, int n0
     }
 }
 
+// Epilogue of the 4-wave 256x256 tile through LDS: each half of the tile
+// (128 rows, float32, 128 KB) is written to LDS by the two waves that own it,
+// then all 256 threads apply the epilogue to 8 consecutive columns at a time,
+// so every global access (the output, and for the gated residual the x row
+// and the gate vector) is a 16- or 32-byte vector access instead of a 2- or
+// 4-byte one per element.  Same per-element arithmetic as epi_store.
+template <int EPI>
+__device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, int n0, const f32x16 (&acc)[4][4],
+                                               bf16* smem) {
+  float* T = reinterpret_cast<float*>(smem);   // [128][256]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+            T[r * 256 + wn * 128 + j * 32 + l32] = acc[i][j][v];
+          }
+    }
+    __syncthreads();
+    for (int e = tid; e < 128 * 32; e += 256) {
+      const int r = e >> 5, ch = e & 31;
+      const int64_t m = m0 + half * 128 + r;
+      if (m >= P.M) continue;
+      const int n = n0 + ch * 8;
+      float a[8];
+      *reinterpret_cast<f32x4*>(a) = *reinterpret_cast<const f32x4*>(T + r * 256 + ch * 8);
+      *reinterpret_cast<f32x4*>(a + 4) = *reinterpret_cast<const f32x4*>(T + r * 256 + ch * 8 + 4);
+      if constexpr (EPI == MMDIT_EPI_STORE_F32) {
+        float* y = static_cast<float*>(P.Y) + m * P.ldy + n;
+        *reinterpret_cast<f32x4*>(y) = *reinterpret_cast<const f32x4*>(a);
+        *reinterpret_cast<f32x4*>(y + 4) = *reinterpret_cast<const f32x4*>(a + 4);
+      } else {
+        bf16* y = static_cast<bf16*>(P.Y) + m * P.ldy + n;
+        float o[8];
+        if constexpr (EPI == MMDIT_EPI_STORE) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = a[k];
+        } else if constexpr (EPI == MMDIT_EPI_GELU) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = gelu_f(a[k]);
+        } else {
+          float xv[8], gv[8];
+          Vec8<bf16>::load(y, xv);
+          Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + n, gv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
+        }
+        Vec8<bf16>::store(y, o);
+      }
+    }
+  }
+}
+
 // SITE only separates the MLP down projection's instantiation from the output
 // projection's (same epilogue) so profiles can tell the two apart.
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
@@ -579,7 +640,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2) {
     // whole K, explicitly pipelined 4-wave mainloop (no split-K on this shape)
     mma_tile_pipe(P, m0, n0, smem, acc);
-    store_tile<BM, BN, WM, WN, EPI>(P, m0, n0, acc, nullptr);
+    store_tile_lds<EPI>(P, m0, n0, acc, smem);
     return;
   }
   // this block's k steps (all of K unless split-K)
