@@ -347,10 +347,11 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// One BK=64 step of mma_tile_pipe.  NEXT: a next stage exists (switch to it
-// at the end of this step); ISSUE: the stage after that exists (its loads
-// issue right after the switch, into the buffer this step just finished).
-template <bool NEXT, bool ISSUE>
+// One BK=64 step of mma_tile_pipe.  NEXT: a next stage exists: its loads
+// issue between the MFMAs of slice 0 (into the buffer the previous step
+// finished, which every wave left behind at the previous barrier) and the
+// step ends by switching to it.
+template <bool NEXT>
 __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
                                           const uint32_t (&offb)[8], int kt, bf16* smem, const lds_char* lsm,
                                           const uint32_t (&aoff)[4], const uint32_t (&boff)[4],
@@ -381,43 +382,45 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   // into the other; each slice starts with MFMAs
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
+    if constexpr (NEXT) {
+      if (kk == 0) {
+        const char* ab = reinterpret_cast<const char*>(atile + (kt + 1) * BK);
+        const char* bb = reinterpret_cast<const char*>(btile + (kt + 1) * BK);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          load_lds16(ab + offa[i], smem + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
+          load_lds16(bb + offb[i], smem + 2 * BM * BK + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
+        }
+      }
+    }
     read_slice(st, kk + 1, (kk + 1) & 1);
     mma_rows(kk & 1, 0, 4);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      if (NEXT && kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // slice 3: a quarter of its MFMAs, the stage switch, then the loads of the
-  // stage after next and the next stage's slice 0 while the rest issue
+  // slice 3: a quarter of its MFMAs, the stage switch, then the next stage's
+  // slice 0 while the rest issue
   mma_rows(1, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NEXT) {
     // vmcnt(0) lgkmcnt(0): this wave's loads of the next stage have landed
     // and its reads of stage st are done; after the barrier the same holds
-    // for every wave, so stage st's buffer may be refilled
+    // for every wave, so stage st's buffer may be refilled next step
     __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ISSUE) {
-      const char* ab = reinterpret_cast<const char*>(atile + (kt + 2) * BK);
-      const char* bb = reinterpret_cast<const char*>(btile + (kt + 2) * BK);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        load_lds16(ab + offa[i], smem + st * BM * BK + (wave + i * 4) * 512);
-        load_lds16(bb + offb[i], smem + 2 * BM * BK + st * BM * BK + (wave + i * 4) * 512);
-      }
-    }
     read_slice(st ^ 1, 0, 0);
   }
   mma_rows(1, 1, 4);
   if constexpr (NEXT) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if constexpr (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
@@ -472,17 +475,15 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
   issue(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if (KT > 1) issue(1);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     fb[0][j] = *reinterpret_cast<const lds_bf16x8*>(lsm + boff[(j & 1) ? 2 : 0] + j * 4096);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
-  for (int kt = 0; kt < KT - 2; ++kt)
-    pipe_step<true, true>(atile, btile, offa, offb, kt, smem, lsm, aoff, boff, fa, fb, acc);
-  if (KT > 1) pipe_step<true, false>(atile, btile, offa, offb, KT - 2, smem, lsm, aoff, boff, fa, fb, acc);
-  pipe_step<false, false>(atile, btile, offa, offb, KT - 1, smem, lsm, aoff, boff, fa, fb, acc);
+  for (int kt = 0; kt < KT - 1; ++kt)
+    pipe_step<true>(atile, btile, offa, offb, kt, smem, lsm, aoff, boff, fa, fb, acc);
+  pipe_step<false>(atile, btile, offa, offb, KT - 1, smem, lsm, aoff, boff, fa, fb, acc);
   __syncthreads();
 }
 
@@ -745,9 +746,15 @@ template <int EPI, int SITE, int WN>
 mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   const int rounds = tiles / nb;
   const int tail = tiles - rounds * nb;
+  static int smax = -1;
+  if (smax < 0) {
+    const char* e = getenv("MMDIT_TAIL_MAXS");
+    smax = e ? atoi(e) : 8;
+  }
   int S = 1;
-  for (int c = 2; c <= 8; c *= 2)
+  for (int c = 2; c <= smax && c <= 8; c *= 2)
     if (tail * c <= nb) S = c;
+  if (S == 1) S = 2;
   bt.tail_begin = rounds * nb;
   bt.tail_chunks = S;
   const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16);
@@ -955,6 +962,7 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.partial_elems = pa[0].partial_elems;
   bt.tail_begin = 0;
   bt.tail_chunks = 1;
+
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
   switch (epi * 2 + (silu ? 1 : 0)) {
