@@ -263,7 +263,7 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
   const int wm = wave / WN, wn = wave % WN;
   const bf16* A = static_cast<const bf16*>(P.A);
   const bf16* W = static_cast<const bf16*>(P.W);
-  auto swz = [](int r) { return CPR == 8 ? swz8(r) : ((r >> 2) & 3); };
+  auto swz = [](int r) { return CPR == 16 ? (r & 15) : CPR == 8 ? swz8(r) : ((r >> 2) & 3); };
 
   // per-lane source of each 1-KB block this wave fills: row rr = lane / CPR of
   // the block, LDS chunk position p = lane % CPR holds global chunk p ^ swz(row)
@@ -606,7 +606,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       // last-round fill by sub-tiles: each block takes a 256x128, 128x128 or
       // 64x128 part of the tile over the whole K (same per-element k order as
       // a full tile, so the result does not depend on which round a row is in).
-      // The two smaller ones run a 4-stage ring in the same 128 KB of LDS.
+      // The two smaller ones step 128 deep in k when K allows (half the
+      // barriers, the same k order), otherwise a 4-stage ring of 64-deep
+      // steps, in the same 128 KB of LDS.
       static_assert(NS * (BM + BN) * BK >= 4 * (128 + 128) * BK, "LDS of the sub-tile ring");
       constexpr int T2 = 128 / WN / 32;   // 128-wide sub-tiles: MFMA columns per wave
       const int KT = P.K / BK;
@@ -624,7 +626,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
         for (int i = 0; i < 2; ++i)
           for (int j = 0; j < T2; ++j)
             for (int v = 0; v < 16; ++v) a4[i][j][v] = 0.f;
-        mma_tile<128, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a4);
+        if (P.K % 128 == 0)
+          mma_tile<128, 128, WM, WN, SILU, 128, 2>(P, sm0, n0 + (chunk & 1) * 128, 0, P.K / 128, smem, a4);
+        else
+          mma_tile<128, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a4);
         store_tile<128, 128, WM, WN, EPI>(P, sm0, n0 + (chunk & 1) * 128, a4, nullptr);
       } else {
         const int64_t sm0 = m0 + (chunk >> 1) * 64;
@@ -632,7 +637,11 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
         f32x16 a8[1][T2];
         for (int j = 0; j < T2; ++j)
           for (int v = 0; v < 16; ++v) a8[0][j][v] = 0.f;
-        mma_tile<64, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a8);
+        // 128-deep k steps (half the barriers) when K allows; same k order
+        if (P.K % 128 == 0)
+          mma_tile<64, 128, WM, WN, SILU, 128, 2>(P, sm0, n0 + (chunk & 1) * 128, 0, P.K / 128, smem, a8);
+        else
+          mma_tile<64, 128, WM, WN, SILU, BK, 4>(P, sm0, n0 + (chunk & 1) * 128, 0, KT, smem, a8);
         store_tile<64, 128, WM, WN, EPI>(P, sm0, n0 + (chunk & 1) * 128, a8, nullptr);
       }
       return;
@@ -796,11 +805,14 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   for (int i = 0; i < bt.nprob; ++i) thin = thin && bt.p[i].N <= 256 && bt.p[i].N % 128 == 0 && bt.p[i].K >= 1024;
   if (cfg < 0) {
     // measured on MI355X: the 256x256 tile wins once it fills two rounds of
-    // 256 CUs, and for short K (where the epilogue dominates) at any count;
-    // otherwise the 128x128 tile (two per CU) quantizes better
+    // 256 CUs (or one round at least 70% full), and for short K (where the
+    // epilogue dominates) at any count; otherwise the 128x128 tile (two per
+    // CU) quantizes better.  Between one and two rounds the last-round split
+    // below applies.
     if (thin) cfg = 6;
     else if (!n128) cfg = 0;
-    else if (n256 && (t256 >= 512 || kmax <= 256)) cfg = big_tile_cfg(EPI);
+    else if (n256 && (t256 >= 512 || kmax <= 256 || (t256 * 10 >= cu_count() * 7 && t256 <= cu_count())))
+      cfg = big_tile_cfg(EPI);
     else cfg = 1;
   }
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
