@@ -54,6 +54,18 @@ __global__ void __launch_bounds__(64 * kRmsRows) rms_modulate_kernel(RmsBatch bt
   const int nch = H >> 3;
   const int64_t src0 = P.row_map ? (int64_t)P.row_map[r0] : r0;
   const int seg0 = P.seg[src0];
+  // this wave's row is loaded first, so its latency overlaps the staging
+  const int64_t i = r0 + wave;
+  const bool live = i < P.n_rows;
+  const T* x = static_cast<const T*>(P.x);
+  T* y = static_cast<T*>(P.y);
+  const int64_t src = live ? (P.row_map ? (int64_t)P.row_map[i] : i) : src0;
+  float v[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nch) Vec8<T>::load(x + src * H + c * 8, v[j]);
+  }
   {
     const float* mrow = P.mod + (int64_t)seg0 * P.mod_stride;
     for (int c = threadIdx.x; c < H / 4; c += 64 * kRmsRows) {
@@ -66,18 +78,12 @@ __global__ void __launch_bounds__(64 * kRmsRows) rms_modulate_kernel(RmsBatch bt
     }
   }
   __syncthreads();
-  const int64_t i = r0 + wave;
-  if (i >= P.n_rows) return;
-  const T* x = static_cast<const T*>(P.x);
-  T* y = static_cast<T*>(P.y);
-  const int64_t src = P.row_map ? (int64_t)P.row_map[i] : i;
-  float v[NCH][8];
+  if (!live) return;
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = lane + 64 * j;
     if (c < nch) {
-      Vec8<T>::load(x + src * H + c * 8, v[j]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
     }
