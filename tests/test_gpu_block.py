@@ -77,6 +77,13 @@ BLOCK_CASES = {
     "pack256_bf16": (CF.B4, "bf16", CF.WORKLOADS["pack256_bf16"].samples, "default"),
     "pack256_bf16_stress": (CF.B4, "bf16", CF.WORKLOADS["pack256_bf16"].samples, "stress"),
     "ragged_bf16_stress": (CF.B4, "bf16", [(13, 11, 2, 33), (7, 20, 1, 0), (1, 1, 1, 5)], "stress"),
+    # no text rows at all: single-problem launches, attention over image tokens only
+    "no_text_bf16_stress": (CF.B4, "bf16", [(9, 14, 1, 0), (5, 6, 2, 0), (1, 3, 1, 0)], "stress"),
+    # the largest pack the library takes (256 samples): per-sample offsets
+    # crossing the 64-sample chunks of the pack kernels, many tiny attention
+    # problems, per-sample adaLN vectors
+    "max_samples_bf16_stress": (CF.B4, "bf16", [(1 + i % 3, 1 + i % 4, 1 + (i % 7 == 0), i % 5) for i in range(256)],
+                                "stress"),
 }
 
 

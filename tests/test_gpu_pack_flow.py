@@ -17,6 +17,7 @@ SAMPLE_SETS = {
     "ragged": [(3, 5, 2, 7), (1, 1, 1, 0), (4, 2, 2, 3)],
     "no_text": [(7, 9, 1, 0)],
     "many": [(1 + i % 3, 2 + i % 5, 1 + i % 2, i % 4) for i in range(70)],
+    "max_samples": [(1 + i % 4, 1 + i % 3, 1 + i % 2, i % 6) for i in range(256)],
 }
 
 
