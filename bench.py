@@ -143,7 +143,9 @@ def cpu_baseline(wl, W, inputs, n_samples, min_seconds=10.0):
 
 def bench_sampler(steps, warmup):
     """ms per 4-step packed-CFG pack: cond + uncond (64x64 grid + 256 text
-    tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0."""
+    tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0.
+    The same sampler with the two CFG branches as separate forwards is timed
+    beside it, and both must end on the same bits."""
     import torch
 
     from resolution_image_gen_amd import configs as CF
@@ -157,19 +159,26 @@ def bench_sampler(steps, warmup):
     eps = S.normal((h * w, d.c_lat), 1.0, "bf16", wl.name, "eps")
     tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
     tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
+
+    def timed(sm):
+        sm.capture()                          # one pack = one HIP graph (~1,600 launches)
+        for _ in range(warmup):
+            sm.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            sm.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     sm = R.Sampler(wl, W, eps, tau_c, tau_u)
-    sm.capture()                              # one pack = one HIP graph (~1,600 launches)
-    for _ in range(warmup):
-        sm.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        sm.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = timed(sm)
+    sm2 = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
+    ms2 = timed(sm2)
     assert torch.isfinite(sm.z).all()
+    assert torch.equal(sm.z, sm2.z), "packed and two-pass CFG samplers disagree"
     from resolution_image_gen_amd.configs import block_flops
 
     blk = block_flops(d, sm.samples)[0] * wl.depth * (len(wl.schedule) - 1)
@@ -177,7 +186,9 @@ def bench_sampler(steps, warmup):
     return {"workload": f"{wl.name}: {wl.note}", "ms_per_4step_pack": round(ms, 2), "packs_timed": steps,
             "block_tokens_per_s": round(n * wl.depth * (len(wl.schedule) - 1) / (ms * 1e-3), 1),
             "block_tflops": round(blk / (ms * 1e-3) / 1e12, 1),
-            "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "two_pass_ms_per_4step_pack": round(ms2, 2),
+            "packed_speedup_vs_two_pass": round(ms2 / ms, 3)}
 
 
 def main():

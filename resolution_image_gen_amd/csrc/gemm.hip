@@ -804,14 +804,17 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
   bool thin = true;
   for (int i = 0; i < bt.nprob; ++i) thin = thin && bt.p[i].N <= 256 && bt.p[i].N % 128 == 0 && bt.p[i].K >= 1024;
   if (cfg < 0) {
-    // measured on MI355X: the 256x256 tile wins once it fills two rounds of
-    // 256 CUs (or one round at least 70% full), and for short K (where the
-    // epilogue dominates) at any count; otherwise the 128x128 tile (two per
-    // CU) quantizes better.  Between one and two rounds the last-round split
-    // below applies.
+    // measured on MI355X: a 128x128 tile (two per CU) runs at about 0.64 of
+    // the 256x256 tile's time per round of the chip, so the big tile wins
+    // unless the 128x128 grid needs clearly fewer rounds: from 1.5 rounds of
+    // 256 CUs up (1.5-2 rounds: 2 big rounds against 4 small ones), for one
+    // round at least 70% full, and for short K (where the epilogue dominates)
+    // at any count.  From one round up to 1.5 the last-round split below
+    // applies where the epilogue allows it.
     if (thin) cfg = 6;
     else if (!n128) cfg = 0;
-    else if (n256 && (t256 >= 512 || kmax <= 256 || (t256 * 10 >= cu_count() * 7 && t256 <= cu_count())))
+    else if (n256 && (2 * t256 > 3 * cu_count() || kmax <= 256 ||
+                      (t256 * 10 >= cu_count() * 7 && t256 <= cu_count())))
       cfg = big_tile_cfg(EPI);
     else cfg = 1;
   }
@@ -844,12 +847,14 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
     }
   }
   if (cfg == 6 && bt.partial && bt.nprob == 1) {
-    // too few thin tiles to fill the chip: split K (deterministic, fixed-order sum)
-    const int tiles = (int)cdiv(bt.p[0].M, 32) * (bt.p[0].N / 128);
+    // thin tiles alone cannot fill the chip: split K, partials summed in a
+    // fixed order.  The split depends on K (and the partial buffer, sized per
+    // row) only, never on M, so a row's result does not depend on how many
+    // rows share the launch.
     const int KT = bt.p[0].K / 64;
     int sk = 1;
     for (int c = 2; c <= 8; ++c)
-      if (KT % c == 0 && tiles * c <= 1024 && (int64_t)c * bt.p[0].M * bt.p[0].N <= bt.partial_elems) sk = c;
+      if (KT % c == 0 && (int64_t)c * bt.p[0].M * bt.p[0].N <= bt.partial_elems) sk = c;
     bt.splitk = sk;
   }
   switch (cfg) {

@@ -174,9 +174,17 @@ class TrainForward:
 
 class Sampler:
     """Packed-CFG Euler sampler: one pack [cond, uncond] of the same grid,
-    `steps` forwards through the block stack, CFG combine + Euler per step."""
+    `steps` forwards through the block stack, CFG combine + Euler per step.
 
-    def __init__(self, wl, W, eps, tau_c, tau_u, device="cuda", guidance=None, schedule=None):
+    two_pass=True samples the unpacked way, as the comparison point for
+    packing: per step one forward over the conditional sample and one over
+    the unconditional sample (each a one-sample pack), writing the two
+    velocities into the halves of the same buffer, then the same CFG combine
+    + Euler launch.  Every row's arithmetic is the same in both forms, so the
+    two give the same bits."""
+
+    def __init__(self, wl, W, eps, tau_c, tau_u, device="cuda", guidance=None, schedule=None,
+                 two_pass=False):
         self.wl, self.W = wl, W
         d = wl.dims
         self.dims = W.dims
@@ -198,6 +206,9 @@ class Sampler:
         self.v = torch.empty(self.pk.n_tgt, d.c_lat, **e)
         self.tsched = torch.tensor([[t, t] for t in self.schedule[:-1]], dtype=torch.float32, device=device)
         self.ws = torch.empty(B.workspace_size(self.dims, self.pk), dtype=torch.uint8, device=device)
+        self.two_pass = two_pass
+        if two_pass:   # one-sample packs; the two-sample workspace covers each
+            self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
 
     def capture(self):
         """Record one whole pack (every launch of the 4 steps) as a HIP graph.
@@ -216,16 +227,35 @@ class Sampler:
         self.graph.replay()
         return self.z
 
+    def _two_pass_forward(self, i, stream):
+        """Velocities of step i as two forwards: cond rows, then uncond rows."""
+        W, dm = self.W, self.dims
+        ib = it = 0
+        for pk in self.pk_one:
+            ni, nt = pk.n_img, pk.n_txt
+            B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i, :1], self.c[:1], self.ws, stream)
+            B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt[ib:ib + ni], self.tau[it:it + nt],
+                    self.x_img[:ni], self.x_txt[:nt], stream)
+            for bw in W.bw:
+                B.block_fwd(dm, bw, pk, self.c[:1], self.x_img[:ni], self.x_txt[:nt], self.ws, stream)
+            B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c[:1], self.x_img[:ni],
+                    self.v[ib:ib + ni], self.ws, stream)
+            ib, it = ib + ni, it + nt
+
     def run(self, stream=None, on_step=None):
         W, pk, dm = self.W, self.pk, self.dims
         self.z.copy_(self.eps)               # z_1 = eps
         B.rf_pack_latent(pk, self.z, 0, 1, self.zt, stream)
         for i in range(len(self.schedule) - 1):
-            B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i], self.c, self.ws, stream)
-            B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
-            for bw in W.bw:
-                B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
-            B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
+            if self.two_pass:
+                self._two_pass_forward(i, stream)
+            else:
+                B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i], self.c, self.ws, stream)
+                B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt,
+                        stream)
+                for bw in W.bw:
+                    B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
+                B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
             if on_step is not None:
                 on_step(i, self)
             B.rf_euler_step(pk, self.v, 0, 1, self.g, self.schedule[i], self.schedule[i + 1], self.z,

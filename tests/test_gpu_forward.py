@@ -143,6 +143,44 @@ def test_packed_cfg_equals_two_pass_on_gpu():
     assert torch.equal(vp[n:], vu)
 
 
+@pytest.mark.parametrize("case,tu_len", [("small", 24), ("small", 9), ("wide64x64", 256)])
+def test_two_pass_sampler_equals_packed(case, tu_len):
+    """The 4-step sampler with its CFG branches as two separate forwards per
+    step ends on the same bits as the packed one (eager and graph-replayed);
+    the unconditional text may be shorter than the conditional one.  The
+    64x64-grid case runs every launch at twice the rows in the packed form
+    (8,704 vs 4,352), where tile and split choices would differ if they
+    depended on the row count."""
+    from resolution_image_gen_amd import runner as R
+
+    if case == "small":
+        wl = _small_sampler_wl("bf16", depth=2)
+        W = R.Weights(wl, recipe="stress")
+    else:
+        d = CF.Dims(hidden=1024, heads=8, head_dim=128, mlp=4096, c_lat=128, d_txt=1024)
+        wl = CF.Workload("sampler_wide_bf16", d, "bf16", ((64, 64, 1, 256), (64, 64, 1, 256)), img_budget=8192,
+                         depth=2, steps=4, guidance=4.0)
+        W = R.Weights(wl, source="torch")
+    h, w = wl.samples[0][:2]
+    eps = S.normal((h * w, wl.dims.c_lat), 1.0, "bf16", wl.name, "eps2")
+    tau_c = S.text(24, wl.dims.d_txt, "bf16", wl.name, "tau_c2")
+    tau_u = S.text(tu_len, wl.dims.d_txt, "bf16", wl.name, "tau_u2")
+    print(f"two-pass sampler {case} tu={tu_len}", flush=True)
+    packed = R.Sampler(wl, W, eps, tau_c, tau_u)
+    two = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
+    packed.run()
+    two.run()
+    torch.cuda.synchronize()
+    assert torch.isfinite(packed.z).all()
+    assert torch.equal(packed.z, two.z), (packed.z - two.z).abs().max()
+    eager = two.z.clone()
+    two.capture()
+    two.z.zero_()
+    two.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(two.z, eager)
+
+
 def test_sampler_graph_replays_match_eager():
     """A whole 4-step pack recorded as a HIP graph replays to the eager result,
     every time, with eager work and synchronisations in between."""
