@@ -145,7 +145,8 @@ def bench_sampler(steps, warmup):
     """ms per 4-step packed-CFG pack: cond + uncond (64x64 grid + 256 text
     tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0.
     The same sampler with the two CFG branches as separate forwards is timed
-    beside it, and both must end on the same bits."""
+    beside it, and both must end on the same bits; then one 20-step pack
+    (uniform steps from 1 to 0) of the packed sampler."""
     import torch
 
     from resolution_image_gen_amd import configs as CF
@@ -160,8 +161,8 @@ def bench_sampler(steps, warmup):
     tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
     tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
 
-    def timed(sm):
-        sm.capture()                          # one pack = one HIP graph (~1,600 launches)
+    def timed(sm, steps=steps):
+        sm.capture()                          # one pack = one HIP graph (~1,600 launches at 4 steps)
         for _ in range(warmup):
             sm.replay()
         torch.cuda.synchronize()
@@ -171,7 +172,9 @@ def bench_sampler(steps, warmup):
             sm.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        ms = e0.elapsed_time(e1) / steps
+        del sm.graph
+        return ms
 
     sm = R.Sampler(wl, W, eps, tau_c, tau_u)
     ms = timed(sm)
@@ -179,6 +182,10 @@ def bench_sampler(steps, warmup):
     ms2 = timed(sm2)
     assert torch.isfinite(sm.z).all()
     assert torch.equal(sm.z, sm2.z), "packed and two-pass CFG samplers disagree"
+    # the base (non-distilled) sampler: 20 uniform Euler steps, packed CFG
+    sm20 = R.Sampler(wl, W, eps, tau_c, tau_u, schedule=[1.0 - i / 20 for i in range(21)])
+    ms20 = timed(sm20, steps=1)
+    assert torch.isfinite(sm20.z).all()
     from resolution_image_gen_amd.configs import block_flops
 
     blk = block_flops(d, sm.samples)[0] * wl.depth * (len(wl.schedule) - 1)
@@ -188,7 +195,8 @@ def bench_sampler(steps, warmup):
             "block_tflops": round(blk / (ms * 1e-3) / 1e12, 1),
             "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "two_pass_ms_per_4step_pack": round(ms2, 2),
-            "packed_speedup_vs_two_pass": round(ms2 / ms, 3)}
+            "packed_speedup_vs_two_pass": round(ms2 / ms, 3),
+            "ms_per_20step_pack": round(ms20, 2)}
 
 
 def main():

@@ -69,11 +69,18 @@ def _small_sampler_wl(dtype, depth=2):
                        depth=depth, steps=4, guidance=4.0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_sampler_vs_oracle(dtype):
+BASE20 = tuple(1.0 - i / 20 for i in range(21))   # 20 uniform Euler steps, 1 -> 0
+
+
+@pytest.mark.parametrize("dtype,schedule", [("f32", None), ("bf16", None), ("f32", BASE20)])
+def test_sampler_vs_oracle(dtype, schedule):
     from resolution_image_gen_amd import runner as R
 
     wl = _small_sampler_wl(dtype)
+    if schedule is not None:
+        wl = CF.Workload(wl.name, wl.dims, dtype, wl.samples, wl.img_budget, depth=wl.depth,
+                         steps=len(schedule) - 1, guidance=wl.guidance, schedule=schedule)
+    print(f"sampler {dtype} {len(wl.schedule) - 1} steps", flush=True)
     W = R.Weights(wl, recipe="stress")
     h, w = wl.samples[0][:2]
     eps = S.normal((h * w, wl.dims.c_lat), 1.0, dtype, wl.name, "eps")
@@ -86,7 +93,8 @@ def test_sampler_vs_oracle(dtype):
     Wd = {k: np.asarray(v, np.float64) for k, v in W.np_wrap.items()}
     Wd["blocks"] = [f64_block(nb) for nb in W.np_blocks]
     g = wl.guidance
-    z_ref, vhat_ref = OF.sample_packed_cfg(eps, tau_c, tau_u, Wd, (h, w), wl.dims.heads, g)
+    z_ref, vhat_ref = OF.sample_packed_cfg(eps, tau_c, tau_u, Wd, (h, w), wl.dims.heads, g, wl.schedule)
+    assert len(vs) == len(vhat_ref) == len(wl.schedule) - 1
     tol = TOL[dtype]
     n = h * w
     # step 0 runs on identical inputs: each branch's raw velocity is held to the bar
