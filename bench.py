@@ -146,12 +146,15 @@ def bench_sampler(steps, warmup):
     tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0.
     The same sampler with the two CFG branches as separate forwards is timed
     beside it, and both must end on the same bits; then one 20-step pack
-    (uniform steps from 1 to 0) of the packed sampler."""
+    (uniform steps from 1 to 0) of the packed sampler, and the 4-step editing
+    sampler (target + clean source of the same grid per sample), packed and
+    two-pass, on the same blocks."""
     import torch
 
     from resolution_image_gen_amd import configs as CF
     from resolution_image_gen_amd import runner as R
     from resolution_image_gen_amd import synthetic as S
+    from resolution_image_gen_amd.configs import block_flops
 
     wl = CF.WORKLOADS["sampler1024_cfg_bf16"]
     d = wl.dims
@@ -182,21 +185,36 @@ def bench_sampler(steps, warmup):
     ms2 = timed(sm2)
     assert torch.isfinite(sm.z).all()
     assert torch.equal(sm.z, sm2.z), "packed and two-pass CFG samplers disagree"
+    sm_samples = sm.samples
     # the base (non-distilled) sampler: 20 uniform Euler steps, packed CFG
     sm20 = R.Sampler(wl, W, eps, tau_c, tau_u, schedule=[1.0 - i / 20 for i in range(21)])
     ms20 = timed(sm20, steps=1)
     assert torch.isfinite(sm20.z).all()
-    from resolution_image_gen_amd.configs import block_flops
-
-    blk = block_flops(d, sm.samples)[0] * wl.depth * (len(wl.schedule) - 1)
-    n = sum(hh * ww * f + t for hh, ww, f, t in sm.samples)
+    del sm, sm2, sm20
+    # the 4-step editing sampler on the same blocks: each sample a noised 64x64
+    # target + the clean 64x64 source (frames 0 / 1) + text; packed and two-pass
+    ewl = CF.WORKLOADS["edit_sampler1024_cfg_bf16"]
+    src = S.normal((h * w, d.c_lat), 1.0, "bf16", ewl.name, "src")
+    se = R.Sampler(ewl, W, eps, tau_c, tau_u, src=src)
+    ms_e = timed(se)
+    se2 = R.Sampler(ewl, W, eps, tau_c, tau_u, src=src, two_pass=True)
+    ms_e2 = timed(se2)
+    assert torch.isfinite(se.z).all()
+    assert torch.equal(se.z, se2.z), "packed and two-pass CFG edit samplers disagree"
+    eblk = block_flops(d, se.samples)[0] * ewl.depth * (len(ewl.schedule) - 1)
+    blk = block_flops(d, sm_samples)[0] * wl.depth * (len(wl.schedule) - 1)
+    n = sum(hh * ww * f + t for hh, ww, f, t in sm_samples)
     return {"workload": f"{wl.name}: {wl.note}", "ms_per_4step_pack": round(ms, 2), "packs_timed": steps,
             "block_tokens_per_s": round(n * wl.depth * (len(wl.schedule) - 1) / (ms * 1e-3), 1),
             "block_tflops": round(blk / (ms * 1e-3) / 1e12, 1),
             "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "two_pass_ms_per_4step_pack": round(ms2, 2),
             "packed_speedup_vs_two_pass": round(ms2 / ms, 3),
-            "ms_per_20step_pack": round(ms20, 2)}
+            "ms_per_20step_pack": round(ms20, 2),
+            "edit": {"workload": f"{ewl.name}: {ewl.note}", "ms_per_4step_pack": round(ms_e, 2),
+                     "block_tflops": round(eblk / (ms_e * 1e-3) / 1e12, 1),
+                     "two_pass_ms_per_4step_pack": round(ms_e2, 2),
+                     "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3)}}
 
 
 def main():
@@ -240,7 +258,7 @@ def main():
 
     wl = CF.WORKLOADS[args.workload]
     if wl.steps:
-        raise SystemExit("the sampler workload is timed with --sampler-packs N next to a training-forward "
+        raise SystemExit("the sampler workloads are timed with --sampler-packs N next to a training-forward "
                          "workload")
     torch.cuda.set_device(0)
     W = R.Weights(wl)

@@ -95,43 +95,56 @@ def velocity_model(zt_img, tau, t, W, pk, heads):
     return _blk.final_layer(x_img, c, W["w_fmod"], W["w_out"], pk)
 
 
-def sample_packed_cfg(eps, tau_c, tau_u, W, grid, heads, g, schedule=SCHEDULE):
+def _image_rows(z, src):
+    """A sample's image rows: the target latent, then (editing) the clean
+    source latent (R6, R25: slot 0 target, slot 1 source)."""
+    return z if src is None else np.concatenate([z, np.asarray(src, np.float64)])
+
+
+def sample_packed_cfg(eps, tau_c, tau_u, W, grid, heads, g, schedule=SCHEDULE, src=None):
     """Euler sampling with packed CFG (R19, R20).
 
     One pack holds [cond, uncond], both with the same image grid (h, w) and
     latent z; each step runs one packed forward, combines the two velocities
-    and takes an Euler step.  Returns (z_final, list of guided velocities).
+    and takes an Euler step.  With src (the clean source latent of an edit,
+    [h*w, C]) both samples are editing samples: target rows noised, then the
+    source rows, unchanged through the steps (R25); only the target moves.
+    Returns (z_final, list of guided velocities).
     """
     from . import pack as _pack
 
     h, w = grid
-    pk = _pack.pack([(h, w, 1, len(tau_c)), (h, w, 1, len(tau_u))])
+    f = 1 if src is None else 2
+    pk = _pack.pack([(h, w, f, len(tau_c)), (h, w, f, len(tau_u))])
     z = np.asarray(eps, np.float64).copy()
     tau = np.concatenate([np.asarray(tau_c, np.float64), np.asarray(tau_u, np.float64)])
     vs = []
     n = h * w
     for i in range(len(schedule) - 1):
         t = np.full(2, schedule[i])
-        v = velocity_model(np.concatenate([z, z]), tau, t, W, pk, heads)
+        rows = _image_rows(z, src)
+        v = velocity_model(np.concatenate([rows, rows]), tau, t, W, pk, heads)
         vhat = cfg_combine(v[:n], v[n:], g)
         vs.append(vhat)
         z = euler_step(z, vhat, schedule[i], schedule[i + 1])
     return z, vs
 
 
-def sample_two_pass_cfg(eps, tau_c, tau_u, W, grid, heads, g, schedule=SCHEDULE):
+def sample_two_pass_cfg(eps, tau_c, tau_u, W, grid, heads, g, schedule=SCHEDULE, src=None):
     """The same sampler with cond and uncond run as two separate forwards."""
     from . import pack as _pack
 
     h, w = grid
-    pc = _pack.pack([(h, w, 1, len(tau_c))])
-    pu = _pack.pack([(h, w, 1, len(tau_u))])
+    f = 1 if src is None else 2
+    pc = _pack.pack([(h, w, f, len(tau_c))])
+    pu = _pack.pack([(h, w, f, len(tau_u))])
     z = np.asarray(eps, np.float64).copy()
     vs = []
     for i in range(len(schedule) - 1):
         t = np.full(1, schedule[i])
-        vc = velocity_model(z, tau_c, t, W, pc, heads)
-        vu = velocity_model(z, tau_u, t, W, pu, heads)
+        rows = _image_rows(z, src)
+        vc = velocity_model(rows, tau_c, t, W, pc, heads)
+        vu = velocity_model(rows, tau_u, t, W, pu, heads)
         vhat = cfg_combine(vc, vu, g)
         vs.append(vhat)
         z = euler_step(z, vhat, schedule[i], schedule[i + 1])

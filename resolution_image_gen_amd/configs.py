@@ -53,6 +53,11 @@ WORKLOADS = {
         "sampler1024_cfg_bf16", B4, "bf16", ((64, 64, 1, 256), (64, 64, 1, 256)), img_budget=8192,
         depth=28, steps=4, guidance=4.0,
         note="4-step Euler, packed CFG (cond + uncond, 64x64 grid + 256 text each), 28 blocks"),
+    "edit_sampler1024_cfg_bf16": Workload(
+        "edit_sampler1024_cfg_bf16", B4, "bf16", ((64, 64, 2, 256), (64, 64, 2, 256)), img_budget=16384,
+        depth=28, steps=4, guidance=4.0,
+        note="4-step Euler edit, packed CFG (cond + uncond, each 64x64 noised target + 64x64 clean source "
+             "+ 256 text), 28 blocks"),
     "edit2048_bf16": Workload(
         "edit2048_bf16", B4, "bf16", ((128, 128, 2, 512),), img_budget=32768,
         note="2048^2 edit: target + source 128x128 grids (3D RoPE frames 0/1) + 512 text"),

@@ -181,16 +181,22 @@ class Sampler:
     the unconditional sample (each a one-sample pack), writing the two
     velocities into the halves of the same buffer, then the same CFG combine
     + Euler launch.  Every row's arithmetic is the same in both forms, so the
-    two give the same bits."""
+    two give the same bits.
+
+    src (the clean source latent [h*w, C] of an edit) makes both samples
+    editing samples: image rows [target (frame 0); source (frame 1)], the
+    source rows written once per pack and never updated; the velocity, the
+    CFG combine and the Euler step touch the target rows only."""
 
     def __init__(self, wl, W, eps, tau_c, tau_u, device="cuda", guidance=None, schedule=None,
-                 two_pass=False):
+                 two_pass=False, src=None):
         self.wl, self.W = wl, W
         d = wl.dims
         self.dims = W.dims
         dt = self.dims.torch_dtype
         h, w = wl.samples[0][0], wl.samples[0][1]
-        self.samples = [(h, w, 1, len(tau_c)), (h, w, 1, len(tau_u))]
+        f = 1 if src is None else 2
+        self.samples = [(h, w, f, len(tau_c)), (h, w, f, len(tau_u))]
         self.pk = B.pack(self.samples, device)
         self.g = float(wl.guidance if guidance is None else guidance)
         self.schedule = list(wl.schedule if schedule is None else schedule)
@@ -206,6 +212,8 @@ class Sampler:
         self.v = torch.empty(self.pk.n_tgt, d.c_lat, **e)
         self.tsched = torch.tensor([[t, t] for t in self.schedule[:-1]], dtype=torch.float32, device=device)
         self.ws = torch.empty(B.workspace_size(self.dims, self.pk), dtype=torch.uint8, device=device)
+        # an edit sample's image rows at z_1 = eps: [eps; source], both in dtype
+        self.img_rows = None if src is None else torch.cat([_dev(eps, dt, device), _dev(src, dt, device)])
         self.two_pass = two_pass
         if two_pass:   # one-sample packs; the two-sample workspace covers each
             self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
@@ -230,21 +238,23 @@ class Sampler:
     def _two_pass_forward(self, i, stream):
         """Velocities of step i as two forwards: cond rows, then uncond rows."""
         W, dm = self.W, self.dims
-        ib = it = 0
+        ib = it = iv = 0
         for pk in self.pk_one:
-            ni, nt = pk.n_img, pk.n_txt
+            ni, nt, nv = pk.n_img, pk.n_txt, pk.n_tgt
             B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i, :1], self.c[:1], self.ws, stream)
             B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt[ib:ib + ni], self.tau[it:it + nt],
                     self.x_img[:ni], self.x_txt[:nt], stream)
             for bw in W.bw:
                 B.block_fwd(dm, bw, pk, self.c[:1], self.x_img[:ni], self.x_txt[:nt], self.ws, stream)
             B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c[:1], self.x_img[:ni],
-                    self.v[ib:ib + ni], self.ws, stream)
-            ib, it = ib + ni, it + nt
+                    self.v[iv:iv + nv], self.ws, stream)
+            ib, it, iv = ib + ni, it + nt, iv + nv
 
     def run(self, stream=None, on_step=None):
         W, pk, dm = self.W, self.pk, self.dims
         self.z.copy_(self.eps)               # z_1 = eps
+        if self.img_rows is not None:         # source rows of both samples (targets too, as eps)
+            B.pack_gather(pk, 0, [self.img_rows, self.img_rows], self.zt, stream)
         B.rf_pack_latent(pk, self.z, 0, 1, self.zt, stream)
         for i in range(len(self.schedule) - 1):
             if self.two_pass:

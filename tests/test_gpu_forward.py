@@ -72,34 +72,41 @@ def _small_sampler_wl(dtype, depth=2):
 BASE20 = tuple(1.0 - i / 20 for i in range(21))   # 20 uniform Euler steps, 1 -> 0
 
 
-@pytest.mark.parametrize("dtype,schedule", [("f32", None), ("bf16", None), ("f32", BASE20)])
-def test_sampler_vs_oracle(dtype, schedule):
+@pytest.mark.parametrize("dtype,schedule,edit", [("f32", None, False), ("bf16", None, False),
+                                                  ("f32", BASE20, False), ("f32", None, True),
+                                                  ("bf16", None, True)])
+def test_sampler_vs_oracle(dtype, schedule, edit):
+    """Generation and (edit=True) editing samplers: each sample holds a noised
+    target and, for an edit, the clean source latent of the same grid."""
     from resolution_image_gen_amd import runner as R
 
     wl = _small_sampler_wl(dtype)
     if schedule is not None:
         wl = CF.Workload(wl.name, wl.dims, dtype, wl.samples, wl.img_budget, depth=wl.depth,
                          steps=len(schedule) - 1, guidance=wl.guidance, schedule=schedule)
-    print(f"sampler {dtype} {len(wl.schedule) - 1} steps", flush=True)
+    print(f"sampler {dtype} {len(wl.schedule) - 1} steps edit={edit}", flush=True)
     W = R.Weights(wl, recipe="stress")
     h, w = wl.samples[0][:2]
     eps = S.normal((h * w, wl.dims.c_lat), 1.0, dtype, wl.name, "eps")
     tau_c = S.text(24, wl.dims.d_txt, dtype, wl.name, "tau_c")
     tau_u = S.text(24, wl.dims.d_txt, dtype, wl.name, "tau_u")
+    src = S.normal((h * w, wl.dims.c_lat), 1.0, dtype, wl.name, "src") if edit else None
     vs = []
-    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u, src=src)
     sm.run(on_step=lambda i, s: vs.append(to_np(s.v)))
     torch.cuda.synchronize()
     Wd = {k: np.asarray(v, np.float64) for k, v in W.np_wrap.items()}
     Wd["blocks"] = [f64_block(nb) for nb in W.np_blocks]
     g = wl.guidance
-    z_ref, vhat_ref = OF.sample_packed_cfg(eps, tau_c, tau_u, Wd, (h, w), wl.dims.heads, g, wl.schedule)
+    z_ref, vhat_ref = OF.sample_packed_cfg(eps, tau_c, tau_u, Wd, (h, w), wl.dims.heads, g, wl.schedule, src=src)
     assert len(vs) == len(vhat_ref) == len(wl.schedule) - 1
     tol = TOL[dtype]
     n = h * w
     # step 0 runs on identical inputs: each branch's raw velocity is held to the bar
-    pk = oracle_pack([(h, w, 1, 24), (h, w, 1, 24)])
-    v0 = OF.velocity_model(np.concatenate([eps, eps]), np.concatenate([tau_c, tau_u]), np.ones(2), Wd, pk,
+    f = 2 if edit else 1
+    pk = oracle_pack([(h, w, f, 24), (h, w, f, 24)])
+    rows = np.concatenate([eps, src]) if edit else eps
+    v0 = OF.velocity_model(np.concatenate([rows, rows]), np.concatenate([tau_c, tau_u]), np.ones(2), Wd, pk,
                            wl.dims.heads)
     assert_close("v_cond step 0", vs[0][:n], v0[:n], tol)
     assert_close("v_uncond step 0", vs[0][n:], v0[n:], tol)
@@ -111,6 +118,10 @@ def test_sampler_vs_oracle(dtype, schedule):
     # z_final = eps + sum_i dt_i vhat_i: the same bound carried through the four steps
     zb = (abs(1 - g) + g) * tol * vmax / np.max(np.abs(z_ref))
     assert_close("z_final", to_np(sm.z), z_ref, zb)
+    if edit:   # the source rows of both samples still hold the clean source, bit for bit
+        zt = to_np(sm.zt)
+        np.testing.assert_array_equal(zt[n:2 * n], src)
+        np.testing.assert_array_equal(zt[3 * n:], src)
 
 
 def test_packed_cfg_equals_two_pass_on_gpu():
@@ -151,7 +162,8 @@ def test_packed_cfg_equals_two_pass_on_gpu():
     assert torch.equal(vp[n:], vu)
 
 
-@pytest.mark.parametrize("case,tu_len", [("small", 24), ("small", 9), ("wide64x64", 256)])
+@pytest.mark.parametrize("case,tu_len", [("small", 24), ("small", 9), ("wide64x64", 256), ("edit_small", 9),
+                                         ("edit_wide64x64", 256)])
 def test_two_pass_sampler_equals_packed(case, tu_len):
     """The 4-step sampler with its CFG branches as two separate forwards per
     step ends on the same bits as the packed one (eager and graph-replayed);
@@ -161,7 +173,7 @@ def test_two_pass_sampler_equals_packed(case, tu_len):
     depended on the row count."""
     from resolution_image_gen_amd import runner as R
 
-    if case == "small":
+    if case.endswith("small"):
         wl = _small_sampler_wl("bf16", depth=2)
         W = R.Weights(wl, recipe="stress")
     else:
@@ -173,9 +185,10 @@ def test_two_pass_sampler_equals_packed(case, tu_len):
     eps = S.normal((h * w, wl.dims.c_lat), 1.0, "bf16", wl.name, "eps2")
     tau_c = S.text(24, wl.dims.d_txt, "bf16", wl.name, "tau_c2")
     tau_u = S.text(tu_len, wl.dims.d_txt, "bf16", wl.name, "tau_u2")
+    src = S.normal((h * w, wl.dims.c_lat), 1.0, "bf16", wl.name, "src2") if case.startswith("edit") else None
     print(f"two-pass sampler {case} tu={tu_len}", flush=True)
-    packed = R.Sampler(wl, W, eps, tau_c, tau_u)
-    two = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
+    packed = R.Sampler(wl, W, eps, tau_c, tau_u, src=src)
+    two = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True, src=src)
     packed.run()
     two.run()
     torch.cuda.synchronize()
