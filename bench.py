@@ -71,16 +71,20 @@ def kernel_sources_sha256():
 
 
 def measured_traffic(tag, workload):
+    """HBM bytes per launch of kernel `tag` on `workload` from the committed
+    counter record, or None when there is none or the GEMM sources changed
+    since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            recs = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel") != tag or rec.get("workload") != workload:
-        return None
-    if rec.get("sources_sha256") != kernel_sources_sha256():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if rec.get("kernel") == tag and rec.get("workload") == workload:
+            if rec.get("sources_sha256") != kernel_sources_sha256():
+                return None
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def step_flops(wl):
