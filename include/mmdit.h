@@ -206,6 +206,56 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* dims, const mmdit_block_w* w,
                              const mmdit_pack_t* pack, const void* c, void* x_img, void* x_txt,
                              void* ws, size_t ws_bytes, mmdit_stream stream);
 
+/* ------------------------------------------------------------- training */
+
+/* The block's training forward and its backward.  The pages train the
+ * backbone with the flow-matching objective on packed native-resolution
+ * samples ([hyper] 方法; [blog] 2.2(2)) and report the whole training step as
+ * their systems figure ([blog] 证据二, Table 4); the gradients here are those
+ * of the block's own definition (mmdit_block_fwd) by the chain rule. */
+
+/* Bytes of the buffer that mmdit_block_fwd_train fills and mmdit_block_bwd
+ * reads for this pack (0 on invalid arguments): per stream the block input,
+ * both modulated norms, q/k before and after their norm, v, the attention
+ * output and its log-sum-exp, both branch outputs, the residual after the
+ * attention branch and the MLP pre-activation, plus the adaLN vectors. */
+size_t mmdit_block_saved_size(const mmdit_dims* dims, const mmdit_pack_t* pack);
+
+/* Same result as mmdit_block_fwd (x_img, x_txt updated in place, the same
+ * arithmetic), and every intermediate the backward needs is kept in saved
+ * (caller-owned, >= mmdit_block_saved_size bytes, 16-byte aligned; read by
+ * mmdit_block_bwd of the same pack, weights and c).  ws as for
+ * mmdit_block_fwd. */
+mmdit_status mmdit_block_fwd_train(const mmdit_dims* dims, const mmdit_block_w* w,
+                                   const mmdit_pack_t* pack, const void* c, void* x_img,
+                                   void* x_txt, void* saved, size_t saved_bytes, void* ws,
+                                   size_t ws_bytes, mmdit_stream stream);
+
+/* Weight gradients of one stream, float32, each the shape of its weight. */
+typedef struct {
+  float *w_mod, *w_qkv, *g_q, *g_k, *w_o, *w_up, *w_down;
+} mmdit_stream_grad;
+typedef struct {
+  mmdit_stream_grad img, txt;
+} mmdit_block_grad;
+
+/* Workspace bytes of mmdit_block_bwd for this pack (0 on invalid arguments). */
+size_t mmdit_block_bwd_workspace_size(const mmdit_dims* dims, const mmdit_pack_t* pack);
+
+/* Backward of one block.  In: dx_img [n_img, H], dx_txt [n_txt, H] (dtype)
+ * hold dL/dx_out; out: they hold dL/dx_in (in place).  Every gradient in g
+ * is overwritten (float32; a stream without rows gets zeros); dc [B, H]
+ * float32 is accumulated (+=), as c feeds every block: zero it before the
+ * first block.  The two streams' gradients stay separate even when their
+ * weights are the same arrays (single-stream blocks: add them).  saved: as
+ * filled by mmdit_block_fwd_train; ws >= mmdit_block_bwd_workspace_size.
+ * Deterministic: every sum runs in a fixed order (no atomics). */
+mmdit_status mmdit_block_bwd(const mmdit_dims* dims, const mmdit_block_w* w,
+                             const mmdit_pack_t* pack, const void* c, const void* saved,
+                             size_t saved_bytes, void* dx_img, void* dx_txt,
+                             const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                             mmdit_stream stream);
+
 /* Sub-steps of the block, exposed so every intermediate can be checked. */
 
 /* y = rms(x[row_map[i]]) * (1 + scale[s]) + shift[s], s = seg[row_map[i]]

@@ -137,7 +137,7 @@ def block_backward(x_img, x_txt, c, wb, pk, heads, dy_img, dy_txt):
         # attention output projection and its gated residual
         d_g1 = seg_sum(d_xmid * fw[f"attn_out_{s}"], seg[s], B)
         d_a = g1 * d_xmid
-        o = fw[f"o_{s}"].reshape(d_a.shape[0], -1)
+        o = fw[f"o_{s}"].reshape(d_a.shape[0], H)
         dw_o = d_a.T @ o
         d_o[s] = (d_a @ w["w_o"]).reshape(fw[f"o_{s}"].shape)
         post[s] = dict(w=w, sh1=sh1, sc1=sc1, d_xmid=d_xmid, d_g1=d_g1, d_sh2=d_sh2, d_sc2=d_sc2, d_g2=d_g2,

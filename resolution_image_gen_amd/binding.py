@@ -62,6 +62,17 @@ class _BlockW(ctypes.Structure):
     _fields_ = [("img", _StreamW), ("txt", _StreamW)]
 
 
+GRAD_KEYS = ("w_mod", "w_qkv", "g_q", "g_k", "w_o", "w_up", "w_down")
+
+
+class _StreamG(ctypes.Structure):
+    _fields_ = [(k, _vp) for k in GRAD_KEYS]
+
+
+class _BlockG(ctypes.Structure):
+    _fields_ = [("img", _StreamG), ("txt", _StreamG)]
+
+
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(f"{lib_path} is missing: build it with `python -m resolution_image_gen_amd.build`")
@@ -80,6 +91,11 @@ def _load():
         "mmdit_modulation": (_i32, [D, _vp, _i32, _i32, _vp, _vp, _vp]),
         "mmdit_embed": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_block_fwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_block_saved_size": (_sz, [D, P]),
+        "mmdit_block_fwd_train": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
+        "mmdit_block_bwd_workspace_size": (_sz, [D, P]),
+        "mmdit_block_bwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(_BlockG),
+                                   _vp, _vp, _sz, _vp]),
         "mmdit_rms_modulate": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
         "mmdit_qk_norm_rope": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_attention": (_i32, [D, P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -258,6 +274,35 @@ def block_fwd(dims, wb, pk, c, x_img, x_txt, ws, stream=None):
     bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
     _ck(_lib.mmdit_block_fwd(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(x_img),
                              _p(x_txt), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def block_saved_size(dims, pk):
+    return int(_lib.mmdit_block_saved_size(ctypes.byref(dims.c), pk.ref))
+
+
+def block_bwd_workspace_size(dims, pk):
+    return int(_lib.mmdit_block_bwd_workspace_size(ctypes.byref(dims.c), pk.ref))
+
+
+def block_fwd_train(dims, wb, pk, c, x_img, x_txt, saved, ws, stream=None):
+    bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
+    _ck(_lib.mmdit_block_fwd_train(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(x_img), _p(x_txt),
+                                   _p(saved), saved.numel() * saved.element_size(), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def block_grads(g):
+    """ctypes struct for {"img": {...}, "txt": {...}} dicts of float32 gradient tensors (keep g alive)."""
+    return _BlockG(*[_StreamG(*[g[s][k].data_ptr() for k in GRAD_KEYS]) for s in ("img", "txt")])
+
+
+def block_bwd(dims, wb, pk, c, saved, dx_img, dx_txt, grads, dc, ws, stream=None):
+    """dx_img, dx_txt: dL/dx_out in, dL/dx_in out; grads overwritten; dc accumulated."""
+    bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
+    bg = grads if isinstance(grads, _BlockG) else block_grads(grads)
+    _ck(_lib.mmdit_block_bwd(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(saved),
+                             saved.numel() * saved.element_size(), _p(dx_img), _p(dx_txt), ctypes.byref(bg),
+                             _p(dc), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rms_modulate(dims, x, seg, mod, shift_off, scale_off, y, row_map=None, stream=None):

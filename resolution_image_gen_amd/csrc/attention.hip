@@ -18,6 +18,7 @@
 #include "common.h"
 
 #include <math.h>
+#include <string.h>
 
 namespace mmdit {
 
@@ -32,6 +33,8 @@ struct AttnArgs {
   const int32_t* cu_txt;
   int32_t heads, H;
   float scale_log2;  // log2(e) / sqrt(head_dim)
+  float* lse;        // optional [heads][njp] float32: log2 of each query's softmax denominator
+  int32_t njp;       // padded joint length of the lse rows (samples start at multiples of 64)
 };
 
 template <typename T>
@@ -45,6 +48,19 @@ template <typename T>
 __device__ __forceinline__ T* out_row(const AttnArgs& a, int32_t j, int32_t Tb, int32_t t0, int32_t i0) {
   return j < Tb ? static_cast<T*>(a.o_txt) + (int64_t)(t0 + j) * a.H
                 : static_cast<T*>(a.o_img) + (int64_t)(i0 + j - Tb) * a.H;
+}
+
+// Start of sample b in the 64-padded joint axis of the V^T buffer.
+__device__ __forceinline__ int32_t padded_start(const AttnArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  int32_t acc = 0;
+  for (int i = lane; i < b; i += 64) {
+    const int32_t L = (a.cu_txt[i + 1] - a.cu_txt[i]) + (a.cu_img[i + 1] - a.cu_img[i]);
+    acc += (L + 63) & ~63;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  return acc;
 }
 
 // ------------------------------------------------------------------- SIMT
@@ -110,6 +126,10 @@ __global__ void __launch_bounds__(256) attn_simt_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DQ; ++e) o[e] = from_f<T>(acc[e] * inv);
   }
+  if (a.lse) {
+    const int32_t pstart = padded_start(a, b);
+    if (valid && sub == 0) a.lse[(int64_t)head * a.njp + pstart + j] = m + log2f(l);
+  }
 }
 
 // ------------------------------------------------------------------- MFMA
@@ -118,19 +138,6 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
-}
-
-// Start of sample b in the 64-padded joint axis of the V^T buffer.
-__device__ __forceinline__ int32_t padded_start(const AttnArgs& a, int b) {
-  const int lane = threadIdx.x & 63;
-  int32_t acc = 0;
-  for (int i = lane; i < b; i += 64) {
-    const int32_t L = (a.cu_txt[i + 1] - a.cu_txt[i]) + (a.cu_img[i + 1] - a.cu_img[i]);
-    acc += (L + 63) & ~63;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  return acc;
 }
 
 // V^T[head][d][padded joint token] (bf16) from the v columns of the QKV
@@ -329,6 +336,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
     __syncthreads();
   }
   lsum += __shfl_xor(lsum, 32, 64);
+  if (a.lse && jq < L && g == 0) a.lse[(int64_t)head * a.njp + pstart + jq] = m + log2f(lsum);
   if (jq < L) {
     bf16* o = out_row<bf16>(a, jq, Tb, t0, i0) + head * D;
     const float inv = 1.0f / lsum;
@@ -344,6 +352,218 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
   }
 }
 
+// --------------------------------------------------------------- backward
+// Gradients of o = softmax(q k^T / sqrt(d)) v, per sample and head, from the
+// forward's log2 softmax denominators: with s2 = q.k log2(e)/sqrt(d) and
+// P = 2^(s2 - lse),  D_i = dO_i . O_i,  dP = dO V^T,  dS = P (dP - D_i),
+// dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
+// Deterministic: dQ is summed over keys by the query's own lanes and dK, dV
+// over queries by the key's own lanes (no atomics).
+struct AttnBwdArgs {
+  AttnArgs f;           // q, k, v after QK-norm and RoPE; o; lse (input)
+  const void* do_img;   // [rows, H] gradient of o
+  const void* do_txt;
+  void* dqkv_img;       // [rows, 3H] output: dq | dk | dv (head-contiguous, like qkv)
+  void* dqkv_txt;
+  float* dsum;          // [heads][njp] D_i
+  float inv_sqrt_d;
+};
+
+template <typename T>
+__device__ __forceinline__ const T* grad_row(const AttnBwdArgs& a, int32_t j, int32_t Tb, int32_t t0, int32_t i0) {
+  return j < Tb ? static_cast<const T*>(a.do_txt) + (int64_t)(t0 + j) * a.f.H
+                : static_cast<const T*>(a.do_img) + (int64_t)(i0 + j - Tb) * a.f.H;
+}
+template <typename T>
+__device__ __forceinline__ T* dqkv_row(const AttnBwdArgs& a, int32_t j, int32_t Tb, int32_t t0, int32_t i0) {
+  const int64_t H3 = 3 * (int64_t)a.f.H;
+  return j < Tb ? static_cast<T*>(a.dqkv_txt) + (int64_t)(t0 + j) * H3
+                : static_cast<T*>(a.dqkv_img) + (int64_t)(i0 + j - Tb) * H3;
+}
+
+// D_i = dO_i . O_i for every query (four lanes per query).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_bwd_dsum_kernel(AttnBwdArgs a) {
+  constexpr int DQ = D / 4;
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t qbase = blockIdx.x * 64;
+  if (qbase >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  const int sub = threadIdx.x & 3;
+  const int32_t j = qbase + (threadIdx.x >> 2);
+  float acc = 0.f;
+  if (j < L) {
+    const T* go = grad_row<T>(a, j, Tb, t0, i0) + head * D + sub * DQ;
+    const T* o = out_row<T>(a.f, j, Tb, t0, i0) + head * D + sub * DQ;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) acc = fmaf(to_f(go[e]), to_f(o[e]), acc);
+  }
+  acc = group_sum(acc, 4);
+  if (j < L && sub == 0) a.dsum[(int64_t)head * a.f.njp + pstart + j] = acc;
+}
+
+// dQ: 64 queries per block, four lanes per query, keys streamed through LDS.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_bwd_dq_simt_kernel(AttnBwdArgs a) {
+  constexpr int DQ = D / 4;
+  constexpr int KB = 32;
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t qbase = blockIdx.x * 64;
+  if (qbase >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  __shared__ float Ks[KB][D + 1], Vs[KB][D + 1];
+  const int sub = threadIdx.x & 3;
+  const int32_t j = qbase + (threadIdx.x >> 2);
+  const bool valid = j < L;
+  float q[DQ], go[DQ], dq[DQ];
+  float lse = 0.f, dsum = 0.f;
+  if (valid) {
+    const T* r = joint_row<T>(a.f, j, Tb, t0, i0) + head * D + sub * DQ;
+    const T* g = grad_row<T>(a, j, Tb, t0, i0) + head * D + sub * DQ;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      q[e] = to_f(r[e]) * a.f.scale_log2;
+      go[e] = to_f(g[e]);
+    }
+    lse = a.f.lse[(int64_t)head * a.f.njp + pstart + j];
+    dsum = a.dsum[(int64_t)head * a.f.njp + pstart + j];
+  } else {
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) q[e] = go[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) dq[e] = 0.f;
+  for (int32_t kv0 = 0; kv0 < L; kv0 += KB) {
+    for (int idx = threadIdx.x; idx < KB * D; idx += 256) {
+      const int r = idx / D, c = idx % D;
+      const int32_t key = kv0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (key < L) {
+        const T* p = joint_row<T>(a.f, key, Tb, t0, i0);
+        kv = to_f(p[a.f.H + head * D + c]);
+        vv = to_f(p[2 * a.f.H + head * D + c]);
+      }
+      Ks[r][c] = kv;
+      Vs[r][c] = vv;
+    }
+    __syncthreads();
+    const int nk = min(KB, L - kv0);
+    for (int kk = 0; kk < nk; ++kk) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        s = fmaf(q[e], Ks[kk][sub * DQ + e], s);
+        dp = fmaf(go[e], Vs[kk][sub * DQ + e], dp);
+      }
+      s = group_sum(s, 4);
+      dp = group_sum(dp, 4);
+      const float ds = exp2f(s - lse) * (dp - dsum);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) dq[e] = fmaf(ds, Ks[kk][sub * DQ + e], dq[e]);
+    }
+    __syncthreads();
+  }
+  if (valid) {
+    T* o = dqkv_row<T>(a, j, Tb, t0, i0) + head * D + sub * DQ;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) o[e] = from_f<T>(dq[e] * a.inv_sqrt_d);
+  }
+}
+
+// dK and dV: 64 keys per block, four lanes per key, queries streamed through LDS.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_simt_kernel(AttnBwdArgs a) {
+  constexpr int DQ = D / 4;
+  constexpr int QB = 32;
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t kbase = blockIdx.x * 64;
+  if (kbase >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  __shared__ float Qs[QB][D + 1], Gs[QB][D + 1], Ls[QB], Ds[QB];
+  const int sub = threadIdx.x & 3;
+  const int32_t j = kbase + (threadIdx.x >> 2);
+  const bool valid = j < L;
+  float k[DQ], v[DQ], dk[DQ], dv[DQ];
+  if (valid) {
+    const T* r = joint_row<T>(a.f, j, Tb, t0, i0) + head * D + sub * DQ;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      k[e] = to_f(r[a.f.H + e]);
+      v[e] = to_f(r[2 * a.f.H + e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) k[e] = v[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) dk[e] = dv[e] = 0.f;
+  for (int32_t q0 = 0; q0 < L; q0 += QB) {
+    for (int idx = threadIdx.x; idx < QB * D; idx += 256) {
+      const int r = idx / D, c = idx % D;
+      const int32_t qi = q0 + r;
+      float qv = 0.f, gv = 0.f;
+      if (qi < L) {
+        qv = to_f(joint_row<T>(a.f, qi, Tb, t0, i0)[head * D + c]);
+        gv = to_f(grad_row<T>(a, qi, Tb, t0, i0)[head * D + c]);
+      }
+      Qs[r][c] = qv;
+      Gs[r][c] = gv;
+    }
+    if (threadIdx.x < QB) {
+      const int32_t qi = q0 + threadIdx.x;
+      Ls[threadIdx.x] = qi < L ? a.f.lse[(int64_t)head * a.f.njp + pstart + qi] : 0.f;
+      Ds[threadIdx.x] = qi < L ? a.dsum[(int64_t)head * a.f.njp + pstart + qi] : 0.f;
+    }
+    __syncthreads();
+    const int nq = min(QB, L - q0);
+    for (int qq = 0; qq < nq; ++qq) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        s = fmaf(Qs[qq][sub * DQ + e], k[e], s);
+        dp = fmaf(Gs[qq][sub * DQ + e], v[e], dp);
+      }
+      s = group_sum(s, 4);
+      dp = group_sum(dp, 4);
+      const float p = exp2f(s * a.f.scale_log2 - Ls[qq]);
+      const float ds = p * (dp - Ds[qq]);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        dv[e] = fmaf(p, Gs[qq][sub * DQ + e], dv[e]);
+        dk[e] = fmaf(ds, Qs[qq][sub * DQ + e], dk[e]);
+      }
+    }
+    __syncthreads();
+  }
+  if (valid) {
+    T* o = dqkv_row<T>(a, j, Tb, t0, i0) + head * D + sub * DQ;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      o[a.f.H + e] = from_f<T>(dk[e] * a.inv_sqrt_d);
+      o[2 * a.f.H + e] = from_f<T>(dv[e]);
+    }
+  }
+}
+
+template <typename T, int D>
+mmdit_status launch_attn_bwd(const AttnBwdArgs& a, dim3 grid, hipStream_t s) {
+  MMDIT_LAUNCH((attn_bwd_dsum_kernel<T, D>), grid, dim3(256), 0, s, a);
+  MMDIT_TRY(launch_check("attn_bwd_dsum_kernel", s));
+  MMDIT_LAUNCH((attn_bwd_dq_simt_kernel<T, D>), grid, dim3(256), 0, s, a);
+  MMDIT_TRY(launch_check("attn_bwd_dq_kernel", s));
+  MMDIT_LAUNCH((attn_bwd_dkdv_simt_kernel<T, D>), grid, dim3(256), 0, s, a);
+  return launch_check("attn_bwd_dkdv_kernel", s);
+}
+
 }  // namespace
 
 int64_t attention_vt_elems(const mmdit_pack_t* pk, int32_t H) {
@@ -357,9 +577,11 @@ int64_t attention_vt_elems(const mmdit_pack_t* pk, int32_t H) {
 
 mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t heads, int32_t D,
                             const void* qkv_img, const void* qkv_txt, void* o_img, void* o_txt,
-                            void* ws, size_t ws_bytes, hipStream_t s) {
+                            void* ws, size_t ws_bytes, hipStream_t s, float* lse) {
   if (pk->B == 0 || pk->max_joint == 0) return MMDIT_OK;
   AttnArgs a;
+  a.lse = lse;
+  a.njp = (int32_t)(attention_vt_elems(pk, heads * D) / (heads * D));
   a.qkv_img = qkv_img;
   a.qkv_txt = qkv_txt;
   a.o_img = o_img;
@@ -415,6 +637,45 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
   else
     MMDIT_LAUNCH((attn_simt_kernel<float, 64>), grid, dim3(256), 0, s, a);
   return launch_check("attn_simt_kernel", s);
+}
+
+size_t attention_bwd_ws_bytes(const mmdit_pack_t* pk, int32_t heads, int32_t D) {
+  return (size_t)(attention_vt_elems(pk, heads * D) / D) * sizeof(float);
+}
+
+mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t heads, int32_t D,
+                                const void* qkv_img, const void* qkv_txt, const void* o_img, const void* o_txt,
+                                const float* lse, const void* do_img, const void* do_txt, void* dqkv_img,
+                                void* dqkv_txt, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (pk->B == 0 || pk->max_joint == 0) return MMDIT_OK;
+  AttnBwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.f.qkv_img = qkv_img;
+  a.f.qkv_txt = qkv_txt;
+  a.f.o_img = const_cast<void*>(o_img);
+  a.f.o_txt = const_cast<void*>(o_txt);
+  a.f.cu_img = pk->cu_img;
+  a.f.cu_txt = pk->cu_txt;
+  a.f.heads = heads;
+  a.f.H = heads * D;
+  a.f.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  a.f.lse = const_cast<float*>(lse);
+  a.f.njp = (int32_t)(attention_vt_elems(pk, heads * D) / (heads * D));
+  a.do_img = do_img;
+  a.do_txt = do_txt;
+  a.dqkv_img = dqkv_img;
+  a.dqkv_txt = dqkv_txt;
+  a.inv_sqrt_d = (float)(1.0 / sqrt((double)D));
+  const size_t need = attention_bwd_ws_bytes(pk, heads, D);
+  if (!ws || ws_bytes < need) {
+    set_error("attention backward: workspace needs %zu bytes, got %zu", need, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  a.dsum = static_cast<float*>(ws);
+  dim3 grid((unsigned)cdiv(pk->max_joint, 64), heads, pk->B);
+  if (dt == MMDIT_BF16)
+    return D == 128 ? launch_attn_bwd<bf16, 128>(a, grid, s) : launch_attn_bwd<bf16, 64>(a, grid, s);
+  return D == 128 ? launch_attn_bwd<float, 128>(a, grid, s) : launch_attn_bwd<float, 64>(a, grid, s);
 }
 
 }  // namespace mmdit

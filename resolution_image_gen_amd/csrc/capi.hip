@@ -93,7 +93,7 @@ mmdit_status pack_latent_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const f
 mmdit_status rms_modulate_impl(mmdit_dtype, int64_t, int32_t, const void*, const int32_t*, const int32_t*, const float*, int64_t, int64_t, int64_t, void*, float, hipStream_t);
 mmdit_status qk_norm_rope_impl(mmdit_dtype, int64_t, int32_t, int32_t, void*, const int32_t*, const float*, const float*, float, float, hipStream_t);
 mmdit_status temb_impl(mmdit_dtype, int32_t, int32_t, const float*, void*, hipStream_t);
-mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, void*, size_t, hipStream_t);
+mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, void*, size_t, hipStream_t, float* lse = nullptr);
 int64_t attention_vt_elems(const mmdit_pack_t*, int32_t);
 
 namespace {
@@ -484,9 +484,44 @@ mmdit_status mmdit_linear(mmdit_dtype dt, int64_t M, int32_t N, int32_t K, const
   return linear(dt, &a, 1, (hipStream_t)stream);
 }
 
-mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
-                             void* x_img, void* x_txt, void* ws, size_t ws_bytes, mmdit_stream stream) {
-  const char* who = "mmdit_block_fwd";
+namespace {
+
+// Saved intermediates of one block for its backward, image rows then text rows
+// in every buffer (all in the model dtype except mod and lse, float32).
+struct SavedLayout {
+  size_t mod_img, mod_txt, x_in, h1, qkv, qk_raw, o, a, x_mid, h2, u_pre, dmlp, lse, end;
+};
+
+SavedLayout saved_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  const size_t es = esize(d->dtype);
+  const size_t N = (size_t)(pk->n_img + pk->n_txt);
+  const size_t H = d->hidden;
+  SavedLayout S;
+  size_t o = 0;
+  S.mod_img = o; o = align256(o + (size_t)pk->B * 6 * H * 4);
+  S.mod_txt = o; o = align256(o + (size_t)pk->B * 6 * H * 4);
+  S.x_in = o;    o = align256(o + N * H * es);
+  S.h1 = o;      o = align256(o + N * H * es);
+  S.qkv = o;     o = align256(o + N * 3 * H * es);
+  S.qk_raw = o;  o = align256(o + N * 2 * H * es);
+  S.o = o;       o = align256(o + N * H * es);
+  S.a = o;       o = align256(o + N * H * es);
+  S.x_mid = o;   o = align256(o + N * H * es);
+  S.h2 = o;      o = align256(o + N * H * es);
+  S.u_pre = o;   o = align256(o + N * (size_t)d->mlp * es);
+  S.dmlp = o;    o = align256(o + N * H * es);
+  S.lse = o;     o = align256(o + (size_t)(attention_vt_elems(pk, d->hidden) / d->head_dim) * 4);
+  S.end = o;
+  return S;
+}
+
+mmdit_status copy_rows(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return MMDIT_OK;
+  return hip_check(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+}
+
+mmdit_status check_block_args(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                              void* x_img, void* x_txt, void* ws, size_t ws_bytes, const char* who) {
   MMDIT_TRY(check_dims(d, who));
   MMDIT_TRY(check_pack(pk, who));
   if (!w) {
@@ -504,23 +539,34 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     set_error("%s: workspace needs %zu bytes, got %zu", who, L.end, ws_bytes);
     return MMDIT_E_WORKSPACE;
   }
-  MMDIT_TRY(need(ws, who, "ws"));
-  hipStream_t s = (hipStream_t)stream;
+  return need(ws, who, "ws");
+}
+
+// The block's launch sequence.  With sv (training) every intermediate the
+// backward needs is kept in sv (layout S); the arithmetic is the same.
+mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                                void* x_img, void* x_txt, void* ws, char* sv, const SavedLayout* S,
+                                hipStream_t s) {
+  const Layout L = block_layout(d, pk);
   const mmdit_dtype dt = d->dtype;
   const size_t es = esize(dt);
   const int32_t H = d->hidden;
   const int64_t ni = pk->n_img, nt = pk->n_txt;
   char* base = static_cast<char*>(ws);
-  float* mod_i = reinterpret_cast<float*>(base + L.mod_img);
-  float* mod_t = reinterpret_cast<float*>(base + L.mod_txt);
-  char* h = base + L.h;
-  char* qkv = base + L.qkv;
-  char* o = base + L.o;
+  float* mod_i = reinterpret_cast<float*>(sv ? sv + S->mod_img : base + L.mod_img);
+  float* mod_t = reinterpret_cast<float*>(sv ? sv + S->mod_txt : base + L.mod_txt);
+  char* h = sv ? sv + S->h1 : base + L.h;
+  char* qkv = sv ? sv + S->qkv : base + L.qkv;
+  char* o = sv ? sv + S->o : base + L.o;
   char* u = base + L.u;
   char* h_t = h + ni * H * es;
   char* qkv_t = qkv + ni * 3 * H * es;
   char* o_t = o + ni * H * es;
   char* u_t = u + ni * (int64_t)d->mlp * es;
+  if (sv) {
+    MMDIT_TRY(copy_rows(sv + S->x_in, x_img, ni * H * es, s));
+    MMDIT_TRY(copy_rows(sv + S->x_in + ni * H * es, x_txt, nt * H * es, s));
+  }
 
   // adaLN vectors of both streams: mod = W_mod SiLU(c)
   {
@@ -543,24 +589,44 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].tag = "qkv_proj";
     MMDIT_TRY(linear(dt, a, 2, s));
   }
+  if (sv) {   // q and k before their norm
+    const size_t w2 = 2 * (size_t)H * es, w3 = 3 * (size_t)H * es;
+    if (ni > 0)
+      MMDIT_TRY(hip_check(hipMemcpy2DAsync(sv + S->qk_raw, w2, qkv, w3, w2, ni, hipMemcpyDeviceToDevice, s),
+                          "hipMemcpy2DAsync"));
+    if (nt > 0)
+      MMDIT_TRY(hip_check(hipMemcpy2DAsync(sv + S->qk_raw + ni * w2, w2, qkv_t, w3, w2, nt,
+                                           hipMemcpyDeviceToDevice, s), "hipMemcpy2DAsync"));
+  }
   // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
   {
     QkArgs q[2] = {{qkv, pk->pos_img, w->img.g_q, w->img.g_k, ni}, {qkv_t, nullptr, w->txt.g_q, w->txt.g_k, nt}};
     MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_theta, d->eps, q, 2, s));
   }
   // o = block-diagonal joint attention
-  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s));
+  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s,
+                           sv ? reinterpret_cast<float*>(sv + S->lse) : nullptr));
   // x += gate1 * (o W_o^T)
   {
-    LinearArgs a[2] = {mk(ni, H, H, o, w->img.w_o, x_img, MMDIT_EPI_GATED_RES),
-                       mk(nt, H, H, o_t, w->txt.w_o, x_txt, MMDIT_EPI_GATED_RES)};
+    LinearArgs a[2] = {mk(ni, H, H, o, w->img.w_o, x_img, sv ? kEpiGatedResAux : MMDIT_EPI_GATED_RES),
+                       mk(nt, H, H, o_t, w->txt.w_o, x_txt, sv ? kEpiGatedResAux : MMDIT_EPI_GATED_RES)};
     a[0].gate = mod_i + 2 * H;
     a[1].gate = mod_t + 2 * H;
     a[0].gate_stride = a[1].gate_stride = 6 * H;
     a[0].seg = pk->seg_img;
     a[1].seg = pk->seg_txt;
     a[0].tag = "out_proj_gated";
+    if (sv) {
+      a[0].aux = sv + S->a;
+      a[1].aux = sv + S->a + ni * H * es;
+    }
     MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  if (sv) {
+    MMDIT_TRY(copy_rows(sv + S->x_mid, x_img, ni * H * es, s));
+    MMDIT_TRY(copy_rows(sv + S->x_mid + ni * H * es, x_txt, nt * H * es, s));
+    h = sv + S->h2;
+    h_t = h + ni * H * es;
   }
   // h = rms(x)(1 + scale2) + shift2
   {
@@ -570,15 +636,19 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   }
   // u = GELU(h W_up^T)
   {
-    LinearArgs a[2] = {mk(ni, d->mlp, H, h, w->img.w_up, u, MMDIT_EPI_GELU),
-                       mk(nt, d->mlp, H, h_t, w->txt.w_up, u_t, MMDIT_EPI_GELU)};
+    LinearArgs a[2] = {mk(ni, d->mlp, H, h, w->img.w_up, u, sv ? kEpiGeluAux : MMDIT_EPI_GELU),
+                       mk(nt, d->mlp, H, h_t, w->txt.w_up, u_t, sv ? kEpiGeluAux : MMDIT_EPI_GELU)};
     a[0].tag = "mlp_up_gelu";
+    if (sv) {
+      a[0].aux = sv + S->u_pre;
+      a[1].aux = sv + S->u_pre + ni * (int64_t)d->mlp * es;
+    }
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   // x += gate2 * (u W_down^T)
   {
-    LinearArgs a[2] = {mk(ni, H, d->mlp, u, w->img.w_down, x_img, MMDIT_EPI_GATED_RES),
-                       mk(nt, H, d->mlp, u_t, w->txt.w_down, x_txt, MMDIT_EPI_GATED_RES)};
+    LinearArgs a[2] = {mk(ni, H, d->mlp, u, w->img.w_down, x_img, sv ? kEpiGatedResAux : MMDIT_EPI_GATED_RES),
+                       mk(nt, H, d->mlp, u_t, w->txt.w_down, x_txt, sv ? kEpiGatedResAux : MMDIT_EPI_GATED_RES)};
     a[0].gate = mod_i + 5 * H;
     a[1].gate = mod_t + 5 * H;
     a[0].gate_stride = a[1].gate_stride = 6 * H;
@@ -586,9 +656,366 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[1].seg = pk->seg_txt;
     a[0].tag = "mlp_down_gated";
     a[0].site = 1;
+    if (sv) {
+      a[0].aux = sv + S->dmlp;
+      a[1].aux = sv + S->dmlp + ni * H * es;
+    }
     MMDIT_TRY(linear(dt, a, 2, s));
   }
   return MMDIT_OK;
+}
+
+}  // namespace
+
+mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                             void* x_img, void* x_txt, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  MMDIT_TRY(check_block_args(d, w, pk, c, x_img, x_txt, ws, ws_bytes, "mmdit_block_fwd"));
+  if (pk->B == 0) return MMDIT_OK;
+  return block_forward_impl(d, w, pk, c, x_img, x_txt, ws, nullptr, nullptr, (hipStream_t)stream);
+}
+
+size_t mmdit_block_saved_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  if (check_dims(d, "mmdit_block_saved_size") != MMDIT_OK || check_pack(pk, "mmdit_block_saved_size") != MMDIT_OK)
+    return 0;
+  return saved_layout(d, pk).end;
+}
+
+mmdit_status mmdit_block_fwd_train(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk,
+                                   const void* c, void* x_img, void* x_txt, void* saved, size_t saved_bytes,
+                                   void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_block_fwd_train";
+  MMDIT_TRY(check_block_args(d, w, pk, c, x_img, x_txt, ws, ws_bytes, who));
+  if (pk->B == 0) return MMDIT_OK;
+  const SavedLayout S = saved_layout(d, pk);
+  if (!saved || saved_bytes < S.end) {
+    set_error("%s: saved buffer needs %zu bytes, got %zu", who, S.end, saved_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  MMDIT_TRY(need(saved, who, "saved"));
+  return block_forward_impl(d, w, pk, c, x_img, x_txt, ws, static_cast<char*>(saved), &S, (hipStream_t)stream);
+}
+
+namespace {
+
+int64_t pad64(int64_t n) { return (n + 63) & ~(int64_t)63; }
+
+// Workspace of the block backward.
+struct BwdLayout {
+  size_t wt_down, wt_up, wt_o, wt_qkv, dd, ddT, guT, du, duT, h2T, dh2, dxmid, inv_r, da, daT, oT, dO, dqkv, dqkvT,
+      h1T, dh1, dmod, partial, gpart, attn, end;
+};
+
+BwdLayout bwd_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  const size_t es = esize(d->dtype);
+  const size_t N = (size_t)(pk->n_img + pk->n_txt);
+  const size_t NP = (size_t)(pad64(pk->n_img) + pad64(pk->n_txt));
+  const size_t H = d->hidden, M = d->mlp;
+  BwdLayout Lb;
+  size_t o = 0;
+  Lb.wt_down = o; o = align256(o + 2 * M * H * es);
+  Lb.wt_up = o;   o = align256(o + 2 * M * H * es);
+  Lb.wt_o = o;    o = align256(o + 2 * H * H * es);
+  Lb.wt_qkv = o;  o = align256(o + 2 * 3 * H * H * es);
+  Lb.dd = o;      o = align256(o + N * H * es);
+  Lb.ddT = o;     o = align256(o + H * NP * es);
+  Lb.guT = o;     o = align256(o + M * NP * es);
+  Lb.du = o;      o = align256(o + N * M * es);
+  Lb.duT = o;     o = align256(o + M * NP * es);
+  Lb.h2T = o;     o = align256(o + H * NP * es);
+  Lb.dh2 = o;     o = align256(o + N * H * es);
+  Lb.dxmid = o;   o = align256(o + N * H * 4);
+  Lb.inv_r = o;   o = align256(o + N * 4);
+  Lb.da = o;      o = align256(o + N * H * es);
+  Lb.daT = o;     o = align256(o + H * NP * es);
+  Lb.oT = o;      o = align256(o + H * NP * es);
+  Lb.dO = o;      o = align256(o + N * H * es);
+  Lb.dqkv = o;    o = align256(o + N * 3 * H * es);
+  Lb.dqkvT = o;   o = align256(o + 3 * H * NP * es);
+  Lb.h1T = o;     o = align256(o + H * NP * es);
+  Lb.dh1 = o;     o = align256(o + N * H * es);
+  Lb.dmod = o;    o = align256(o + 2 * (size_t)pk->B * 6 * H * 4);
+  const int64_t ch = colsum_chunks(pk->h_cu_img, pk->B, kColsumRows) + colsum_chunks(pk->h_cu_txt, pk->B, kColsumRows);
+  Lb.partial = o; o = align256(o + (size_t)ch * 3 * H * 4);
+  Lb.gpart = o;   o = align256(o + (size_t)(qk_bwd_blocks(pk->n_img) + qk_bwd_blocks(pk->n_txt)) * 2 * d->head_dim * 4);
+  Lb.attn = o;    o = align256(o + attention_bwd_ws_bytes(pk, d->heads, d->head_dim));
+  Lb.end = o;
+  return Lb;
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+mmdit_status fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return MMDIT_OK;
+  const int64_t blocks = cdiv(n, 256) < 4096 ? cdiv(n, 256) : 4096;
+  MMDIT_LAUNCH(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return launch_check("fill_zero_kernel", s);
+}
+
+mmdit_status check_grads(const mmdit_stream_grad& g, const char* who) {
+  const float* p[7] = {g.w_mod, g.w_qkv, g.g_q, g.g_k, g.w_o, g.w_up, g.w_down};
+  const char* n[7] = {"dw_mod", "dw_qkv", "dg_q", "dg_k", "dw_o", "dw_up", "dw_down"};
+  for (int i = 0; i < 7; ++i) MMDIT_TRY(need(p[i], who, n[i]));
+  return MMDIT_OK;
+}
+
+// Weight gradient dW [out, in] = sum over rows of dY[r, out] X[r, in] for both
+// streams: A = dY^T [out, rows padded], W = X^T [in, rows padded], float32 out.
+// A stream without rows gets a zero gradient.
+mmdit_status weight_grad(mmdit_dtype dt, int32_t out, int32_t in, const int64_t np[2], const char* dyT[2],
+                         const char* xT[2], float* dw[2], const char* tag, hipStream_t s) {
+  LinearArgs a[2];
+  int n = 0;
+  for (int i = 0; i < 2; ++i) {
+    if (np[i] == 0) {
+      MMDIT_TRY(fill_zero(dw[i], (int64_t)out * in, s));
+      continue;
+    }
+    a[n] = mk(out, in, (int32_t)np[i], dyT[i], xT[i], dw[i], MMDIT_EPI_STORE_F32);
+    a[n].tag = tag;
+    ++n;
+  }
+  return n ? linear(dt, a, n, s) : MMDIT_OK;
+}
+
+}  // namespace
+
+size_t mmdit_block_bwd_workspace_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  if (check_dims(d, "mmdit_block_bwd_workspace_size") != MMDIT_OK ||
+      check_pack(pk, "mmdit_block_bwd_workspace_size") != MMDIT_OK)
+    return 0;
+  return bwd_layout(d, pk).end;
+}
+
+mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                             const void* saved, size_t saved_bytes, void* dx_img, void* dx_txt,
+                             const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                             mmdit_stream stream) {
+  const char* who = "mmdit_block_bwd";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  if (!w || !g) {
+    set_error("%s: weights or gradients are NULL", who);
+    return MMDIT_E_INVALID;
+  }
+  MMDIT_TRY(check_stream_w(w->img, who));
+  MMDIT_TRY(check_stream_w(w->txt, who));
+  MMDIT_TRY(check_grads(g->img, who));
+  MMDIT_TRY(check_grads(g->txt, who));
+  if (pk->B == 0) return MMDIT_OK;
+  MMDIT_TRY(need(c, who, "c"));
+  MMDIT_TRY(need(dc, who, "dc"));
+  if (pk->n_img > 0) MMDIT_TRY(need(dx_img, who, "dx_img"));
+  if (pk->n_txt > 0) MMDIT_TRY(need(dx_txt, who, "dx_txt"));
+  const SavedLayout S = saved_layout(d, pk);
+  if (!saved || saved_bytes < S.end) {
+    set_error("%s: saved buffer needs %zu bytes, got %zu", who, S.end, saved_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  MMDIT_TRY(need(saved, who, "saved"));
+  const BwdLayout Lb = bwd_layout(d, pk);
+  if (!ws || ws_bytes < Lb.end) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, Lb.end, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  MMDIT_TRY(need(ws, who, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  const mmdit_dtype dt = d->dtype;
+  const size_t es = esize(dt);
+  const int32_t H = d->hidden, M = d->mlp, D = d->head_dim;
+  const int64_t ni = pk->n_img, nt = pk->n_txt;
+  const int64_t np[2] = {pad64(ni), pad64(nt)};
+  const int64_t nr[2] = {ni, nt};
+  const char* sv = static_cast<const char*>(saved);
+  char* base = static_cast<char*>(ws);
+  const float* mod[2] = {reinterpret_cast<const float*>(sv + S.mod_img), reinterpret_cast<const float*>(sv + S.mod_txt)};
+  const int32_t* seg[2] = {pk->seg_img, pk->seg_txt};
+  const mmdit_stream_w* ws_w[2] = {&w->img, &w->txt};
+  const mmdit_stream_grad* gr[2] = {&g->img, &g->txt};
+  void* dx[2] = {dx_img, dx_txt};
+  // row offset (in elements of width C) of stream i in a rows-major buffer, and
+  // in a transposed buffer with padded row counts
+  auto rows = [&](size_t off, int i, int64_t C) { return base + off + (i ? ni * C * (int64_t)es : 0); };
+  auto srows = [&](size_t off, int i, int64_t C) { return sv + off + (i ? ni * C * (int64_t)es : 0); };
+  auto trows = [&](size_t off, int i, int64_t C) { return base + off + (i ? C * np[0] * (int64_t)es : 0); };
+  auto wt = [&](size_t off, int i, int64_t elems) { return base + off + (i ? elems * (int64_t)es : 0); };
+  float* dmod[2] = {reinterpret_cast<float*>(base + Lb.dmod),
+                    reinterpret_cast<float*>(base + Lb.dmod) + (size_t)pk->B * 6 * H};
+
+  // transposed weights: W_down^T [M, H], W_up^T [H, M], W_o^T [H, H], W_qkv^T [H, 3H]
+  {
+    const struct { size_t off; int wi; int32_t O, I; } tw[4] = {
+        {Lb.wt_down, 6, H, M}, {Lb.wt_up, 5, M, H}, {Lb.wt_o, 4, H, H}, {Lb.wt_qkv, 1, 3 * H, H}};
+    for (const auto& t : tw) {
+      TransposeArgs ta[2];
+      memset(ta, 0, sizeof(ta));
+      for (int i = 0; i < 2; ++i) {
+        const void* src = t.wi == 6 ? ws_w[i]->w_down : t.wi == 5 ? ws_w[i]->w_up : t.wi == 4 ? ws_w[i]->w_o
+                                                                                              : ws_w[i]->w_qkv;
+        ta[i] = {src, wt(t.off, i, (int64_t)t.O * t.I), nullptr, nullptr, nullptr, t.I, t.O, t.O, 0, t.I};
+      }
+      MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    }
+  }
+  // MLP branch: dd = gate2 * dy (and dd^T), du = (dd W_down) * GELU'(u_pre)
+  {
+    TransposeArgs ta[2];
+    for (int i = 0; i < 2; ++i)
+      ta[i] = {dx[i], trows(Lb.ddT, i, H), rows(Lb.dd, i, H), mod[i] + 5 * H, seg[i], H, nr[i], np[i], 6 * H, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 2, s));
+  }
+  {
+    LinearArgs a[2] = {mk(ni, M, H, rows(Lb.dd, 0, H), wt(Lb.wt_down, 0, 0), rows(Lb.du, 0, M), kEpiGeluBwd),
+                       mk(nt, M, H, rows(Lb.dd, 1, H), wt(Lb.wt_down, 1, (int64_t)M * H), rows(Lb.du, 1, M), kEpiGeluBwd)};
+    a[0].aux = const_cast<char*>(srows(S.u_pre, 0, M));
+    a[1].aux = const_cast<char*>(srows(S.u_pre, 1, M));
+    a[0].tag = "bwd_mlp_down_dx";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  {
+    TransposeArgs ta[2];
+    memset(ta, 0, sizeof(ta));
+    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.u_pre, i, M), trows(Lb.guT, i, M), nullptr, nullptr, nullptr, M, nr[i], np[i], 0, M};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 1, s));
+    const char* A[2] = {trows(Lb.ddT, 0, H), trows(Lb.ddT, 1, H)};
+    const char* X[2] = {trows(Lb.guT, 0, M), trows(Lb.guT, 1, M)};
+    float* dw[2] = {gr[0]->w_down, gr[1]->w_down};
+    MMDIT_TRY(weight_grad(dt, H, M, np, A, X, dw, "bwd_mlp_down_dw", s));
+  }
+  {
+    TransposeArgs ta[2];
+    memset(ta, 0, sizeof(ta));
+    for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.du, i, M), trows(Lb.duT, i, M), nullptr, nullptr, nullptr, M, nr[i], np[i], 0, M};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.h2, i, H), trows(Lb.h2T, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    const char* A[2] = {trows(Lb.duT, 0, M), trows(Lb.duT, 1, M)};
+    const char* X[2] = {trows(Lb.h2T, 0, H), trows(Lb.h2T, 1, H)};
+    float* dw[2] = {gr[0]->w_up, gr[1]->w_up};
+    MMDIT_TRY(weight_grad(dt, M, H, np, A, X, dw, "bwd_mlp_up_dw", s));
+  }
+  {
+    LinearArgs a[2] = {mk(ni, H, M, rows(Lb.du, 0, M), wt(Lb.wt_up, 0, 0), rows(Lb.dh2, 0, H), MMDIT_EPI_STORE),
+                       mk(nt, H, M, rows(Lb.du, 1, M), wt(Lb.wt_up, 1, (int64_t)M * H), rows(Lb.dh2, 1, H), MMDIT_EPI_STORE)};
+    a[0].tag = "bwd_mlp_up_dx";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // pre-MLP norm: dx_mid = dy + rms backward; da = gate1 * dx_mid
+  float* dxmid = reinterpret_cast<float*>(base + Lb.dxmid);
+  float* inv_r = reinterpret_cast<float*>(base + Lb.inv_r);
+  {
+    NormBwdSpec nb[2];
+    for (int i = 0; i < 2; ++i)
+      nb[i] = {srows(S.x_mid, i, H), rows(Lb.dh2, i, H), mod[i], seg[i], dx[i], dxmid + (i ? ni * H : 0),
+               inv_r + (i ? ni : 0), mod[i], rows(Lb.da, i, H), nr[i], 6 * H, 4 * H, 2 * H, 0, 1};
+    MMDIT_TRY(norm_bwd2_impl(dt, H, d->eps, nb, 2, s));
+  }
+  float* partial = reinterpret_cast<float*>(base + Lb.partial);
+  auto colsums = [&](int i, int nterms, const void* const* A, const void* const* Bm, const float* const* rs,
+                     const int32_t* af, const int32_t* bf, const int32_t* off) -> mmdit_status {
+    ColsumSpec sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.nterms = nterms;
+    for (int k = 0; k < nterms; ++k) {
+      sp.a[k] = A[k];
+      sp.b[k] = Bm[k];
+      sp.rs[k] = rs[k];
+      sp.a_f32[k] = af[k];
+      sp.b_f32[k] = bf[k];
+      sp.out_off[k] = off[k];
+    }
+    sp.cu = i ? pk->cu_txt : pk->cu_img;
+    sp.h_cu = i ? pk->h_cu_txt : pk->h_cu_img;
+    sp.B = pk->B;
+    sp.H = H;
+    sp.partial = partial;
+    sp.out = dmod[i];
+    sp.out_stride = 6 * H;
+    return seg_colsum_impl(dt, sp, s);
+  };
+  for (int i = 0; i < 2; ++i) {
+    // d shift2 = sum dh2, d scale2 = sum dh2 * rms(x_mid), d gate2 = sum dy * mlp_out
+    const void* A[3] = {rows(Lb.dh2, i, H), rows(Lb.dh2, i, H), dx[i]};
+    const void* Bm[3] = {nullptr, srows(S.x_mid, i, H), srows(S.dmlp, i, H)};
+    const float* rs[3] = {nullptr, inv_r + (i ? ni : 0), nullptr};
+    const int32_t af[3] = {0, 0, 0}, bf[3] = {0, 0, 0}, off[3] = {3 * H, 4 * H, 5 * H};
+    MMDIT_TRY(colsums(i, 3, A, Bm, rs, af, bf, off));
+    // d gate1 = sum dx_mid * attn_out
+    const void* A1[1] = {dxmid + (i ? ni * H : 0)};
+    const void* B1[1] = {srows(S.a, i, H)};
+    const float* r1[1] = {nullptr};
+    const int32_t af1[1] = {1}, bf1[1] = {0}, off1[1] = {2 * H};
+    MMDIT_TRY(colsums(i, 1, A1, B1, r1, af1, bf1, off1));
+  }
+  // attention output projection: dO = da W_o, dW_o = da^T o
+  {
+    LinearArgs a[2] = {mk(ni, H, H, rows(Lb.da, 0, H), wt(Lb.wt_o, 0, 0), rows(Lb.dO, 0, H), MMDIT_EPI_STORE),
+                       mk(nt, H, H, rows(Lb.da, 1, H), wt(Lb.wt_o, 1, (int64_t)H * H), rows(Lb.dO, 1, H), MMDIT_EPI_STORE)};
+    a[0].tag = "bwd_out_proj_dx";
+    MMDIT_TRY(linear(dt, a, 2, s));
+    TransposeArgs ta[2];
+    memset(ta, 0, sizeof(ta));
+    for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.da, i, H), trows(Lb.daT, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.o, i, H), trows(Lb.oT, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    const char* A[2] = {trows(Lb.daT, 0, H), trows(Lb.daT, 1, H)};
+    const char* X[2] = {trows(Lb.oT, 0, H), trows(Lb.oT, 1, H)};
+    float* dw[2] = {gr[0]->w_o, gr[1]->w_o};
+    MMDIT_TRY(weight_grad(dt, H, H, np, A, X, dw, "bwd_out_proj_dw", s));
+  }
+  // joint attention, then QK-norm + RoPE
+  MMDIT_TRY(attention_bwd_impl(dt, pk, d->heads, D, srows(S.qkv, 0, 3 * H), srows(S.qkv, 1, 3 * H), srows(S.o, 0, H),
+                               srows(S.o, 1, H), reinterpret_cast<const float*>(sv + S.lse), rows(Lb.dO, 0, H),
+                               rows(Lb.dO, 1, H), rows(Lb.dqkv, 0, 3 * H), rows(Lb.dqkv, 1, 3 * H), base + Lb.attn,
+                               Lb.end - Lb.attn, s));
+  {
+    float* gp = reinterpret_cast<float*>(base + Lb.gpart);
+    QkBwdSpec q[2] = {{rows(Lb.dqkv, 0, 3 * H), srows(S.qk_raw, 0, 2 * H), pk->pos_img, w->img.g_q, w->img.g_k, gp,
+                       g->img.g_q, g->img.g_k, ni},
+                      {rows(Lb.dqkv, 1, 3 * H), srows(S.qk_raw, 1, 2 * H), nullptr, w->txt.g_q, w->txt.g_k,
+                       gp + qk_bwd_blocks(ni) * 2 * D, g->txt.g_q, g->txt.g_k, nt}};
+    MMDIT_TRY(qk_bwd2_impl(dt, d->heads, D, d->rope_theta, d->eps, q, 2, s));
+  }
+  // QKV projection: dW_qkv = dqkv^T h1, dh1 = dqkv W_qkv
+  {
+    TransposeArgs ta[2];
+    memset(ta, 0, sizeof(ta));
+    for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.dqkv, i, 3 * H), trows(Lb.dqkvT, i, 3 * H), nullptr, nullptr, nullptr, 3 * H, nr[i], np[i], 0, 3 * H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.h1, i, H), trows(Lb.h1T, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    const char* A[2] = {trows(Lb.dqkvT, 0, 3 * H), trows(Lb.dqkvT, 1, 3 * H)};
+    const char* X[2] = {trows(Lb.h1T, 0, H), trows(Lb.h1T, 1, H)};
+    float* dw[2] = {gr[0]->w_qkv, gr[1]->w_qkv};
+    MMDIT_TRY(weight_grad(dt, 3 * H, H, np, A, X, dw, "bwd_qkv_dw", s));
+    LinearArgs a[2] = {mk(ni, H, 3 * H, rows(Lb.dqkv, 0, 3 * H), wt(Lb.wt_qkv, 0, 0), rows(Lb.dh1, 0, H), MMDIT_EPI_STORE),
+                       mk(nt, H, 3 * H, rows(Lb.dqkv, 1, 3 * H), wt(Lb.wt_qkv, 1, (int64_t)3 * H * H), rows(Lb.dh1, 1, H),
+                          MMDIT_EPI_STORE)};
+    a[0].tag = "bwd_qkv_dx";
+    MMDIT_TRY(linear(dt, a, 2, s));
+  }
+  // pre-attention norm: dx_in = dx_mid + rms backward (written over dy)
+  {
+    NormBwdSpec nb[2];
+    for (int i = 0; i < 2; ++i)
+      nb[i] = {srows(S.x_in, i, H), rows(Lb.dh1, i, H), mod[i], seg[i], dxmid + (i ? ni * H : 0), dx[i],
+               inv_r + (i ? ni : 0), nullptr, nullptr, nr[i], 6 * H, H, 0, 1, 0};
+    MMDIT_TRY(norm_bwd2_impl(dt, H, d->eps, nb, 2, s));
+  }
+  for (int i = 0; i < 2; ++i) {
+    // d shift1 = sum dh1, d scale1 = sum dh1 * rms(x_in)
+    const void* A[2] = {rows(Lb.dh1, i, H), rows(Lb.dh1, i, H)};
+    const void* Bm[2] = {nullptr, srows(S.x_in, i, H)};
+    const float* rs[2] = {nullptr, inv_r + (i ? ni : 0)};
+    const int32_t af[2] = {0, 0}, bf[2] = {0, 0}, off[2] = {0, H};
+    MMDIT_TRY(colsums(i, 2, A, Bm, rs, af, bf, off));
+  }
+  // adaLN: dW_mod = d_mod^T SiLU(c), dc += (d_mod W_mod) SiLU'(c)
+  return mod_grads_impl(dt, pk->B, H, c, dmod[0], dmod[1], w->img.w_mod, w->txt.w_mod, g->img.w_mod, g->txt.w_mod,
+                        dc, s);
 }
 
 mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,

@@ -101,6 +101,10 @@ __device__ __forceinline__ float erf_as(float x) {
 }
 // GELU in its erf form, 0.5 x (1 + erf(x / sqrt 2)).
 __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
+// Its derivative Phi(x) + x phi(x), with the same erf.
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  return 0.5f * (1.0f + erf_as(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+}
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -123,7 +127,12 @@ struct LinearArgs {
   int32_t site;            // 1: MLP down projection (own kernel instantiation for profiling)
   float* partial;          // optional float32 workspace for split-K (single problem)
   int64_t partial_elems;
+  void* aux;               // [M, N] dense, model dtype: second output or input of the epilogues below
 };
+// Epilogues used inside the library only (the public ones are mmdit_epilogue):
+constexpr int kEpiGeluAux = 4;      // Y = GELU(acc) and aux = acc (the pre-activation kept for backward)
+constexpr int kEpiGatedResAux = 5;  // Y += gate[seg] * acc and aux = acc (the branch kept for backward)
+constexpr int kEpiGeluBwd = 6;      // Y = acc * GELU'(aux), aux the saved pre-activation
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 
 // RMSNorm + adaLN modulate of up to two row sets in one launch.
@@ -147,5 +156,89 @@ struct QkArgs {
 };
 mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkArgs* a,
                                 int n, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+// [n, C] (row stride ldx) -> [C, npad] with zero columns n..npad; op 0 copy,
+// 1 GELU of the input, 2 rows scaled by gate[seg[m] * gate_stride + c] (the
+// scaled rows also written to y_rows [n, C] when it is not NULL).
+struct TransposeArgs {
+  const void* x;
+  void* y;
+  void* y_rows;
+  const float* gate;
+  const int32_t* seg;
+  int64_t ldx, n, npad, gate_stride;
+  int32_t C;
+};
+mmdit_status transpose2_impl(mmdit_dtype dt, const TransposeArgs* t, int n, int op, hipStream_t s);
+
+// Per-sample column sums out[b][out_off[k] + c] = sum over the rows of sample
+// b of a_k[r][c] * b_k[r][c] * rs_k[r] (b_k, rs_k optional), in row chunks of
+// kColsumRows summed in a fixed order.  partial: [chunks][nterms][H] floats.
+constexpr int kColsumRows = 256;
+struct ColsumSpec {
+  const void* a[3];
+  const void* b[3];
+  const float* rs[3];
+  int32_t a_f32[3], b_f32[3], out_off[3];
+  int32_t nterms;
+  const int32_t* cu;     // device [B + 1]
+  const int32_t* h_cu;   // host copy
+  int32_t B, H;
+  float* partial;
+  float* out;
+  int64_t out_stride;
+};
+int64_t colsum_chunks(const int32_t* h_cu, int32_t B, int32_t rc);
+mmdit_status seg_colsum_impl(mmdit_dtype dt, const ColsumSpec& sp, hipStream_t s);
+
+// Backward of h = rms(x)(1 + scale) + shift for up to two row sets:
+// dx = dres + (dn - n mean(dn n)) / rms(x) with dn = dh (1 + scale); also
+// 1/rms per row and, optionally, dgated = gate * dx.
+struct NormBwdSpec {
+  const void* x;
+  const void* dh;
+  const float* mod;
+  const int32_t* seg;
+  const void* dres;
+  void* dx;
+  float* inv_r;
+  const float* gate;
+  void* dgated;
+  int64_t n, mod_stride;
+  int32_t scale_off, gate_off, dres_f32, dx_f32;
+};
+mmdit_status norm_bwd2_impl(mmdit_dtype dt, int32_t H, float eps, const NormBwdSpec* p, int n, hipStream_t s);
+
+// Backward of q' = RoPE(g_q * rms(q)) (and k) per head, in place on the q, k
+// columns of dqkv [n, 3H]; raw [n, 2H] holds q, k before the norm.  The gain
+// gradients go to dg_q, dg_k [D] (float32) through per-block partials gpart.
+struct QkBwdSpec {
+  void* dqkv;
+  const void* raw;
+  const int32_t* pos;
+  const float* g_q;
+  const float* g_k;
+  float* gpart;
+  float* dg_q;
+  float* dg_k;
+  int64_t n;
+};
+int64_t qk_bwd_blocks(int64_t n_rows);
+mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkBwdSpec* p,
+                          int n, hipStream_t s);
+
+// dW_mod = d_mod^T SiLU(c) per stream ([6H, H] float32) and
+// dc += (d_mod W_mod) * SiLU'(c) summed over both streams.
+mmdit_status mod_grads_impl(mmdit_dtype dt, int32_t B, int32_t H, const void* c, const float* dmod_i,
+                            const float* dmod_t, const void* w_i, const void* w_t, float* dw_i, float* dw_t,
+                            float* dc, hipStream_t s);
+
+// Attention backward over a pack (see attention.hip); ws >= attention_bwd_ws_bytes.
+size_t attention_bwd_ws_bytes(const mmdit_pack_t* pk, int32_t heads, int32_t D);
+mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t heads, int32_t D,
+                                const void* qkv_img, const void* qkv_txt, const void* o_img, const void* o_txt,
+                                const float* lse, const void* do_img, const void* do_txt, void* dqkv_img,
+                                void* dqkv_txt, void* ws, size_t ws_bytes, hipStream_t s);
 
 }  // namespace mmdit

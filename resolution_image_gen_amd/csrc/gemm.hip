@@ -28,6 +28,7 @@ struct GemmProb {
   void* Y;
   const float* gate;
   const int32_t* seg;
+  void* aux;            // [M, N] dense (kEpi*Aux outputs, kEpiGeluBwd input)
   int64_t lda, ldy, gate_stride, M;
   int32_t N, K;
   int32_t tiles_n;
@@ -63,10 +64,17 @@ __device__ __forceinline__ void epi_store(const GemmProb& P, int64_t m, int n, f
     static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(acc);
   } else if constexpr (EPI == MMDIT_EPI_GELU) {
     static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(gelu_f(acc));
+  } else if constexpr (EPI == kEpiGeluAux) {
+    static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(gelu_f(acc));
+    static_cast<T*>(P.aux)[m * P.N + n] = from_f<T>(acc);
+  } else if constexpr (EPI == kEpiGeluBwd) {
+    const float x = to_f(static_cast<const T*>(P.aux)[m * P.N + n]);
+    static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(acc * gelu_grad_f(x));
   } else {
     T* y = static_cast<T*>(P.Y) + m * P.ldy + n;
     const float g = P.gate[(int64_t)P.seg[m] * P.gate_stride + n];
     *y = from_f<T>(to_f(*y) + g * acc);
+    if constexpr (EPI == kEpiGatedResAux) static_cast<T*>(P.aux)[m * P.N + n] = from_f<T>(acc);
   }
 }
 
@@ -557,15 +565,22 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
         if constexpr (EPI == MMDIT_EPI_STORE) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = a[k];
-        } else if constexpr (EPI == MMDIT_EPI_GELU) {
+        } else if constexpr (EPI == MMDIT_EPI_GELU || EPI == kEpiGeluAux) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = gelu_f(a[k]);
+          if constexpr (EPI == kEpiGeluAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
+        } else if constexpr (EPI == kEpiGeluBwd) {
+          float xv[8];
+          Vec8<bf16>::load(static_cast<const bf16*>(P.aux) + m * P.N + n, xv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = a[k] * gelu_grad_f(xv[k]);
         } else {
           float xv[8], gv[8];
           Vec8<bf16>::load(y, xv);
           Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + n, gv);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
+          if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
         }
         Vec8<bf16>::store(y, o);
       }
@@ -951,7 +966,9 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
       return MMDIT_E_INVALID;
     }
     if (a.M == 0) continue;
-    if (!a.A || !a.W || !a.Y || (epi == MMDIT_EPI_GATED_RES && (!a.gate || !a.seg))) {
+    const bool gated = epi == MMDIT_EPI_GATED_RES || epi == kEpiGatedResAux;
+    const bool with_aux = epi == kEpiGeluAux || epi == kEpiGatedResAux || epi == kEpiGeluBwd;
+    if (!a.A || !a.W || !a.Y || (gated && (!a.gate || !a.seg)) || (with_aux && !a.aux)) {
       set_error("linear: NULL pointer");
       return MMDIT_E_INVALID;
     }
@@ -961,6 +978,7 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     p.Y = a.Y;
     p.gate = a.gate;
     p.seg = a.seg;
+    p.aux = a.aux;
     p.lda = a.lda;
     p.ldy = a.ldy;
     p.gate_stride = a.gate_stride;
@@ -989,6 +1007,9 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     case MMDIT_EPI_STORE_F32 * 2 + 1: return dispatch<MMDIT_EPI_STORE_F32, true>(dt, path, bt, s);
     case MMDIT_EPI_GELU * 2: return dispatch<MMDIT_EPI_GELU, false>(dt, path, bt, s);
     case MMDIT_EPI_GATED_RES * 2: return dispatch<MMDIT_EPI_GATED_RES, false>(dt, path, bt, s);
+    case kEpiGeluAux * 2: return dispatch<kEpiGeluAux, false>(dt, path, bt, s);
+    case kEpiGatedResAux * 2: return dispatch<kEpiGatedResAux, false>(dt, path, bt, s);
+    case kEpiGeluBwd * 2: return dispatch<kEpiGeluBwd, false>(dt, path, bt, s);
     default:
       set_error("linear: unsupported epilogue %d (a_silu=%d)", epi, silu);
       return MMDIT_E_UNSUPPORTED;
