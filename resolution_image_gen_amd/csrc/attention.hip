@@ -554,6 +554,389 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_simt_kernel(AttnBwdArgs a) 
   }
 }
 
+// ------------------------------------------------------ backward (MFMA)
+// bf16 path.  A pre-pass writes D_i and the transposes Q^T, K^T, dO^T
+// ([head][d][padded joint token], zeros past a sample's end); then
+//   attn_bwd_dq_kernel   the forward's shape: 4 waves x 32 queries, q and dO
+//                        in registers, 32-key tiles of K, V, K^T staged in LDS;
+//                        S^T = K Q^T and dP^T = V dO^T per tile, then
+//                        dQ^T += K^T dS^T with dS^T straight from registers
+//   attn_bwd_dkdv_kernel the transpose roles: 4 waves x 32 keys, k (and v) in
+//                        registers, 32-query tiles in LDS; S = Q K^T, then
+//                        either dV^T += dO^T P (tiles Q, dO^T, lse) or, with
+//                        dP = dO V^T, dK^T += Q^T dS (tiles Q, dO, Q^T, lse, D).
+//                        Two launches: S is computed twice, but each kernel
+//                        fits two waves per SIMD without spilling.
+// The rows of the 32-row A operands are read in the order kperm (bits 2 and 3
+// swapped) so that each lane's 8 values of a 16-deep k-step are 8 consecutive
+// tokens and the matching transposed operand is one 16-byte LDS read.
+
+// 64-byte rows (32 tokens): chunk c of row d sits at c ^ tsw(d).
+__device__ __forceinline__ int tsw(int d) { return (d >> 1) & 3; }
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_prep_kernel(AttnBwdArgs a, bf16* __restrict__ qt, bf16* __restrict__ kt,
+                                                            bf16* __restrict__ gt) {
+  __shared__ bf16 t[64][D + 2];
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t kv0 = blockIdx.x * 64;
+  if (kv0 >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  constexpr int DCH = D / 8;
+  // D_i = dO_i . O_i, four lanes per token
+  {
+    const int sub = threadIdx.x & 3, r = threadIdx.x >> 2;
+    const int32_t j = kv0 + r;
+    float acc = 0.f;
+    if (j < L) {
+      const bf16* go = grad_row<bf16>(a, j, Tb, t0, i0) + head * D + sub * (D / 4);
+      const bf16* o = out_row<bf16>(a.f, j, Tb, t0, i0) + head * D + sub * (D / 4);
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) acc = fmaf((float)go[e], (float)o[e], acc);
+    }
+    acc = group_sum(acc, 4);
+    if (sub == 0) a.dsum[(int64_t)head * a.f.njp + pstart + j] = j < L ? acc : 0.f;
+  }
+  for (int which = 0; which < 3; ++which) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < 64 * DCH; q += 256) {
+      const int r = q / DCH, c = q % DCH;
+      bf16x8 v = {};
+      const int32_t j = kv0 + r;
+      if (j < L) {
+        const bf16* src = which == 2 ? grad_row<bf16>(a, j, Tb, t0, i0) + head * D
+                                     : joint_row<bf16>(a.f, j, Tb, t0, i0) + which * a.f.H + head * D;
+        v = *reinterpret_cast<const bf16x8*>(src + c * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[r][c * 8 + e] = v[e];
+    }
+    __syncthreads();
+    bf16* dst = which == 0 ? qt : which == 1 ? kt : gt;
+    for (int q = threadIdx.x; q < D * 8; q += 256) {
+      const int d = q >> 3, c = q & 7;
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = t[c * 8 + e][d];
+      *reinterpret_cast<bf16x8*>(dst + ((int64_t)head * D + d) * a.f.njp + pstart + kv0 + c * 8) = v;
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a, const bf16* __restrict__ kt) {
+  constexpr int BK = 32;                 // keys per stage
+  constexpr int DT = D / 32, QS = D / 16;
+  constexpr int KROWS = 512 / D;         // rows of a row-major tile per 1-KB block
+  constexpr int RB = D / 64;             // 1-KB blocks per wave per tile
+  constexpr int TILE = BK * D;
+  constexpr int STAGE = 3 * TILE;        // K, V, K^T
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t qbase = blockIdx.x * 128;
+  if (qbase >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int32_t jq = qbase + wave * 32 + l32;
+  bf16x8 qf[QS], gf[QS];
+  float lse = 0.f, dsum = 0.f;
+  if (jq < L) {
+    const bf16* r = joint_row<bf16>(a.f, jq, Tb, t0, i0) + head * D + g * 8;
+    const bf16* gr = grad_row<bf16>(a, jq, Tb, t0, i0) + head * D + g * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) {
+      qf[s2] = *reinterpret_cast<const bf16x8*>(r + s2 * 16);
+      gf[s2] = *reinterpret_cast<const bf16x8*>(gr + s2 * 16);
+    }
+    lse = a.f.lse[(int64_t)head * a.f.njp + pstart + jq];
+    dsum = a.dsum[(int64_t)head * a.f.njp + pstart + jq];
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) qf[s2] = gf[s2] = bf16x8{};
+  }
+
+  const int kr = lane / (D / 8), kp = lane % (D / 8);
+  const uint32_t rowb = 3u * (uint32_t)a.f.H * 2u;
+  const char* ktxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_txt) + (int64_t)t0 * 3 * a.f.H + a.f.H + head * D);
+  const char* kimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_img) + ((int64_t)i0 - Tb) * 3 * a.f.H + a.f.H + head * D);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kswc[RB];
+  const bf16* tsrc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    kswc[i] = ((kp ^ ksw<D>((wave + 4 * i) * KROWS + kr)) << 4);
+    const int d = (wave + 4 * i) * 16 + (lane >> 2);
+    tsrc[i] = kt + ((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3);
+  }
+  auto issue = [&](int32_t kv0, int st) {
+    bf16* ks = smem + st * STAGE;
+    bf16* vs = ks + TILE;
+    bf16* ts = vs + TILE;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int blk = wu + 4 * i;
+      const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);   // keys past L are masked
+      const char* kb = (key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]);
+      load_lds16(kb, ks + blk * 512);
+      load_lds16(kb + a.f.H * 2, vs + blk * 512);
+      load_lds16(tsrc[i] + kv0, ts + blk * 512);
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dq[t][v] = 0.f;
+  const int ntile = (L + BK - 1) / BK;
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int prow = (l32 & 16) | kperm(l32 & 15);
+  for (int it = 0; it < ntile; ++it) {
+    const int st = it & 1;
+    const int32_t kv0 = it * BK;
+    if (it + 1 < ntile) issue(kv0 + BK, st ^ 1);
+    const bf16* ks = smem + st * STAGE;
+    const bf16* vs = ks + TILE;
+    const bf16* ts = vs + TILE;
+    f32x16 sc, dp;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = dp[v] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) {
+      const int off = prow * D + (((s2 * 2 + g) ^ ksw<D>(prow)) << 3);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ks + off), qf[s2], sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vs + off), gf[s2], dp, 0, 0, 0);
+    }
+    // register v holds key kv0 + 16 (v / 8) + 8 g + v % 8 of this lane's query
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int32_t key = kv0 + 16 * (v >> 3) + 8 * g + (v & 7);
+      const float p = key < L ? __builtin_amdgcn_exp2f(fmaf(sc[v], a.f.scale_log2, -lse)) : 0.f;
+      sc[v] = p * (dp[v] - dsum);
+    }
+    // dQ^T[d][query] += K^T[d][keys] dS^T[keys][query]
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      bf16x8 pf;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pf[u] = (bf16)sc[8 * ks2 + u];
+      const int c = 2 * ks2 + g;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int d = t * 32 + l32;
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(ts + d * BK + ((c ^ tsw(d)) << 3));
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, pf, dq[t], 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (jq < L) {
+    bf16* o = dqkv_row<bf16>(a, jq, Tb, t0, i0) + head * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        bf16x4 w = {(bf16)(dq[t][4 * vg] * a.inv_sqrt_d), (bf16)(dq[t][4 * vg + 1] * a.inv_sqrt_d),
+                    (bf16)(dq[t][4 * vg + 2] * a.inv_sqrt_d), (bf16)(dq[t][4 * vg + 3] * a.inv_sqrt_d)};
+        *reinterpret_cast<bf16x4*>(o + t * 32 + 8 * vg + 4 * g) = w;
+      }
+  }
+}
+
+template <int D, bool DK>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, const bf16* __restrict__ qt,
+                                                               const bf16* __restrict__ gt) {
+  constexpr int BQ = 32;                 // queries per stage
+  constexpr int DT = D / 32, QS = D / 16;
+  constexpr int KROWS = 512 / D;
+  constexpr int RB = D / 64;
+  constexpr int TILE = BQ * D;
+  // Q, then dO and Q^T (dK) or dO^T (dV), then lse and D (float)
+  constexpr int NT = DK ? 3 : 2;
+  constexpr int STAGE = NT * TILE + 2 * BQ * 2;
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
+  const int32_t Tb = a.f.cu_txt[b + 1] - t0;
+  const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
+  const int32_t kbase = blockIdx.x * 128;
+  if (kbase >= L) return;
+  const int32_t pstart = padded_start(a.f, b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int32_t jk = kbase + wave * 32 + l32;
+  bf16x8 kf[QS], vf[DK ? QS : 1];
+  if (jk < L) {
+    const bf16* r = joint_row<bf16>(a.f, jk, Tb, t0, i0) + head * D + g * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) {
+      kf[s2] = *reinterpret_cast<const bf16x8*>(r + a.f.H + s2 * 16);
+      if constexpr (DK) vf[s2] = *reinterpret_cast<const bf16x8*>(r + 2 * a.f.H + s2 * 16);
+    }
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) {
+      kf[s2] = bf16x8{};
+      if constexpr (DK) vf[s2] = bf16x8{};
+    }
+  }
+
+  const int kr = lane / (D / 8), kp = lane % (D / 8);
+  const uint32_t rowq = 3u * (uint32_t)a.f.H * 2u, rowg = (uint32_t)a.f.H * 2u;
+  const char* qtxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_txt) + (int64_t)t0 * 3 * a.f.H + head * D);
+  const char* qimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_img) + ((int64_t)i0 - Tb) * 3 * a.f.H + head * D);
+  const char* gtxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.do_txt) + (int64_t)t0 * a.f.H + head * D);
+  const char* gimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.do_img) + ((int64_t)i0 - Tb) * a.f.H + head * D);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kswc[RB];
+  int64_t toff[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    kswc[i] = ((kp ^ ksw<D>((wave + 4 * i) * KROWS + kr)) << 4);
+    const int d = (wave + 4 * i) * 16 + (lane >> 2);
+    toff[i] = ((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3);
+  }
+  const bf16* tsrc = DK ? qt : gt;   // the transposed operand: Q^T (dK) or dO^T (dV)
+  const float* lse_g = a.f.lse + (int64_t)head * a.f.njp + pstart;
+  const float* ds_g = a.dsum + (int64_t)head * a.f.njp + pstart;
+  auto issue = [&](int32_t q0, int st) {
+    bf16* qs = smem + st * STAGE;
+    bf16* gs = qs + TILE;                  // dO (dK only)
+    bf16* ts = qs + (NT - 1) * TILE;       // the transposed tile
+    float* lf = reinterpret_cast<float*>(qs + NT * TILE);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int blk = wu + 4 * i;
+      const int32_t q = min(q0 + blk * KROWS + kr, L - 1);   // queries past L are masked
+      load_lds16((q < Tb ? qtxt : qimg) + ((uint32_t)q * rowq + kswc[i]), qs + blk * 512);
+      if constexpr (DK) load_lds16((q < Tb ? gtxt : gimg) + ((uint32_t)q * rowg + kswc[i]), gs + blk * 512);
+      load_lds16(tsrc + toff[i] + q0, ts + blk * 512);
+    }
+    if (tid < BQ) {   // padded positions hold values that the mask never uses
+      lf[tid] = lse_g[q0 + tid];
+      if constexpr (DK) lf[BQ + tid] = ds_g[q0 + tid];
+    }
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  const int ntile = (L + BQ - 1) / BQ;
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int prow = (l32 & 16) | kperm(l32 & 15);
+  for (int it = 0; it < ntile; ++it) {
+    const int st = it & 1;
+    const int32_t q0 = it * BQ;
+    if (it + 1 < ntile) issue(q0 + BQ, st ^ 1);
+    const bf16* qs = smem + st * STAGE;
+    const bf16* gs = qs + TILE;
+    const bf16* ts = qs + (NT - 1) * TILE;
+    const float* lf = reinterpret_cast<const float*>(qs + NT * TILE);
+    f32x16 sc, dp;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = dp[v] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < QS; ++s2) {
+      const int off = prow * D + (((s2 * 2 + g) ^ ksw<D>(prow)) << 3);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qs + off), kf[s2], sc, 0, 0, 0);
+      if constexpr (DK)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gs + off), vf[s2], dp, 0, 0, 0);
+    }
+    // register v holds query q0 + 16 (v / 8) + 8 g + v % 8 of this lane's key
+    bf16x8 pf[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float lv[8], dv8[8];
+      const int qi = 16 * h + 8 * g;
+      *reinterpret_cast<f32x4*>(lv) = *reinterpret_cast<const f32x4*>(lf + qi);
+      *reinterpret_cast<f32x4*>(lv + 4) = *reinterpret_cast<const f32x4*>(lf + qi + 4);
+      if constexpr (DK) {
+        *reinterpret_cast<f32x4*>(dv8) = *reinterpret_cast<const f32x4*>(lf + BQ + qi);
+        *reinterpret_cast<f32x4*>(dv8 + 4) = *reinterpret_cast<const f32x4*>(lf + BQ + qi + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = 8 * h + u;
+        const float p = (q0 + qi + u < L) ? __builtin_amdgcn_exp2f(fmaf(sc[v], a.f.scale_log2, -lv[u])) : 0.f;
+        pf[h][u] = DK ? (bf16)(p * (dp[v] - dv8[u])) : (bf16)p;
+      }
+    }
+    // dV^T[d][key] += dO^T[d][queries] P[queries][key], or dK^T += Q^T dS
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int c = 2 * ks2 + g;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int d = t * 32 + l32;
+        const int off = d * BQ + ((c ^ tsw(d)) << 3);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ts + off), pf[ks2], acc[t], 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (jk < L) {
+    bf16* o = dqkv_row<bf16>(a, jk, Tb, t0, i0) + head * D + (DK ? a.f.H : 2 * a.f.H);
+    const float sc = DK ? a.inv_sqrt_d : 1.0f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        bf16x4 w = {(bf16)(acc[t][4 * vg] * sc), (bf16)(acc[t][4 * vg + 1] * sc), (bf16)(acc[t][4 * vg + 2] * sc),
+                    (bf16)(acc[t][4 * vg + 3] * sc)};
+        *reinterpret_cast<bf16x4*>(o + t * 32 + 8 * vg + 4 * g) = w;
+      }
+  }
+}
+
+template <int D>
+mmdit_status launch_attn_bwd_mfma(const AttnBwdArgs& a, const mmdit_pack_t* pk, bf16* qt, bf16* kt, bf16* gt,
+                                  hipStream_t s) {
+  const int heads = a.f.heads;
+  MMDIT_LAUNCH(attn_bwd_prep_kernel<D>, dim3((unsigned)cdiv(pk->max_joint, 64), heads, pk->B), dim3(256), 0, s, a, qt,
+               kt, gt);
+  MMDIT_TRY(launch_check("attn_bwd_prep_kernel", s));
+  const size_t lds_dq = 2 * 3 * 32 * D * sizeof(bf16);
+  const size_t lds_dk = 2 * (3 * 32 * D * sizeof(bf16) + 2 * 32 * sizeof(float));
+  const size_t lds_dv = 2 * (2 * 32 * D * sizeof(bf16) + 2 * 32 * sizeof(float));
+  static bool attr = false;
+  if (!attr) {
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<D>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq),
+                        "hipFuncSetAttribute(attn_bwd_dq_kernel)"));
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, true>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dk),
+                        "hipFuncSetAttribute(attn_bwd_dk_kernel)"));
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, false>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dv),
+                        "hipFuncSetAttribute(attn_bwd_dv_kernel)"));
+    attr = true;
+  }
+  dim3 grid((unsigned)cdiv(pk->max_joint, 128), heads, pk->B);
+  MMDIT_LAUNCH(attn_bwd_dq_kernel<D>, grid, dim3(256), lds_dq, s, a, kt);
+  MMDIT_TRY(launch_check("attn_bwd_dq_kernel", s));
+  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, true>), grid, dim3(256), lds_dk, s, a, qt, gt);
+  MMDIT_TRY(launch_check("attn_bwd_dk_kernel", s));
+  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, false>), grid, dim3(256), lds_dv, s, a, qt, gt);
+  return launch_check("attn_bwd_dv_kernel", s);
+}
+
 template <typename T, int D>
 mmdit_status launch_attn_bwd(const AttnBwdArgs& a, dim3 grid, hipStream_t s) {
   MMDIT_LAUNCH((attn_bwd_dsum_kernel<T, D>), grid, dim3(256), 0, s, a);
@@ -640,7 +1023,9 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
 }
 
 size_t attention_bwd_ws_bytes(const mmdit_pack_t* pk, int32_t heads, int32_t D) {
-  return (size_t)(attention_vt_elems(pk, heads * D) / D) * sizeof(float);
+  // D_i (float32) + Q^T, K^T, dO^T (bf16), all over the padded joint axis
+  const size_t njp_h = (size_t)(attention_vt_elems(pk, heads * D) / D);   // heads x njp
+  return ((njp_h * sizeof(float) + 255) & ~(size_t)255) + 3 * njp_h * D * sizeof(bf16);
 }
 
 mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t heads, int32_t D,
@@ -671,10 +1056,19 @@ mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t 
     set_error("attention backward: workspace needs %zu bytes, got %zu", need, ws_bytes);
     return MMDIT_E_WORKSPACE;
   }
+  const size_t njp_h = (size_t)(attention_vt_elems(pk, heads * D) / D);
   a.dsum = static_cast<float*>(ws);
+  if (dt == MMDIT_BF16) {
+    if ((double)pk->max_joint * 3.0 * a.f.H * 2.0 >= 2147483648.0) {
+      set_error("attention backward: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31)");
+      return MMDIT_E_UNSUPPORTED;
+    }
+    bf16* qt = reinterpret_cast<bf16*>(static_cast<char*>(ws) + ((njp_h * sizeof(float) + 255) & ~(size_t)255));
+    bf16* kt = qt + njp_h * D;
+    bf16* gt = kt + njp_h * D;
+    return D == 128 ? launch_attn_bwd_mfma<128>(a, pk, qt, kt, gt, s) : launch_attn_bwd_mfma<64>(a, pk, qt, kt, gt, s);
+  }
   dim3 grid((unsigned)cdiv(pk->max_joint, 64), heads, pk->B);
-  if (dt == MMDIT_BF16)
-    return D == 128 ? launch_attn_bwd<bf16, 128>(a, grid, s) : launch_attn_bwd<bf16, 64>(a, grid, s);
   return D == 128 ? launch_attn_bwd<float, 128>(a, grid, s) : launch_attn_bwd<float, 64>(a, grid, s);
 }
 

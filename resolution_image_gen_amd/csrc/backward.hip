@@ -17,7 +17,9 @@
 //   qk_bwd_kernel         through q' = RoPE(g * rms(q)) per head: inverse
 //                         rotation, gain gradient partials, norm backward
 //   dwmod_kernel          dW_mod = d_mod^T SiLU(c)
-//   dc_kernel             dc += (d_mod W_mod) * SiLU'(c)
+//   dc_part_kernel, dc_finalize_kernel
+//                         dc += (d_mod W_mod) * SiLU'(c), over row chunks of
+//                         W_mod, the chunk products added in chunk order
 // All sums run in a fixed order: results do not depend on scheduling.
 #include "common.h"
 
@@ -78,6 +80,52 @@ __global__ void __launch_bounds__(256) transpose_kernel(TrBatch bt) {
   }
 }
 
+// bf16, C % 8 == 0: 16-byte loads along c and 16-byte stores along m through
+// a 64 x 64 tile in LDS.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(TrBatch bt) {
+  __shared__ bf16 t[64][64 + 8];
+  const TrProb& P = bt.p[blockIdx.z];
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  if (m0 >= P.npad || c0 >= P.C) return;
+  const bf16* x = static_cast<const bf16*>(P.x);
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int r = i >> 3, ch = i & 7;
+    const int64_t m = m0 + r;
+    const int c = c0 + ch * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < P.n && c < P.C) {
+      Vec8<bf16>::load(x + m * P.ldx + c, v);
+      if (bt.op == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gelu_f(v[e]);
+      } else if (bt.op == 2) {
+        float g8[8];
+        Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + c, g8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= g8[e];
+        if (P.y_rows) Vec8<bf16>::store(static_cast<bf16*>(P.y_rows) + m * P.C + c, v);
+      }
+    }
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(&t[r][ch * 8]) = w;
+  }
+  __syncthreads();
+  bf16* y = static_cast<bf16*>(P.y);
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int cc = i >> 3, mch = i & 7;
+    const int c = c0 + cc;
+    const int64_t m = m0 + mch * 8;
+    if (c >= P.C || m >= P.npad) continue;
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = t[mch * 8 + e][cc];
+    *reinterpret_cast<bf16x8*>(y + (int64_t)c * P.npad + m) = w;
+  }
+}
+
 // ------------------------------------------------------- per-sample sums
 struct ColTerm {
   const void* a;        // [n, H]
@@ -114,24 +162,44 @@ __device__ __forceinline__ bool chunk_rows(const ColsumArgs& a, int ci, int& b, 
 }
 
 template <typename T>
+__device__ __forceinline__ float term(const ColTerm& t, int64_t i, int32_t r) {
+  float v = ld<T>(t.a, i, t.a_f32);
+  if (t.b) v *= ld<T>(t.b, i, t.b_f32);
+  if (t.rs) v *= t.rs[r];
+  return v;
+}
+
+// Every term in one pass over the chunk's rows (rows in order, so each sum
+// has a fixed order), several rows' loads in flight.
+template <typename T>
 __global__ void __launch_bounds__(256) colsum_kernel(ColsumArgs a) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int ci = blockIdx.y;
   int b;
   int32_t r0, r1;
   if (!chunk_rows(a, ci, b, r0, r1) || c >= a.H) return;
-  for (int k = 0; k < a.nterms; ++k) {
-    const ColTerm& t = a.t[k];
-    float s = 0.f;
-    for (int32_t r = r0; r < r1; ++r) {
-      const int64_t i = (int64_t)r * a.H + c;
-      float v = ld<T>(t.a, i, t.a_f32);
-      if (t.b) v *= ld<T>(t.b, i, t.b_f32);
-      if (t.rs) v *= t.rs[r];
-      s += v;
-    }
-    a.partial[((int64_t)ci * a.nterms + k) * a.H + c] = s;
+  float s[3] = {0.f, 0.f, 0.f};
+  int32_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float v[3][4];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < a.nterms)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[k][u] = term<T>(a.t[k], (int64_t)(r + u) * a.H + c, r + u);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < a.nterms)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[k] += v[k][u];
   }
+  for (; r < r1; ++r)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < a.nterms) s[k] += term<T>(a.t[k], (int64_t)r * a.H + c, r);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < a.nterms) a.partial[((int64_t)ci * a.nterms + k) * a.H + c] = s[k];
 }
 
 __global__ void __launch_bounds__(256) colsum_finalize_kernel(ColsumArgs a) {
@@ -141,9 +209,10 @@ __global__ void __launch_bounds__(256) colsum_finalize_kernel(ColsumArgs a) {
   int first = 0;
   for (int s = 0; s < b; ++s) first += (a.cu[s + 1] - a.cu[s] + a.rc - 1) / a.rc;
   const int ch = (a.cu[b + 1] - a.cu[b] + a.rc - 1) / a.rc;
-  float s = 0.f;
-  for (int i = 0; i < ch; ++i) s += a.partial[((int64_t)(first + i) * a.nterms + k) * a.H + c];
-  a.out[(int64_t)b * a.out_stride + a.out_off[k] + c] = s;
+  // eight interleaved running sums combined in a fixed tree: a fixed order
+  float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < ch; ++i) p[i & 7] += a.partial[((int64_t)(first + i) * a.nterms + k) * a.H + c];
+  a.out[(int64_t)b * a.out_stride + a.out_off[k] + c] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
 // ------------------------------------------------------------ norm bwd
@@ -330,54 +399,94 @@ __global__ void __launch_bounds__(256) qk_gain_finalize_kernel(const float* gpar
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * D) return;
   const int which = i / D, dd = i % D;
-  float s = 0.f;
-  for (int64_t b = 0; b < blocks; ++b) s += gpart[(b * 2 + which) * D + dd];
-  (which ? dg_k : dg_q)[dd] = s;
+  float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t b = 0; b < blocks; ++b) p[b & 7] += gpart[(b * 2 + which) * D + dd];
+  (which ? dg_k : dg_q)[dd] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
 // ------------------------------------------------------- modulation grads
-// dW_mod[i][j] = sum_b d_mod[b][i] SiLU(c[b][j])   ([6H, H] float32)
+// SiLU(c) and SiLU'(c) [B, H] float32, once per backward.
 template <typename T>
-__global__ void __launch_bounds__(256) dwmod_kernel(const float* __restrict__ dmod, const T* __restrict__ c,
-                                                    float* __restrict__ dw, int32_t B, int32_t H, int32_t rows) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  const int i = blockIdx.y;
-  if (j >= H || i >= rows) return;
-  float s = 0.f;
-  for (int b = 0; b < B; ++b) s = fmaf(dmod[(int64_t)b * rows + i], silu_f(to_f(c[(int64_t)b * H + j])), s);
-  dw[(int64_t)i * H + j] = s;
+__global__ void __launch_bounds__(256) silu_pair_kernel(const T* __restrict__ c, float* __restrict__ sl,
+                                                        float* __restrict__ dsl, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float x = to_f(c[i]);
+  const float sg = 1.0f / (1.0f + __expf(-x));
+  sl[i] = x * sg;
+  dsl[i] = sg * (1.0f + x * (1.0f - sg));
 }
 
-// dc[b][j] += SiLU'(c[b][j]) * sum over both streams of sum_i d_mod[b][i] W_mod[i][j]
-template <typename T>
-__global__ void __launch_bounds__(256) dc_kernel(const float* __restrict__ dmod_i, const float* __restrict__ dmod_t,
-                                                 const T* __restrict__ w_i, const T* __restrict__ w_t,
-                                                 const T* __restrict__ c, float* __restrict__ dc, int32_t B,
-                                                 int32_t H, int32_t rows) {
-  constexpr int GB = 8;   // samples per block
+// dW_mod[i][j] = sum_b d_mod[b][i] SiLU(c[b][j]) ([rows, H] float32): 16
+// rows of 256 columns per block (rows = 6H is a multiple of 16).
+__global__ void __launch_bounds__(256) dwmod_kernel(const float* __restrict__ dmod, const float* __restrict__ sl,
+                                                    float* __restrict__ dw, int32_t B, int32_t H, int32_t rows) {
   const int j = blockIdx.x * 256 + threadIdx.x;
-  const int b0 = blockIdx.y * GB;
+  const int i0 = blockIdx.y * 16;
   if (j >= H) return;
-  float acc[GB];
+  float acc[16];
 #pragma unroll
-  for (int u = 0; u < GB; ++u) acc[u] = 0.f;
-  for (int st = 0; st < 2; ++st) {
-    const float* dm = st ? dmod_t : dmod_i;
-    const T* w = st ? w_t : w_i;
-    for (int i = 0; i < rows; ++i) {
-      const float wv = to_f(w[(int64_t)i * H + j]);
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float x = sl[(int64_t)b * H + j];
+    const float* dm = dmod + (int64_t)b * rows + i0;
 #pragma unroll
-      for (int u = 0; u < GB; ++u)
-        if (b0 + u < B) acc[u] = fmaf(dm[(int64_t)(b0 + u) * rows + i], wv, acc[u]);
+    for (int r = 0; r < 16; ++r) acc[r] = fmaf(dm[r], x, acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (i0 + r < rows) dw[(int64_t)(i0 + r) * H + j] = acc[r];
+}
+
+// Partial products for dc: part[kc][b][j] = sum over the rows i of chunk kc
+// (chunks of kr rows; the image stream's chunks, then the text stream's) of
+// d_mod[b][i] W_mod[i][j].  d_mod of 16 samples x kr rows staged in LDS.
+template <typename T>
+__global__ void __launch_bounds__(256) dc_part_kernel(const float* __restrict__ dmod_i, const float* __restrict__ dmod_t,
+                                                      const T* __restrict__ w_i, const T* __restrict__ w_t,
+                                                      float* __restrict__ part, int32_t B, int32_t H, int32_t rows,
+                                                      int32_t kr, int32_t kch) {
+  __shared__ float sd[16][128];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int kc = blockIdx.y;
+  const int b0 = blockIdx.z * 16;
+  const int st = kc >= kch;
+  const float* dm = st ? dmod_t : dmod_i;
+  const T* w = st ? w_t : w_i;
+  const int i0 = (kc - st * kch) * kr;
+  const int i1 = min(i0 + kr, rows);
+  float acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+  for (int ib = i0; ib < i1; ib += 128) {
+    const int n = min(128, i1 - ib);
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * 128; e += 256) {
+      const int u = e >> 7, ii = e & 127;
+      sd[u][ii] = (b0 + u < B && ii < n) ? dm[(int64_t)(b0 + u) * rows + ib + ii] : 0.f;
     }
-  }
+    __syncthreads();
+    if (j < H)
+      for (int ii = 0; ii < n; ++ii) {
+        const float wv = to_f(w[(int64_t)(ib + ii) * H + j]);
 #pragma unroll
-  for (int u = 0; u < GB; ++u) {
-    if (b0 + u >= B) break;
-    const float x = to_f(c[(int64_t)(b0 + u) * H + j]);
-    const float sg = 1.0f / (1.0f + __expf(-x));
-    dc[(int64_t)(b0 + u) * H + j] += acc[u] * sg * (1.0f + x * (1.0f - sg));
+        for (int u = 0; u < 16; ++u) acc[u] = fmaf(sd[u][ii], wv, acc[u]);
+      }
   }
+  if (j >= H) return;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (b0 + u < B) part[((int64_t)kc * B + b0 + u) * H + j] = acc[u];
+}
+
+// dc[b][j] += SiLU'(c[b][j]) * sum over the chunks, in chunk order.
+__global__ void __launch_bounds__(256) dc_finalize_kernel(const float* __restrict__ part, const float* __restrict__ dsl,
+                                                          float* __restrict__ dc, int32_t B, int32_t H, int32_t nk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * H) return;
+  float s = 0.f;
+  for (int k = 0; k < nk; ++k) s += part[(int64_t)k * B * H + i];
+  dc[i] += s * dsl[i];
 }
 
 }  // namespace
@@ -406,7 +515,10 @@ mmdit_status transpose2_impl(mmdit_dtype dt, const TransposeArgs* t, int n, int 
   }
   if (npad == 0 || C == 0) return MMDIT_OK;
   dim3 grid((unsigned)cdiv(npad, 64), (unsigned)cdiv(C, 64), n);
-  if (dt == MMDIT_BF16) MMDIT_LAUNCH(transpose_kernel<bf16>, grid, dim3(256), 0, s, bt);
+  bool vec = dt == MMDIT_BF16;
+  for (int i = 0; i < n; ++i) vec = vec && t[i].C % 8 == 0 && t[i].ldx % 8 == 0 && t[i].npad % 8 == 0;
+  if (vec) MMDIT_LAUNCH(transpose_bf16_kernel, grid, dim3(256), 0, s, bt);
+  else if (dt == MMDIT_BF16) MMDIT_LAUNCH(transpose_kernel<bf16>, grid, dim3(256), 0, s, bt);
   else MMDIT_LAUNCH(transpose_kernel<float>, grid, dim3(256), 0, s, bt);
   return launch_check("transpose_kernel", s);
 }
@@ -534,27 +646,55 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
   return MMDIT_OK;
 }
 
+size_t mod_grads_ws_bytes(int32_t B, int32_t H) {
+  return (size_t)2 * B * H * 4 + (size_t)2 * mod_grads_chunks(B, H) * B * H * 4;
+}
+
+// chunks per stream of the dc partial products: enough blocks to fill the
+// chip, partials bounded to about 64 MB
+int32_t mod_grads_chunks(int32_t B, int32_t H) {
+  const int32_t rows = 6 * H;
+  int64_t kch = rows / 128;
+  const int64_t cap = (int64_t)16 * 1024 * 1024 / ((int64_t)2 * (B > 0 ? B : 1) * H);
+  if (kch > cap) kch = cap;
+  return (int32_t)(kch < 1 ? 1 : kch);
+}
+
 mmdit_status mod_grads_impl(mmdit_dtype dt, int32_t B, int32_t H, const void* c, const float* dmod_i,
                             const float* dmod_t, const void* w_i, const void* w_t, float* dw_i, float* dw_t,
-                            float* dc, hipStream_t s) {
+                            float* dc, void* ws, size_t ws_bytes, hipStream_t s) {
   if (B == 0) return MMDIT_OK;
   const int32_t rows = 6 * H;
+  if (!ws || ws_bytes < mod_grads_ws_bytes(B, H)) {
+    set_error("modulation gradients: workspace needs %zu bytes, got %zu", mod_grads_ws_bytes(B, H), ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  float* sl = static_cast<float*>(ws);
+  float* dsl = sl + (size_t)B * H;
+  float* part = dsl + (size_t)B * H;
+  const int64_t n = (int64_t)B * H;
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(silu_pair_kernel<bf16>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, static_cast<const bf16*>(c), sl, dsl, n);
+  else
+    MMDIT_LAUNCH(silu_pair_kernel<float>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, static_cast<const float*>(c), sl, dsl, n);
+  MMDIT_TRY(launch_check("silu_pair_kernel", s));
   for (int st = 0; st < 2; ++st) {
-    const float* dm = st ? dmod_t : dmod_i;
-    float* dw = st ? dw_t : dw_i;
-    dim3 g((unsigned)cdiv(H, 256), rows);
-    if (dt == MMDIT_BF16) MMDIT_LAUNCH(dwmod_kernel<bf16>, g, dim3(256), 0, s, dm, static_cast<const bf16*>(c), dw, B, H, rows);
-    else MMDIT_LAUNCH(dwmod_kernel<float>, g, dim3(256), 0, s, dm, static_cast<const float*>(c), dw, B, H, rows);
+    MMDIT_LAUNCH(dwmod_kernel, dim3((unsigned)cdiv(H, 256), (unsigned)cdiv(rows, 16)), dim3(256), 0, s,
+                 st ? dmod_t : dmod_i, sl, st ? dw_t : dw_i, B, H, rows);
     MMDIT_TRY(launch_check("dwmod_kernel", s));
   }
-  dim3 g((unsigned)cdiv(H, 256), (unsigned)cdiv(B, 8));
+  const int32_t kch = mod_grads_chunks(B, H);
+  const int32_t kr = (int32_t)cdiv(rows, kch);
+  dim3 g((unsigned)cdiv(H, 256), (unsigned)(2 * kch), (unsigned)cdiv(B, 16));
   if (dt == MMDIT_BF16)
-    MMDIT_LAUNCH(dc_kernel<bf16>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const bf16*>(w_i),
-                 static_cast<const bf16*>(w_t), static_cast<const bf16*>(c), dc, B, H, rows);
+    MMDIT_LAUNCH(dc_part_kernel<bf16>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const bf16*>(w_i),
+                 static_cast<const bf16*>(w_t), part, B, H, rows, kr, kch);
   else
-    MMDIT_LAUNCH(dc_kernel<float>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const float*>(w_i),
-                 static_cast<const float*>(w_t), static_cast<const float*>(c), dc, B, H, rows);
-  return launch_check("dc_kernel", s);
+    MMDIT_LAUNCH(dc_part_kernel<float>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const float*>(w_i),
+                 static_cast<const float*>(w_t), part, B, H, rows, kr, kch);
+  MMDIT_TRY(launch_check("dc_part_kernel", s));
+  MMDIT_LAUNCH(dc_finalize_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, dsl, dc, B, H, 2 * kch);
+  return launch_check("dc_finalize_kernel", s);
 }
 
 }  // namespace mmdit

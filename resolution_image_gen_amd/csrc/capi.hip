@@ -702,7 +702,7 @@ int64_t pad64(int64_t n) { return (n + 63) & ~(int64_t)63; }
 // Workspace of the block backward.
 struct BwdLayout {
   size_t wt_down, wt_up, wt_o, wt_qkv, dd, ddT, guT, du, duT, h2T, dh2, dxmid, inv_r, da, daT, oT, dO, dqkv, dqkvT,
-      h1T, dh1, dmod, partial, gpart, attn, end;
+      h1T, dh1, dmod, partial, gpart, modg, attn, end;
 };
 
 BwdLayout bwd_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -737,6 +737,7 @@ BwdLayout bwd_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   const int64_t ch = colsum_chunks(pk->h_cu_img, pk->B, kColsumRows) + colsum_chunks(pk->h_cu_txt, pk->B, kColsumRows);
   Lb.partial = o; o = align256(o + (size_t)ch * 3 * H * 4);
   Lb.gpart = o;   o = align256(o + (size_t)(qk_bwd_blocks(pk->n_img) + qk_bwd_blocks(pk->n_txt)) * 2 * d->head_dim * 4);
+  Lb.modg = o;    o = align256(o + mod_grads_ws_bytes(pk->B, d->hidden));
   Lb.attn = o;    o = align256(o + attention_bwd_ws_bytes(pk, d->heads, d->head_dim));
   Lb.end = o;
   return Lb;
@@ -1015,7 +1016,7 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   }
   // adaLN: dW_mod = d_mod^T SiLU(c), dc += (d_mod W_mod) SiLU'(c)
   return mod_grads_impl(dt, pk->B, H, c, dmod[0], dmod[1], w->img.w_mod, w->txt.w_mod, g->img.w_mod, g->txt.w_mod,
-                        dc, s);
+                        dc, base + Lb.modg, Lb.attn - Lb.modg, s);
 }
 
 mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,

@@ -175,7 +175,7 @@ mmdit_status transpose2_impl(mmdit_dtype dt, const TransposeArgs* t, int n, int 
 // Per-sample column sums out[b][out_off[k] + c] = sum over the rows of sample
 // b of a_k[r][c] * b_k[r][c] * rs_k[r] (b_k, rs_k optional), in row chunks of
 // kColsumRows summed in a fixed order.  partial: [chunks][nterms][H] floats.
-constexpr int kColsumRows = 256;
+constexpr int kColsumRows = 64;
 struct ColsumSpec {
   const void* a[3];
   const void* b[3];
@@ -230,9 +230,11 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
 
 // dW_mod = d_mod^T SiLU(c) per stream ([6H, H] float32) and
 // dc += (d_mod W_mod) * SiLU'(c) summed over both streams.
+int32_t mod_grads_chunks(int32_t B, int32_t H);
+size_t mod_grads_ws_bytes(int32_t B, int32_t H);
 mmdit_status mod_grads_impl(mmdit_dtype dt, int32_t B, int32_t H, const void* c, const float* dmod_i,
                             const float* dmod_t, const void* w_i, const void* w_t, float* dw_i, float* dw_t,
-                            float* dc, hipStream_t s);
+                            float* dc, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Attention backward over a pack (see attention.hip); ws >= attention_bwd_ws_bytes.
 size_t attention_bwd_ws_bytes(const mmdit_pack_t* pk, int32_t heads, int32_t D);
