@@ -170,3 +170,78 @@ def block_backward(x_img, x_txt, c, wb, pk, heads, dy_img, dy_txt):
         grads.update(dw_o=p["dw_o"], dw_up=p["dw_up"], dw_down=p["dw_down"], d_mod=d_mod)
         out[s] = grads
     return out
+
+
+# ------------------------------------------------------ the whole training step
+
+def final_layer_backward(x_img, c, w_fmod, w_out, pk, dv):
+    """Gradients through v = (rms(x)(1 + sc) + sh) W_out^T on the target rows,
+    [sh, sc] = W_fmod SiLU(c).  Returns (dx_img [n_img, H] (zero on rows that
+    are not targets), dc [B, H], dw_fmod, dw_out)."""
+    x_img = np.asarray(x_img, np.float64)
+    c = np.asarray(c, np.float64)
+    w_fmod = np.asarray(w_fmod, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    B = c.shape[0]
+    rows = pk["tgt_rows"]
+    seg = pk["seg_img"][rows]
+    sh, sc = _blk.modulation(c, w_fmod, chunks=2)
+    x = x_img[rows]
+    n = _blk.rms_norm(x)
+    h = _blk.modulate(n, sh[seg], sc[seg])
+    dw_out = dv.T @ h
+    dh = dv @ w_out
+    d_mod = np.concatenate([seg_sum(dh, seg, B), seg_sum(dh * n, seg, B)], axis=1)
+    dx = np.zeros_like(x_img)
+    dx[rows] = rms_backward(x, dh * (1.0 + sc[seg]))
+    dw_fmod = d_mod.T @ _blk.silu(c)
+    dc = (d_mod @ w_fmod) * silu_grad(c)
+    return dx, dc, dw_fmod, dw_out
+
+
+def cond_backward(t, w_t1, w_t2, dc):
+    """Gradients of c = W_t2 SiLU(W_t1 emb(t)) for the two weights."""
+    w_t1 = np.asarray(w_t1, np.float64)
+    w_t2 = np.asarray(w_t2, np.float64)
+    emb = _blk.timestep_embedding(t, w_t1.shape[1])
+    hid = _blk.linear(emb, w_t1)
+    dw_t2 = dc.T @ _blk.silu(hid)
+    dhid = (dc @ w_t2) * silu_grad(hid)
+    return dhid.T @ emb, dw_t2
+
+
+def training_step_grads(zt_img, tau, t, W, pk, heads, z, eps):
+    """Every gradient of the flow-matching loss of one pack (hyper.ai
+    2607.19064, 方法, the objective; blog close-reading, 2.2(2)): the model is
+    cond -> embed -> blocks -> final layer on target rows; the loss is
+    mean_b SSE_b / (tgt_len_b C) with SSE_b = sum (v - (z - eps))^2 over the
+    target rows of sample b.  W as for flow.velocity_model.  Returns
+    {"loss", "dv", "w_t1", "w_t2", "w_in", "w_txt", "w_fmod", "w_out",
+    "blocks": [block_backward's stream dicts per block]}."""
+    from . import flow as _flow
+
+    c = _blk.cond(t, W["w_t1"], W["w_t2"])
+    x_img, x_txt = _blk.embed(zt_img, tau, W["w_in"], W["w_txt"])
+    xs = []
+    for wb in W["blocks"]:
+        xs.append((x_img, x_txt))
+        o = _blk.block_forward(x_img, x_txt, c, wb, pk, heads)
+        x_img, x_txt = o["x_out_img"], o["x_out_txt"]
+    v = _blk.final_layer(x_img, c, W["w_fmod"], W["w_out"], pk)
+    _, loss = _flow.loss(v, z, eps, pk)
+    C = v.shape[1]
+    scale = np.asarray(pk["tgt_len"], np.float64)[pk["seg_img"][pk["tgt_rows"]]] * C * pk["B"]
+    dv = 2.0 * (v - _flow.velocity_target(z, eps, pk)) / scale[:, None]
+    out = {"loss": loss, "dv": dv}
+    dx_img, dc, out["w_fmod"], out["w_out"] = final_layer_backward(x_img, c, W["w_fmod"], W["w_out"], pk, dv)
+    dx_txt = np.zeros_like(x_txt)
+    out["blocks"] = [None] * len(W["blocks"])
+    for i in range(len(W["blocks"]) - 1, -1, -1):
+        g = block_backward(xs[i][0], xs[i][1], c, W["blocks"][i], pk, heads, dx_img, dx_txt)
+        dx_img, dx_txt = g["dx_img"], g["dx_txt"]
+        dc = dc + g["dc"]
+        out["blocks"][i] = {"img": g["img"], "txt": g["txt"]}
+    out["w_in"] = dx_img.T @ np.asarray(zt_img, np.float64)
+    out["w_txt"] = dx_txt.T @ np.asarray(tau, np.float64)
+    out["w_t1"], out["w_t2"] = cond_backward(t, W["w_t1"], W["w_t2"], dc)
+    return out

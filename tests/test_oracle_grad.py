@@ -153,3 +153,64 @@ def test_zero_gates_pass_the_gradient_straight_through():
     np.testing.assert_allclose(g["dx_img"], dy_img, atol=1e-14)
     np.testing.assert_allclose(g["dx_txt"], dy_txt, atol=1e-14)
     assert np.max(np.abs(g["img"]["d_mod"][:, 2 * H:3 * H])) > 0
+
+
+def _tiny_model(seed=11, depth=2, C=8, t_dim=16):
+    r = np.random.default_rng(seed)
+
+    def w(o, i, s=1.0):
+        return r.standard_normal((o, i)) * s / math.sqrt(i)
+
+    blocks = []
+    for _ in range(depth):
+        blocks.append({s: {"w_mod": w(6 * H, H), "w_qkv": w(3 * H, H), "g_q": 1 + 0.2 * r.standard_normal(H // HEADS),
+                           "g_k": 1 + 0.2 * r.standard_normal(H // HEADS), "w_o": w(H, H), "w_up": w(MLP, H),
+                           "w_down": w(H, MLP)} for s in ("img", "txt")})
+    return {"w_t1": w(H, t_dim), "w_t2": w(H, H), "w_in": w(H, C), "w_txt": w(H, H), "blocks": blocks,
+            "w_fmod": w(2 * H, H), "w_out": w(C, H)}
+
+
+def test_training_step_gradients_match_finite_differences():
+    # the whole loss of one pack (generation + editing sample) against central
+    # differences along random directions, for every weight of the model
+    from oracle import flow as F
+
+    pk = P.pack(SAMPLES)
+    r = np.random.default_rng(12)
+    W = _tiny_model()
+    n_img, n_txt = pk["cu_img"][-1], pk["cu_txt"][-1]
+    z, eps = r.standard_normal((n_img, 8)), r.standard_normal((n_img, 8))
+    tau = r.standard_normal((n_txt, H))
+    t = np.array([0.3, 0.8])
+    zt = F.make_xt(z, eps, t, pk)
+    g = G.training_step_grads(zt, tau, t, W, pk, HEADS, z, eps)
+
+    def loss_of(Wm):
+        v = F.velocity_model(zt, tau, t, Wm, pk, HEADS)
+        return F.loss(v, z, eps, pk)[1]
+
+    assert abs(loss_of(W) - g["loss"]) < 1e-12
+    checks = [(k, None, None) for k in ("w_t1", "w_t2", "w_in", "w_txt", "w_fmod", "w_out")]
+    checks += [(k, i, s) for i in range(2) for s in ("img", "txt") for k in ("w_mod", "w_qkv", "g_q", "w_down")]
+    for key, bi, s in checks:
+        base = W[key] if bi is None else W["blocks"][bi][s][key]
+        grad = g[key] if bi is None else g["blocks"][bi][s]["d" + key]
+        u = r.standard_normal(np.shape(base))
+
+        def f(v):
+            W2 = dict(W)
+            if bi is None:
+                W2[key] = v
+            else:
+                W2["blocks"] = [{ss: dict(b[ss]) for ss in b} for b in W["blocks"]]
+                W2["blocks"][bi][s][key] = v
+            return loss_of(W2)
+
+        fd = _fd(f, np.asarray(base, np.float64), u)
+        an = float(np.sum(grad * u))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (key, bi, s, fd, an)
+    # dv is the loss gradient with respect to the velocity, per target row
+    v = F.velocity_model(zt, tau, t, W, pk, HEADS)
+    du = r.standard_normal(v.shape)
+    fd = (F.loss(v + 1e-5 * du, z, eps, pk)[1] - F.loss(v - 1e-5 * du, z, eps, pk)[1]) / 2e-5
+    assert abs(fd - np.sum(g["dv"] * du)) < 1e-9
