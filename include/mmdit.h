@@ -256,6 +256,43 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* dims, const mmdit_block_w* w,
                              const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
                              mmdit_stream stream);
 
+/* The rest of the training step's backward.  Loss ([hyper] 方法 objective;
+ * [blog] 2.2(2), target latent only):  loss = mean_b SSE_b / (tgt_len_b C). */
+
+/* dv [n_tgt, C] (dtype) = dL/dv = 2 (v - (z - eps)) / (B tgt_len_b C) on the
+ * target rows; v as rf_loss. */
+mmdit_status rf_loss_grad(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* v,
+                          const void* z, const void* eps, void* dv, mmdit_stream stream);
+
+/* Workspace bytes of mmdit_final_bwd and mmdit_embed_bwd for this pack. */
+size_t mmdit_wrap_bwd_workspace_size(const mmdit_dims* dims, const mmdit_pack_t* pack);
+
+/* Backward of mmdit_final: from dv [n_tgt, C], writes dx_img [n_img, H]
+ * (dtype; zero on rows that are not targets), dw_fmod [2H, H] and dw_out
+ * [c_lat, H] (float32, overwritten) and adds the conditioning gradient to dc
+ * [B, H] (float32).  x_img: the last block's output. */
+mmdit_status mmdit_final_bwd(const mmdit_dims* dims, const void* w_fmod, const void* w_out,
+                             const mmdit_pack_t* pack, const void* c, const void* x_img,
+                             const void* dv, void* dx_img, float* dw_fmod, float* dw_out, float* dc,
+                             void* ws, size_t ws_bytes, mmdit_stream stream);
+
+/* Backward of mmdit_embed: dw_in [H, c_lat] = dx_img^T zt and dw_txt
+ * [H, d_txt] = dx_txt^T tau (float32, overwritten; zero for a stream without
+ * rows).  dx_img, dx_txt: the gradients reaching the first block's input. */
+mmdit_status mmdit_embed_bwd(const mmdit_dims* dims, const mmdit_pack_t* pack, const void* zt,
+                             const void* tau, const void* dx_img, const void* dx_txt, float* dw_in,
+                             float* dw_txt, void* ws, size_t ws_bytes, mmdit_stream stream);
+
+/* Workspace bytes of mmdit_cond_bwd for B samples. */
+size_t mmdit_cond_bwd_workspace_size(const mmdit_dims* dims, int32_t B);
+
+/* Backward of mmdit_cond from dc [B, H] (float32, the sum over the final
+ * layer and every block): dw_t1 [H, t_dim], dw_t2 [H, H] (float32,
+ * overwritten).  t [B] float32 device, as in the forward. */
+mmdit_status mmdit_cond_bwd(const mmdit_dims* dims, const void* w_t1, const void* w_t2, const float* t,
+                            int32_t B, const float* dc, float* dw_t1, float* dw_t2, void* ws,
+                            size_t ws_bytes, mmdit_stream stream);
+
 /* Sub-steps of the block, exposed so every intermediate can be checked. */
 
 /* y = rms(x[row_map[i]]) * (1 + scale[s]) + shift[s], s = seg[row_map[i]]

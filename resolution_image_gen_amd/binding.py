@@ -92,6 +92,12 @@ def _load():
         "mmdit_embed": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_block_fwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "mmdit_block_saved_size": (_sz, [D, P]),
+        "rf_loss_grad": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+        "mmdit_wrap_bwd_workspace_size": (_sz, [D, P]),
+        "mmdit_final_bwd": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_embed_bwd": (_i32, [D, P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_cond_bwd_workspace_size": (_sz, [D, _i32]),
+        "mmdit_cond_bwd": (_i32, [D, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
         "mmdit_block_fwd_train": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
         "mmdit_block_bwd_workspace_size": (_sz, [D, P]),
         "mmdit_block_bwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(_BlockG),
@@ -303,6 +309,34 @@ def block_bwd(dims, wb, pk, c, saved, dx_img, dx_txt, grads, dc, ws, stream=None
     _ck(_lib.mmdit_block_bwd(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(saved),
                              saved.numel() * saved.element_size(), _p(dx_img), _p(dx_txt), ctypes.byref(bg),
                              _p(dc), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rf_loss_grad(pk, v, z, eps, dv, stream=None):
+    _ck(_lib.rf_loss_grad(pk.ref, _dt(v), v.shape[-1], _p(v), _p(z), _p(eps), _p(dv), _stream(stream)))
+
+
+def wrap_bwd_workspace_size(dims, pk):
+    return int(_lib.mmdit_wrap_bwd_workspace_size(ctypes.byref(dims.c), pk.ref))
+
+
+def final_bwd(dims, w_fmod, w_out, pk, c, x_img, dv, dx_img, dw_fmod, dw_out, dc, ws, stream=None):
+    _ck(_lib.mmdit_final_bwd(ctypes.byref(dims.c), _p(w_fmod), _p(w_out), pk.ref, _p(c), _p(x_img), _p(dv),
+                             _p(dx_img), _p(dw_fmod), _p(dw_out), _p(dc), _p(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)))
+
+
+def embed_bwd(dims, pk, zt, tau, dx_img, dx_txt, dw_in, dw_txt, ws, stream=None):
+    _ck(_lib.mmdit_embed_bwd(ctypes.byref(dims.c), pk.ref, _p(zt), _p(tau), _p(dx_img), _p(dx_txt), _p(dw_in),
+                             _p(dw_txt), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def cond_bwd_workspace_size(dims, B):
+    return int(_lib.mmdit_cond_bwd_workspace_size(ctypes.byref(dims.c), B))
+
+
+def cond_bwd(dims, w_t1, w_t2, t, dc, dw_t1, dw_t2, ws, stream=None):
+    _ck(_lib.mmdit_cond_bwd(ctypes.byref(dims.c), _p(w_t1), _p(w_t2), _p(t), t.numel(), _p(dc), _p(dw_t1),
+                            _p(dw_t2), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rms_modulate(dims, x, seg, mod, shift_off, scale_off, y, row_map=None, stream=None):

@@ -16,10 +16,10 @@
 //                         dx = dres + (dn - n mean(dn n)) / rms, dn = dh (1 + scale)
 //   qk_bwd_kernel         through q' = RoPE(g * rms(q)) per head: inverse
 //                         rotation, gain gradient partials, norm backward
-//   dwmod_kernel          dW_mod = d_mod^T SiLU(c)
-//   dc_part_kernel, dc_finalize_kernel
-//                         dc += (d_mod W_mod) * SiLU'(c), over row chunks of
-//                         W_mod, the chunk products added in chunk order
+//   outer_kernel          dW = dy^T f(x) over the sample axis (adaLN, conditioning)
+//   vecmat_part_kernel, vecmat_finalize_kernel
+//                         dx += (dy W) * f'(x), over row chunks of W, the
+//                         chunk products added in chunk order
 // All sums run in a fixed order: results do not depend on scheduling.
 #include "common.h"
 
@@ -129,8 +129,9 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(TrBatch bt) {
 // ------------------------------------------------------- per-sample sums
 struct ColTerm {
   const void* a;        // [n, H]
-  const void* b;        // [n, H] or NULL
+  const void* b;        // [n, H] or NULL (row b_map[r] when b_map is set)
   const float* rs;      // [n] row scale or NULL
+  const int32_t* b_map;
   int32_t a_f32, b_f32;
 };
 struct ColsumArgs {
@@ -162,9 +163,9 @@ __device__ __forceinline__ bool chunk_rows(const ColsumArgs& a, int ci, int& b, 
 }
 
 template <typename T>
-__device__ __forceinline__ float term(const ColTerm& t, int64_t i, int32_t r) {
-  float v = ld<T>(t.a, i, t.a_f32);
-  if (t.b) v *= ld<T>(t.b, i, t.b_f32);
+__device__ __forceinline__ float term(const ColTerm& t, int32_t r, int c, int H) {
+  float v = ld<T>(t.a, (int64_t)r * H + c, t.a_f32);
+  if (t.b) v *= ld<T>(t.b, (int64_t)(t.b_map ? t.b_map[r] : r) * H + c, t.b_f32);
   if (t.rs) v *= t.rs[r];
   return v;
 }
@@ -186,7 +187,7 @@ __global__ void __launch_bounds__(256) colsum_kernel(ColsumArgs a) {
     for (int k = 0; k < 3; ++k)
       if (k < a.nterms)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[k][u] = term<T>(a.t[k], (int64_t)(r + u) * a.H + c, r + u);
+        for (int u = 0; u < 4; ++u) v[k][u] = term<T>(a.t[k], r + u, c, a.H);
 #pragma unroll
     for (int k = 0; k < 3; ++k)
       if (k < a.nterms)
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(256) colsum_kernel(ColsumArgs a) {
   for (; r < r1; ++r)
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-      if (k < a.nterms) s[k] += term<T>(a.t[k], (int64_t)r * a.H + c, r);
+      if (k < a.nterms) s[k] += term<T>(a.t[k], r, c, a.H);
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     if (k < a.nterms) a.partial[((int64_t)ci * a.nterms + k) * a.H + c] = s[k];
@@ -217,11 +218,12 @@ __global__ void __launch_bounds__(256) colsum_finalize_kernel(ColsumArgs a) {
 
 // ------------------------------------------------------------ norm bwd
 struct NormBwdProb {
+  const int32_t* row_map;   // optional: x, seg and dx rows are row_map[row]
   const void* x;        // [n, H] norm input
   const void* dh;       // [n, H] gradient of rms(x)(1 + scale) + shift
   const float* mod;     // scale at mod[seg * mod_stride + scale_off]
   const int32_t* seg;
-  const void* dres;     // [n, H] gradient reaching x along the residual
+  const void* dres;     // [n, H] gradient reaching x along the residual, or NULL
   void* dx;             // [n, H] output (may alias dres)
   float* inv_r;         // [n] output: 1 / rms(x)
   const float* gate;    // optional: dgated = gate[seg * mod_stride + gate_off] * dx
@@ -247,9 +249,10 @@ __global__ void __launch_bounds__(512) norm_bwd_kernel(NormBwdBatch bt) {
   if (row >= P.n) return;
   const int lane = threadIdx.x & 63;
   const int H = bt.H;
-  const int32_t sg = P.seg[row];
+  const int64_t xr = P.row_map ? (int64_t)P.row_map[row] : row;   // row of x, seg and dx
+  const int32_t sg = P.seg[xr];
   const float* sc = P.mod + (int64_t)sg * P.mod_stride + P.scale_off;
-  const T* x = static_cast<const T*>(P.x) + row * H;
+  const T* x = static_cast<const T*>(P.x) + xr * H;
   const T* dh = static_cast<const T*>(P.dh) + row * H;
   float ss = 0.f, sd = 0.f;
   for (int c = lane * 8; c < H; c += 512) {
@@ -274,12 +277,18 @@ __global__ void __launch_bounds__(512) norm_bwd_kernel(NormBwdBatch bt) {
     Vec8<T>::load(x + c, xv);
     Vec8<T>::load(dh + c, dv);
     Vec8<float>::load(sc + c, s8);
-    if (P.dres_f32) Vec8<float>::load(static_cast<const float*>(P.dres) + row * H + c, rv);
-    else Vec8<T>::load(static_cast<const T*>(P.dres) + row * H + c, rv);
+    if (!P.dres) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rv[e] = 0.f;
+    } else if (P.dres_f32) {
+      Vec8<float>::load(static_cast<const float*>(P.dres) + row * H + c, rv);
+    } else {
+      Vec8<T>::load(static_cast<const T*>(P.dres) + row * H + c, rv);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = rv[e] + (dv[e] * (1.0f + s8[e]) - xv[e] * r * cm) * r;
-    if (P.dx_f32) Vec8<float>::store(static_cast<float*>(P.dx) + row * H + c, o);
-    else Vec8<T>::store(static_cast<T*>(P.dx) + row * H + c, o);
+    if (P.dx_f32) Vec8<float>::store(static_cast<float*>(P.dx) + xr * H + c, o);
+    else Vec8<T>::store(static_cast<T*>(P.dx) + xr * H + c, o);
     if (gt) {
       float g8[8];
       Vec8<float>::load(gt + c, g8);
@@ -404,55 +413,63 @@ __global__ void __launch_bounds__(256) qk_gain_finalize_kernel(const float* gpar
   (which ? dg_k : dg_q)[dd] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// ------------------------------------------------------- modulation grads
-// SiLU(c) and SiLU'(c) [B, H] float32, once per backward.
+// ------------------------------------------- products over the sample axis
+// For a linear y = W f(x) applied to one vector per sample (adaLN, the
+// conditioning MLP): dW = dy^T f(x) and df(x) = dy W, both sums over samples
+// or rows in a fixed order.
+
+// f(X) and f'(X) [B, cols] float32: SiLU (mode 0) or the identity (mode 1).
 template <typename T>
-__global__ void __launch_bounds__(256) silu_pair_kernel(const T* __restrict__ c, float* __restrict__ sl,
-                                                        float* __restrict__ dsl, int64_t n) {
+__global__ void __launch_bounds__(256) act_pair_kernel(const void* __restrict__ x, int32_t x_f32, int32_t mode,
+                                                       float* __restrict__ f, float* __restrict__ df, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const float x = to_f(c[i]);
-  const float sg = 1.0f / (1.0f + __expf(-x));
-  sl[i] = x * sg;
-  dsl[i] = sg * (1.0f + x * (1.0f - sg));
+  const float v = ld<T>(x, i, x_f32);
+  if (mode == 1) {
+    f[i] = v;
+    df[i] = 1.0f;
+    return;
+  }
+  const float sg = 1.0f / (1.0f + __expf(-v));
+  f[i] = v * sg;
+  df[i] = sg * (1.0f + v * (1.0f - sg));
 }
 
-// dW_mod[i][j] = sum_b d_mod[b][i] SiLU(c[b][j]) ([rows, H] float32): 16
-// rows of 256 columns per block (rows = 6H is a multiple of 16).
-__global__ void __launch_bounds__(256) dwmod_kernel(const float* __restrict__ dmod, const float* __restrict__ sl,
-                                                    float* __restrict__ dw, int32_t B, int32_t H, int32_t rows) {
+// dW[i][j] = sum_b dy[b][i] f[b][j] ([rows, cols] float32): 16 rows of 256
+// columns per block (rows a multiple of 16).
+__global__ void __launch_bounds__(256) outer_kernel(const float* __restrict__ dy, const float* __restrict__ f,
+                                                    float* __restrict__ dw, int32_t B, int32_t cols, int32_t rows) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int i0 = blockIdx.y * 16;
-  if (j >= H) return;
+  if (j >= cols) return;
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   for (int b = 0; b < B; ++b) {
-    const float x = sl[(int64_t)b * H + j];
-    const float* dm = dmod + (int64_t)b * rows + i0;
+    const float x = f[(int64_t)b * cols + j];
+    const float* dm = dy + (int64_t)b * rows + i0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = fmaf(dm[r], x, acc[r]);
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (i0 + r < rows) dw[(int64_t)(i0 + r) * H + j] = acc[r];
+  for (int r = 0; r < 16; ++r) dw[(int64_t)(i0 + r) * cols + j] = acc[r];
 }
 
-// Partial products for dc: part[kc][b][j] = sum over the rows i of chunk kc
-// (chunks of kr rows; the image stream's chunks, then the text stream's) of
-// d_mod[b][i] W_mod[i][j].  d_mod of 16 samples x kr rows staged in LDS.
+// Partial products part[kc][b][j] = sum over the rows i of chunk kc (chunks
+// of kr rows; stream 0's chunks, then stream 1's) of dy[b][i] W[i][j];
+// dy of 16 samples x 128 rows staged in LDS.
 template <typename T>
-__global__ void __launch_bounds__(256) dc_part_kernel(const float* __restrict__ dmod_i, const float* __restrict__ dmod_t,
-                                                      const T* __restrict__ w_i, const T* __restrict__ w_t,
-                                                      float* __restrict__ part, int32_t B, int32_t H, int32_t rows,
-                                                      int32_t kr, int32_t kch) {
+__global__ void __launch_bounds__(256) vecmat_part_kernel(const float* __restrict__ dy0, const float* __restrict__ dy1,
+                                                          const T* __restrict__ w0, const T* __restrict__ w1,
+                                                          float* __restrict__ part, int32_t B, int32_t cols,
+                                                          int32_t rows, int32_t kr, int32_t kch) {
   __shared__ float sd[16][128];
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int kc = blockIdx.y;
   const int b0 = blockIdx.z * 16;
   const int st = kc >= kch;
-  const float* dm = st ? dmod_t : dmod_i;
-  const T* w = st ? w_t : w_i;
+  const float* dm = st ? dy1 : dy0;
+  const T* w = st ? w1 : w0;
   const int i0 = (kc - st * kch) * kr;
   const int i1 = min(i0 + kr, rows);
   float acc[16];
@@ -466,27 +483,27 @@ __global__ void __launch_bounds__(256) dc_part_kernel(const float* __restrict__ 
       sd[u][ii] = (b0 + u < B && ii < n) ? dm[(int64_t)(b0 + u) * rows + ib + ii] : 0.f;
     }
     __syncthreads();
-    if (j < H)
+    if (j < cols)
       for (int ii = 0; ii < n; ++ii) {
-        const float wv = to_f(w[(int64_t)(ib + ii) * H + j]);
+        const float wv = to_f(w[(int64_t)(ib + ii) * cols + j]);
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = fmaf(sd[u][ii], wv, acc[u]);
       }
   }
-  if (j >= H) return;
+  if (j >= cols) return;
 #pragma unroll
   for (int u = 0; u < 16; ++u)
-    if (b0 + u < B) part[((int64_t)kc * B + b0 + u) * H + j] = acc[u];
+    if (b0 + u < B) part[((int64_t)kc * B + b0 + u) * cols + j] = acc[u];
 }
 
-// dc[b][j] += SiLU'(c[b][j]) * sum over the chunks, in chunk order.
-__global__ void __launch_bounds__(256) dc_finalize_kernel(const float* __restrict__ part, const float* __restrict__ dsl,
-                                                          float* __restrict__ dc, int32_t B, int32_t H, int32_t nk) {
+// dx[b][j] += f'(x[b][j]) * sum over the chunks, in chunk order.
+__global__ void __launch_bounds__(256) vecmat_finalize_kernel(const float* __restrict__ part, const float* __restrict__ df,
+                                                              float* __restrict__ dx, int64_t n, int32_t nk) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)B * H) return;
+  if (i >= n) return;
   float s = 0.f;
-  for (int k = 0; k < nk; ++k) s += part[(int64_t)k * B * H + i];
-  dc[i] += s * dsl[i];
+  for (int k = 0; k < nk; ++k) s += part[(int64_t)k * n + i];
+  dx[i] += s * df[i];
 }
 
 }  // namespace
@@ -536,6 +553,7 @@ mmdit_status seg_colsum_impl(mmdit_dtype dt, const ColsumSpec& sp, hipStream_t s
   for (int k = 0; k < sp.nterms; ++k) {
     a.t[k].a = sp.a[k];
     a.t[k].b = sp.b[k];
+    a.t[k].b_map = sp.b_map[k];
     a.t[k].rs = sp.rs[k];
     a.t[k].a_f32 = sp.a_f32[k];
     a.t[k].b_f32 = sp.b_f32[k];
@@ -568,6 +586,7 @@ mmdit_status norm_bwd2_impl(mmdit_dtype dt, int32_t H, float eps, const NormBwdS
   int64_t blocks[2] = {0, 0};
   for (int i = 0; i < n; ++i) {
     NormBwdProb& q = bt.p[i];
+    q.row_map = p[i].row_map;
     q.x = p[i].x;
     q.dh = p[i].dh;
     q.mod = p[i].mod;
@@ -646,55 +665,61 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
   return MMDIT_OK;
 }
 
-size_t mod_grads_ws_bytes(int32_t B, int32_t H) {
-  return (size_t)2 * B * H * 4 + (size_t)2 * mod_grads_chunks(B, H) * B * H * 4;
-}
-
-// chunks per stream of the dc partial products: enough blocks to fill the
-// chip, partials bounded to about 64 MB
-int32_t mod_grads_chunks(int32_t B, int32_t H) {
-  const int32_t rows = 6 * H;
+// chunks per stream of the vector-matrix partial products: enough blocks to
+// fill the chip, partials bounded to about 64 MB
+int32_t outer_vecmat_chunks(int32_t B, int32_t rows, int32_t cols) {
   int64_t kch = rows / 128;
-  const int64_t cap = (int64_t)16 * 1024 * 1024 / ((int64_t)2 * (B > 0 ? B : 1) * H);
+  const int64_t cap = (int64_t)16 * 1024 * 1024 / ((int64_t)2 * (B > 0 ? B : 1) * cols);
   if (kch > cap) kch = cap;
   return (int32_t)(kch < 1 ? 1 : kch);
 }
 
-mmdit_status mod_grads_impl(mmdit_dtype dt, int32_t B, int32_t H, const void* c, const float* dmod_i,
-                            const float* dmod_t, const void* w_i, const void* w_t, float* dw_i, float* dw_t,
-                            float* dc, void* ws, size_t ws_bytes, hipStream_t s) {
+size_t outer_vecmat_ws_bytes(int32_t B, int32_t rows, int32_t cols) {
+  return (size_t)2 * B * cols * 4 + (size_t)2 * outer_vecmat_chunks(B, rows, cols) * B * cols * 4;
+}
+
+mmdit_status outer_vecmat_impl(mmdit_dtype dt, int32_t B, int32_t rows, int32_t cols, int ns, const float* const* dy,
+                               const void* const* w, const void* x, int32_t x_f32, int32_t mode, float* const* dw,
+                               float* dx, void* ws, size_t ws_bytes, hipStream_t s) {
   if (B == 0) return MMDIT_OK;
-  const int32_t rows = 6 * H;
-  if (!ws || ws_bytes < mod_grads_ws_bytes(B, H)) {
-    set_error("modulation gradients: workspace needs %zu bytes, got %zu", mod_grads_ws_bytes(B, H), ws_bytes);
+  if (rows % 16 || ns < 1 || ns > 2) {
+    set_error("outer/vector-matrix product: rows %d must be a multiple of 16, streams %d in 1..2", rows, ns);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  if (!ws || ws_bytes < outer_vecmat_ws_bytes(B, rows, cols)) {
+    set_error("outer/vector-matrix product: workspace needs %zu bytes, got %zu", outer_vecmat_ws_bytes(B, rows, cols),
+              ws_bytes);
     return MMDIT_E_WORKSPACE;
   }
-  float* sl = static_cast<float*>(ws);
-  float* dsl = sl + (size_t)B * H;
-  float* part = dsl + (size_t)B * H;
-  const int64_t n = (int64_t)B * H;
+  float* f = static_cast<float*>(ws);
+  float* df = f + (size_t)B * cols;
+  float* part = df + (size_t)B * cols;
+  const int64_t n = (int64_t)B * cols;
   if (dt == MMDIT_BF16)
-    MMDIT_LAUNCH(silu_pair_kernel<bf16>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, static_cast<const bf16*>(c), sl, dsl, n);
+    MMDIT_LAUNCH(act_pair_kernel<bf16>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, x, x_f32, mode, f, df, n);
   else
-    MMDIT_LAUNCH(silu_pair_kernel<float>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, static_cast<const float*>(c), sl, dsl, n);
-  MMDIT_TRY(launch_check("silu_pair_kernel", s));
-  for (int st = 0; st < 2; ++st) {
-    MMDIT_LAUNCH(dwmod_kernel, dim3((unsigned)cdiv(H, 256), (unsigned)cdiv(rows, 16)), dim3(256), 0, s,
-                 st ? dmod_t : dmod_i, sl, st ? dw_t : dw_i, B, H, rows);
-    MMDIT_TRY(launch_check("dwmod_kernel", s));
+    MMDIT_LAUNCH(act_pair_kernel<float>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, x, x_f32, mode, f, df, n);
+  MMDIT_TRY(launch_check("act_pair_kernel", s));
+  for (int st = 0; st < ns; ++st) {
+    MMDIT_LAUNCH(outer_kernel, dim3((unsigned)cdiv(cols, 256), (unsigned)(rows / 16)), dim3(256), 0, s, dy[st], f,
+                 dw[st], B, cols, rows);
+    MMDIT_TRY(launch_check("outer_kernel", s));
   }
-  const int32_t kch = mod_grads_chunks(B, H);
+  if (!dx) return MMDIT_OK;
+  const int32_t kch = outer_vecmat_chunks(B, rows, cols);
   const int32_t kr = (int32_t)cdiv(rows, kch);
-  dim3 g((unsigned)cdiv(H, 256), (unsigned)(2 * kch), (unsigned)cdiv(B, 16));
+  dim3 g((unsigned)cdiv(cols, 256), (unsigned)(ns * kch), (unsigned)cdiv(B, 16));
+  const void* w1 = ns > 1 ? w[1] : w[0];
+  const float* dy1 = ns > 1 ? dy[1] : dy[0];
   if (dt == MMDIT_BF16)
-    MMDIT_LAUNCH(dc_part_kernel<bf16>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const bf16*>(w_i),
-                 static_cast<const bf16*>(w_t), part, B, H, rows, kr, kch);
+    MMDIT_LAUNCH(vecmat_part_kernel<bf16>, g, dim3(256), 0, s, dy[0], dy1, static_cast<const bf16*>(w[0]),
+                 static_cast<const bf16*>(w1), part, B, cols, rows, kr, kch);
   else
-    MMDIT_LAUNCH(dc_part_kernel<float>, g, dim3(256), 0, s, dmod_i, dmod_t, static_cast<const float*>(w_i),
-                 static_cast<const float*>(w_t), part, B, H, rows, kr, kch);
-  MMDIT_TRY(launch_check("dc_part_kernel", s));
-  MMDIT_LAUNCH(dc_finalize_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, dsl, dc, B, H, 2 * kch);
-  return launch_check("dc_finalize_kernel", s);
+    MMDIT_LAUNCH(vecmat_part_kernel<float>, g, dim3(256), 0, s, dy[0], dy1, static_cast<const float*>(w[0]),
+                 static_cast<const float*>(w1), part, B, cols, rows, kr, kch);
+  MMDIT_TRY(launch_check("vecmat_part_kernel", s));
+  MMDIT_LAUNCH(vecmat_finalize_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, df, dx, n, ns * kch);
+  return launch_check("vecmat_finalize_kernel", s);
 }
 
 }  // namespace mmdit

@@ -88,6 +88,7 @@ mmdit_status pack_impl(const mmdit_sample*, int32_t, mmdit_pack_t*, hipStream_t)
 mmdit_status gather_impl(const mmdit_pack_t*, int32_t, const void* const*, int32_t, mmdit_dtype, void*, hipStream_t);
 mmdit_status make_xt_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const float*, void*, hipStream_t);
 mmdit_status loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, void*, size_t, hipStream_t);
+mmdit_status loss_grad_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, void*, hipStream_t);
 mmdit_status euler_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, int32_t, int32_t, float, float, float, float*, void*, hipStream_t);
 mmdit_status pack_latent_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const float*, int32_t, int32_t, void*, hipStream_t);
 mmdit_status rms_modulate_impl(mmdit_dtype, int64_t, int32_t, const void*, const int32_t*, const int32_t*, const float*, int64_t, int64_t, int64_t, void*, float, hipStream_t);
@@ -737,7 +738,7 @@ BwdLayout bwd_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   const int64_t ch = colsum_chunks(pk->h_cu_img, pk->B, kColsumRows) + colsum_chunks(pk->h_cu_txt, pk->B, kColsumRows);
   Lb.partial = o; o = align256(o + (size_t)ch * 3 * H * 4);
   Lb.gpart = o;   o = align256(o + (size_t)(qk_bwd_blocks(pk->n_img) + qk_bwd_blocks(pk->n_txt)) * 2 * d->head_dim * 4);
-  Lb.modg = o;    o = align256(o + mod_grads_ws_bytes(pk->B, d->hidden));
+  Lb.modg = o;    o = align256(o + outer_vecmat_ws_bytes(pk->B, 6 * d->hidden, d->hidden));
   Lb.attn = o;    o = align256(o + attention_bwd_ws_bytes(pk, d->heads, d->head_dim));
   Lb.end = o;
   return Lb;
@@ -909,7 +910,7 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   {
     NormBwdSpec nb[2];
     for (int i = 0; i < 2; ++i)
-      nb[i] = {srows(S.x_mid, i, H), rows(Lb.dh2, i, H), mod[i], seg[i], dx[i], dxmid + (i ? ni * H : 0),
+      nb[i] = {nullptr, srows(S.x_mid, i, H), rows(Lb.dh2, i, H), mod[i], seg[i], dx[i], dxmid + (i ? ni * H : 0),
                inv_r + (i ? ni : 0), mod[i], rows(Lb.da, i, H), nr[i], 6 * H, 4 * H, 2 * H, 0, 1};
     MMDIT_TRY(norm_bwd2_impl(dt, H, d->eps, nb, 2, s));
   }
@@ -1002,7 +1003,7 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   {
     NormBwdSpec nb[2];
     for (int i = 0; i < 2; ++i)
-      nb[i] = {srows(S.x_in, i, H), rows(Lb.dh1, i, H), mod[i], seg[i], dxmid + (i ? ni * H : 0), dx[i],
+      nb[i] = {nullptr, srows(S.x_in, i, H), rows(Lb.dh1, i, H), mod[i], seg[i], dxmid + (i ? ni * H : 0), dx[i],
                inv_r + (i ? ni : 0), nullptr, nullptr, nr[i], 6 * H, H, 0, 1, 0};
     MMDIT_TRY(norm_bwd2_impl(dt, H, d->eps, nb, 2, s));
   }
@@ -1015,8 +1016,264 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     MMDIT_TRY(colsums(i, 2, A, Bm, rs, af, bf, off));
   }
   // adaLN: dW_mod = d_mod^T SiLU(c), dc += (d_mod W_mod) SiLU'(c)
-  return mod_grads_impl(dt, pk->B, H, c, dmod[0], dmod[1], w->img.w_mod, w->txt.w_mod, g->img.w_mod, g->txt.w_mod,
-                        dc, base + Lb.modg, Lb.attn - Lb.modg, s);
+  const float* dm[2] = {dmod[0], dmod[1]};
+  const void* wm[2] = {w->img.w_mod, w->txt.w_mod};
+  float* dwm[2] = {g->img.w_mod, g->txt.w_mod};
+  return outer_vecmat_impl(dt, pk->B, 6 * H, H, 2, dm, wm, c, 0, 0, dwm, dc, base + Lb.modg, Lb.attn - Lb.modg, s);
+}
+
+namespace {
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// bytes % 4 == 0; a kernel rather than a memset so the call can be captured in a graph
+mmdit_status zero_bytes(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n <= 0) return MMDIT_OK;
+  const int64_t blocks = cdiv(n, 256) < 4096 ? cdiv(n, 256) : 4096;
+  MMDIT_LAUNCH(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
+  return launch_check("zero_words_kernel", s);
+}
+
+// Workspace of the final-layer and embedding backward calls.
+struct WrapLayout {
+  size_t modf, hf, dhf, inv_r, dvT, hfT, woT, partial, dmodf, ov, dxiT, ztT, dxtT, tauT, end;
+};
+
+WrapLayout wrap_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  const size_t es = esize(d->dtype);
+  const size_t H = d->hidden, C = d->c_lat, B = pk->B;
+  const size_t ntp = pad64(pk->n_tgt), nip = pad64(pk->n_img), nxp = pad64(pk->n_txt);
+  WrapLayout W;
+  size_t o = 0;
+  W.modf = o;    o = align256(o + B * 2 * H * 4);
+  W.hf = o;      o = align256(o + (size_t)pk->n_tgt * H * es);
+  W.dhf = o;     o = align256(o + (size_t)pk->n_tgt * H * es);
+  W.inv_r = o;   o = align256(o + (size_t)pk->n_tgt * 4);
+  W.dvT = o;     o = align256(o + C * ntp * es);
+  W.hfT = o;     o = align256(o + H * ntp * es);
+  W.woT = o;     o = align256(o + H * C * es);
+  W.partial = o; o = align256(o + (size_t)colsum_chunks(pk->h_cu_tgt, pk->B, kColsumRows) * 2 * H * 4);
+  W.dmodf = o;   o = align256(o + B * 2 * H * 4);
+  size_t ov = outer_vecmat_ws_bytes(pk->B, 2 * d->hidden, d->hidden);
+  W.ov = o;      o = align256(o + ov);
+  W.dxiT = o;    o = align256(o + H * nip * es);
+  W.ztT = o;     o = align256(o + C * nip * es);
+  W.dxtT = o;    o = align256(o + H * nxp * es);
+  W.tauT = o;    o = align256(o + (size_t)d->d_txt * nxp * es);
+  W.end = o;
+  return W;
+}
+
+mmdit_status check_ws(void* ws, size_t ws_bytes, size_t need_b, const char* who) {
+  if (!ws || ws_bytes < need_b) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, need_b, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  return need(ws, who, "ws");
+}
+
+}  // namespace
+
+mmdit_status rf_loss_grad(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                          const void* eps, void* dv, mmdit_stream stream) {
+  return loss_grad_impl(pk, dt, C, v, z, eps, dv, (hipStream_t)stream);
+}
+
+size_t mmdit_wrap_bwd_workspace_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
+  if (check_dims(d, "mmdit_wrap_bwd_workspace_size") != MMDIT_OK ||
+      check_pack(pk, "mmdit_wrap_bwd_workspace_size") != MMDIT_OK)
+    return 0;
+  return wrap_layout(d, pk).end;
+}
+
+mmdit_status mmdit_final_bwd(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,
+                             const void* c, const void* x_img, const void* dv, void* dx_img, float* dw_fmod,
+                             float* dw_out, float* dc, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_final_bwd";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  const void* req[] = {w_fmod, w_out, dw_fmod, dw_out};
+  const char* nm[] = {"w_fmod", "w_out", "dw_fmod", "dw_out"};
+  for (int i = 0; i < 4; ++i) MMDIT_TRY(need(req[i], who, nm[i]));
+  const WrapLayout W = wrap_layout(d, pk);
+  MMDIT_TRY(check_ws(ws, ws_bytes, W.end, who));
+  hipStream_t s = (hipStream_t)stream;
+  const mmdit_dtype dt = d->dtype;
+  const int32_t H = d->hidden, C = d->c_lat;
+  const int64_t nt = pk->n_tgt, ntp = pad64(pk->n_tgt);
+  char* base = static_cast<char*>(ws);
+  if (pk->n_img > 0) {
+    MMDIT_TRY(need(dx_img, who, "dx_img"));
+    MMDIT_TRY(zero_bytes(dx_img, (size_t)pk->n_img * H * esize(dt), s));
+  }
+  if (nt == 0 || pk->B == 0) {
+    MMDIT_TRY(fill_zero(dw_out, (int64_t)C * H, s));
+    return fill_zero(dw_fmod, (int64_t)2 * H * H, s);
+  }
+  MMDIT_TRY(need(c, who, "c"));
+  MMDIT_TRY(need(dc, who, "dc"));
+  MMDIT_TRY(need(x_img, who, "x_img"));
+  MMDIT_TRY(need(dv, who, "dv"));
+  float* modf = reinterpret_cast<float*>(base + W.modf);
+  // recompute [shift, scale] = W_fmod SiLU(c) and h = rms(x_tgt)(1 + scale) + shift
+  LinearArgs a = mk(pk->B, 2 * H, H, c, w_fmod, modf, MMDIT_EPI_STORE_F32);
+  a.a_silu = 1;
+  a.tag = "final_mod";
+  MMDIT_TRY(linear(dt, &a, 1, s));
+  MMDIT_TRY(rms_modulate_impl(dt, nt, H, x_img, pk->tgt_row, pk->seg_img, modf, 2 * H, 0, H, base + W.hf, d->eps, s));
+  // dW_out = dv^T h, dh = dv W_out
+  {
+    TransposeArgs ta[1];
+    memset(ta, 0, sizeof(ta));
+    ta[0] = {dv, base + W.dvT, nullptr, nullptr, nullptr, C, nt, ntp, 0, C};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    ta[0] = {base + W.hf, base + W.hfT, nullptr, nullptr, nullptr, H, nt, ntp, 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    ta[0] = {w_out, base + W.woT, nullptr, nullptr, nullptr, H, C, C, 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    LinearArgs g = mk(C, H, (int32_t)ntp, base + W.dvT, base + W.hfT, dw_out, MMDIT_EPI_STORE_F32);
+    g.tag = "bwd_final_out_dw";
+    MMDIT_TRY(linear(dt, &g, 1, s));
+    LinearArgs x = mk(nt, H, C, dv, base + W.woT, base + W.dhf, MMDIT_EPI_STORE);
+    x.tag = "bwd_final_out_dx";
+    MMDIT_TRY(linear(dt, &x, 1, s));
+  }
+  // through the norm of the target rows into dx_img; adaLN sums per sample
+  float* inv_r = reinterpret_cast<float*>(base + W.inv_r);
+  {
+    NormBwdSpec nb = {pk->tgt_row, x_img, base + W.dhf, modf, pk->seg_img, nullptr, dx_img, inv_r, nullptr, nullptr,
+                      nt, 2 * H, H, 0, 0, 0};
+    MMDIT_TRY(norm_bwd2_impl(dt, H, d->eps, &nb, 1, s));
+  }
+  float* dmodf = reinterpret_cast<float*>(base + W.dmodf);
+  {
+    ColsumSpec sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.nterms = 2;
+    sp.a[0] = base + W.dhf;
+    sp.a[1] = base + W.dhf;
+    sp.b[1] = x_img;
+    sp.b_map[1] = pk->tgt_row;
+    sp.rs[1] = inv_r;
+    sp.out_off[0] = 0;
+    sp.out_off[1] = H;
+    sp.cu = pk->cu_tgt;
+    sp.h_cu = pk->h_cu_tgt;
+    sp.B = pk->B;
+    sp.H = H;
+    sp.partial = reinterpret_cast<float*>(base + W.partial);
+    sp.out = dmodf;
+    sp.out_stride = 2 * H;
+    MMDIT_TRY(seg_colsum_impl(dt, sp, s));
+  }
+  const float* dm[1] = {dmodf};
+  const void* wm[1] = {w_fmod};
+  float* dwm[1] = {dw_fmod};
+  return outer_vecmat_impl(dt, pk->B, 2 * H, H, 1, dm, wm, c, 0, 0, dwm, dc, base + W.ov, W.dxiT - W.ov, s);
+}
+
+mmdit_status mmdit_embed_bwd(const mmdit_dims* d, const mmdit_pack_t* pk, const void* zt, const void* tau,
+                             const void* dx_img, const void* dx_txt, float* dw_in, float* dw_txt, void* ws,
+                             size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_embed_bwd";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  MMDIT_TRY(need(dw_in, who, "dw_in"));
+  MMDIT_TRY(need(dw_txt, who, "dw_txt"));
+  const WrapLayout W = wrap_layout(d, pk);
+  MMDIT_TRY(check_ws(ws, ws_bytes, W.end, who));
+  hipStream_t s = (hipStream_t)stream;
+  const mmdit_dtype dt = d->dtype;
+  const int32_t H = d->hidden, C = d->c_lat, T = d->d_txt;
+  const int64_t ni = pk->n_img, nx = pk->n_txt, nip = pad64(ni), nxp = pad64(nx);
+  char* base = static_cast<char*>(ws);
+  LinearArgs a[2];
+  int n = 0;
+  if (ni > 0) {
+    MMDIT_TRY(need(zt, who, "zt"));
+    MMDIT_TRY(need(dx_img, who, "dx_img"));
+    TransposeArgs ta[1];
+    ta[0] = {dx_img, base + W.dxiT, nullptr, nullptr, nullptr, H, ni, nip, 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    ta[0] = {zt, base + W.ztT, nullptr, nullptr, nullptr, C, ni, nip, 0, C};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    a[n++] = mk(H, C, (int32_t)nip, base + W.dxiT, base + W.ztT, dw_in, MMDIT_EPI_STORE_F32);
+  } else {
+    MMDIT_TRY(fill_zero(dw_in, (int64_t)H * C, s));
+  }
+  if (nx > 0) {
+    MMDIT_TRY(need(tau, who, "tau"));
+    MMDIT_TRY(need(dx_txt, who, "dx_txt"));
+    TransposeArgs ta[1];
+    ta[0] = {dx_txt, base + W.dxtT, nullptr, nullptr, nullptr, H, nx, nxp, 0, H};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    ta[0] = {tau, base + W.tauT, nullptr, nullptr, nullptr, T, nx, nxp, 0, T};
+    MMDIT_TRY(transpose2_impl(dt, ta, 1, 0, s));
+    a[n++] = mk(H, T, (int32_t)nxp, base + W.dxtT, base + W.tauT, dw_txt, MMDIT_EPI_STORE_F32);
+  } else {
+    MMDIT_TRY(fill_zero(dw_txt, (int64_t)H * T, s));
+  }
+  if (n == 0) return MMDIT_OK;
+  a[0].tag = "bwd_embed_dw";
+  return linear(dt, a, n, s);
+}
+
+mmdit_status mmdit_cond_bwd(const mmdit_dims* d, const void* w_t1, const void* w_t2, const float* t, int32_t B,
+                            const float* dc, float* dw_t1, float* dw_t2, void* ws, size_t ws_bytes,
+                            mmdit_stream stream) {
+  const char* who = "mmdit_cond_bwd";
+  MMDIT_TRY(check_dims(d, who));
+  if (B < 0 || B > MMDIT_MAX_SAMPLES) {
+    set_error("%s: B=%d", who, B);
+    return MMDIT_E_INVALID;
+  }
+  const void* req[] = {w_t1, w_t2, dw_t1, dw_t2};
+  const char* nm[] = {"w_t1", "w_t2", "dw_t1", "dw_t2"};
+  for (int i = 0; i < 4; ++i) MMDIT_TRY(need(req[i], who, nm[i]));
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t H = d->hidden;
+  if (B == 0) {
+    MMDIT_TRY(fill_zero(dw_t1, (int64_t)H * d->t_dim, s));
+    return fill_zero(dw_t2, (int64_t)H * H, s);
+  }
+  MMDIT_TRY(need4(t, who, "t"));
+  MMDIT_TRY(need(dc, who, "dc"));
+  const size_t es = esize(d->dtype);
+  size_t ov = outer_vecmat_ws_bytes(B, H, H);
+  const size_t ov3 = outer_vecmat_ws_bytes(B, H, d->t_dim);
+  ov = align256(ov > ov3 ? ov : ov3);
+  const size_t o_emb = ov, o_h1 = o_emb + align256((size_t)B * d->t_dim * es), o_dh = o_h1 + align256((size_t)B * H * es);
+  MMDIT_TRY(check_ws(ws, ws_bytes, o_dh + (size_t)B * H * 4, who));
+  char* base = static_cast<char*>(ws);
+  // recompute emb(t) and h1 = W_t1 emb exactly as the forward
+  MMDIT_TRY(temb_impl(d->dtype, B, d->t_dim, t, base + o_emb, s));
+  LinearArgs a = mk(B, H, d->t_dim, base + o_emb, w_t1, base + o_h1, MMDIT_EPI_STORE);
+  a.tag = "cond_mlp1";
+  MMDIT_TRY(linear(d->dtype, &a, 1, s));
+  float* dh = reinterpret_cast<float*>(base + o_dh);
+  MMDIT_TRY(fill_zero(dh, (int64_t)B * H, s));
+  // c = W_t2 SiLU(h1): dW_t2 = dc^T SiLU(h1), dh1 = (dc W_t2) SiLU'(h1); then dW_t1 = dh1^T emb
+  const float* dy[1] = {dc};
+  const void* w2[1] = {w_t2};
+  float* dw2[1] = {dw_t2};
+  MMDIT_TRY(outer_vecmat_impl(d->dtype, B, H, H, 1, dy, w2, base + o_h1, 0, 0, dw2, dh, base, ov, s));
+  const float* dy1[1] = {dh};
+  const void* w1[1] = {w_t1};
+  float* dw1[1] = {dw_t1};
+  return outer_vecmat_impl(d->dtype, B, H, d->t_dim, 1, dy1, w1, base + o_emb, 0, 1, dw1, nullptr, base, ov, s);
+}
+
+size_t mmdit_cond_bwd_workspace_size(const mmdit_dims* d, int32_t B) {
+  if (check_dims(d, "mmdit_cond_bwd_workspace_size") != MMDIT_OK || B < 0) return 0;
+  const size_t es = esize(d->dtype);
+  size_t ov = outer_vecmat_ws_bytes(B, d->hidden, d->hidden);
+  const size_t ov3 = outer_vecmat_ws_bytes(B, d->hidden, d->t_dim);
+  ov = align256(ov > ov3 ? ov : ov3);
+  return ov + align256((size_t)B * d->t_dim * es) + align256((size_t)B * d->hidden * es) + (size_t)B * d->hidden * 4;
 }
 
 mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,

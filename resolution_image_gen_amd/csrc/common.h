@@ -179,6 +179,7 @@ constexpr int kColsumRows = 64;
 struct ColsumSpec {
   const void* a[3];
   const void* b[3];
+  const int32_t* b_map[3];   // optional: b's row is b_map[r]
   const float* rs[3];
   int32_t a_f32[3], b_f32[3], out_off[3];
   int32_t nterms;
@@ -196,6 +197,7 @@ mmdit_status seg_colsum_impl(mmdit_dtype dt, const ColsumSpec& sp, hipStream_t s
 // dx = dres + (dn - n mean(dn n)) / rms(x) with dn = dh (1 + scale); also
 // 1/rms per row and, optionally, dgated = gate * dx.
 struct NormBwdSpec {
+  const int32_t* row_map;   // optional: x, seg and dx rows are row_map[row]; dh, inv_r rows are row
   const void* x;
   const void* dh;
   const float* mod;
@@ -230,11 +232,15 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
 
 // dW_mod = d_mod^T SiLU(c) per stream ([6H, H] float32) and
 // dc += (d_mod W_mod) * SiLU'(c) summed over both streams.
-int32_t mod_grads_chunks(int32_t B, int32_t H);
-size_t mod_grads_ws_bytes(int32_t B, int32_t H);
-mmdit_status mod_grads_impl(mmdit_dtype dt, int32_t B, int32_t H, const void* c, const float* dmod_i,
-                            const float* dmod_t, const void* w_i, const void* w_t, float* dw_i, float* dw_t,
-                            float* dc, void* ws, size_t ws_bytes, hipStream_t s);
+// For y = W f(x), one vector per sample (b < B): dw[s] = dy[s]^T f(x)
+// ([rows, cols] float32, s < ns streams sharing x) and, when dx is not NULL,
+// dx += f'(x) * sum_s dy[s] W[s]  ([B, cols] float32).  W [rows, cols] in the
+// model dtype; x [B, cols] in the model dtype or float32 (x_f32); f is SiLU
+// (mode 0) or the identity (mode 1).  rows % 16 == 0.
+size_t outer_vecmat_ws_bytes(int32_t B, int32_t rows, int32_t cols);
+mmdit_status outer_vecmat_impl(mmdit_dtype dt, int32_t B, int32_t rows, int32_t cols, int ns, const float* const* dy,
+                               const void* const* w, const void* x, int32_t x_f32, int32_t mode, float* const* dw,
+                               float* dx, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Attention backward over a pack (see attention.hip); ws >= attention_bwd_ws_bytes.
 size_t attention_bwd_ws_bytes(const mmdit_pack_t* pk, int32_t heads, int32_t D);

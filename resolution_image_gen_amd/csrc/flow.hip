@@ -70,6 +70,31 @@ __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
   if (row < n_tgt && lane16 == 0) row_sse[row] = acc;
 }
 
+// dL/dv of the loss mean_b SSE_b / (tgt_len_b C): 2 (v - (z - eps)) / (B tgt_len_b C)
+// on every target row (one thread per 8 channels).
+template <typename T>
+__global__ void loss_grad_kernel(int64_t n_tgt, int32_t C, int32_t B, const T* __restrict__ v,
+                                 const T* __restrict__ z, const T* __restrict__ eps,
+                                 const int32_t* __restrict__ tgt_row, const int32_t* __restrict__ seg,
+                                 const int32_t* __restrict__ tgt_len, T* __restrict__ dv) {
+  const int32_t upr = C >> 3;
+  const int64_t n_units = n_tgt * upr;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = u / upr;
+    const int64_t c8 = (u - row * upr) * 8;
+    const int64_t src = tgt_row[row];
+    const float k = 2.0f / ((float)B * (float)tgt_len[seg[src]] * (float)C);
+    float vv[8], zv[8], ev[8];
+    Vec8<T>::load(v + row * C + c8, vv);
+    Vec8<T>::load(z + src * C + c8, zv);
+    Vec8<T>::load(eps + src * C + c8, ev);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vv[i] = k * (vv[i] - (zv[i] - ev[i]));
+    Vec8<T>::store(dv + row * C + c8, vv);
+  }
+}
+
 // One block of 16 waves.  Per sample, in order: thread t sums rows
 // r0 + t, r0 + t + 1024, ...; each wave reduces its lanes; the 16 wave sums
 // are added in wave order.  Then one thread forms the mean loss over the
@@ -183,6 +208,25 @@ mmdit_status make_xt_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, con
     MMDIT_LAUNCH(make_xt_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_img, C,
                        (const float*)z, (const float*)eps, t, pk->seg_img, pk->pos_img, (float*)zt);
   return launch_check("make_xt_kernel", s);
+}
+
+mmdit_status loss_grad_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                            const void* eps, void* dv, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_loss_grad"));
+  MMDIT_TRY(check_c(C, "rf_loss_grad"));
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  if (!v || !z || !eps || !dv || !pk->tgt_row || !pk->tgt_len) {
+    set_error("rf_loss_grad: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  const int g = grid_for(pk->n_tgt * (C >> 3), 256);
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(loss_grad_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, pk->B, (const bf16*)v,
+                 (const bf16*)z, (const bf16*)eps, pk->tgt_row, pk->seg_img, pk->tgt_len, (bf16*)dv);
+  else
+    MMDIT_LAUNCH(loss_grad_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, pk->B, (const float*)v,
+                 (const float*)z, (const float*)eps, pk->tgt_row, pk->seg_img, pk->tgt_len, (float*)dv);
+  return launch_check("loss_grad_kernel", s);
 }
 
 mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v,

@@ -172,6 +172,64 @@ class TrainForward:
         return pk
 
 
+WRAP_KEYS = ("w_t1", "w_t2", "w_in", "w_txt", "w_fmod", "w_out")
+
+
+class TrainStep(TrainForward):
+    """One training step over a pack: the forward of TrainForward with every
+    block's intermediates kept (one saved buffer per block), then the whole
+    backward: loss gradient, final layer, the blocks in reverse order, the
+    embeddings and the conditioning.  Every weight gradient lands in
+    self.grads (float32, the shape of its weight): self.grads["wrap"][name]
+    and self.grads["blocks"][i]["img" | "txt"][name]."""
+
+    def __init__(self, wl, W, inputs, device="cuda", samples=None, img_budget=None):
+        super().__init__(wl, W, inputs, device, samples, img_budget)
+        pk, dm = self.pk, self.dims
+        d = wl.dims
+        f32 = dict(dtype=torch.float32, device=device)
+        nsv = B.block_saved_size(dm, pk)
+        self.saved = [torch.empty(nsv, dtype=torch.uint8, device=device) for _ in W.bw]
+        self.ws_bwd = torch.empty(max(B.block_bwd_workspace_size(dm, pk), B.wrap_bwd_workspace_size(dm, pk),
+                                      B.cond_bwd_workspace_size(dm, pk.B), 256), dtype=torch.uint8, device=device)
+        e = dict(dtype=dm.torch_dtype, device=device)
+        self.dv = torch.empty(max(pk.n_tgt, 1), d.c_lat, **e)
+        self.dx_img = torch.empty(max(pk.n_img, 1), d.hidden, **e)
+        self.dx_txt = torch.empty(max(pk.n_txt, 1), d.hidden, **e)
+        self.dc = torch.empty(max(pk.B, 1), d.hidden, **f32)
+        self.grads = {"wrap": {k: torch.empty(tuple(W.wrap[k].shape), **f32) for k in WRAP_KEYS},
+                      "blocks": [{s: {k: torch.empty(tuple(blk[s][k].shape), **f32) for k in B.GRAD_KEYS}
+                                  for s in ("img", "txt")} for blk in W.blocks]}
+        self.bg = [B.block_grads(g) for g in self.grads["blocks"]]
+
+    def run(self, stream=None, repack=True):
+        W, pk, dm = self.W, self.pk, self.dims
+        if repack:
+            pk = self._repack(stream)
+        B.pack_gather(pk, 0, self.z_s, self.z, stream)
+        B.pack_gather(pk, 0, self.eps_s, self.eps, stream)
+        B.pack_gather(pk, 1, self.tau_s, self.tau, stream)
+        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, stream)
+        B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.c, self.ws, stream)
+        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
+        for bw, sv in zip(W.bw, self.saved):
+            B.block_fwd_train(dm, bw, pk, self.c, self.x_img, self.x_txt, sv, self.ws, stream)
+        B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
+        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, stream)
+        # backward
+        g = self.grads["wrap"]
+        self.dc.zero_()
+        B.rf_loss_grad(pk, self.v, self.z, self.eps, self.dv, stream)
+        B.final_bwd(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.dv, self.dx_img,
+                    g["w_fmod"], g["w_out"], self.dc, self.ws_bwd, stream)
+        self.dx_txt.zero_()
+        for i in range(len(W.bw) - 1, -1, -1):
+            B.block_bwd(dm, W.bw[i], pk, self.c, self.saved[i], self.dx_img, self.dx_txt, self.bg[i], self.dc,
+                        self.ws_bwd, stream)
+        B.embed_bwd(dm, pk, self.zt, self.tau, self.dx_img, self.dx_txt, g["w_in"], g["w_txt"], self.ws_bwd, stream)
+        B.cond_bwd(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.dc, g["w_t1"], g["w_t2"], self.ws_bwd, stream)
+
+
 class Sampler:
     """Packed-CFG Euler sampler: one pack [cond, uncond] of the same grid,
     `steps` forwards through the block stack, CFG combine + Euler per step.

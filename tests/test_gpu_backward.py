@@ -120,3 +120,37 @@ def test_training_forward_matches_inference_forward_and_is_deterministic(B, case
     for s in ("img", "txt"):
         for k in B.GRAD_KEYS:
             assert torch.equal(r1["grads"][s][k], r2["grads"][s][k]), (s, k)
+
+
+@pytest.mark.parametrize("name,depth", [("tiny_f32", 2), ("tiny_f32_edit", 2), ("small_bf16", 2)])
+def test_training_step_vs_oracle(B, name, depth):
+    """The whole training step: forward with the RF loss, then every weight
+    gradient of the model (conditioning MLP, embeddings, each block, final
+    layer) against the oracle's chain rule."""
+    from oracle import grad as OGr
+    from oracle import flow as OF
+    from resolution_image_gen_amd import runner as R
+
+    d, dtype, samples = CASES[name]
+    wl = CF.Workload(f"train_{name}", d, dtype, tuple(samples), img_budget=10 ** 6, depth=depth)
+    print(f"training step {name} depth {depth}", flush=True)
+    W = R.Weights(wl, recipe="stress")
+    inp = R.training_inputs(wl)
+    ts = R.TrainStep(wl, W, inp)
+    ts.run()
+    torch.cuda.synchronize()
+    ref = oracle_pack(samples)
+    Wd = {k: np.asarray(v, np.float64) for k, v in W.np_wrap.items()}
+    Wd["blocks"] = [f64_block(nb) for nb in W.np_blocks]
+    zt = OF.make_xt(inp["z"], inp["eps"], inp["t"], ref)
+    want = OGr.training_step_grads(zt, inp["tau"], inp["t"], Wd, ref, d.heads, inp["z"], inp["eps"])
+    tol = TOL[dtype]
+    assert abs(ts.loss.item() - want["loss"]) <= tol * abs(want["loss"]), (ts.loss.item(), want["loss"])
+    assert_close("dv", to_np(ts.dv)[:ref["cu_tgt"][-1]], want["dv"], tol)
+    for k in ("w_t1", "w_t2", "w_in", "w_txt", "w_fmod", "w_out"):
+        assert_close(f"d{k}", to_np(ts.grads["wrap"][k]), want[k], tol)
+    for i in range(depth):
+        for s in ("img", "txt"):
+            for k in B.GRAD_KEYS:
+                assert_close(f"block{i} d{k}_{s}", to_np(ts.grads["blocks"][i][s][k]), want["blocks"][i][s]["d" + k],
+                             tol)
