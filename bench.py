@@ -221,6 +221,54 @@ def bench_sampler(steps, warmup):
                      "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3)}}
 
 
+def train_step_flops(wl, depth):
+    """Algorithmic FLOPs of one training step: per block the forward
+    (24 H^2 N + 4 H sum L_b^2) and the backward (twice the linears, 2.5 times
+    the attention), plus the wrapper GEMMs forward and backward (three times)."""
+    from resolution_image_gen_amd.configs import block_flops
+
+    _, lin, att = block_flops(wl.dims, wl.samples)
+    _, wrap = step_flops(wl)
+    wrap -= 2.0 * len(wl.samples) * 12 * wl.dims.hidden ** 2 * (wl.depth - depth)   # modulation of absent blocks
+    return depth * (3 * lin + 3.5 * att) + 3 * wrap
+
+
+def bench_train_step(steps, warmup, depth):
+    """ms per training step over the pages' per-GPU workload: one 50,048-token
+    native-resolution pack, `depth` random-init blocks forward with saved
+    intermediates, the RF loss, then the whole backward (every weight
+    gradient, float32)."""
+    import torch
+
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import runner as R
+
+    wl = CF.WORKLOADS["train50k_bf16"]
+    W = R.Weights(wl, source="torch", depth=depth)
+    ts = R.TrainStep(wl, W, R.training_inputs(wl))
+    for _ in range(warmup):
+        ts.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ts.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(ts.loss).all()
+    for g in [ts.grads["wrap"]] + [gb[s] for gb in ts.grads["blocks"] for s in gb]:
+        for t in g.values():
+            assert torch.isfinite(t).all()
+    n = sum(h * w * f + t for h, w, f, t in wl.samples)
+    fl = train_step_flops(wl, depth)
+    return {"workload": f"{wl.name}: {wl.note}", "depth": depth, "ms_per_step": round(ms, 2), "steps_timed": steps,
+            "tokens_per_s": round(n / (ms * 1e-3), 1), "tflop_per_step": round(fl / 1e12, 2),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "loss": round(ts.loss.item(), 6)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +282,10 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--train-steps", type=int, default=0,
+                    help="also time N training steps (forward + backward, every weight gradient) over one "
+                         "50,048-token pack and report them under 'train_step' (0: skip)")
+    ap.add_argument("--train-depth", type=int, default=28, help="blocks of the timed training step")
     ap.add_argument("--sampler-packs", type=int, default=0,
                     help="also time N packs of the 4-step packed-CFG sampler (28 blocks) and report them "
                          "under 'sampler' (0: skip)")
@@ -366,10 +418,14 @@ def main():
         "roofline": roof,
         "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
     }
-    if args.sampler_packs > 0:
+    if args.sampler_packs > 0 or args.train_steps > 0:
         del tf, W
         torch.cuda.empty_cache()
+    if args.sampler_packs > 0:
         out["sampler"] = bench_sampler(args.sampler_packs, 1)
+        torch.cuda.empty_cache()
+    if args.train_steps > 0:
+        out["train_step"] = bench_train_step(args.train_steps, 1, args.train_depth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, W_np, inputs, args.cpu_samples)
     print(json.dumps(out), flush=True)

@@ -58,6 +58,16 @@ WORKLOADS = {
         depth=28, steps=4, guidance=4.0,
         note="4-step Euler edit, packed CFG (cond + uncond, each 64x64 noised target + 64x64 clean source "
              "+ 256 text), 28 blocks"),
+    # the pages' per-GPU training workload: one ~50,000-token native-resolution
+    # pack (1024^2-class grids of four aspect ratios and one 768^2 grid, 256
+    # text tokens each), forward and backward through 28 blocks
+    "train50k_bf16": Workload(
+        "train50k_bf16", B4, "bf16",
+        tuple((h, w, 1, 256) for h, w in [(64, 64), (48, 84), (84, 48), (32, 128)] * 2
+              + [(64, 64), (48, 84), (84, 48), (48, 48)]),
+        img_budget=50000, depth=28,
+        note="training step: 12 samples (grids 64x64, 48x84, 84x48, 32x128 x3, 48x48) + 256 text each = 50,048 "
+             "tokens, 28 blocks forward + backward, every weight gradient"),
     "edit2048_bf16": Workload(
         "edit2048_bf16", B4, "bf16", ((128, 128, 2, 512),), img_budget=32768,
         note="2048^2 edit: target + source 128x128 grids (3D RoPE frames 0/1) + 512 text"),

@@ -163,6 +163,28 @@ __device__ __forceinline__ bool chunk_rows(const ColsumArgs& a, int ci, int& b, 
 }
 
 template <typename T>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, bool f32, float* v) {
+  if (f32) Vec8<float>::load(static_cast<const float*>(p) + i, v);
+  else Vec8<T>::load(static_cast<const T*>(p) + i, v);
+}
+
+template <typename T>
+__device__ __forceinline__ void term8(const ColTerm& t, int32_t r, int c, int H, float* v) {
+  ld8<T>(t.a, (int64_t)r * H + c, t.a_f32, v);
+  if (t.b) {
+    float w[8];
+    ld8<T>(t.b, (int64_t)(t.b_map ? t.b_map[r] : r) * H + c, t.b_f32, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= w[e];
+  }
+  if (t.rs) {
+    const float q = t.rs[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= q;
+  }
+}
+
+template <typename T>
 __device__ __forceinline__ float term(const ColTerm& t, int32_t r, int c, int H) {
   float v = ld<T>(t.a, (int64_t)r * H + c, t.a_f32);
   if (t.b) v *= ld<T>(t.b, (int64_t)(t.b_map ? t.b_map[r] : r) * H + c, t.b_f32);
@@ -201,6 +223,36 @@ __global__ void __launch_bounds__(256) colsum_kernel(ColsumArgs a) {
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     if (k < a.nterms) a.partial[((int64_t)ci * a.nterms + k) * a.H + c] = s[k];
+}
+
+// 8 columns per thread (16-byte loads), rows in order: the same per-column
+// sums as colsum_kernel.
+template <typename T>
+__global__ void __launch_bounds__(256) colsum8_kernel(ColsumArgs a) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  const int ci = blockIdx.y;
+  int b;
+  int32_t r0, r1;
+  if (!chunk_rows(a, ci, b, r0, r1) || c >= a.H) return;
+  float s[3][8];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[k][e] = 0.f;
+#pragma unroll 4
+  for (int32_t r = r0; r < r1; ++r) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < a.nterms) {
+        float v[8];
+        term8<T>(a.t[k], r, c, a.H, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[k][e] += v[e];
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < a.nterms) Vec8<float>::store(a.partial + ((int64_t)ci * a.nterms + k) * a.H + c, s[k]);
 }
 
 __global__ void __launch_bounds__(256) colsum_finalize_kernel(ColsumArgs a) {
@@ -403,14 +455,16 @@ __global__ void __launch_bounds__(256) qk_bwd_kernel(QkBwdBatch bt, RopeTabB tab
   }
 }
 
-__global__ void __launch_bounds__(256) qk_gain_finalize_kernel(const float* gpart, int64_t blocks, int32_t D,
-                                                               float* dg_q, float* dg_k) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= 2 * D) return;
+// One wave per gain element: lane l adds the partials of blocks l, l + 64,
+// ... in order, then a fixed butterfly over the lanes (a fixed order).
+__global__ void __launch_bounds__(64) qk_gain_finalize_kernel(const float* gpart, int64_t blocks, int32_t D,
+                                                              float* dg_q, float* dg_k) {
+  const int i = blockIdx.x;
   const int which = i / D, dd = i % D;
-  float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t b = 0; b < blocks; ++b) p[b & 7] += gpart[(b * 2 + which) * D + dd];
-  (which ? dg_k : dg_q)[dd] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  float s = 0.f;
+  for (int64_t b = threadIdx.x; b < blocks; b += 64) s += gpart[(b * 2 + which) * D + dd];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) (which ? dg_k : dg_q)[dd] = s;
 }
 
 // ------------------------------------------- products over the sample axis
@@ -569,9 +623,15 @@ mmdit_status seg_colsum_impl(mmdit_dtype dt, const ColsumSpec& sp, hipStream_t s
   const int64_t chunks = colsum_chunks(sp.h_cu, sp.B, kColsumRows);
   if (sp.B == 0) return MMDIT_OK;
   if (chunks > 0) {
-    dim3 grid((unsigned)cdiv(sp.H, 256), (unsigned)chunks);
-    if (dt == MMDIT_BF16) MMDIT_LAUNCH(colsum_kernel<bf16>, grid, dim3(256), 0, s, a);
-    else MMDIT_LAUNCH(colsum_kernel<float>, grid, dim3(256), 0, s, a);
+    if (sp.H % 8 == 0) {
+      dim3 grid((unsigned)cdiv(sp.H / 8, 256), (unsigned)chunks);
+      if (dt == MMDIT_BF16) MMDIT_LAUNCH(colsum8_kernel<bf16>, grid, dim3(256), 0, s, a);
+      else MMDIT_LAUNCH(colsum8_kernel<float>, grid, dim3(256), 0, s, a);
+    } else {
+      dim3 grid((unsigned)cdiv(sp.H, 256), (unsigned)chunks);
+      if (dt == MMDIT_BF16) MMDIT_LAUNCH(colsum_kernel<bf16>, grid, dim3(256), 0, s, a);
+      else MMDIT_LAUNCH(colsum_kernel<float>, grid, dim3(256), 0, s, a);
+    }
     MMDIT_TRY(launch_check("colsum_kernel", s));
   }
   MMDIT_LAUNCH(colsum_finalize_kernel, dim3((unsigned)cdiv(sp.H, 256), sp.B, sp.nterms), dim3(256), 0, s, a);
@@ -658,8 +718,8 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
     MMDIT_TRY(launch_check("qk_bwd_kernel", s));
   }
   for (int i = 0; i < n; ++i) {
-    MMDIT_LAUNCH(qk_gain_finalize_kernel, dim3((unsigned)cdiv(2 * D, 256)), dim3(256), 0, s, p[i].gpart, blocks[i],
-                 D, p[i].dg_q, p[i].dg_k);
+    MMDIT_LAUNCH(qk_gain_finalize_kernel, dim3((unsigned)(2 * D)), dim3(64), 0, s, p[i].gpart, blocks[i], D,
+                 p[i].dg_q, p[i].dg_k);
     MMDIT_TRY(launch_check("qk_gain_finalize_kernel", s));
   }
   return MMDIT_OK;
