@@ -53,6 +53,27 @@ def kernel_work(wl):
     }
 
 
+def train_kernel_work(wl):
+    """Work per launch of the kernels of a training step's backward (GEMMs:
+    2 M N K; attention backward kernels: the score-sized products each one
+    runs, 2 d sum L_b^2 per head each: dQ 3 (S^T, dP^T, dQ), dK 3 (S, dP,
+    dK), dV 2 (S, dV))."""
+    d = wl.dims
+    H, M = d.hidden, d.mlp
+    n = sum(f * h * w + t for h, w, f, t in wl.samples)
+    unit = 2.0 * H * sum((f * h * w + t) ** 2 for h, w, f, t in wl.samples)
+    work = kernel_work(wl)
+    work.update({
+        "bwd_mlp_down_dx": ("mfma", 2.0 * n * H * M), "bwd_mlp_down_dw": ("mfma", 2.0 * n * H * M),
+        "bwd_mlp_up_dx": ("mfma", 2.0 * n * H * M), "bwd_mlp_up_dw": ("mfma", 2.0 * n * H * M),
+        "bwd_qkv_dx": ("mfma", 6.0 * n * H * H), "bwd_qkv_dw": ("mfma", 6.0 * n * H * H),
+        "bwd_out_proj_dx": ("mfma", 2.0 * n * H * H), "bwd_out_proj_dw": ("mfma", 2.0 * n * H * H),
+        "attn_bwd_dq_kernel": ("mfma", 3 * unit), "attn_bwd_dk_kernel": ("mfma", 3 * unit),
+        "attn_bwd_dv_kernel": ("mfma", 2 * unit),
+    })
+    return work
+
+
 # HBM bytes per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a plain copy's counter reading (profiles/traffic.json); valid only
 # while the kernel's sources are unchanged since the counters were taken.
@@ -262,11 +283,26 @@ def bench_train_step(steps, warmup, depth):
             assert torch.isfinite(t).all()
     n = sum(h * w * f + t for h, w, f, t in wl.samples)
     fl = train_step_flops(wl, depth)
+    # one more step with every launch bracketed by hipEvents on its stream
+    from resolution_image_gen_amd import binding as B
+
+    B.timing_enable(True)
+    torch.cuda.synchronize()
+    ts.run()
+    kernels = B.timing_report()
+    B.timing_enable(False)
+    work = train_kernel_work(wl)
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
+    avg_ms = kernels[dom][0] / kernels[dom][1]
+    achieved = work[dom][1] / (avg_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dom, "avg_launch_us": round(avg_ms * 1e3, 2)}
+    table = {k: round(v[0] / depth * 1e3, 1) for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][0])[:24]}
     return {"workload": f"{wl.name}: {wl.note}", "depth": depth, "ms_per_step": round(ms, 2), "steps_timed": steps,
             "tokens_per_s": round(n / (ms * 1e-3), 1), "tflop_per_step": round(fl / 1e12, 2),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
             "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "loss": round(ts.loss.item(), 6)}
+            "loss": round(ts.loss.item(), 6), "roofline": roof, "kernels_us_per_block": table}
 
 
 def main():

@@ -754,7 +754,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a, cons
   }
 }
 
-template <int D, bool DK>
+template <int D, bool DK, int KS>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, const bf16* __restrict__ qt,
                                                                const bf16* __restrict__ gt) {
   constexpr int BQ = 32;                 // queries per stage
@@ -771,25 +771,30 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
   const int32_t t0 = a.f.cu_txt[b], i0 = a.f.cu_img[b];
   const int32_t Tb = a.f.cu_txt[b + 1] - t0;
   const int32_t L = Tb + a.f.cu_img[b + 1] - i0;
-  const int32_t kbase = blockIdx.x * 128;
+  const int32_t kbase = blockIdx.x * 128 * KS;
   if (kbase >= L) return;
   const int32_t pstart = padded_start(a.f, b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int32_t jk = kbase + wave * 32 + l32;
-  bf16x8 kf[QS], vf[DK ? QS : 1];
-  if (jk < L) {
-    const bf16* r = joint_row<bf16>(a.f, jk, Tb, t0, i0) + head * D + g * 8;
+  // this wave's KS x 32 keys: key subtile ks holds keys kbase + (wave * KS + ks) * 32 + 0..31
+  int32_t jk[KS];
+  bf16x8 kf[KS][QS], vf[KS][DK ? QS : 1];
 #pragma unroll
-    for (int s2 = 0; s2 < QS; ++s2) {
-      kf[s2] = *reinterpret_cast<const bf16x8*>(r + a.f.H + s2 * 16);
-      if constexpr (DK) vf[s2] = *reinterpret_cast<const bf16x8*>(r + 2 * a.f.H + s2 * 16);
-    }
-  } else {
+  for (int ks = 0; ks < KS; ++ks) {
+    jk[ks] = kbase + (wave * KS + ks) * 32 + l32;
+    if (jk[ks] < L) {
+      const bf16* r = joint_row<bf16>(a.f, jk[ks], Tb, t0, i0) + head * D + g * 8;
 #pragma unroll
-    for (int s2 = 0; s2 < QS; ++s2) {
-      kf[s2] = bf16x8{};
-      if constexpr (DK) vf[s2] = bf16x8{};
+      for (int s2 = 0; s2 < QS; ++s2) {
+        kf[ks][s2] = *reinterpret_cast<const bf16x8*>(r + a.f.H + s2 * 16);
+        if constexpr (DK) vf[ks][s2] = *reinterpret_cast<const bf16x8*>(r + 2 * a.f.H + s2 * 16);
+      }
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < QS; ++s2) {
+        kf[ks][s2] = bf16x8{};
+        if constexpr (DK) vf[ks][s2] = bf16x8{};
+      }
     }
   }
 
@@ -830,11 +835,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
     }
   };
 
-  f32x16 acc[DT];
+  f32x16 acc[KS][DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ks][t][v] = 0.f;
   const int ntile = (L + BQ - 1) / BQ;
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -848,18 +855,25 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
     const bf16* gs = qs + TILE;
     const bf16* ts = qs + (NT - 1) * TILE;
     const float* lf = reinterpret_cast<const float*>(qs + NT * TILE);
-    f32x16 sc, dp;
+    f32x16 sc[KS], dp[KS];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = dp[v] = 0.f;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[ks][v] = dp[ks][v] = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < QS; ++s2) {
       const int off = prow * D + (((s2 * 2 + g) ^ ksw<D>(prow)) << 3);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qs + off), kf[s2], sc, 0, 0, 0);
-      if constexpr (DK)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gs + off), vf[s2], dp, 0, 0, 0);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + off);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks][s2], sc[ks], 0, 0, 0);
+      if constexpr (DK) {
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gs + off);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dp[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks][s2], dp[ks], 0, 0, 0);
+      }
     }
     // register v holds query q0 + 16 (v / 8) + 8 g + v % 8 of this lane's key
-    bf16x8 pf[2];
+    bf16x8 pf[KS][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float lv[8], dv8[8];
@@ -871,11 +885,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
         *reinterpret_cast<f32x4*>(dv8 + 4) = *reinterpret_cast<const f32x4*>(lf + BQ + qi + 4);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int v = 8 * h + u;
-        const float p = (q0 + qi + u < L) ? __builtin_amdgcn_exp2f(fmaf(sc[v], a.f.scale_log2, -lv[u])) : 0.f;
-        pf[h][u] = DK ? (bf16)(p * (dp[v] - dv8[u])) : (bf16)p;
-      }
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int v = 8 * h + u;
+          const float p = (q0 + qi + u < L) ? __builtin_amdgcn_exp2f(fmaf(sc[ks][v], a.f.scale_log2, -lv[u])) : 0.f;
+          pf[ks][h][u] = DK ? (bf16)(p * (dp[ks][v] - dv8[u])) : (bf16)p;
+        }
     }
     // dV^T[d][key] += dO^T[d][queries] P[queries][key], or dK^T += Q^T dS
 #pragma unroll
@@ -884,26 +900,33 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const int d = t * 32 + l32;
-        const int off = d * BQ + ((c ^ tsw(d)) << 3);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ts + off), pf[ks2], acc[t], 0, 0, 0);
+        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(ts + d * BQ + ((c ^ tsw(d)) << 3));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[ks][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pf[ks][ks2], acc[ks][t], 0, 0, 0);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if (jk < L) {
-    bf16* o = dqkv_row<bf16>(a, jk, Tb, t0, i0) + head * D + (DK ? a.f.H : 2 * a.f.H);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (jk[ks] >= L) continue;
+    bf16* o = dqkv_row<bf16>(a, jk[ks], Tb, t0, i0) + head * D + (DK ? a.f.H : 2 * a.f.H);
     const float sc = DK ? a.inv_sqrt_d : 1.0f;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
-        bf16x4 w = {(bf16)(acc[t][4 * vg] * sc), (bf16)(acc[t][4 * vg + 1] * sc), (bf16)(acc[t][4 * vg + 2] * sc),
-                    (bf16)(acc[t][4 * vg + 3] * sc)};
+        bf16x4 w = {(bf16)(acc[ks][t][4 * vg] * sc), (bf16)(acc[ks][t][4 * vg + 1] * sc),
+                    (bf16)(acc[ks][t][4 * vg + 2] * sc), (bf16)(acc[ks][t][4 * vg + 3] * sc)};
         *reinterpret_cast<bf16x4*>(o + t * 32 + 8 * vg + 4 * g) = w;
       }
   }
 }
+
+// key subtiles (of 32) per wave of the dK and dV kernels
+constexpr int DKS = 1, DVS = 1;
 
 template <int D>
 mmdit_status launch_attn_bwd_mfma(const AttnBwdArgs& a, const mmdit_pack_t* pk, bf16* qt, bf16* kt, bf16* gt,
@@ -920,10 +943,10 @@ mmdit_status launch_attn_bwd_mfma(const AttnBwdArgs& a, const mmdit_pack_t* pk, 
     MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<D>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq),
                         "hipFuncSetAttribute(attn_bwd_dq_kernel)"));
-    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, true>,
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, true, DKS>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dk),
                         "hipFuncSetAttribute(attn_bwd_dk_kernel)"));
-    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, false>,
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)attn_bwd_dkdv_kernel<D, false, DVS>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dv),
                         "hipFuncSetAttribute(attn_bwd_dv_kernel)"));
     attr = true;
@@ -931,9 +954,11 @@ mmdit_status launch_attn_bwd_mfma(const AttnBwdArgs& a, const mmdit_pack_t* pk, 
   dim3 grid((unsigned)cdiv(pk->max_joint, 128), heads, pk->B);
   MMDIT_LAUNCH(attn_bwd_dq_kernel<D>, grid, dim3(256), lds_dq, s, a, kt);
   MMDIT_TRY(launch_check("attn_bwd_dq_kernel", s));
-  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, true>), grid, dim3(256), lds_dk, s, a, qt, gt);
+  dim3 gk((unsigned)cdiv(pk->max_joint, 128 * DKS), heads, pk->B);
+  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, true, DKS>), gk, dim3(256), lds_dk, s, a, qt, gt);
   MMDIT_TRY(launch_check("attn_bwd_dk_kernel", s));
-  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, false>), grid, dim3(256), lds_dv, s, a, qt, gt);
+  dim3 gv((unsigned)cdiv(pk->max_joint, 128 * DVS), heads, pk->B);
+  MMDIT_LAUNCH((attn_bwd_dkdv_kernel<D, false, DVS>), gv, dim3(256), lds_dv, s, a, qt, gt);
   return launch_check("attn_bwd_dv_kernel", s);
 }
 
