@@ -829,10 +829,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
       if constexpr (DK) load_lds16((q < Tb ? gtxt : gimg) + ((uint32_t)q * rowg + kswc[i]), gs + blk * 512);
       load_lds16(tsrc + toff[i] + q0, ts + blk * 512);
     }
-    if (tid < BQ) {   // padded positions hold values that the mask never uses
-      lf[tid] = lse_g[q0 + tid];
-      if constexpr (DK) lf[BQ + tid] = ds_g[q0 + tid];
-    }
+    // lse (and D) of the tile's 32 queries by direct loads too: a plain load
+    // into registers would make the LDS store wait for every load in flight,
+    // this stage's tiles included (padded positions hold values the mask
+    // never uses)
+    if (wu == 0 && lane < (DK ? 16 : 8))
+      load_lds16((lane < 8 ? lse_g + q0 + lane * 4 : ds_g + q0 + (lane - 8) * 4), lf);
   };
 
   f32x16 acc[KS][DT];
