@@ -166,3 +166,47 @@ def test_validation_errors_before_launch(B):
     arr = (B._Sample * 300)(*[B._Sample(1, 1, 1, 0)] * 300)
     assert lib.mmdit_pack(arr, 300, ctypes.byref(B._PackT()), None) == -1
     assert lib.mmdit_workspace_size(ctypes.byref(_dims(B, head_dim=96, heads=32)), P) == 0
+
+
+def test_training_calls_validate_before_launch(B):
+    lib = B._lib
+    pk = _fake_pack(B, [(16, 16, 1, 128), (8, 8, 2, 3)])
+    P = ctypes.byref(pk)
+    ok = ctypes.byref(_dims(B))
+    fake = ctypes.c_void_p(1 << 20)
+    w = B._BlockW(B._StreamW(*([1 << 20] * 7)), B._StreamW(*([1 << 20] * 7)))
+    g = B._BlockG(B._StreamG(*([1 << 20] * 7)), B._StreamG(*([1 << 20] * 7)))
+    need_ws = lib.mmdit_workspace_size(ok, P)
+    saved = lib.mmdit_block_saved_size(ok, P)
+    bws = lib.mmdit_block_bwd_workspace_size(ok, P)
+    assert saved > 0 and bws > 0 and lib.mmdit_wrap_bwd_workspace_size(ok, P) > 0
+    assert lib.mmdit_cond_bwd_workspace_size(ok, 2) > 0
+    # per row: block input, both modulated norms, q/k/v after their norm and q/k before it, o, both branch
+    # outputs, the residual after attention and the MLP pre-activation (mlp = 4H): 16 H bf16 values
+    assert saved >= (pk.n_img + pk.n_txt) * 16 * 3072 * 2
+    # saved buffer and backward workspace one byte short
+    assert lib.mmdit_block_fwd_train(ok, ctypes.byref(w), P, fake, fake, fake, fake, saved - 1, fake, need_ws,
+                                     None) == -4
+    assert b"saved" in lib.mmdit_last_error()
+    assert lib.mmdit_block_bwd(ok, ctypes.byref(w), P, fake, fake, saved, fake, fake, ctypes.byref(g), fake, fake,
+                               bws - 1, None) == -4
+    # a NULL gradient pointer, a NULL gradient struct, a misaligned dc
+    g2 = B._BlockG(B._StreamG(*([1 << 20] * 7)), B._StreamG(*([1 << 20] * 6 + [0])))
+    assert lib.mmdit_block_bwd(ok, ctypes.byref(w), P, fake, fake, saved, fake, fake, ctypes.byref(g2), fake, fake,
+                               bws, None) == -1
+    assert lib.mmdit_block_bwd(ok, ctypes.byref(w), P, fake, fake, saved, fake, fake, None, fake, fake, bws,
+                               None) == -1
+    assert lib.mmdit_block_bwd(ok, ctypes.byref(w), P, fake, fake, saved, fake, fake, ctypes.byref(g),
+                               ctypes.c_void_p((1 << 20) + 4), fake, bws, None) == -3
+    # wrapper backward: workspace, NULL weight gradient, sample count
+    wr = lib.mmdit_wrap_bwd_workspace_size(ok, P)
+    assert lib.mmdit_final_bwd(ok, fake, fake, P, fake, fake, fake, fake, fake, fake, fake, fake, wr - 1, None) == -4
+    assert lib.mmdit_embed_bwd(ok, P, fake, fake, fake, fake, None, fake, fake, wr, None) == -1
+    assert lib.mmdit_cond_bwd(ok, fake, fake, fake, 300, fake, fake, fake, fake, 1 << 30, None) == -1
+    assert lib.rf_loss_grad(P, 1, 12, fake, fake, fake, fake, None) == -3     # C % 8
+
+
+def test_gradient_struct_layout(B):
+    assert ctypes.sizeof(B._BlockG) == 14 * ctypes.sizeof(ctypes.c_void_p)
+    assert B._BlockG.txt.offset == 7 * ctypes.sizeof(ctypes.c_void_p)
+    assert [f for f, _ in B._StreamG._fields_] == ["w_mod", "w_qkv", "g_q", "g_k", "w_o", "w_up", "w_down"]
