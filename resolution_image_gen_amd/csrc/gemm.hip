@@ -361,12 +361,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 // step ends by switching to it.
 template <bool NEXT>
 __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
-                                          const uint32_t (&offb)[8], int kt, bf16* smem, const lds_char* lsm,
+                                          const uint32_t (&offb)[8], int kt, int KT, uint32_t pfa, uint32_t pfb,
+                                          bf16* smem, const lds_char* lsm,
                                           const uint32_t (&aoff)[4], const uint32_t (&boff)[4],
                                           bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4], f32x16 (&acc)[4][4]) {
   constexpr int BM = 256, BK = 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int st = kt & 1;
+  const bool pf = NEXT && kt + 2 < KT;
   // slice kk of stage s into fragment buffer buf (odd row blocks use the
   // offset of slice kk ^ 2: their swizzle differs in bit 2)
   auto read_slice = [&](int s, int kk, int buf) {
@@ -399,6 +401,17 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
           load_lds16(ab + offa[i], smem + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
           load_lds16(bb + offb[i], smem + 2 * BM * BK + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
         }
+        // touch the stage after next (one 4-byte load per 128-byte row
+        // segment, into a scratch strip past the stages) so that its loads
+        // next step find the rows in L2; issued after the stage's loads, so
+        // waiting for those leaves these two in flight
+        if (pf) {
+          bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + 2) * BK) + pfa),
+                                           (lds_ptr_t)junk, 4, 0, 0);
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + 2) * BK) + pfb),
+                                           (lds_ptr_t)junk, 4, 0, 0);
+        }
       }
     }
     read_slice(st, kk + 1, (kk + 1) & 1);
@@ -419,8 +432,11 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   if constexpr (NEXT) {
     // vmcnt(0) lgkmcnt(0): this wave's loads of the next stage have landed
     // and its reads of stage st are done; after the barrier the same holds
-    // for every wave, so stage st's buffer may be refilled next step
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    // for every wave, so stage st's buffer may be refilled next step.  With
+    // the two L2 touches issued last, vmcnt(2) waits for the stage's loads
+    // only (loads complete in issue order).
+    if (pf) __builtin_amdgcn_s_waitcnt(0x0072);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_slice(st ^ 1, 0, 0);
@@ -489,9 +505,13 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
+  // per-lane row of the L2 touches: A rows (wave 64 + lane), B rows likewise
+  const int prow = wave * 64 + lane;
+  const int64_t pm = (m0 + prow < P.M) ? prow : P.M - 1 - m0;
+  const uint32_t pfa = (uint32_t)(pm * P.lda * 2), pfb = (uint32_t)((int64_t)prow * P.K * 2);
   for (int kt = 0; kt < KT - 1; ++kt)
-    pipe_step<true>(atile, btile, offa, offb, kt, smem, lsm, aoff, boff, fa, fb, acc);
-  pipe_step<false>(atile, btile, offa, offb, KT - 1, smem, lsm, aoff, boff, fa, fb, acc);
+    pipe_step<true>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+  pipe_step<false>(atile, btile, offa, offb, KT - 1, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
   __syncthreads();
 }
 
@@ -696,7 +716,9 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
     tiles += (int)(cdiv(bt.p[i].M, BM) * bt.p[i].tiles_n);
   }
   if (tiles == 0) return MMDIT_OK;
-  const size_t lds = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
+  // the 4-wave pipelined 256x256 tile also keeps a 1 KB strip for its L2 touches
+  constexpr bool pipe = BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2;
+  const size_t lds = (size_t)NS * (BM + BN) * BK * sizeof(bf16) + (pipe ? 1024 : 0);
   auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -781,7 +803,7 @@ mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   if (S == 1) S = 2;
   bt.tail_begin = rounds * nb;
   bt.tail_chunks = S;
-  const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16);
+  const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16) + (WN == 2 ? 1024 : 0);
   auto kern = gemm_mfma_kernel<256, 256, 2, WN, EPI, false, SITE>;
   static bool attr_set = false;
   if (!attr_set) {
