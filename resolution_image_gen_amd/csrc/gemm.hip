@@ -359,6 +359,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 // issue between the MFMAs of slice 0 (into the buffer the previous step
 // finished, which every wave left behind at the previous barrier) and the
 // step ends by switching to it.
+// stages ahead of the one being computed whose rows the mainloop touches in L2
+// (measured: 3 is no better than 2)
+constexpr int PFD = 2;
+
 template <bool NEXT>
 __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
                                           const uint32_t (&offb)[8], int kt, int KT, uint32_t pfa, uint32_t pfb,
@@ -368,7 +372,7 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   constexpr int BM = 256, BK = 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int st = kt & 1;
-  const bool pf = NEXT && kt + 2 < KT;
+  const bool pf = NEXT && kt + PFD < KT;
   // slice kk of stage s into fragment buffer buf (odd row blocks use the
   // offset of slice kk ^ 2: their swizzle differs in bit 2)
   auto read_slice = [&](int s, int kk, int buf) {
@@ -401,15 +405,15 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
           load_lds16(ab + offa[i], smem + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
           load_lds16(bb + offb[i], smem + 2 * BM * BK + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
         }
-        // touch the stage after next (one 4-byte load per 128-byte row
-        // segment, into a scratch strip past the stages) so that its loads
-        // next step find the rows in L2; issued after the stage's loads, so
-        // waiting for those leaves these two in flight
+        // touch stage kt + PFD (one 4-byte load per 128-byte row segment, into
+        // a scratch strip past the stages) so that its loads find the rows in
+        // L2; issued after the stage's loads, so waiting for those leaves
+        // these two in flight
         if (pf) {
           bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + 2) * BK) + pfa),
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + PFD) * BK) + pfa),
                                            (lds_ptr_t)junk, 4, 0, 0);
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + 2) * BK) + pfb),
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + PFD) * BK) + pfb),
                                            (lds_ptr_t)junk, 4, 0, 0);
         }
       }
@@ -496,8 +500,21 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
       load_lds16(bb + offb[i], smem + 2 * BM * BK + s2 * BM * BK + (wave + i * 4) * 512);
     }
   };
+  // per-lane row of the L2 touches: A rows (wave 64 + lane), B rows likewise
+  const int prow = wave * 64 + lane;
+  const int64_t pm = (m0 + prow < P.M) ? prow : P.M - 1 - m0;
+  const uint32_t pfa = (uint32_t)(pm * P.lda * 2), pfb = (uint32_t)((int64_t)prow * P.K * 2);
   issue(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (KT > 1) {   // stage 1 touched in L2 while stage 0 lands (stage 2 on is touched by the mainloop)
+    bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + BK) + pfa), (lds_ptr_t)junk,
+                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + BK) + pfb), (lds_ptr_t)junk,
+                                     4, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2): stage 0 landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -505,10 +522,6 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
-  // per-lane row of the L2 touches: A rows (wave 64 + lane), B rows likewise
-  const int prow = wave * 64 + lane;
-  const int64_t pm = (m0 + prow < P.M) ? prow : P.M - 1 - m0;
-  const uint32_t pfa = (uint32_t)(pm * P.lda * 2), pfb = (uint32_t)((int64_t)prow * P.K * 2);
   for (int kt = 0; kt < KT - 1; ++kt)
     pipe_step<true>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
   pipe_step<false>(atile, btile, offa, offb, KT - 1, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
