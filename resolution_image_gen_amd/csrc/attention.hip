@@ -35,7 +35,25 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
   float* lse;        // optional [heads][njp] float32: log2 of each query's softmax denominator
   int32_t njp;       // padded joint length of the lse rows (samples start at multiples of 64)
+  int32_t nq;        // 128-query blocks per (sample, head) of the MFMA forward grid
+  int32_t nB;        // samples
 };
+
+// The MFMA forward's 1-D grid is numbered so that each XCD (workgroups go to
+// the 8 XCDs round-robin by id) takes a contiguous range of (query block,
+// head, sample) items, query blocks fastest: the blocks sharing a head's K
+// and V run on one XCD and share its L2.  False for the padding ids.
+__device__ __forceinline__ bool attn_item(const AttnArgs& a, int& qb, int& head, int& b) {
+  const int total = a.nq * a.heads * a.nB;
+  const int per = (total + 7) / 8;
+  const int id = blockIdx.x;
+  const int item = (id & 7) * per + (id >> 3);
+  if (item >= total) return false;
+  qb = item % a.nq;
+  head = (item / a.nq) % a.heads;
+  b = item / (a.nq * a.heads);
+  return true;
+}
 
 template <typename T>
 __device__ __forceinline__ const T* joint_row(const AttnArgs& a, int32_t j, int32_t Tb, int32_t t0,
@@ -195,11 +213,12 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
   constexpr int STAGE = 2 * BKV * D;     // bf16 elements per stage (K then V^T)
   extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
 
-  const int b = blockIdx.z, head = blockIdx.y;
+  int qb, head, b;
+  if (!attn_item(a, qb, head, b)) return;
   const int32_t t0 = a.cu_txt[b], i0 = a.cu_img[b];
   const int32_t Tb = a.cu_txt[b + 1] - t0;
   const int32_t L = Tb + a.cu_img[b + 1] - i0;
-  const int32_t qbase = blockIdx.x * 128;
+  const int32_t qbase = qb * 128;
   if (qbase >= L) return;
   const int32_t pstart = padded_start(a, b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -990,6 +1009,7 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
                             void* ws, size_t ws_bytes, hipStream_t s, float* lse) {
   if (pk->B == 0 || pk->max_joint == 0) return MMDIT_OK;
   AttnArgs a;
+  memset(&a, 0, sizeof(a));
   a.lse = lse;
   a.njp = (int32_t)(attention_vt_elems(pk, heads * D) / (heads * D));
   a.qkv_img = qkv_img;
@@ -1019,7 +1039,9 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
     else
       MMDIT_LAUNCH(v_transpose_kernel<64>, tgrid, dim3(256), 0, s, a, vt, njp);
     MMDIT_TRY(launch_check("v_transpose_kernel", s));
-    dim3 grid((unsigned)cdiv(pk->max_joint, 128), heads, pk->B);
+    a.nq = (int32_t)cdiv(pk->max_joint, 128);
+    a.nB = pk->B;
+    dim3 grid((unsigned)(8 * cdiv((int64_t)a.nq * heads * pk->B, 8)));
     const size_t lds = 2 * 2 * 64 * D * sizeof(bf16);
     static bool attr[2] = {false, false};
     if (D == 128) {
