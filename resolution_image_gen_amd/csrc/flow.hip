@@ -95,34 +95,29 @@ __global__ void loss_grad_kernel(int64_t n_tgt, int32_t C, int32_t B, const T* _
   }
 }
 
-// One block of 16 waves.  Per sample, in order: thread t sums rows
-// r0 + t, r0 + t + 1024, ...; each wave reduces its lanes; the 16 wave sums
-// are added in wave order.  Then one thread forms the mean loss over the
-// samples in order.  The summation order depends only on the sample's rows,
-// so the result is deterministic and independent of the other samples.
+// One block of 16 waves.  Wave w takes samples w, w + 16, ...: its lanes sum
+// the sample's rows r0 + lane, r0 + lane + 64, ... and the wave reduces them
+// (a fixed order that depends only on the sample's rows, so the result is
+// deterministic and independent of the other samples).  Then one thread
+// forms the mean loss over the samples in order.
 __global__ void __launch_bounds__(1024) loss_finalize_kernel(int32_t B, int32_t C,
                                                              const int32_t* __restrict__ cu_tgt,
                                                              const float* __restrict__ row_sse,
                                                              float* __restrict__ sse,
                                                              float* __restrict__ loss) {
   __shared__ float sh[MMDIT_MAX_SAMPLES];
-  __shared__ float part[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int b = 0; b < B; ++b) {
+  for (int b = wave; b < B; b += 16) {
     const int32_t r0 = cu_tgt[b], r1 = cu_tgt[b + 1];
     float acc = 0.f;
-    for (int32_t r = r0 + (int32_t)threadIdx.x; r < r1; r += 1024) acc += row_sse[r];
+    for (int32_t r = r0 + lane; r < r1; r += 64) acc += row_sse[r];
     acc = wave_sum(acc);
-    if (lane == 0) part[wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = 0.f;
-      for (int w = 0; w < 16; ++w) t += part[w];
-      sse[b] = t;
-      sh[b] = t;
+    if (lane == 0) {
+      sse[b] = acc;
+      sh[b] = acc;
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (threadIdx.x == 0) {
     float total = 0.f;
     for (int b = 0; b < B; ++b)
