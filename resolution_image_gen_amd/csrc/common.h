@@ -87,14 +87,17 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// x sigmoid(x) with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
+// IEEE division (a ten-instruction sequence); 1 + exp(-x) >= 1 is never denormal.
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
 // t = 1 / (1 + p x), for x >= 0 (odd for x < 0); absolute error <= 1.5e-7.
-// About a dozen instructions, against the several-branch library erff.
+// About a dozen instructions, against the several-branch library erff; t
+// takes the hardware reciprocal (1 ulp; its argument is >= 1).
 __device__ __forceinline__ float erf_as(float x) {
   const float ax = fabsf(x);
-  const float t = __frcp_rn(1.0f + 0.3275911f * ax);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
   const float poly =
       t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
   return copysignf(1.0f - poly * __expf(-ax * ax), x);

@@ -347,23 +347,23 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
 // explicitly pipelined schedule.  Per BK=64 step a wave issues 64 MFMAs in
 // four k-slices of 16; the fragments of slice kk+1 are read from LDS while
 // the MFMAs of slice kk issue, each slice starting with MFMAs so its reads
-// have a whole slice to land.  The next stage's 16 direct-to-LDS loads issue
-// between the first slice's MFMAs; the stage switch (own loads landed, then a
-// barrier) sits after the first quarter of the last slice, so the next
-// stage's first fragments are read while the rest of that slice issues.
+// have a whole slice to land.  The stage switch (own loads landed, then a
+// barrier) sits after the first quarter of the last slice; right after it the
+// next stage's first fragments are read and the 16 direct-to-LDS loads of the
+// stage after next issue (into the buffer just finished), between the rest of
+// that slice's MFMAs, so the loads have a whole step to land.
 // The order of the MFMAs on each accumulator is the same as mma_tile's.
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// One BK=64 step of mma_tile_pipe.  NEXT: a next stage exists: its loads
-// issue between the MFMAs of slice 0 (into the buffer the previous step
-// finished, which every wave left behind at the previous barrier) and the
-// step ends by switching to it.
-// stages ahead of the one being computed whose rows the mainloop touches in L2
-// (measured: 3 is no better than 2)
-constexpr int PFD = 2;
-
-template <bool NEXT>
+// One BK=64 step of mma_tile_pipe.  NEXT: a next stage exists and the step
+// ends by switching to it.  LOAD2: stage kt + 2 exists; its loads issue right
+// after that switch's barrier, into the buffer of stage kt, which every wave
+// has finished reading by then (a whole step of MFMAs for them to land), and
+// are followed by two 4-byte direct loads that touch every 128-byte row
+// segment of stage kt + 3 (into a scratch strip past the stages) so that its
+// loads find the rows in L2.
+template <bool NEXT, bool LOAD2>
 __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
                                           const uint32_t (&offb)[8], int kt, int KT, uint32_t pfa, uint32_t pfb,
                                           bf16* smem, const lds_char* lsm,
@@ -372,9 +372,6 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   constexpr int BM = 256, BK = 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int st = kt & 1;
-  const bool pf = NEXT && kt + PFD < KT;
-  // slice kk of stage s into fragment buffer buf (odd row blocks use the
-  // offset of slice kk ^ 2: their swizzle differs in bit 2)
   auto read_slice = [&](int s, int kk, int buf) {
     const uint32_t so = s * BM * BK * 2;
 #pragma unroll
@@ -396,54 +393,48 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   // into the other; each slice starts with MFMAs
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    if constexpr (NEXT) {
-      if (kk == 0) {
-        const char* ab = reinterpret_cast<const char*>(atile + (kt + 1) * BK);
-        const char* bb = reinterpret_cast<const char*>(btile + (kt + 1) * BK);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          load_lds16(ab + offa[i], smem + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
-          load_lds16(bb + offb[i], smem + 2 * BM * BK + (st ^ 1) * BM * BK + (wave + i * 4) * 512);
-        }
-        // touch stage kt + PFD (one 4-byte load per 128-byte row segment, into
-        // a scratch strip past the stages) so that its loads find the rows in
-        // L2; issued after the stage's loads, so waiting for those leaves
-        // these two in flight
-        if (pf) {
-          bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + PFD) * BK) + pfa),
-                                           (lds_ptr_t)junk, 4, 0, 0);
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + PFD) * BK) + pfb),
-                                           (lds_ptr_t)junk, 4, 0, 0);
-        }
-      }
-    }
     read_slice(st, kk + 1, (kk + 1) & 1);
     mma_rows(kk & 1, 0, 4);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      if (NEXT && kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // slice 3: a quarter of its MFMAs, the stage switch, then the next stage's
-  // slice 0 while the rest issue
+  // slice 0 and the loads of stage kt + 2 while the rest issue
   mma_rows(1, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NEXT) {
-    // vmcnt(0) lgkmcnt(0): this wave's loads of the next stage have landed
-    // and its reads of stage st are done; after the barrier the same holds
-    // for every wave, so stage st's buffer may be refilled next step.  With
-    // the two L2 touches issued last, vmcnt(2) waits for the stage's loads
-    // only (loads complete in issue order).
-    if (pf) __builtin_amdgcn_s_waitcnt(0x0072);
+    // vmcnt(0) lgkmcnt(0): this wave's loads of stage kt + 1 have landed and
+    // its reads of stage kt are done; after the barrier the same holds for
+    // every wave.  The touch of stage kt + 2 was issued after those loads
+    // (when stage kt + 2 exists, i.e. LOAD2), and loads complete in issue
+    // order, so vmcnt(2) waits for the stage's loads only.
+    if constexpr (LOAD2) __builtin_amdgcn_s_waitcnt(0x0072);
     else __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_slice(st ^ 1, 0, 0);
+    if constexpr (LOAD2) {
+      // stage kt + 2 into the buffer every wave has just finished (stage kt)
+      const char* ab = reinterpret_cast<const char*>(atile + (kt + 2) * BK);
+      const char* bb = reinterpret_cast<const char*>(btile + (kt + 2) * BK);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        load_lds16(ab + offa[i], smem + st * BM * BK + (wave + i * 4) * 512);
+        load_lds16(bb + offb[i], smem + 2 * BM * BK + st * BM * BK + (wave + i * 4) * 512);
+      }
+      if (kt + 3 < KT) {
+        bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + 3) * BK) + pfa),
+                                         (lds_ptr_t)junk, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + 3) * BK) + pfb),
+                                         (lds_ptr_t)junk, 4, 0, 0);
+      }
+    }
   }
   mma_rows(1, 1, 4);
   if constexpr (NEXT) {
@@ -451,6 +442,7 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
     for (int t = 0; t < 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (LOAD2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
@@ -504,14 +496,19 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
   const int prow = wave * 64 + lane;
   const int64_t pm = (m0 + prow < P.M) ? prow : P.M - 1 - m0;
   const uint32_t pfa = (uint32_t)(pm * P.lda * 2), pfb = (uint32_t)((int64_t)prow * P.K * 2);
+  // stages 0 and 1, then the touch of stage 2 (stage 3 on is touched by the
+  // mainloop)
   issue(0);
-  if (KT > 1) {   // stage 1 touched in L2 while stage 0 lands (stage 2 on is touched by the mainloop)
+  if (KT > 1) issue(1);
+  if (KT > 2) {
     bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + BK) + pfa), (lds_ptr_t)junk,
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + 2 * BK) + pfa), (lds_ptr_t)junk,
                                      4, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + BK) + pfb), (lds_ptr_t)junk,
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + 2 * BK) + pfb), (lds_ptr_t)junk,
                                      4, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2): stage 0 landed
+    __builtin_amdgcn_s_waitcnt(0x4F72);   // vmcnt(18): stage 0 landed
+  } else if (KT == 2) {
+    __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
@@ -522,9 +519,14 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
-  for (int kt = 0; kt < KT - 1; ++kt)
-    pipe_step<true>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
-  pipe_step<false>(atile, btile, offa, offb, KT - 1, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt)
+    pipe_step<true, true>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+  if (KT >= 2) {
+    pipe_step<true, false>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+    ++kt;
+  }
+  pipe_step<false, false>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
   __syncthreads();
 }
 
@@ -565,6 +567,15 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
   float* T = reinterpret_cast<float*>(smem);   // [128][256]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g = lane >> 5;
+  // the problem's fields in registers once (the compiler would otherwise
+  // reload them after every store, which it cannot prove does not alias them)
+  void* const Yp = P.Y;
+  void* const auxp = P.aux;
+  const float* const gatep = P.gate;
+  const int32_t* const segp = P.seg;
+  const int64_t ldy = P.ldy, M = P.M, gs = P.gate_stride;
+  const int N = P.N;
+  const int ch = tid & 31, r0 = tid >> 5, n = n0 + ch * 8;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
@@ -580,20 +591,20 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
           }
     }
     __syncthreads();
-    for (int e = tid; e < 128 * 32; e += 256) {
-      const int r = e >> 5, ch = e & 31;
-      const int64_t m = m0 + half * 128 + r;
-      if (m >= P.M) continue;
-      const int n = n0 + ch * 8;
+    // thread tid takes columns n..n+7 of rows r0, r0 + 8, ..., r0 + 120
+    const int64_t mb = m0 + half * 128 + r0;
+    auto chunk = [&](int i) {
+      const int64_t m = mb + 8 * i;
+      const float* t = T + (r0 + 8 * i) * 256 + ch * 8;
       float a[8];
-      *reinterpret_cast<f32x4*>(a) = *reinterpret_cast<const f32x4*>(T + r * 256 + ch * 8);
-      *reinterpret_cast<f32x4*>(a + 4) = *reinterpret_cast<const f32x4*>(T + r * 256 + ch * 8 + 4);
+      *reinterpret_cast<f32x4*>(a) = *reinterpret_cast<const f32x4*>(t);
+      *reinterpret_cast<f32x4*>(a + 4) = *reinterpret_cast<const f32x4*>(t + 4);
       if constexpr (EPI == MMDIT_EPI_STORE_F32) {
-        float* y = static_cast<float*>(P.Y) + m * P.ldy + n;
+        float* y = static_cast<float*>(Yp) + m * ldy + n;
         *reinterpret_cast<f32x4*>(y) = *reinterpret_cast<const f32x4*>(a);
         *reinterpret_cast<f32x4*>(y + 4) = *reinterpret_cast<const f32x4*>(a + 4);
       } else {
-        bf16* y = static_cast<bf16*>(P.Y) + m * P.ldy + n;
+        bf16* y = static_cast<bf16*>(Yp) + m * ldy + n;
         float o[8];
         if constexpr (EPI == MMDIT_EPI_STORE) {
 #pragma unroll
@@ -601,22 +612,28 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
         } else if constexpr (EPI == MMDIT_EPI_GELU || EPI == kEpiGeluAux) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = gelu_f(a[k]);
-          if constexpr (EPI == kEpiGeluAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
+          if constexpr (EPI == kEpiGeluAux) Vec8<bf16>::store(static_cast<bf16*>(auxp) + m * N + n, a);
         } else if constexpr (EPI == kEpiGeluBwd) {
           float xv[8];
-          Vec8<bf16>::load(static_cast<const bf16*>(P.aux) + m * P.N + n, xv);
+          Vec8<bf16>::load(static_cast<const bf16*>(auxp) + m * N + n, xv);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = a[k] * gelu_grad_f(xv[k]);
         } else {
           float xv[8], gv[8];
           Vec8<bf16>::load(y, xv);
-          Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + n, gv);
+          Vec8<float>::load(gatep + (int64_t)segp[m] * gs + n, gv);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
-          if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
+          if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(auxp) + m * N + n, a);
         }
         Vec8<bf16>::store(y, o);
       }
+    };
+    if (mb + 120 < M) {   // all 16 rows of this thread exist
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) chunk(i);
+    } else {
+      for (int i = 0; i < 16 && mb + 8 * i < M; ++i) chunk(i);
     }
   }
 }
