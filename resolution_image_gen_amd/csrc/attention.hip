@@ -285,18 +285,39 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
     if (it + 1 < ntile) issue(kv0 + BKV, st ^ 1);
     const bf16* ks = smem + st * STAGE;
     const bf16* vs = ks + BKV * D;
+    // S^T for the two 32-key halves, their k steps interleaved (independent
+    // accumulators back to back) and the K fragments read two steps ahead
     f32x16 sc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
-      const int r = kt * 32 + prow;
+    const int r0 = prow, r1 = 32 + prow;
+    auto kfrag = [&](int r, int s) {
+      return *reinterpret_cast<const bf16x8*>(ks + r * D + (((s * 2 + g) ^ ksw<D>(r)) << 3));
+    };
+    bf16x8 kf[3][2];
+    __builtin_amdgcn_sched_barrier(0);
+    kf[0][0] = kfrag(r0, 0);
+    kf[0][1] = kfrag(r1, 0);
+    kf[1][0] = kfrag(r0, 1);
+    kf[1][1] = kfrag(r1, 1);
 #pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + r * D + (((s * 2 + g) ^ ksw<D>(r)) << 3));
-        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kt], 0, 0, 0);
+    for (int s = 0; s < QS; ++s) {
+      if (s + 2 < QS) {
+        kf[(s + 2) % 3][0] = kfrag(r0, s + 2);
+        kf[(s + 2) % 3][1] = kfrag(r1, s + 2);
       }
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3][0], qf[s], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3][1], qf[s], sc[1], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read: steps 0, 1
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      if (s + 2 < QS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // register v of tile kt holds key kv0 + 32 kt + 16 (v / 8) + 8 g + v % 8;
     // only the last tile of a sample has keys past its end to mask
     float mx = -INFINITY;
@@ -320,16 +341,10 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
     const float mn = fmaxf(m, mx * a.scale_log2);
     const float corr = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
-    float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], a.scale_log2, -mn));
-        sc[kt][v] = p;
-        ps += p;
-      }
-    lsum = lsum * corr + ps;
+      for (int v = 0; v < 16; ++v) sc[kt][v] = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], a.scale_log2, -mn));
     if (__any(corr != 1.0f)) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
@@ -337,12 +352,20 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
         for (int v = 0; v < 16; ++v) oacc[t][v] *= corr;
     }
     // O^T[d][query] += V^T[d][keys] P^T[keys][query]; step ks covers keys
-    // 16 ks .. 16 ks + 15, this lane's 8 of them being 16 ks + 8 g + 0..7
+    // 16 ks .. 16 ks + 15, this lane's 8 of them being 16 ks + 8 g + 0..7.
+    // The row sum takes the same bf16-rounded P as the product, two at a
+    // time (v_dot2 against (1, 1)), so the normaliser matches the weights.
+    float ps = 0.f;
+    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2) {
       bf16x8 pf;
 #pragma unroll
       for (int u = 0; u < 8; ++u) pf[u] = (bf16)sc[ks2 >> 1][8 * (ks2 & 1) + u];
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, ps, false);
       const int c = 2 * ks2 + g;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
@@ -351,6 +374,7 @@ __global__ void __launch_bounds__(256, 2) attn_mfma_kernel(AttnArgs a, const bf1
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
       }
     }
+    lsum = lsum * corr + ps;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
