@@ -242,6 +242,67 @@ def bench_sampler(steps, warmup):
                      "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3)}}
 
 
+def bench_rf_kernels(reps=20):
+    """Kernel-duration bandwidth of the rectified-flow kernels (noising, loss,
+    CFG combine + Euler) at their own pack shapes, where they are launch-bound,
+    and at a 64 M-element shape, where they reach steady state.  Bytes are
+    algorithmic: noising reads z and eps and writes z_t (3 x 2 B per element);
+    the loss reads v, z and eps of every target element (3 x 2 B); the Euler
+    step reads v_c, v_u (2 x 2 B) and the float32 z, writes z and the next
+    bf16 input of both CFG samples (4 + 4 + 2 x 2 B)."""
+    import torch
+
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import configs as CF
+
+    C = CF.B4.c_lat
+    gen = torch.Generator(device="cuda").manual_seed(0)
+
+    def rnd(*shape, dtype=torch.bfloat16):
+        return torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32).to(dtype)
+
+    def timed(fn, tags):
+        fn()
+        B.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        rep = B.timing_report()
+        B.timing_enable(False)
+        return sum(rep[t][0] for t in tags if t in rep) / reps * 1e3   # us per call
+
+    res = {}
+    noise_shapes = {"256^2 pack": CF.WORKLOADS["pack256_bf16"].samples,
+                    "1024^2 pack": CF.WORKLOADS["native1024_bf16"].samples,
+                    "64M elements": [(128, 128, 1, 0)] * 32}
+    for name, samples in noise_shapes.items():
+        pk = B.pack(list(samples))
+        n, nt = pk.n_img, pk.n_tgt
+        z, eps, zt, v = rnd(n, C), rnd(n, C), torch.empty(n, C, dtype=torch.bfloat16, device="cuda"), rnd(nt, C)
+        t = torch.rand(pk.B, generator=gen, device="cuda")
+        sse = torch.empty(pk.B, dtype=torch.float32, device="cuda")
+        loss = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws = torch.empty(nt * 4 + 4, dtype=torch.uint8, device="cuda")
+        us = timed(lambda: B.rf_make_xt(pk, z, eps, t, zt), ["make_xt_kernel"])
+        res[f"noise {name}"] = {"elements": n * C, "us": round(us, 2), "GB/s": round(6.0 * n * C / us / 1e3, 1)}
+        us = timed(lambda: B.rf_loss(pk, v, z, eps, sse, loss, ws), ["row_sse_kernel", "loss_finalize_kernel"])
+        res[f"loss {name}"] = {"elements": nt * C, "us": round(us, 2), "GB/s": round(6.0 * nt * C / us / 1e3, 1)}
+        del z, eps, zt, v
+    euler_shapes = {"1024^2 CFG pack": [(64, 64, 1, 256)] * 2, "64M elements": [(512, 1024, 1, 0)] * 2}
+    for name, samples in euler_shapes.items():
+        pk = B.pack(list(samples))
+        per = pk.n_tgt // 2
+        v = rnd(pk.n_tgt, C)
+        z = rnd(per, C, dtype=torch.float32)
+        zt = torch.empty(pk.n_img, C, dtype=torch.bfloat16, device="cuda")
+        us = timed(lambda: B.rf_euler_step(pk, v, 0, 1, 4.0, 0.75, 0.5, z, zt), ["euler_kernel"])
+        res[f"cfg+euler {name}"] = {"elements": per * C, "us": round(us, 2),
+                                    "GB/s": round(16.0 * per * C / us / 1e3, 1)}
+        del v, z, zt
+    for r in res.values():
+        r["frac_hbm"] = round(r["GB/s"] / PEAK_HBM_GBS, 3)
+    return res
+
+
 def train_step_flops(wl, depth):
     """Algorithmic FLOPs of one training step: per block the forward
     (24 H^2 N + 4 H sum L_b^2) and the backward (twice the linears, 2.5 times
@@ -454,6 +515,7 @@ def main():
         "roofline": roof,
         "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
     }
+    out["rf_kernels"] = bench_rf_kernels()
     if args.sampler_packs > 0 or args.train_steps > 0:
         del tf, W
         torch.cuda.empty_cache()

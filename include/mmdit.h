@@ -355,7 +355,8 @@ mmdit_status rf_make_xt(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, 
 /* Flow-matching loss ([hyper] 方法 objective; [blog] 2.2(2), target latent
  * only): sse[b] = sum over sample b's target rows of (v - (z - eps))^2 and
  * loss[0] = mean_b sse[b] / (tgt_len_b * C), float32.  v [n_tgt, C]; z, eps
- * [n_img, C].  Deterministic fixed-order reduction; ws >= n_tgt*4 bytes. */
+ * [n_img, C].  Deterministic fixed-order reduction; ws (16-byte aligned) >=
+ * n_tgt*4 + 4 bytes (per-row sums; never empty). */
 mmdit_status rf_loss(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* v,
                      const void* z, const void* eps, float* sse, float* loss, void* ws,
                      size_t ws_bytes, mmdit_stream stream);

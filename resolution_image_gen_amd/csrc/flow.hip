@@ -109,8 +109,29 @@ __global__ void __launch_bounds__(1024) loss_finalize_kernel(int32_t B, int32_t 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int b = wave; b < B; b += 16) {
     const int32_t r0 = cu_tgt[b], r1 = cu_tgt[b + 1];
-    float acc = 0.f;
-    for (int32_t r = r0 + lane; r < r1; r += 64) acc += row_sse[r];
+    // the 16-byte-aligned middle of the sample's rows as float4, lane-strided,
+    // eight loads in flight per lane (eight accumulators, summed in a fixed
+    // tree); the up to 3 + 3 rows outside it go to lanes 0..5
+    const int32_t a0 = min((r0 + 3) & ~3, r1), a1 = max(r1 & ~3, a0);
+    const f32x4* mid = reinterpret_cast<const f32x4*>(row_sse + a0);
+    const int32_t nv = (a1 - a0) >> 2;
+    f32x4 s8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s8[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int32_t j = lane;
+    for (; j + 7 * 64 < nv; j += 8 * 64) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s8[k] += mid[j + k * 64];
+    }
+    for (int k = 0; j < nv; j += 64, ++k) s8[k] += mid[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s8[k] += s8[k + 4];
+    s8[0] += s8[2];
+    s8[1] += s8[3];
+    s8[0] += s8[1];
+    float acc = (s8[0][0] + s8[0][1]) + (s8[0][2] + s8[0][3]);
+    if (lane < 3 && r0 + lane < a0) acc += row_sse[r0 + lane];
+    if (lane >= 3 && lane < 6 && a1 + lane - 3 < r1) acc += row_sse[a1 + lane - 3];
     acc = wave_sum(acc);
     if (lane == 0) {
       sse[b] = acc;
@@ -240,6 +261,10 @@ mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const 
   if (!ws || ws_bytes < (size_t)pk->n_tgt * 4 + 4) {
     set_error("rf_loss: workspace needs %zu bytes, got %zu", (size_t)pk->n_tgt * 4 + 4, ws_bytes);
     return MMDIT_E_WORKSPACE;
+  }
+  if (((uintptr_t)ws & 15) != 0) {
+    set_error("rf_loss: workspace is not 16-byte aligned");
+    return MMDIT_E_UNSUPPORTED;
   }
   float* row_sse = static_cast<float*>(ws);
   if (pk->n_tgt > 0) {

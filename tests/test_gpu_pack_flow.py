@@ -18,6 +18,8 @@ SAMPLE_SETS = {
     "no_text": [(7, 9, 1, 0)],
     "many": [(1 + i % 3, 2 + i % 5, 1 + i % 2, i % 4) for i in range(70)],
     "max_samples": [(1 + i % 4, 1 + i % 3, 1 + i % 2, i % 6) for i in range(256)],
+    # long samples whose target rows start and end off 4-row boundaries
+    "long_ragged": [(3, 5, 1, 0), (127, 129, 1, 0), (1, 7, 2, 3), (64, 65, 1, 0)],
 }
 
 
@@ -116,7 +118,7 @@ def test_make_xt(B, dtype, name):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many"])
+@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged"])
 def test_rf_loss(B, dtype, name):
     samples = SAMPLE_SETS[name]
     C = 64

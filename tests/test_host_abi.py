@@ -158,6 +158,10 @@ def test_validation_errors_before_launch(B):
     assert lib.rf_euler_step(P, 1, 128, fake, 0, 1, ctypes.c_float(4.0), ctypes.c_float(1.0),
                              ctypes.c_float(0.75), fake, None, None) == -1    # different target sizes
     assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, fake, 16, None) == -4
+    # the documented minimum, n_tgt * 4 + 4 bytes, minus one
+    n_tgt = 16 * 16 + 8 * 8
+    assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, fake, n_tgt * 4 + 3, None) == -4
+    assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, ctypes.c_void_p((1 << 20) + 4), 1 << 20, None) == -3
     assert lib.rf_make_xt(P, 1, 12, fake, fake, fake, fake, None) == -3        # C % 8
     # linear shape errors
     assert lib.mmdit_linear(1, -1, 64, 64, fake, fake, fake, 0, None, 0, None, 0, None) == -1
