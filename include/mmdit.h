@@ -206,6 +206,21 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* dims, const mmdit_block_w* w,
                              const mmdit_pack_t* pack, const void* c, void* x_img, void* x_txt,
                              void* ws, size_t ws_bytes, mmdit_stream stream);
 
+/* The block's adaLN vectors alone ([blog] 5 "MMDiT": the conditioning only
+ * enters through them): mod float32 [2][B][6H], mod[0] the image stream's
+ * W_mod SiLU(c) and mod[1] the text stream's, one grouped launch.  They depend
+ * on c and the weights only, so a caller may compute them on another stream
+ * while the embeddings run. */
+mmdit_status mmdit_block_modulation(const mmdit_dims* dims, const mmdit_block_w* w, int32_t B,
+                                    const void* c, float* mod, mmdit_stream stream);
+
+/* mmdit_block_fwd with the adaLN vectors from mmdit_block_modulation (mod, as
+ * above, for the pack's B samples, read only) instead of c; the same launches
+ * otherwise, and bit for bit the same result. */
+mmdit_status mmdit_block_fwd_mod(const mmdit_dims* dims, const mmdit_block_w* w,
+                                 const mmdit_pack_t* pack, const float* mod, void* x_img,
+                                 void* x_txt, void* ws, size_t ws_bytes, mmdit_stream stream);
+
 /* ------------------------------------------------------------- training */
 
 /* The block's training forward and its backward.  The pages train the
@@ -343,6 +358,13 @@ mmdit_status mmdit_linear(mmdit_dtype dtype, int64_t M, int32_t N, int32_t K, co
 mmdit_status mmdit_final(const mmdit_dims* dims, const void* w_fmod, const void* w_out,
                          const mmdit_pack_t* pack, const void* c, const void* x_img, void* v,
                          void* ws, size_t ws_bytes, mmdit_stream stream);
+
+/* mmdit_final with its adaLN vectors computed beforehand: modf float32 [B][2H]
+ * = mmdit_modulation(w_fmod, chunks 2, c) (shift, then scale), read only.
+ * Same workspace and bit for bit the same v. */
+mmdit_status mmdit_final_mod(const mmdit_dims* dims, const void* w_out, const mmdit_pack_t* pack,
+                             const float* modf, const void* x_img, void* v, void* ws, size_t ws_bytes,
+                             mmdit_stream stream);
 
 /* ------------------------------------------------------- rectified flow */
 

@@ -91,6 +91,8 @@ def _load():
         "mmdit_modulation": (_i32, [D, _vp, _i32, _i32, _vp, _vp, _vp]),
         "mmdit_embed": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_block_fwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_block_modulation": (_i32, [D, ctypes.POINTER(_BlockW), _i32, _vp, _vp, _vp]),
+        "mmdit_block_fwd_mod": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "mmdit_block_saved_size": (_sz, [D, P]),
         "rf_loss_grad": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_wrap_bwd_workspace_size": (_sz, [D, P]),
@@ -108,6 +110,7 @@ def _load():
         "mmdit_attention_workspace_size": (_sz, [D, P]),
         "mmdit_linear": (_i32, [_i32, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _vp]),
         "mmdit_final": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "mmdit_final_mod": (_i32, [D, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_make_xt": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "rf_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_euler_step": (_i32, [P, _i32, _i32, _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _vp]),
@@ -282,6 +285,20 @@ def block_fwd(dims, wb, pk, c, x_img, x_txt, ws, stream=None):
                              _p(x_txt), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def block_modulation(dims, wb, c, mod, stream=None):
+    """Both streams' adaLN vectors of a block into mod (float32 [2, B, 6H])."""
+    bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
+    _ck(_lib.mmdit_block_modulation(ctypes.byref(dims.c), ctypes.byref(bw), c.shape[0], _p(c), _p(mod),
+                                    _stream(stream)))
+
+
+def block_fwd_mod(dims, wb, pk, mod, x_img, x_txt, ws, stream=None):
+    """block_fwd with the adaLN vectors from block_modulation."""
+    bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
+    _ck(_lib.mmdit_block_fwd_mod(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(mod), _p(x_img),
+                                 _p(x_txt), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def block_saved_size(dims, pk):
     return int(_lib.mmdit_block_saved_size(ctypes.byref(dims.c), pk.ref))
 
@@ -371,6 +388,12 @@ def linear(A, W, Y, epilogue=EPI_STORE, gate=None, gate_stride=0, seg=None, a_si
 def final(dims, w_fmod, w_out, pk, c, x_img, v, ws, stream=None):
     _ck(_lib.mmdit_final(ctypes.byref(dims.c), _p(w_fmod), _p(w_out), pk.ref, _p(c), _p(x_img), _p(v),
                          _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def final_mod(dims, w_out, pk, modf, x_img, v, ws, stream=None):
+    """final with its adaLN vectors from modulation(w_fmod, 2, c)."""
+    _ck(_lib.mmdit_final_mod(ctypes.byref(dims.c), _p(w_out), pk.ref, _p(modf), _p(x_img), _p(v),
+                             _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rf_make_xt(pk, z, eps, t, zt, stream=None):

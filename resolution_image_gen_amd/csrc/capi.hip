@@ -543,11 +543,23 @@ mmdit_status check_block_args(const mmdit_dims* d, const mmdit_block_w* w, const
   return need(ws, who, "ws");
 }
 
+// adaLN vectors of both streams of a block in one grouped launch:
+// mod = W_mod SiLU(c), float32 [B][6H] each.
+mmdit_status block_modulation_impl(const mmdit_dims* d, const mmdit_block_w* w, int32_t B, const void* c,
+                                   float* mod_i, float* mod_t, hipStream_t s) {
+  const int32_t H = d->hidden;
+  LinearArgs a[2] = {mk(B, 6 * H, H, c, w->img.w_mod, mod_i, MMDIT_EPI_STORE_F32),
+                     mk(B, 6 * H, H, c, w->txt.w_mod, mod_t, MMDIT_EPI_STORE_F32)};
+  a[0].a_silu = a[1].a_silu = 1;
+  a[0].tag = "adaln_mod";
+  return linear(d->dtype, a, 2, s);
+}
+
 // The block's launch sequence.  With sv (training) every intermediate the
 // backward needs is kept in sv (layout S); the arithmetic is the same.
 mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
                                 void* x_img, void* x_txt, void* ws, char* sv, const SavedLayout* S,
-                                hipStream_t s) {
+                                hipStream_t s, const float* premod = nullptr) {
   const Layout L = block_layout(d, pk);
   const mmdit_dtype dt = d->dtype;
   const size_t es = esize(dt);
@@ -569,13 +581,13 @@ mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, con
     MMDIT_TRY(copy_rows(sv + S->x_in + ni * H * es, x_txt, nt * H * es, s));
   }
 
-  // adaLN vectors of both streams: mod = W_mod SiLU(c)
-  {
-    LinearArgs a[2] = {mk(pk->B, 6 * H, H, c, w->img.w_mod, mod_i, MMDIT_EPI_STORE_F32),
-                       mk(pk->B, 6 * H, H, c, w->txt.w_mod, mod_t, MMDIT_EPI_STORE_F32)};
-    a[0].a_silu = a[1].a_silu = 1;
-    a[0].tag = "adaln_mod";
-    MMDIT_TRY(linear(dt, a, 2, s));
+  // adaLN vectors of both streams: mod = W_mod SiLU(c), unless the caller
+  // computed them beforehand (mmdit_block_modulation; read only from here on)
+  if (premod) {
+    mod_i = const_cast<float*>(premod);
+    mod_t = const_cast<float*>(premod) + (size_t)pk->B * 6 * H;
+  } else {
+    MMDIT_TRY(block_modulation_impl(d, w, pk->B, c, mod_i, mod_t, s));
   }
   // h = rms(x)(1 + scale1) + shift1   (both streams, one launch)
   {
@@ -673,6 +685,34 @@ mmdit_status mmdit_block_fwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   MMDIT_TRY(check_block_args(d, w, pk, c, x_img, x_txt, ws, ws_bytes, "mmdit_block_fwd"));
   if (pk->B == 0) return MMDIT_OK;
   return block_forward_impl(d, w, pk, c, x_img, x_txt, ws, nullptr, nullptr, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_block_modulation(const mmdit_dims* d, const mmdit_block_w* w, int32_t B, const void* c,
+                                    float* mod, mmdit_stream stream) {
+  const char* who = "mmdit_block_modulation";
+  MMDIT_TRY(check_dims(d, who));
+  if (!w) {
+    set_error("%s: weights are NULL", who);
+    return MMDIT_E_INVALID;
+  }
+  if (B < 0 || B > MMDIT_MAX_SAMPLES) {
+    set_error("%s: B = %d outside [0, %d]", who, B, MMDIT_MAX_SAMPLES);
+    return MMDIT_E_INVALID;
+  }
+  if (B == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w->img.w_mod, who, "img.w_mod"));
+  MMDIT_TRY(need(w->txt.w_mod, who, "txt.w_mod"));
+  MMDIT_TRY(need(c, who, "c"));
+  MMDIT_TRY(need(mod, who, "mod"));
+  return block_modulation_impl(d, w, B, c, mod, mod + (size_t)B * 6 * d->hidden, (hipStream_t)stream);
+}
+
+mmdit_status mmdit_block_fwd_mod(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk,
+                                 const float* mod, void* x_img, void* x_txt, void* ws, size_t ws_bytes,
+                                 mmdit_stream stream) {
+  MMDIT_TRY(check_block_args(d, w, pk, mod, x_img, x_txt, ws, ws_bytes, "mmdit_block_fwd_mod"));
+  if (pk->B == 0) return MMDIT_OK;
+  return block_forward_impl(d, w, pk, nullptr, x_img, x_txt, ws, nullptr, nullptr, (hipStream_t)stream, mod);
 }
 
 size_t mmdit_block_saved_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -1276,31 +1316,14 @@ size_t mmdit_cond_bwd_workspace_size(const mmdit_dims* d, int32_t B) {
   return ov + align256((size_t)B * d->t_dim * es) + align256((size_t)B * d->hidden * es) + (size_t)B * d->hidden * 4;
 }
 
-mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,
-                         const void* c, const void* x_img, void* v, void* ws, size_t ws_bytes, mmdit_stream stream) {
-  const char* who = "mmdit_final";
-  MMDIT_TRY(check_dims(d, who));
-  MMDIT_TRY(check_pack(pk, who));
-  if (pk->n_tgt == 0) return MMDIT_OK;
-  MMDIT_TRY(need(w_fmod, who, "w_fmod"));
-  MMDIT_TRY(need(w_out, who, "w_out"));
-  MMDIT_TRY(need(c, who, "c"));
-  MMDIT_TRY(need(x_img, who, "x_img"));
-  MMDIT_TRY(need(v, who, "v"));
-  const size_t need_b = final_ws(d, pk);
-  if (!ws || ws_bytes < need_b) {
-    set_error("%s: workspace needs %zu bytes, got %zu", who, need_b, ws_bytes);
-    return MMDIT_E_WORKSPACE;
-  }
-  MMDIT_TRY(need(ws, who, "ws"));
-  hipStream_t s = (hipStream_t)stream;
+namespace {
+
+// Final layer after its modulation: h = rms(x)(1 + scale_f) + shift_f on the
+// target rows, v = h W_out^T.  modf float32 [B][2H] (shift, scale).
+mmdit_status final_rest_impl(const mmdit_dims* d, const void* w_out, const mmdit_pack_t* pk, const float* modf,
+                             const void* x_img, void* v, void* ws, hipStream_t s) {
   const int32_t H = d->hidden;
-  float* modf = static_cast<float*>(ws);
   void* hf = static_cast<char*>(ws) + align256((size_t)pk->B * 2 * H * 4);
-  LinearArgs a = mk(pk->B, 2 * H, H, c, w_fmod, modf, MMDIT_EPI_STORE_F32);
-  a.a_silu = 1;
-  a.tag = "final_mod";
-  MMDIT_TRY(linear(d->dtype, &a, 1, s));
   MMDIT_TRY(rms_modulate_impl(d->dtype, pk->n_tgt, H, x_img, pk->tgt_row, pk->seg_img, modf, 2 * H, 0, H, hf,
                               d->eps, s));
   LinearArgs b = mk(pk->n_tgt, d->c_lat, H, hf, w_out, v, MMDIT_EPI_STORE);
@@ -1308,6 +1331,54 @@ mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_
   b.partial = reinterpret_cast<float*>(static_cast<char*>(hf) + align256((size_t)pk->n_tgt * H * esize(d->dtype)));
   b.partial_elems = (int64_t)8 * pk->n_tgt * d->c_lat;
   return linear(d->dtype, &b, 1, s);
+}
+
+mmdit_status final_modulation_impl(const mmdit_dims* d, const void* w_fmod, int32_t B, const void* c, float* modf,
+                                   hipStream_t s) {
+  LinearArgs a = mk(B, 2 * d->hidden, d->hidden, c, w_fmod, modf, MMDIT_EPI_STORE_F32);
+  a.a_silu = 1;
+  a.tag = "final_mod";
+  return linear(d->dtype, &a, 1, s);
+}
+
+mmdit_status check_final_args(const mmdit_dims* d, const void* w_out, const mmdit_pack_t* pk, const void* x_img,
+                              void* v, void* ws, size_t ws_bytes, const char* who) {
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w_out, who, "w_out"));
+  MMDIT_TRY(need(x_img, who, "x_img"));
+  MMDIT_TRY(need(v, who, "v"));
+  const size_t need_b = final_ws(d, pk);
+  if (!ws || ws_bytes < need_b) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, need_b, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  return need(ws, who, "ws");
+}
+
+}  // namespace
+
+mmdit_status mmdit_final(const mmdit_dims* d, const void* w_fmod, const void* w_out, const mmdit_pack_t* pk,
+                         const void* c, const void* x_img, void* v, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_final";
+  MMDIT_TRY(check_final_args(d, w_out, pk, x_img, v, ws, ws_bytes, who));
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w_fmod, who, "w_fmod"));
+  MMDIT_TRY(need(c, who, "c"));
+  hipStream_t s = (hipStream_t)stream;
+  float* modf = static_cast<float*>(ws);
+  MMDIT_TRY(final_modulation_impl(d, w_fmod, pk->B, c, modf, s));
+  return final_rest_impl(d, w_out, pk, modf, x_img, v, ws, s);
+}
+
+mmdit_status mmdit_final_mod(const mmdit_dims* d, const void* w_out, const mmdit_pack_t* pk, const float* modf,
+                             const void* x_img, void* v, void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "mmdit_final_mod";
+  MMDIT_TRY(check_final_args(d, w_out, pk, x_img, v, ws, ws_bytes, who));
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  MMDIT_TRY(need(modf, who, "modf"));
+  return final_rest_impl(d, w_out, pk, modf, x_img, v, ws, (hipStream_t)stream);
 }
 
 mmdit_status rf_make_xt(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* z, const void* eps,

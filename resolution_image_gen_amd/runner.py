@@ -96,6 +96,46 @@ def training_inputs(wl, samples=None):
             "t": S.timesteps(len(samples), wl.name)}
 
 
+class _SideMods:
+    """The conditioning and the adaLN vectors of every block and of the final
+    layer, on a side stream.  They depend on t and the weights only, so these
+    weight-streaming (HBM-bound) launches run while the main stream gathers,
+    noises and embeds (MFMA-bound); the main stream waits for block i's
+    vectors right before block i.  Same kernels, so the same bits as the
+    single-stream calls.  Default-priority stream; events without timing."""
+
+    def __init__(self, W, n_samples, device):
+        H, dt = W.dims.c.hidden, W.dims.torch_dtype
+        es = 2 if dt == torch.bfloat16 else 4
+        nb = len(W.bw)
+        self.mods = torch.empty(nb, 2, n_samples, 6 * H, dtype=torch.float32, device=device)
+        self.modf = torch.empty(n_samples, 2 * H, dtype=torch.float32, device=device)
+        self.ws = torch.empty(n_samples * (W.dims.c.t_dim + H) * es + 1024, dtype=torch.uint8, device=device)
+        self.stream = torch.cuda.Stream(device=device)
+        self.ev_start = torch.cuda.Event()
+        self.ev_mod = [torch.cuda.Event() for _ in range(nb)]
+        self.ev_modf = torch.cuda.Event()
+
+    def launch(self, W, dm, t, c, main):
+        """cond, then every block's vectors and the final layer's, after main's current point."""
+        side = self.stream
+        self.ev_start.record(main)
+        side.wait_event(self.ev_start)
+        B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], t, c, self.ws, side)
+        for i, bw in enumerate(W.bw):
+            B.block_modulation(dm, bw, c, self.mods[i], side)
+            self.ev_mod[i].record(side)
+        B.modulation(dm, W.wrap["w_fmod"], 2, c, self.modf, side)
+        self.ev_modf.record(side)
+
+    def blocks_and_final(self, W, dm, pk, x_img, x_txt, ws, v, main):
+        for i, bw in enumerate(W.bw):
+            main.wait_event(self.ev_mod[i])
+            B.block_fwd_mod(dm, bw, pk, self.mods[i], x_img, x_txt, ws, main)
+        main.wait_event(self.ev_modf)
+        B.final_mod(dm, W.wrap["w_out"], pk, self.modf, x_img, v, ws, main)
+
+
 class TrainForward:
     """One training forward over a pack: gather per-sample tensors, noise,
     condition, embed, run the blocks, final layer and RF loss."""
@@ -135,21 +175,21 @@ class TrainForward:
         self.sse = torch.empty(max(pk.B, 1), dtype=torch.float32, device=device)
         self.loss = torch.empty(1, dtype=torch.float32, device=device)
         self.ws = torch.empty(B.workspace_size(self.dims, pk), dtype=torch.uint8, device=device)
+        self.side = _SideMods(W, pk.B, device)
 
     def run(self, stream=None, repack=True):
         W, pk, dm = self.W, self.pk, self.dims
+        main = stream if stream is not None else torch.cuda.current_stream()
         if repack:
-            pk = self._repack(stream)
-        B.pack_gather(pk, 0, self.z_s, self.z, stream)
-        B.pack_gather(pk, 0, self.eps_s, self.eps, stream)
-        B.pack_gather(pk, 1, self.tau_s, self.tau, stream)
-        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, stream)
-        B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.c, self.ws, stream)
-        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
-        for bw in W.bw:
-            B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
-        B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
-        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, stream)
+            pk = self._repack(main)
+        self.side.launch(W, dm, self.t, self.c, main)
+        B.pack_gather(pk, 0, self.z_s, self.z, main)
+        B.pack_gather(pk, 0, self.eps_s, self.eps, main)
+        B.pack_gather(pk, 1, self.tau_s, self.tau, main)
+        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, main)
+        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, main)
+        self.side.blocks_and_final(W, dm, pk, self.x_img, self.x_txt, self.ws, self.v, main)
+        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, main)
 
     def capture(self):
         """Record one whole training forward (every launch) as a HIP graph."""
@@ -273,6 +313,7 @@ class Sampler:
         # an edit sample's image rows at z_1 = eps: [eps; source], both in dtype
         self.img_rows = None if src is None else torch.cat([_dev(eps, dt, device), _dev(src, dt, device)])
         self.two_pass = two_pass
+        self.side = _SideMods(W, 2, device)
         if two_pass:   # one-sample packs; the two-sample workspace covers each
             self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
 
@@ -318,12 +359,11 @@ class Sampler:
             if self.two_pass:
                 self._two_pass_forward(i, stream)
             else:
-                B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.tsched[i], self.c, self.ws, stream)
+                main = stream if stream is not None else torch.cuda.current_stream()
+                self.side.launch(W, dm, self.tsched[i], self.c, main)
                 B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt,
-                        stream)
-                for bw in W.bw:
-                    B.block_fwd(dm, bw, pk, self.c, self.x_img, self.x_txt, self.ws, stream)
-                B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
+                        main)
+                self.side.blocks_and_final(W, dm, pk, self.x_img, self.x_txt, self.ws, self.v, main)
             if on_step is not None:
                 on_step(i, self)
             B.rf_euler_step(pk, self.v, 0, 1, self.g, self.schedule[i], self.schedule[i + 1], self.z,

@@ -138,6 +138,40 @@ def test_block_adaln_zero_is_identity(B):
     assert np.array_equal(to_np(xt)[:len(x_txt)], x_txt.astype(np.float64))
 
 
+@pytest.mark.parametrize("case", ["tiny_f32_edit", "ragged_bf16_stress"])
+def test_split_modulation_calls_match_fused(B, case):
+    """block_modulation + block_fwd_mod and modulation + final_mod, the calls
+    the runner splits over two streams, end on the same bits as block_fwd and
+    final."""
+    d, dtype, samples, recipe = BLOCK_CASES[case]
+    ref, nb, x_img, x_txt, c = _inputs(d, dtype, samples, case, recipe)
+    dims, pk, xi1, xt1, ws = _run_block(B, d, dtype, samples, nb, x_img, x_txt, c)
+    wb = _dev_block(nb, dtype)
+    cd = _dev(c, dtype)
+    mod = torch.full((2, len(samples), 6 * d.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    B.block_modulation(dims, wb, cd, mod)
+    xi2 = _dev(x_img, dtype)
+    xt2 = _dev(x_txt if len(x_txt) else np.zeros((1, d.hidden), np.float32), dtype)
+    B.block_fwd_mod(dims, wb, pk, mod, xi2, xt2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xi1, xi2) and torch.equal(xt1, xt2)
+    # the vectors are W_mod SiLU(c) of each stream
+    for si, st in enumerate(("img", "txt")):
+        want = OB.silu(c.astype(np.float64)) @ nb[st]["w_mod"].astype(np.float64).T
+        assert_close(f"mod[{st}]", to_np(mod[si]), want, TOL[dtype])
+    # final layer
+    wf = S.normal((2 * d.hidden, d.hidden), 0.02, dtype, case, "wf")
+    wo = S.normal((d.c_lat, d.hidden), 0.02, dtype, case, "wo")
+    v1 = torch.empty(pk.n_tgt, d.c_lat, dtype=_tdt(dtype), device="cuda")
+    v2 = torch.full_like(v1, float("nan"))
+    B.final(dims, _dev(wf, dtype), _dev(wo, dtype), pk, cd, xi1, v1, ws)
+    modf = torch.empty(len(samples), 2 * d.hidden, dtype=torch.float32, device="cuda")
+    B.modulation(dims, _dev(wf, dtype), 2, cd, modf)
+    B.final_mod(dims, _dev(wo, dtype), pk, modf, xi1, v2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(v1, v2)
+
+
 def test_block_deterministic_and_sample_order_invariant(B):
     d, dtype = CF.B4, "bf16"
     samples = [(16, 16, 1, 128), (9, 13, 1, 77), (5, 3, 2, 0), (1, 1, 1, 1)]
