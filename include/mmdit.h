@@ -271,6 +271,21 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* dims, const mmdit_block_w* w,
                              const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
                              mmdit_stream stream);
 
+/* mmdit_block_bwd with the weight gradients (their transposed operands and
+ * GEMMs) on a second stream stream_w: each group waits on stream for the
+ * kernel that produces its input, and stream waits for all of them before the
+ * call's last launch returns, so completion on stream means the whole
+ * backward is done, as with mmdit_block_bwd.  The two chains overlap (the
+ * transposes are HBM-bound, the input-gradient chain MFMA-bound).  Bit for
+ * bit the same results; stream_w NULL or equal to stream is mmdit_block_bwd.
+ * Uses a few events per device that the library creates once; one call at a
+ * time per device. */
+mmdit_status mmdit_block_bwd2(const mmdit_dims* dims, const mmdit_block_w* w,
+                              const mmdit_pack_t* pack, const void* c, const void* saved,
+                              size_t saved_bytes, void* dx_img, void* dx_txt,
+                              const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                              mmdit_stream stream, mmdit_stream stream_w);
+
 /* The rest of the training step's backward.  Loss ([hyper] 方法 objective;
  * [blog] 2.2(2), target latent only):  loss = mean_b SSE_b / (tgt_len_b C). */
 

@@ -104,6 +104,8 @@ def _load():
         "mmdit_block_bwd_workspace_size": (_sz, [D, P]),
         "mmdit_block_bwd": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(_BlockG),
                                    _vp, _vp, _sz, _vp]),
+        "mmdit_block_bwd2": (_i32, [D, ctypes.POINTER(_BlockW), P, _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(_BlockG),
+                                   _vp, _vp, _sz, _vp, _vp]),
         "mmdit_rms_modulate": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
         "mmdit_qk_norm_rope": (_i32, [D, _i64, _vp, _vp, _vp, _vp, _vp]),
         "mmdit_attention": (_i32, [D, P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -319,13 +321,20 @@ def block_grads(g):
     return _BlockG(*[_StreamG(*[g[s][k].data_ptr() for k in GRAD_KEYS]) for s in ("img", "txt")])
 
 
-def block_bwd(dims, wb, pk, c, saved, dx_img, dx_txt, grads, dc, ws, stream=None):
-    """dx_img, dx_txt: dL/dx_out in, dL/dx_in out; grads overwritten; dc accumulated."""
+def block_bwd(dims, wb, pk, c, saved, dx_img, dx_txt, grads, dc, ws, stream=None, stream_w=None):
+    """dx_img, dx_txt: dL/dx_out in, dL/dx_in out; grads overwritten; dc accumulated.
+    stream_w: run the weight gradients on this second stream (mmdit_block_bwd2)."""
     bw = wb if isinstance(wb, _BlockW) else block_weights(wb)
     bg = grads if isinstance(grads, _BlockG) else block_grads(grads)
-    _ck(_lib.mmdit_block_bwd(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(saved),
-                             saved.numel() * saved.element_size(), _p(dx_img), _p(dx_txt), ctypes.byref(bg),
-                             _p(dc), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    if stream_w is None:
+        _ck(_lib.mmdit_block_bwd(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(saved),
+                                 saved.numel() * saved.element_size(), _p(dx_img), _p(dx_txt), ctypes.byref(bg),
+                                 _p(dc), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    else:
+        _ck(_lib.mmdit_block_bwd2(ctypes.byref(dims.c), ctypes.byref(bw), pk.ref, _p(c), _p(saved),
+                                  saved.numel() * saved.element_size(), _p(dx_img), _p(dx_txt), ctypes.byref(bg),
+                                  _p(dc), _p(ws), ws.numel() * ws.element_size(), _stream(stream),
+                                  _stream(stream_w)))
 
 
 def rf_loss_grad(pk, v, z, eps, dv, stream=None):

@@ -831,11 +831,26 @@ size_t mmdit_block_bwd_workspace_size(const mmdit_dims* d, const mmdit_pack_t* p
   return bwd_layout(d, pk).end;
 }
 
-mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
-                             const void* saved, size_t saved_bytes, void* dx_img, void* dx_txt,
-                             const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
-                             mmdit_stream stream) {
-  const char* who = "mmdit_block_bwd";
+namespace {
+
+// Fork / join events of the two-stream block backward (no timing), created
+// once per device on first use and reused by every call.
+hipEvent_t bwd_event(int k) {
+  constexpr int kDev = 64, kEv = 8;
+  static hipEvent_t ev[kDev][kEv] = {};
+  int dev = 0;
+  if (k < 0 || k >= kEv || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) return nullptr;
+  if (!ev[dev][k] && hipEventCreateWithFlags(&ev[dev][k], hipEventDisableTiming) != hipSuccess) {
+    ev[dev][k] = nullptr;
+    return nullptr;
+  }
+  return ev[dev][k];
+}
+
+mmdit_status block_bwd_impl(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                            const void* saved, size_t saved_bytes, void* dx_img, void* dx_txt,
+                            const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                            mmdit_stream stream, mmdit_stream stream_w, const char* who) {
   MMDIT_TRY(check_dims(d, who));
   MMDIT_TRY(check_pack(pk, who));
   if (!w || !g) {
@@ -864,6 +879,22 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   }
   MMDIT_TRY(need(ws, who, "ws"));
   hipStream_t s = (hipStream_t)stream;
+  // weight gradients (their transposes and GEMMs) on sw: each group forks
+  // from s once its inputs exist there and sw joins s at the end.  Nothing sw
+  // reads is written again by s within the call, and every region is its own.
+  hipStream_t sw = stream_w ? (hipStream_t)stream_w : s;
+  const bool two = sw != s;
+  int nfork = 0;
+  auto fork = [&]() -> mmdit_status {
+    if (!two) return MMDIT_OK;
+    hipEvent_t e = bwd_event(nfork++);
+    if (!e) {
+      set_error("%s: could not create a stream event", who);
+      return MMDIT_E_HIP;
+    }
+    MMDIT_TRY(hip_check(hipEventRecord(e, s), "hipEventRecord"));
+    return hip_check(hipStreamWaitEvent(sw, e, 0), "hipStreamWaitEvent");
+  };
   const mmdit_dtype dt = d->dtype;
   const size_t es = esize(dt);
   const int32_t H = d->hidden, M = d->mlp, D = d->head_dim;
@@ -908,6 +939,17 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
       ta[i] = {dx[i], trows(Lb.ddT, i, H), rows(Lb.dd, i, H), mod[i] + 5 * H, seg[i], H, nr[i], np[i], 6 * H, H};
     MMDIT_TRY(transpose2_impl(dt, ta, 2, 2, s));
   }
+  MMDIT_TRY(fork());   // dd^T ready
+  {
+    TransposeArgs ta[2];
+    memset(ta, 0, sizeof(ta));
+    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.u_pre, i, M), trows(Lb.guT, i, M), nullptr, nullptr, nullptr, M, nr[i], np[i], 0, M};
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 1, sw));
+    const char* A[2] = {trows(Lb.ddT, 0, H), trows(Lb.ddT, 1, H)};
+    const char* X[2] = {trows(Lb.guT, 0, M), trows(Lb.guT, 1, M)};
+    float* dw[2] = {gr[0]->w_down, gr[1]->w_down};
+    MMDIT_TRY(weight_grad(dt, H, M, np, A, X, dw, "bwd_mlp_down_dw", sw));
+  }
   {
     LinearArgs a[2] = {mk(ni, M, H, rows(Lb.dd, 0, H), wt(Lb.wt_down, 0, 0), rows(Lb.du, 0, M), kEpiGeluBwd),
                        mk(nt, M, H, rows(Lb.dd, 1, H), wt(Lb.wt_down, 1, (int64_t)M * H), rows(Lb.du, 1, M), kEpiGeluBwd)};
@@ -916,27 +958,18 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
     a[0].tag = "bwd_mlp_down_dx";
     MMDIT_TRY(linear(dt, a, 2, s));
   }
-  {
-    TransposeArgs ta[2];
-    memset(ta, 0, sizeof(ta));
-    for (int i = 0; i < 2; ++i) ta[i] = {srows(S.u_pre, i, M), trows(Lb.guT, i, M), nullptr, nullptr, nullptr, M, nr[i], np[i], 0, M};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 1, s));
-    const char* A[2] = {trows(Lb.ddT, 0, H), trows(Lb.ddT, 1, H)};
-    const char* X[2] = {trows(Lb.guT, 0, M), trows(Lb.guT, 1, M)};
-    float* dw[2] = {gr[0]->w_down, gr[1]->w_down};
-    MMDIT_TRY(weight_grad(dt, H, M, np, A, X, dw, "bwd_mlp_down_dw", s));
-  }
+  MMDIT_TRY(fork());   // du ready
   {
     TransposeArgs ta[2];
     memset(ta, 0, sizeof(ta));
     for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.du, i, M), trows(Lb.duT, i, M), nullptr, nullptr, nullptr, M, nr[i], np[i], 0, M};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     for (int i = 0; i < 2; ++i) ta[i] = {srows(S.h2, i, H), trows(Lb.h2T, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     const char* A[2] = {trows(Lb.duT, 0, M), trows(Lb.duT, 1, M)};
     const char* X[2] = {trows(Lb.h2T, 0, H), trows(Lb.h2T, 1, H)};
     float* dw[2] = {gr[0]->w_up, gr[1]->w_up};
-    MMDIT_TRY(weight_grad(dt, M, H, np, A, X, dw, "bwd_mlp_up_dw", s));
+    MMDIT_TRY(weight_grad(dt, M, H, np, A, X, dw, "bwd_mlp_up_dw", sw));
   }
   {
     LinearArgs a[2] = {mk(ni, H, M, rows(Lb.du, 0, M), wt(Lb.wt_up, 0, 0), rows(Lb.dh2, 0, H), MMDIT_EPI_STORE),
@@ -995,18 +1028,19 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   {
     LinearArgs a[2] = {mk(ni, H, H, rows(Lb.da, 0, H), wt(Lb.wt_o, 0, 0), rows(Lb.dO, 0, H), MMDIT_EPI_STORE),
                        mk(nt, H, H, rows(Lb.da, 1, H), wt(Lb.wt_o, 1, (int64_t)H * H), rows(Lb.dO, 1, H), MMDIT_EPI_STORE)};
+    MMDIT_TRY(fork());   // da ready
     a[0].tag = "bwd_out_proj_dx";
     MMDIT_TRY(linear(dt, a, 2, s));
     TransposeArgs ta[2];
     memset(ta, 0, sizeof(ta));
     for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.da, i, H), trows(Lb.daT, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     for (int i = 0; i < 2; ++i) ta[i] = {srows(S.o, i, H), trows(Lb.oT, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     const char* A[2] = {trows(Lb.daT, 0, H), trows(Lb.daT, 1, H)};
     const char* X[2] = {trows(Lb.oT, 0, H), trows(Lb.oT, 1, H)};
     float* dw[2] = {gr[0]->w_o, gr[1]->w_o};
-    MMDIT_TRY(weight_grad(dt, H, H, np, A, X, dw, "bwd_out_proj_dw", s));
+    MMDIT_TRY(weight_grad(dt, H, H, np, A, X, dw, "bwd_out_proj_dw", sw));
   }
   // joint attention, then QK-norm + RoPE
   MMDIT_TRY(attention_bwd_impl(dt, pk, d->heads, D, srows(S.qkv, 0, 3 * H), srows(S.qkv, 1, 3 * H), srows(S.o, 0, H),
@@ -1023,16 +1057,17 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   }
   // QKV projection: dW_qkv = dqkv^T h1, dh1 = dqkv W_qkv
   {
+    MMDIT_TRY(fork());   // dqkv final (after the QK-norm backward)
     TransposeArgs ta[2];
     memset(ta, 0, sizeof(ta));
     for (int i = 0; i < 2; ++i) ta[i] = {rows(Lb.dqkv, i, 3 * H), trows(Lb.dqkvT, i, 3 * H), nullptr, nullptr, nullptr, 3 * H, nr[i], np[i], 0, 3 * H};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     for (int i = 0; i < 2; ++i) ta[i] = {srows(S.h1, i, H), trows(Lb.h1T, i, H), nullptr, nullptr, nullptr, H, nr[i], np[i], 0, H};
-    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, s));
+    MMDIT_TRY(transpose2_impl(dt, ta, 2, 0, sw));
     const char* A[2] = {trows(Lb.dqkvT, 0, 3 * H), trows(Lb.dqkvT, 1, 3 * H)};
     const char* X[2] = {trows(Lb.h1T, 0, H), trows(Lb.h1T, 1, H)};
     float* dw[2] = {gr[0]->w_qkv, gr[1]->w_qkv};
-    MMDIT_TRY(weight_grad(dt, 3 * H, H, np, A, X, dw, "bwd_qkv_dw", s));
+    MMDIT_TRY(weight_grad(dt, 3 * H, H, np, A, X, dw, "bwd_qkv_dw", sw));
     LinearArgs a[2] = {mk(ni, H, 3 * H, rows(Lb.dqkv, 0, 3 * H), wt(Lb.wt_qkv, 0, 0), rows(Lb.dh1, 0, H), MMDIT_EPI_STORE),
                        mk(nt, H, 3 * H, rows(Lb.dqkv, 1, 3 * H), wt(Lb.wt_qkv, 1, (int64_t)3 * H * H), rows(Lb.dh1, 1, H),
                           MMDIT_EPI_STORE)};
@@ -1059,7 +1094,35 @@ mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const 
   const float* dm[2] = {dmod[0], dmod[1]};
   const void* wm[2] = {w->img.w_mod, w->txt.w_mod};
   float* dwm[2] = {g->img.w_mod, g->txt.w_mod};
-  return outer_vecmat_impl(dt, pk->B, 6 * H, H, 2, dm, wm, c, 0, 0, dwm, dc, base + Lb.modg, Lb.attn - Lb.modg, s);
+  MMDIT_TRY(outer_vecmat_impl(dt, pk->B, 6 * H, H, 2, dm, wm, c, 0, 0, dwm, dc, base + Lb.modg, Lb.attn - Lb.modg, s));
+  if (two) {   // s waits for every weight gradient
+    hipEvent_t e = bwd_event(nfork);
+    if (!e) {
+      set_error("%s: could not create a stream event", who);
+      return MMDIT_E_HIP;
+    }
+    MMDIT_TRY(hip_check(hipEventRecord(e, sw), "hipEventRecord"));
+    MMDIT_TRY(hip_check(hipStreamWaitEvent(s, e, 0), "hipStreamWaitEvent"));
+  }
+  return MMDIT_OK;
+}
+
+}  // namespace
+
+mmdit_status mmdit_block_bwd(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                             const void* saved, size_t saved_bytes, void* dx_img, void* dx_txt,
+                             const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                             mmdit_stream stream) {
+  return block_bwd_impl(d, w, pk, c, saved, saved_bytes, dx_img, dx_txt, g, dc, ws, ws_bytes, stream, nullptr,
+                        "mmdit_block_bwd");
+}
+
+mmdit_status mmdit_block_bwd2(const mmdit_dims* d, const mmdit_block_w* w, const mmdit_pack_t* pk, const void* c,
+                              const void* saved, size_t saved_bytes, void* dx_img, void* dx_txt,
+                              const mmdit_block_grad* g, float* dc, void* ws, size_t ws_bytes,
+                              mmdit_stream stream, mmdit_stream stream_w) {
+  return block_bwd_impl(d, w, pk, c, saved, saved_bytes, dx_img, dx_txt, g, dc, ws, ws_bytes, stream, stream_w,
+                        "mmdit_block_bwd2");
 }
 
 namespace {

@@ -241,6 +241,9 @@ class TrainStep(TrainForward):
                       "blocks": [{s: {k: torch.empty(tuple(blk[s][k].shape), **f32) for k in B.GRAD_KEYS}
                                   for s in ("img", "txt")} for blk in W.blocks]}
         self.bg = [B.block_grads(g) for g in self.grads["blocks"]]
+        # the blocks' weight gradients run on their own stream beside the
+        # input-gradient chain (mmdit_block_bwd2); default priority
+        self.wstream = torch.cuda.Stream(device=device)
 
     def run(self, stream=None, repack=True):
         W, pk, dm = self.W, self.pk, self.dims
@@ -265,7 +268,7 @@ class TrainStep(TrainForward):
         self.dx_txt.zero_()
         for i in range(len(W.bw) - 1, -1, -1):
             B.block_bwd(dm, W.bw[i], pk, self.c, self.saved[i], self.dx_img, self.dx_txt, self.bg[i], self.dc,
-                        self.ws_bwd, stream)
+                        self.ws_bwd, stream, stream_w=self.wstream)
         B.embed_bwd(dm, pk, self.zt, self.tau, self.dx_img, self.dx_txt, g["w_in"], g["w_txt"], self.ws_bwd, stream)
         B.cond_bwd(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.dc, g["w_t1"], g["w_t2"], self.ws_bwd, stream)
 

@@ -122,6 +122,27 @@ def test_training_forward_matches_inference_forward_and_is_deterministic(B, case
             assert torch.equal(r1["grads"][s][k], r2["grads"][s][k]), (s, k)
 
 
+@pytest.mark.parametrize("case", ["tiny_f32_edit", "small_bf16", "small_bf16_no_text"])
+def test_two_stream_backward_matches_one_stream(B, case):
+    """mmdit_block_bwd2 (weight gradients on a second stream) gives the same
+    bits as mmdit_block_bwd, twice in a row on the same buffers."""
+    d, dtype, samples, ref, nb, x_img, x_txt, c, dy_img, dy_txt = _setup(case)
+    r = _run(B, d, dtype, samples, nb, x_img, x_txt, c, dy_img, dy_txt)
+    side = torch.cuda.Stream()
+    one = np.zeros((1, d.hidden), np.float32)
+    for _ in range(2):
+        dxi, dxt = _dev(dy_img, dtype), _dev(dy_txt if len(dy_txt) else one, dtype)
+        grads = {s: {k: torch.full(tuple(r["wb"][s][k].shape), float("nan"), dtype=torch.float32, device="cuda")
+                     for k in B.GRAD_KEYS} for s in ("img", "txt")}
+        dc = torch.zeros(len(samples), d.hidden, dtype=torch.float32, device="cuda")
+        B.block_bwd(r["dims"], r["wb"], r["pk"], r["cd"], r["saved"], dxi, dxt, grads, dc, r["wsb"], stream_w=side)
+        torch.cuda.synchronize()
+        assert torch.equal(dxi, r["dxi"]) and torch.equal(dxt, r["dxt"]) and torch.equal(dc, r["dc"])
+        for s in ("img", "txt"):
+            for k in B.GRAD_KEYS:
+                assert torch.equal(grads[s][k], r["grads"][s][k]), (s, k)
+
+
 @pytest.mark.parametrize("name,depth", [("tiny_f32", 2), ("tiny_f32_edit", 2), ("small_bf16", 2)])
 def test_training_step_vs_oracle(B, name, depth):
     """The whole training step: forward with the RF loss, then every weight
