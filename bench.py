@@ -347,11 +347,13 @@ def bench_train_step(steps, warmup, depth):
     # one more step with every launch bracketed by hipEvents on its stream
     from resolution_image_gen_amd import binding as B
 
+    ts.overlap = False          # one stream, so no launch's events span another's work
     B.timing_enable(True)
     torch.cuda.synchronize()
     ts.run()
     kernels = B.timing_report()
     B.timing_enable(False)
+    ts.overlap = True
     work = train_kernel_work(wl)
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
     avg_ms = kernels[dom][0] / kernels[dom][1]
@@ -450,7 +452,9 @@ def main():
         graph_ms = e0.elapsed_time(e1) / args.steps
         del tf.graph
 
-    # per-kernel times: every launch bracketed by hipEvents on its stream
+    # per-kernel times: every launch bracketed by hipEvents on its stream,
+    # all on one stream so no launch's events span another's work
+    tf.overlap = False
     B.timing_enable(True)
     torch.cuda.synchronize()
     for _ in range(args.steps):
@@ -458,6 +462,7 @@ def main():
     torch.cuda.synchronize()
     kernels = B.timing_report()
     B.timing_enable(False)
+    tf.overlap = True
 
     n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
     blk, wrap = step_flops(wl)

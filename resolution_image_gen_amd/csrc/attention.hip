@@ -1069,10 +1069,10 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
     else
       MMDIT_LAUNCH(v_transpose_kernel<64>, tgrid, dim3(256), 0, s, a, vt, njp);
     MMDIT_TRY(launch_check("v_transpose_kernel", s));
-    // 8-wave blocks (256 queries) once a sample is long enough for them to
-    // fill the chip (measured: 3% faster at 16k tokens per sample, neutral at
-    // 4k, 19% slower at 384), else 4-wave blocks
-    const int nw = pk->max_joint >= 8192 ? 8 : 4;
+    // 8-wave blocks (256 queries) once a sample is long enough (measured: 3%
+    // faster at 33k tokens per sample, 3.5% slower at 8.4k, 19% slower at
+    // 384), else 4-wave blocks
+    const int nw = pk->max_joint >= 16384 ? 8 : 4;
     a.nq = (int32_t)cdiv(pk->max_joint, 32 * nw);
     a.nB = pk->B;
     dim3 grid((unsigned)(8 * cdiv((int64_t)a.nq * heads * pk->B, 8)));

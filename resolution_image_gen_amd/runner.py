@@ -116,9 +116,10 @@ class _SideMods:
         self.ev_mod = [torch.cuda.Event() for _ in range(nb)]
         self.ev_modf = torch.cuda.Event()
 
-    def launch(self, W, dm, t, c, main):
-        """cond, then every block's vectors and the final layer's, after main's current point."""
-        side = self.stream
+    def launch(self, W, dm, t, c, main, overlap=True):
+        """cond, then every block's vectors and the final layer's, after main's
+        current point (on main itself when overlap is False)."""
+        side = self.stream if overlap else main
         self.ev_start.record(main)
         side.wait_event(self.ev_start)
         B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], t, c, self.ws, side)
@@ -176,13 +177,16 @@ class TrainForward:
         self.loss = torch.empty(1, dtype=torch.float32, device=device)
         self.ws = torch.empty(B.workspace_size(self.dims, pk), dtype=torch.uint8, device=device)
         self.side = _SideMods(W, pk.B, device)
+        # False: every launch on the one stream (per-kernel timing wants
+        # launches that do not overlap)
+        self.overlap = True
 
     def run(self, stream=None, repack=True):
         W, pk, dm = self.W, self.pk, self.dims
         main = stream if stream is not None else torch.cuda.current_stream()
         if repack:
             pk = self._repack(main)
-        self.side.launch(W, dm, self.t, self.c, main)
+        self.side.launch(W, dm, self.t, self.c, main, self.overlap)
         B.pack_gather(pk, 0, self.z_s, self.z, main)
         B.pack_gather(pk, 0, self.eps_s, self.eps, main)
         B.pack_gather(pk, 1, self.tau_s, self.tau, main)
@@ -268,7 +272,7 @@ class TrainStep(TrainForward):
         self.dx_txt.zero_()
         for i in range(len(W.bw) - 1, -1, -1):
             B.block_bwd(dm, W.bw[i], pk, self.c, self.saved[i], self.dx_img, self.dx_txt, self.bg[i], self.dc,
-                        self.ws_bwd, stream, stream_w=self.wstream)
+                        self.ws_bwd, stream, stream_w=self.wstream if self.overlap else None)
         B.embed_bwd(dm, pk, self.zt, self.tau, self.dx_img, self.dx_txt, g["w_in"], g["w_txt"], self.ws_bwd, stream)
         B.cond_bwd(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.dc, g["w_t1"], g["w_t2"], self.ws_bwd, stream)
 
@@ -317,6 +321,7 @@ class Sampler:
         self.img_rows = None if src is None else torch.cat([_dev(eps, dt, device), _dev(src, dt, device)])
         self.two_pass = two_pass
         self.side = _SideMods(W, 2, device)
+        self.overlap = True
         if two_pass:   # one-sample packs; the two-sample workspace covers each
             self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
 
@@ -363,7 +368,7 @@ class Sampler:
                 self._two_pass_forward(i, stream)
             else:
                 main = stream if stream is not None else torch.cuda.current_stream()
-                self.side.launch(W, dm, self.tsched[i], self.c, main)
+                self.side.launch(W, dm, self.tsched[i], self.c, main, self.overlap)
                 B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt,
                         main)
                 self.side.blocks_and_final(W, dm, pk, self.x_img, self.x_txt, self.ws, self.v, main)

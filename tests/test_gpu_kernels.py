@@ -37,9 +37,9 @@ CASES = {
     "long_bf16_d128": (CF.B4, "bf16", [(48, 50, 1, 37), (40, 52, 1, 100), (3, 5, 1, 7)]),
     "long_bf16_d64": (CF.Dims(hidden=512, heads=8, head_dim=64, mlp=2048, c_lat=64, d_txt=512), "bf16",
                       [(50, 44, 1, 19), (21, 30, 2, 33)]),
-    # a sample past 8192 joint tokens: attention takes 256-query blocks of 8 waves
-    "long8k_bf16_d128": (CF.Dims(hidden=256, heads=2, head_dim=128, mlp=1024, c_lat=64, d_txt=256), "bf16",
-                         [(90, 90, 1, 210), (7, 9, 1, 30)]),
+    # a sample past 16384 joint tokens: attention takes 256-query blocks of 8 waves
+    "long16k_bf16_d128": (CF.Dims(hidden=256, heads=2, head_dim=128, mlp=1024, c_lat=64, d_txt=256), "bf16",
+                          [(128, 130, 1, 210), (7, 9, 1, 30)]),
 }
 
 
