@@ -214,3 +214,36 @@ def test_gradient_struct_layout(B):
     assert ctypes.sizeof(B._BlockG) == 14 * ctypes.sizeof(ctypes.c_void_p)
     assert B._BlockG.txt.offset == 7 * ctypes.sizeof(ctypes.c_void_p)
     assert [f for f, _ in B._StreamG._fields_] == ["w_mod", "w_qkv", "g_q", "g_k", "w_o", "w_up", "w_down"]
+
+
+def test_split_modulation_and_two_stream_calls_validate_before_launch(B):
+    lib = B._lib
+    pk = _fake_pack(B, [(16, 16, 1, 128), (8, 8, 2, 3)])
+    P = ctypes.byref(pk)
+    ok = ctypes.byref(_dims(B))
+    fake = ctypes.c_void_p(1 << 20)
+    w = B._BlockW(B._StreamW(*([1 << 20] * 7)), B._StreamW(*([1 << 20] * 7)))
+    g = B._BlockG(B._StreamG(*([1 << 20] * 7)), B._StreamG(*([1 << 20] * 7)))
+    need_ws = lib.mmdit_workspace_size(ok, P)
+    # block_modulation: B outside [0, 256], NULL and misaligned outputs, a NULL weight
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w), 257, fake, fake, None) == -1
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w), -1, fake, fake, None) == -1
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w), 2, fake, None, None) == -1
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w), 2, fake, ctypes.c_void_p((1 << 20) + 4), None) == -3
+    w0 = B._BlockW(B._StreamW(*([0] + [1 << 20] * 6)), B._StreamW(*([1 << 20] * 7)))
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w0), 2, fake, fake, None) == -1
+    assert lib.mmdit_block_modulation(ok, ctypes.byref(w), 0, None, None, None) == 0    # nothing to do
+    # block_fwd_mod: a NULL modulation, a workspace one byte short
+    assert lib.mmdit_block_fwd_mod(ok, ctypes.byref(w), P, None, fake, fake, fake, need_ws, None) == -1
+    assert lib.mmdit_block_fwd_mod(ok, ctypes.byref(w), P, fake, fake, fake, fake, need_ws - 1, None) == -4
+    # final_mod: NULL modulation, NULL output
+    assert lib.mmdit_final_mod(ok, fake, P, None, fake, fake, fake, 1 << 30, None) == -1
+    assert lib.mmdit_final_mod(ok, fake, P, fake, fake, None, fake, 1 << 30, None) == -1
+    # block_bwd2 validates exactly like block_bwd
+    saved = lib.mmdit_block_saved_size(ok, P)
+    bws = lib.mmdit_block_bwd_workspace_size(ok, P)
+    assert lib.mmdit_block_bwd2(ok, ctypes.byref(w), P, fake, fake, saved, fake, fake, ctypes.byref(g), fake, fake,
+                                bws - 1, None, fake) == -4
+    assert b"mmdit_block_bwd2" in lib.mmdit_last_error()
+    assert lib.mmdit_block_bwd2(ok, ctypes.byref(w), P, fake, fake, saved - 1, fake, fake, ctypes.byref(g), fake,
+                                fake, bws, None, fake) == -4
