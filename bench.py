@@ -353,7 +353,7 @@ def bench_train_step(steps, warmup, depth):
     ts.run()
     kernels = B.timing_report()
     B.timing_enable(False)
-    ts.overlap = True
+    ts.overlap = R.OVERLAP
     work = train_kernel_work(wl)
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
     avg_ms = kernels[dom][0] / kernels[dom][1]
@@ -385,6 +385,9 @@ def main():
                     help="also time N training steps (forward + backward, every weight gradient) over one "
                          "50,048-token pack and report them under 'train_step' (0: skip)")
     ap.add_argument("--train-depth", type=int, default=28, help="blocks of the timed training step")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="every launch on one stream (no side streams), so profiler averages of every launch "
+                         "match the instrumented single-stream pass")
     ap.add_argument("--sampler-packs", type=int, default=0,
                     help="also time N packs of the 4-step packed-CFG sampler (28 blocks) and report them "
                          "under 'sampler' (0: skip)")
@@ -411,6 +414,8 @@ def main():
     from resolution_image_gen_amd import configs as CF
     from resolution_image_gen_amd import runner as R
 
+    if args.one_stream:
+        R.OVERLAP = False
     wl = CF.WORKLOADS[args.workload]
     if wl.steps:
         raise SystemExit("the sampler workloads are timed with --sampler-packs N next to a training-forward "
@@ -462,7 +467,7 @@ def main():
     torch.cuda.synchronize()
     kernels = B.timing_report()
     B.timing_enable(False)
-    tf.overlap = True
+    tf.overlap = R.OVERLAP
 
     n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
     blk, wrap = step_flops(wl)

@@ -96,6 +96,12 @@ def training_inputs(wl, samples=None):
             "t": S.timesteps(len(samples), wl.name)}
 
 
+# Default for new runners: side streams on (conditioning and adaLN vectors
+# beside the embeddings; the backward's weight gradients beside its input
+# gradients).  False puts every launch on the caller's stream.
+OVERLAP = True
+
+
 class _SideMods:
     """The conditioning and the adaLN vectors of every block and of the final
     layer, on a side stream.  They depend on t and the weights only, so these
@@ -179,7 +185,7 @@ class TrainForward:
         self.side = _SideMods(W, pk.B, device)
         # False: every launch on the one stream (per-kernel timing wants
         # launches that do not overlap)
-        self.overlap = True
+        self.overlap = OVERLAP
 
     def run(self, stream=None, repack=True):
         W, pk, dm = self.W, self.pk, self.dims
@@ -321,7 +327,7 @@ class Sampler:
         self.img_rows = None if src is None else torch.cat([_dev(eps, dt, device), _dev(src, dt, device)])
         self.two_pass = two_pass
         self.side = _SideMods(W, 2, device)
-        self.overlap = True
+        self.overlap = OVERLAP
         if two_pass:   # one-sample packs; the two-sample workspace covers each
             self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
 
