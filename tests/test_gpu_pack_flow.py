@@ -207,3 +207,37 @@ def test_pack_latent(B):
     zt = torch.zeros(32, 64, device="cuda", dtype=torch.bfloat16)
     B.rf_pack_latent(pk, z, 0, 1, zt)
     assert torch.equal(zt[:16], z.to(torch.bfloat16)) and torch.equal(zt[16:], z.to(torch.bfloat16))
+
+
+def test_empty_pack_calls_are_no_ops(B):
+    """A pack of no samples: every call returns without launching work on the
+    caller's buffers; the loss of nothing is 0."""
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import synthetic as S
+
+    pk = B.pack([])
+    assert (pk.B, pk.n_img, pk.n_txt, pk.n_tgt) == (0, 0, 0, 0)
+    d = CF.TINY
+    dims = B.Dims(d, "f32")
+    f = dict(dtype=torch.float32, device="cuda")
+    C, H = d.c_lat, d.hidden
+    z, eps, zt = (torch.full((1, C), 7.0, **f) for _ in range(3))
+    t = torch.full((1,), 0.5, **f)
+    B.rf_make_xt(pk, z, eps, t, zt)
+    sse = torch.full((1,), 7.0, **f)
+    loss = torch.full((1,), 7.0, **f)
+    B.rf_loss(pk, z, z, eps, sse, loss, torch.empty(256, dtype=torch.uint8, device="cuda"))
+    wb = {s: {k: torch.from_numpy(v).cuda() for k, v in w.items()}
+          for s, w in S.block_weights(d, "f32", "empty", 0).items()}
+    x_img, x_txt, c = (torch.full((1, H), 7.0, **f) for _ in range(3))
+    ws = torch.empty(max(B.workspace_size(dims, pk), 256), dtype=torch.uint8, device="cuda")
+    B.block_fwd(dims, wb, pk, c, x_img, x_txt, ws)
+    mod = torch.full((2, 1, 6 * H), 7.0, **f)
+    B.block_fwd_mod(dims, wb, pk, mod, x_img, x_txt, ws)
+    v = torch.full((1, C), 7.0, **f)
+    w_f, w_o = torch.zeros(2 * H, H, **f), torch.zeros(C, H, **f)
+    B.final(dims, w_f, w_o, pk, c, x_img, v, ws)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0
+    for a in (zt, sse, x_img, x_txt, v):
+        assert torch.all(a == 7.0)
