@@ -78,14 +78,14 @@ def train_kernel_work(wl):
 # scaled by a plain copy's counter reading (profiles/traffic.json); valid only
 # while the kernel's sources are unchanged since the counters were taken.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("resolution_image_gen_amd/csrc/gemm.hip", "resolution_image_gen_amd/csrc/common.h")
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(sources):
+    """SHA-256 over the given source files (repository-relative), in order."""
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -93,8 +93,8 @@ def kernel_sources_sha256():
 
 def measured_traffic(tag, workload):
     """HBM bytes per launch of kernel `tag` on `workload` from the committed
-    counter record, or None when there is none or the GEMM sources changed
-    since the counters were taken."""
+    counter record, or None when there is none or the record's kernel sources
+    changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             recs = json.load(f)
@@ -102,7 +102,10 @@ def measured_traffic(tag, workload):
         return None
     for rec in recs if isinstance(recs, list) else [recs]:
         if rec.get("kernel") == tag and rec.get("workload") == workload:
-            if rec.get("sources_sha256") != kernel_sources_sha256():
+            try:
+                if rec.get("sources_sha256") != kernel_sources_sha256(rec.get("sources", ())):
+                    return None
+            except OSError:
                 return None
             return rec.get("hbm_bytes_per_launch")
     return None
