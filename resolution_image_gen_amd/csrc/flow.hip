@@ -44,15 +44,19 @@ __global__ void make_xt_kernel(int64_t n_img, int32_t C, const T* __restrict__ z
   }
 }
 
-// Per-target-row sum of squared residuals; 16 lanes per row, 8 channels per lane-step.
+// Per-target-row sum of squared residuals; 16 lanes per row, 8 channels per
+// lane-step; the 16-lane groups stride over the rows with the grid (whose
+// size the host caps).
 template <typename T>
 __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v,
                                const T* __restrict__ z, const T* __restrict__ eps,
                                const int32_t* __restrict__ tgt_row, float* __restrict__ row_sse) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-  float acc = 0.f;
-  if (row < n_tgt) {
+  const int64_t row0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int64_t rstep = ((int64_t)gridDim.x * blockDim.x) >> 4;
+  // every lane of a 16-lane group shares `row`, so the group runs the loop together
+  for (int64_t row = row0; row < n_tgt; row += rstep) {
+    float acc = 0.f;
     const int64_t src = tgt_row[row];
     for (int c8 = lane16; c8 < (C >> 3); c8 += 16) {
       float vv[8], zv[8], ev[8];
@@ -65,9 +69,9 @@ __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
         acc += d * d;
       }
     }
+    acc = group_sum(acc, 16);
+    if (lane16 == 0) row_sse[row] = acc;
   }
-  acc = group_sum(acc, 16);
-  if (row < n_tgt && lane16 == 0) row_sse[row] = acc;
 }
 
 // dL/dv of the loss mean_b SSE_b / (tgt_len_b C): 2 (v - (z - eps)) / (B tgt_len_b C)

@@ -152,6 +152,40 @@ def test_rf_loss(B, dtype, name):
         assert torch.all(sse == 0) and loss.item() == 0.0
 
 
+def test_rf_loss_past_the_launch_grid_cap(B):
+    """More target rows (2 x 8,388,608 + 4,096 > 2^24) than one 16-lane group
+    per row of the largest grid the host launches: the groups stride over the
+    rest (the whole last sample lies past 2^24 rows).  Closed form: z = eps,
+    v = 0 except planted rows of ones, so each SSE is C times its planted
+    rows, exactly."""
+    C = 8
+    samples = [(2048, 4096, 1, 0), (2048, 4096, 1, 0), (64, 64, 1, 0)]
+    lens = [h * w for h, w, _, _ in samples]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    print("rf_loss, 16,781,312 target rows", flush=True)
+    pk = B.pack(samples)
+    n = pk.n_tgt
+    assert n == sum(lens) and n > 1 << 24 and starts[2] >= 1 << 24
+    g = torch.Generator(device="cuda").manual_seed(7)
+    z = torch.randint(-4, 5, (n, C), device="cuda", generator=g).float()
+    eps = z.clone()
+    v = torch.zeros(n, C, device="cuda")
+    planted = {0: [0], 1: [100, lens[1] - 1], 2: [0, 17, lens[2] - 1]}
+    for b, rows in planted.items():
+        for r in rows:
+            v[int(starts[b]) + r] = 1.0
+    sse = torch.empty(len(samples), device="cuda")
+    loss = torch.empty(1, device="cuda")
+    ws = torch.full((n * 4 + 256,), 255, dtype=torch.uint8, device="cuda")   # NaN until written
+    B.rf_loss(pk, v, z, eps, sse, loss, ws)
+    want = torch.tensor([float(C * len(planted[b])) for b in range(len(samples))], device="cuda")
+    assert torch.equal(sse, want), (sse, want)
+    want_loss = sum(C * len(planted[b]) / (lens[b] * C) for b in range(len(samples))) / len(samples)
+    assert abs(loss.item() - want_loss) <= 1e-6 * want_loss
+    del z, eps, v, ws
+    torch.cuda.empty_cache()
+
+
 def test_euler_exact_on_linear_flow(B):
     # z_1 = eps and v == z* - eps: four Euler steps land on z*
     from resolution_image_gen_amd import synthetic as S
