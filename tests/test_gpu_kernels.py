@@ -40,6 +40,8 @@ CASES = {
     # a sample past 16384 joint tokens: attention takes 256-query blocks of 8 waves
     "long16k_bf16_d128": (CF.Dims(hidden=256, heads=2, head_dim=128, mlp=1024, c_lat=64, d_txt=256), "bf16",
                           [(128, 130, 1, 210), (7, 9, 1, 30)]),
+    "long16k_bf16_d64": (CF.Dims(hidden=256, heads=4, head_dim=64, mlp=1024, c_lat=64, d_txt=256), "bf16",
+                         [(128, 130, 1, 210), (3, 5, 1, 7)]),
 }
 
 
