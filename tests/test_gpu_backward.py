@@ -24,6 +24,9 @@ CASES = {
     "small_bf16": (SMALL_BF16, "bf16", [(12, 16, 1, 24), (7, 9, 2, 13), (3, 5, 1, 70)]),
     # no text rows at all: the text stream's weight gradients are zero
     "small_bf16_no_text": (SMALL_BF16, "bf16", [(9, 14, 1, 0), (5, 6, 2, 0)]),
+    # head dim 64: the bf16 attention backward's other instantiation
+    "small_bf16_d64": (CF.Dims(hidden=256, heads=4, head_dim=64, mlp=1024, c_lat=64, d_txt=256), "bf16",
+                       [(12, 16, 1, 24), (7, 9, 2, 13), (3, 5, 1, 70)]),
 }
 
 
@@ -122,7 +125,7 @@ def test_training_forward_matches_inference_forward_and_is_deterministic(B, case
             assert torch.equal(r1["grads"][s][k], r2["grads"][s][k]), (s, k)
 
 
-@pytest.mark.parametrize("case", ["tiny_f32_edit", "small_bf16", "small_bf16_no_text"])
+@pytest.mark.parametrize("case", ["tiny_f32_edit", "small_bf16", "small_bf16_no_text", "small_bf16_d64"])
 def test_two_stream_backward_matches_one_stream(B, case):
     """mmdit_block_bwd2 (weight gradients on a second stream) gives the same
     bits as mmdit_block_bwd, twice in a row on the same buffers."""
