@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the packed NR-MMDiT hot path on one MI355X.
 
-One step = one training forward over one synthetic pack, all on the GPU:
-pack ids -> gather per-sample tensors -> RF noising -> timestep conditioning
--> token embedding -> one dual-stream block -> final layer -> RF loss.
-Default workload: the 256^2-stage pack, 16 samples x (16x16 latent grid +
-128 text tokens), hidden 3072, 24 x 128 heads, MLP 12288, bf16.
+Headline (the default line): the 4-step packed-CFG Euler sampler at 1024^2.
+One step of the benchmark = one whole 4-step pack: cond + uncond samples
+(64x64 latent grid + 256 text tokens each, 8,704 tokens), 28 random-init
+dual-stream blocks (hidden 3072, 24 x 128 heads, MLP 12288, bf16), guidance
+4, t = 1, .75, .5, .25 -> 0; per Euler step the conditioning, every block's
+adaLN vectors, the embeddings, 28 blocks, the final layer, then the CFG
+combine + Euler update.  A pack is captured once as a HIP graph and
+replayed; K replays are bracketed by hipEvents on the launch stream.
+`value` = block-token throughput (8,704 tokens x 28 blocks x 4 steps per
+pack / seconds per pack); `ms_per_step` = ms per 4-step pack.  One more pack
+runs eagerly on one stream with every library launch bracketed by hipEvents
+on its stream: it gives the per-kernel table and the roofline of the
+dominant kernel.  The CPU oracle runs one block-step of the same pack.
 
-Prints ONE JSON line.  `value` is whole-step token throughput (image + text
-tokens per second) over K eagerly launched steps bracketed by hipEvents;
-`graph_ms_per_step` is the same step replayed from a HIP graph.  A second pass
-of K steps brackets every launch with hipEvents on its stream (that would add
-~9% to the step if done in the first pass): it gives the per-kernel table and
-the roofline of the dominant kernel.  The line also carries the block's
-TFLOP/s against the bf16 MFMA peak and the CPU oracle timed on a bounded
-sample.
+Extra keys: the 256^2-stage training forward (16 x (16x16 grid + 128 text)
+tokens, one block + RF loss) as `train_forward_256`, the rectified-flow
+kernels' bandwidth as `rf_kernels`; optional legs behind flags (two-pass
+CFG, 20-step and editing samplers, the 50k-token training step).
+
+Prints ONE JSON line.
 """
 
 import argparse
@@ -31,13 +37,16 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
-def kernel_work(wl):
-    """Algorithmic work per launch of each tagged kernel of one step."""
+def kernel_work(wl, samples=None, depth=None):
+    """Algorithmic work per launch of each tagged kernel of one step over
+    `samples` (default: the workload's) with `depth` blocks."""
     d = wl.dims
     H, M = d.hidden, d.mlp
-    n = sum(f * h * w + t for h, w, f, t in wl.samples)
-    n_tgt = sum(h * w for h, w, _, _ in wl.samples)
-    att = sum((f * h * w + t) ** 2 for h, w, f, t in wl.samples)
+    samples = wl.samples if samples is None else samples
+    depth = wl.depth if depth is None else depth
+    n = sum(f * h * w + t for h, w, f, t in samples)
+    n_tgt = sum(h * w for h, w, _, _ in samples)
+    att = sum((f * h * w + t) ** 2 for h, w, f, t in samples)
     es = 2 if wl.dtype == "bf16" else 4
     return {
         "qkv_proj": ("mfma", 2.0 * n * H * 3 * H),
@@ -45,8 +54,9 @@ def kernel_work(wl):
         "mlp_up_gelu": ("mfma", 2.0 * n * H * M),
         "mlp_down_gated": ("mfma", 2.0 * n * M * H),
         "attn_mfma_kernel": ("mfma", 4.0 * H * att),
-        # read x, write y: two launches over all N rows + one over the target rows, averaged
-        "rms_modulate_kernel": ("hbm", (2 * (2.0 * es * H * n) + 2.0 * es * H * n_tgt) / 3),
+        # read x, write y: per block two launches over all N rows, and one
+        # launch over the target rows per forward (final layer), averaged
+        "rms_modulate_kernel": ("hbm", (2 * depth * (2.0 * es * H * n) + 2.0 * es * H * n_tgt) / (2 * depth + 1)),
         # read and write q and k of every row, one launch
         "qk_norm_rope_kernel": ("hbm", 4.0 * es * H * n),
         "final_out": ("mfma", 2.0 * n_tgt * H * d.c_lat),
@@ -169,14 +179,123 @@ def cpu_baseline(wl, W, inputs, n_samples, min_seconds=10.0):
                       f"(noise, cond, embed, block, final, loss), float64 numpy, {runs} runs, {dt:.1f} s"}
 
 
-def bench_sampler(steps, warmup):
-    """ms per 4-step packed-CFG pack: cond + uncond (64x64 grid + 256 text
-    tokens each), 28 random-init blocks, guidance 4, t = 1, .75, .5, .25 -> 0.
-    The same sampler with the two CFG branches as separate forwards is timed
-    beside it, and both must end on the same bits; then one 20-step pack
-    (uniform steps from 1 to 0) of the packed sampler, and the 4-step editing
-    sampler (target + clean source of the same grid per sample), packed and
-    two-pass, on the same blocks."""
+def _roofline(kernels, work):
+    """Roofline object of the dominant kernel: the tagged kernel with the
+    largest total time among those with a known algorithmic work; achieved =
+    work per launch / average launch time."""
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
+    kind, per_launch = work[dom]
+    avg_ms = kernels[dom][0] / kernels[dom][1]
+    if kind == "mfma":
+        achieved = per_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+    roof["work_per_launch"] = per_launch
+    return roof
+
+
+def _kernel_lines(kernels, work, per, unit):
+    """Per-kernel table (total time per `unit`, launches, and the rate of
+    kernels with a known work), largest first."""
+    out = {}
+    for k, (ms, cnt) in sorted(kernels.items(), key=lambda kv: -kv[1][0]):
+        row = {f"us_per_{unit}": round(ms / per * 1e3, 1), "launches": round(cnt / per, 2)}
+        if k in work:
+            kd, wk = work[k]
+            s = ms / cnt * 1e-3
+            row["TFLOP/s" if kd == "mfma" else "GB/s"] = round(wk / s / (1e12 if kd == "mfma" else 1e9), 1)
+        out[k] = row
+    return out
+
+
+def sampler_inputs(wl):
+    """z_1 = eps (64x64 x C) and the two text conditions of the sampler pack."""
+    from resolution_image_gen_amd import synthetic as S
+
+    d = wl.dims
+    h, w, _, T = wl.samples[0]
+    eps = S.normal((h * w, d.c_lat), 1.0, "bf16", wl.name, "eps")
+    tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
+    tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
+    return eps, tau_c, tau_u
+
+
+def _timed_graph(sm, steps, warmup):
+    """ms per replay of the sampler's pack captured as one HIP graph."""
+    import torch
+
+    sm.capture()                          # one pack = one HIP graph (~1,600 launches at 4 steps)
+    for _ in range(warmup):
+        sm.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        sm.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del sm.graph
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def bench_headline(steps, warmup):
+    """The 4-step packed-CFG sampler at 1024^2 over 28 blocks: ms per pack
+    from `steps` graph replays, then one eager pack on one stream with every
+    launch timed (per-kernel table, roofline of the dominant kernel)."""
+    import torch
+
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import runner as R
+    from resolution_image_gen_amd.configs import block_flops
+
+    wl = CF.WORKLOADS["sampler1024_cfg_bf16"]
+    W = R.Weights(wl, source="torch")            # 28 blocks drawn on the GPU (19 GB bf16)
+    eps, tau_c, tau_u = sampler_inputs(wl)
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    ms, wall = _timed_graph(sm, steps, warmup)
+    assert torch.isfinite(sm.z).all()
+    z_graph = sm.z.clone()
+    # one eager pack, every launch on one stream, bracketed by hipEvents
+    sm.overlap = False
+    torch.cuda.synchronize()
+    B.timing_enable(True)
+    sm.run()
+    kernels = B.timing_report()
+    B.timing_enable(False)
+    sm.overlap = R.OVERLAP
+    assert torch.equal(sm.z, z_graph), "eager and graph-replayed packs disagree"
+    nsteps = len(wl.schedule) - 1
+    blk = block_flops(wl.dims, sm.samples)[0] * wl.depth * nsteps
+    _, wrap1 = step_flops(wl)
+    n = sum(hh * ww * f + t for hh, ww, f, t in sm.samples)
+    work = kernel_work(wl, sm.samples, wl.depth)
+    roof = _roofline(kernels, work)
+    roof["traffic"] = measured_traffic(roof["kernel"], wl.name)
+    return {
+        "wl": wl, "W": W, "inputs": (eps, tau_c, tau_u), "samples": sm.samples,
+        "ms_per_pack": ms, "wall_s_timed": wall, "block_flop_per_pack": blk, "wrap_flop_per_pack": wrap1 * nsteps,
+        "block_tokens_per_pack": n * wl.depth * nsteps, "tokens_per_pack": n,
+        "roofline": roof, "kernels": _kernel_lines(kernels, work, 1, "pack"),
+    }
+
+
+def bench_sampler_extras(W, steps, warmup):
+    """Beside the headline pack, on the same 28 blocks: the same sampler with
+    its two CFG branches as separate forwards (both must end on the same
+    bits), one 20-step pack (uniform steps from 1 to 0), and the 4-step
+    editing sampler (target + clean source of the same grid per sample),
+    packed and two-pass."""
     import torch
 
     from resolution_image_gen_amd import configs as CF
@@ -186,63 +305,86 @@ def bench_sampler(steps, warmup):
 
     wl = CF.WORKLOADS["sampler1024_cfg_bf16"]
     d = wl.dims
-    W = R.Weights(wl, source="torch")            # 28 blocks drawn on the GPU (19 GB bf16)
-    h, w, _, T = wl.samples[0]
-    eps = S.normal((h * w, d.c_lat), 1.0, "bf16", wl.name, "eps")
-    tau_c = S.text(T, d.d_txt, "bf16", wl.name, "tau_c")
-    tau_u = S.text(T, d.d_txt, "bf16", wl.name, "tau_u")
-
-    def timed(sm, steps=steps):
-        sm.capture()                          # one pack = one HIP graph (~1,600 launches at 4 steps)
-        for _ in range(warmup):
-            sm.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            sm.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        del sm.graph
-        return ms
-
+    eps, tau_c, tau_u = sampler_inputs(wl)
+    h, w, _, _ = wl.samples[0]
     sm = R.Sampler(wl, W, eps, tau_c, tau_u)
-    ms = timed(sm)
+    ms, _ = _timed_graph(sm, steps, warmup)
     sm2 = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
-    ms2 = timed(sm2)
+    ms2, _ = _timed_graph(sm2, steps, warmup)
     assert torch.isfinite(sm.z).all()
     assert torch.equal(sm.z, sm2.z), "packed and two-pass CFG samplers disagree"
-    sm_samples = sm.samples
-    # the base (non-distilled) sampler: 20 uniform Euler steps, packed CFG
     sm20 = R.Sampler(wl, W, eps, tau_c, tau_u, schedule=[1.0 - i / 20 for i in range(21)])
-    ms20 = timed(sm20, steps=1)
+    ms20, _ = _timed_graph(sm20, 1, 1)
     assert torch.isfinite(sm20.z).all()
     del sm, sm2, sm20
-    # the 4-step editing sampler on the same blocks: each sample a noised 64x64
-    # target + the clean 64x64 source (frames 0 / 1) + text; packed and two-pass
     ewl = CF.WORKLOADS["edit_sampler1024_cfg_bf16"]
     src = S.normal((h * w, d.c_lat), 1.0, "bf16", ewl.name, "src")
     se = R.Sampler(ewl, W, eps, tau_c, tau_u, src=src)
-    ms_e = timed(se)
+    ms_e, _ = _timed_graph(se, steps, warmup)
     se2 = R.Sampler(ewl, W, eps, tau_c, tau_u, src=src, two_pass=True)
-    ms_e2 = timed(se2)
+    ms_e2, _ = _timed_graph(se2, steps, warmup)
     assert torch.isfinite(se.z).all()
     assert torch.equal(se.z, se2.z), "packed and two-pass CFG edit samplers disagree"
     eblk = block_flops(d, se.samples)[0] * ewl.depth * (len(ewl.schedule) - 1)
-    blk = block_flops(d, sm_samples)[0] * wl.depth * (len(wl.schedule) - 1)
-    n = sum(hh * ww * f + t for hh, ww, f, t in sm_samples)
-    return {"workload": f"{wl.name}: {wl.note}", "ms_per_4step_pack": round(ms, 2), "packs_timed": steps,
-            "block_tokens_per_s": round(n * wl.depth * (len(wl.schedule) - 1) / (ms * 1e-3), 1),
-            "block_tflops": round(blk / (ms * 1e-3) / 1e12, 1),
-            "pct_bf16_peak": round(100 * blk / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "two_pass_ms_per_4step_pack": round(ms2, 2),
-            "packed_speedup_vs_two_pass": round(ms2 / ms, 3),
-            "ms_per_20step_pack": round(ms20, 2),
+    return {"ms_per_4step_pack": round(ms, 2), "two_pass_ms_per_4step_pack": round(ms2, 2),
+            "packed_speedup_vs_two_pass": round(ms2 / ms, 3), "ms_per_20step_pack": round(ms20, 2),
             "edit": {"workload": f"{ewl.name}: {ewl.note}", "ms_per_4step_pack": round(ms_e, 2),
                      "block_tflops": round(eblk / (ms_e * 1e-3) / 1e12, 1),
                      "two_pass_ms_per_4step_pack": round(ms_e2, 2),
                      "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3)}}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_sampler(head, min_seconds=10.0):
+    """The oracle (float64 numpy) on one block-step of the headline pack: the
+    conditioning, the embeddings, block 0 of the 28, the final layer, the CFG
+    combine and the Euler update over the whole 8,704-token pack at t = 1,
+    with the same bf16 weights and inputs; repeated until at least
+    min_seconds of CPU work have been timed.  Rate in block-tokens/s (the
+    headline's unit); a pack is 28 x 4 such block-steps."""
+    import numpy as np
+    import torch
+
+    from oracle import flow as OF
+    from oracle import pack as OP
+
+    wl, W = head["wl"], head["W"]
+    eps, tau_c, tau_u = head["inputs"]
+
+    def host(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    Wd = {k: host(v) for k, v in W.wrap.items()}
+    Wd["blocks"] = [{s: {k: host(v) for k, v in W.blocks[0][s].items()} for s in ("img", "txt")}]
+    samples = head["samples"]
+    ref = OP.pack(samples)
+    n = samples[0][0] * samples[0][1]
+    e64 = np.asarray(eps, np.float64)
+    tau = np.concatenate([np.asarray(tau_c, np.float64), np.asarray(tau_u, np.float64)])
+    t = np.full(2, wl.schedule[0])
+    runs, dt = 0, 0.0
+    while runs == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        v = OF.velocity_model(np.concatenate([e64, e64]), tau, t, Wd, ref, wl.dims.heads)
+        OF.euler_step(e64, OF.cfg_combine(v[:n], v[n:], wl.guidance), wl.schedule[0], wl.schedule[1])
+        dt += time.perf_counter() - t0
+        runs += 1
+    per = dt / runs
+    tok = head["tokens_per_pack"]
+    nblk = head["block_tokens_per_pack"] // tok
+    return {"value": round(tok / per, 1), "unit": "block-tokens/s", "cores": int(_threads()), "kind": "oracle",
+            "sample": f"one block-step (cond, embed, block 0 of {wl.depth}, final layer, CFG + Euler) over the "
+                      f"whole {tok}-token pack at t = 1, float64 numpy, {runs} run(s), {dt:.1f} s",
+            "ms_per_4step_pack_extrapolated": round(per * nblk * 1e3, 1),
+            "extrapolation": f"x{nblk} block-steps ({wl.depth} blocks x {len(wl.schedule) - 1} steps)"}
 
 
 def bench_rf_kernels(reps=20):
@@ -371,19 +513,88 @@ def bench_train_step(steps, warmup, depth):
             "loss": round(ts.loss.item(), 6), "roofline": roof, "kernels_us_per_block": table}
 
 
+def bench_train_forward(name, steps, warmup, graph=True):
+    """One training forward per step (pack ids, gathers, RF noising, cond,
+    embed, the blocks, final layer, RF loss) over workload `name`: eager ms
+    per step over `steps` steps, the same step replayed from a HIP graph, and
+    one more pass of `steps` steps on one stream with every launch timed."""
+    import torch
+
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import configs as CF
+    from resolution_image_gen_amd import runner as R
+
+    wl = CF.WORKLOADS[name]
+    W = R.Weights(wl)
+    inputs = R.training_inputs(wl)
+    tf = R.TrainForward(wl, W, inputs)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        tf.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        tf.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    graph_ms = None
+    if graph:
+        tf.capture()
+        for _ in range(2):
+            tf.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            tf.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+        del tf.graph
+    tf.overlap = False
+    B.timing_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        tf.run()
+    torch.cuda.synchronize()
+    kernels = B.timing_report()
+    B.timing_enable(False)
+    tf.overlap = R.OVERLAP
+    n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
+    blk, wrap = step_flops(wl)
+    tflops = (blk + wrap) / (ms_step * 1e-3) / 1e12
+    work = kernel_work(wl)
+    roof = _roofline(kernels, work)
+    roof["traffic"] = measured_traffic(roof["kernel"], wl.name)
+    out = {"workload": f"{wl.name}: {wl.note}", "ms_per_step": round(ms_step, 4),
+           "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+           "tokens_per_s": round(n_tokens / (ms_step * 1e-3), 1), "tflops": round(tflops, 1),
+           "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+           "block_tflop_per_step": round(blk / 1e12, 4), "roofline": roof,
+           "kernels_us_per_step": {k: v["us_per_step"]
+                                   for k, v in _kernel_lines(kernels, work, steps, "step").items()}}
+    return out, (wl, _NumpyWeights(W), inputs)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="pack256_bf16")
-    ap.add_argument("--cpu-samples", type=int, default=16, help="samples of the pack the CPU oracle runs")
+    ap.add_argument("--steps", type=int, default=10, help="timed 4-step packs")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed packs before the timed ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
-    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the 256^2-stage training forward and the RF-kernel legs")
+    ap.add_argument("--workload", default=None,
+                    help="time only the training forward of this workload (no sampler headline), e.g. "
+                         "pack256_bf16, native1024_bf16, edit2048_bf16; the line then reports it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
                          "scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--sampler-extras", action="store_true",
+                    help="also time the two-pass CFG sampler, a 20-step pack and the 4-step editing sampler "
+                         "(packed and two-pass) on the same 28 blocks, under 'sampler_extras'")
     ap.add_argument("--train-steps", type=int, default=0,
                     help="also time N training steps (forward + backward, every weight gradient) over one "
                          "50,048-token pack and report them under 'train_step' (0: skip)")
@@ -391,9 +602,6 @@ def main():
     ap.add_argument("--one-stream", action="store_true",
                     help="every launch on one stream (no side streams), so profiler averages of every launch "
                          "match the instrumented single-stream pass")
-    ap.add_argument("--sampler-packs", type=int, default=0,
-                    help="also time N packs of the 4-step packed-CFG sampler (28 blocks) and report them "
-                         "under 'sampler' (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: packs are independent, so more GPUs would each take "
@@ -413,132 +621,73 @@ def main():
         print(json.dumps({"copy_calibration_mib": args.copy_calibration_mib, "launches": 3}))
         return
 
-    from resolution_image_gen_amd import binding as B
-    from resolution_image_gen_amd import configs as CF
     from resolution_image_gen_amd import runner as R
 
     if args.one_stream:
         R.OVERLAP = False
-    wl = CF.WORKLOADS[args.workload]
-    if wl.steps:
-        raise SystemExit("the sampler workloads are timed with --sampler-packs N next to a training-forward "
-                         "workload")
     torch.cuda.set_device(0)
-    W = R.Weights(wl)
-    W_np = _NumpyWeights(W)
-    inputs = R.training_inputs(wl)
-    tf = R.TrainForward(wl, W, inputs)
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        tf.run()
-    torch.cuda.synchronize()
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic: seeded N(0,1) latents, noise and text features; random-init N(0,0.02) weights"}
 
-    # timed region (hipEvents on the launch stream bracket the whole region)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        tf.run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    if args.workload:   # one training-forward workload alone
+        res, (wl, Wn, inputs) = bench_train_forward(args.workload, args.steps, args.warmup)
+        n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
+        out = {"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", **common,
+               "ms_per_step": res["ms_per_step"], "dtype": wl.dtype,
+               "config": {"workload": res["workload"], "tokens_per_step": n_tokens, "samples": len(wl.samples),
+                          "hidden": wl.dims.hidden, "heads": wl.dims.heads, "head_dim": wl.dims.head_dim,
+                          "mlp": wl.dims.mlp, "blocks": wl.depth},
+               **{k: v for k, v in res.items() if k not in ("workload", "ms_per_step", "tokens_per_s")}}
+        if args.kernels:
+            for k, v in res["kernels_us_per_step"].items():
+                print(f"{k:48s} {v:10.1f} us/step", file=sys.stderr)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(wl, Wn, inputs, len(wl.samples))
+        print(json.dumps(out), flush=True)
+        return
 
-    # the same step replayed from a HIP graph (launch overhead removed)
-    graph_ms = None
-    if not args.no_graph:
-        tf.capture()
-        for _ in range(2):
-            tf.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            tf.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / args.steps
-        del tf.graph
-
-    # per-kernel times: every launch bracketed by hipEvents on its stream,
-    # all on one stream so no launch's events span another's work
-    tf.overlap = False
-    B.timing_enable(True)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        tf.run()
-    torch.cuda.synchronize()
-    kernels = B.timing_report()
-    B.timing_enable(False)
-    tf.overlap = R.OVERLAP
-
-    n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
-    blk, wrap = step_flops(wl)
-    tflops = (blk + wrap) / (ms_step * 1e-3) / 1e12
-    work = kernel_work(wl)
-    # dominant kernel: largest total time among kernels with a known algorithmic work
-    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
-    kind, per_launch = work[dom]
-    avg_ms = kernels[dom][0] / kernels[dom][1]
-    if kind == "mfma":
-        achieved = per_launch / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    else:
-        achieved = per_launch / (avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = dom
-    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
-    roof["traffic"] = measured_traffic(dom, wl.name)
-
-    table = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] / args.steps}
-             for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][0])}
-    if args.kernels:
-        for k, v in table.items():
-            extra = ""
-            if k in work:
-                kd, wk = work[k]
-                per = v["ms_per_step"] / v["launches_per_step"] * 1e-3
-                extra = (f"  {wk / per / 1e12:8.1f} TFLOP/s" if kd == "mfma" else f"  {wk / per / 1e9:8.1f} GB/s")
-            print(f"{k:48s} {v['ms_per_step'] * 1e3:10.1f} us/step  x{v['launches_per_step']:.0f}{extra}",
-                  file=sys.stderr)
-
+    head = bench_headline(args.steps, args.warmup)
+    wl = head["wl"]
+    ms = head["ms_per_pack"]
+    tflops = head["block_flop_per_pack"] / (ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
-        "value": round(n_tokens / (ms_step * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic: seeded N(0,1) latents, noise and text features; random-init N(0,0.02) weights",
-        "config": {"workload": f"{wl.name}: {wl.note}", "tokens_per_step": n_tokens,
-                   "samples": len(wl.samples), "hidden": wl.dims.hidden, "heads": wl.dims.heads,
-                   "head_dim": wl.dims.head_dim, "mlp": wl.dims.mlp, "blocks": wl.depth},
-        "tflops": round(tflops, 1),
+        "value": round(head["block_tokens_per_pack"] / (ms * 1e-3), 1),
+        "unit": "block-tokens/s",
+        **common,
+        "ms_per_step": round(ms, 3),
+        "ms_per_4step_pack": round(ms, 3),
+        "config": {"workload": f"{wl.name}: {wl.note}", "tokens_per_forward": head["tokens_per_pack"],
+                   "samples": [list(s) for s in head["samples"]], "steps_per_pack": len(wl.schedule) - 1,
+                   "schedule": list(wl.schedule), "guidance": wl.guidance, "hidden": wl.dims.hidden,
+                   "heads": wl.dims.heads, "head_dim": wl.dims.head_dim, "mlp": wl.dims.mlp,
+                   "blocks": wl.depth, "timed": "HIP-graph replays of the whole pack"},
+        "block_tflops": round(tflops, 1),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "block_tflop_per_step": round(blk / 1e12, 4),
-        "wall_s_timed": round(wall, 3),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
-        "roofline": roof,
-        "kernels_us_per_step": {k: round(v["ms_per_step"] * 1e3, 1) for k, v in table.items()},
+        "block_tflop_per_pack": round(head["block_flop_per_pack"] / 1e12, 3),
+        "wrapper_tflop_per_pack": round(head["wrap_flop_per_pack"] / 1e12, 3),
+        "wall_s_timed": round(head["wall_s_timed"], 3),
+        "roofline": head["roofline"],
+        "kernels_per_pack": head["kernels"],
     }
-    out["rf_kernels"] = bench_rf_kernels()
-    if args.sampler_packs > 0 or args.train_steps > 0:
-        del tf, W
-        torch.cuda.empty_cache()
-    if args.sampler_packs > 0:
-        out["sampler"] = bench_sampler(args.sampler_packs, 1)
+    if args.kernels:
+        for k, v in head["kernels"].items():
+            print(f"{k:48s} {json.dumps(v)}", file=sys.stderr)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_sampler(head)
+    if args.sampler_extras:
+        out["sampler_extras"] = bench_sampler_extras(head["W"], max(2, args.steps // 3), 1)
+    W = head.pop("W")
+    del W, head
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        res, _ = bench_train_forward("pack256_bf16", 20, 5)
+        out["train_forward_256"] = res
+        out["rf_kernels"] = bench_rf_kernels()
         torch.cuda.empty_cache()
     if args.train_steps > 0:
         out["train_step"] = bench_train_step(args.train_steps, 1, args.train_depth)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, W_np, inputs, args.cpu_samples)
     print(json.dumps(out), flush=True)
 
 

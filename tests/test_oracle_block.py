@@ -312,3 +312,114 @@ def test_cond_shapes(H, heads):
     assert c.shape == (2, H)
     m = K.modulation(c, r.standard_normal((6 * H, H)))
     assert len(m) == 6 and m[0].shape == (2, H)
+
+
+# ------------------------------------------ conditioning and final layer pins
+#
+# Hand-derivable values.  SiLU(1) = 1 / (1 + e^-1) = 0.7310585786300049 and
+# SiLU(0) = 0; the timestep embedding of R11 at t = 0 is cos(0) = 1 on its
+# first half and sin(0) = 0 on its second half.
+
+SILU1 = 0.7310585786300049
+
+
+def _selector(rows, cols, picks):
+    w = np.zeros((rows, cols))
+    for i, j in enumerate(picks):
+        w[i, j] = 1.0
+    return w
+
+
+def test_cond_closed_form_at_t0():
+    # W_t1 picks embedding entries 0..3 (cos half) and 128..131 (sin half),
+    # scaled by 3; W_t2 = 2 I.  c = W_t2 SiLU(W_t1 emb(0)) = 2 SiLU(3) on the
+    # cos picks and 2 SiLU(0) = 0 on the sin picks.
+    H = 8
+    w1 = 3.0 * _selector(H, 256, [0, 1, 2, 3, 128, 129, 130, 131])
+    w2 = 2.0 * np.eye(H)
+    c = K.cond(np.array([0.0]), w1, w2)
+    silu3 = 3.0 / (1.0 + math.exp(-3.0))                     # 2.857722...
+    np.testing.assert_allclose(c[0], [2 * silu3] * 4 + [0.0] * 4, rtol=0, atol=1e-15)
+    # SiLU after W_t2 instead (silu(6) = 5.985...) or before W_t1 would differ:
+    assert abs(2 * silu3 - 6.0 / (1.0 + math.exp(-6.0))) > 0.1
+
+
+def test_cond_closed_form_factor_1000():
+    # t = pi / 2000: the first frequency turns by 1000 t = pi / 2, so the
+    # embedding's entry 0 is cos(pi/2) = 0 and entry 128 is sin(pi/2) = 1.
+    H = 4
+    w1 = _selector(H, 256, [0, 128, 0, 128])
+    w2 = np.eye(H)
+    c = K.cond(np.array([math.pi / 2000.0]), w1, w2)
+    np.testing.assert_allclose(c[0], [0.0, SILU1, 0.0, SILU1], rtol=0, atol=1e-12)
+
+
+def test_cond_per_sample_and_modulation_chunk_order():
+    # two samples keep their own t; modulation splits W SiLU(c) into six
+    # H-chunks in order: chunk k of row b is rows k*H..(k+1)*H of W applied
+    # to SiLU(c_b)
+    H = 4
+    w1 = _selector(H, 256, [0, 1, 128, 129])
+    c = K.cond(np.array([0.0, math.pi / 2000.0]), w1, np.eye(H))
+    np.testing.assert_allclose(c[0], [SILU1, SILU1, 0.0, 0.0], atol=1e-15)
+    assert abs(c[1][0]) < 1e-12 and abs(c[1][2] - SILU1) < 1e-12
+    w_mod = np.zeros((6 * H, H))
+    for k in range(6):
+        w_mod[k * H, 0] = k + 1.0                             # chunk k, entry 0: (k + 1) SiLU(c[0])
+    m = K.modulation(np.array([[1.0, 0, 0, 0]]), w_mod)
+    assert [float(x[0, 0]) for x in m] == pytest.approx([(k + 1) * SILU1 for k in range(6)], abs=1e-15)
+
+
+def _final_pack():
+    # one sample, 1 x 2 grid, no text: target rows 0 and 1
+    return P.pack([(1, 2, 1, 0)])
+
+
+def test_final_layer_zero_modulation_is_plain_norm():
+    # W_fmod = 0: shift = scale = 0, so v = rms(x) W_out^T.  Row 0 is
+    # (2, -2, ...): mean square 4, so rms(x) = x / sqrt(4 + eps).
+    pk = _final_pack()
+    H = 8
+    x = np.array([[2.0, -2.0] * 4, [1.0, 0, 0, 0, 0, 0, 0, 0]])
+    w_out = _selector(2, H, [0, 1])
+    v = K.final_layer(x, np.ones((1, H)), np.zeros((2 * H, H)), w_out, pk)
+    n0 = 2.0 / math.sqrt(4.0 + 1e-6)
+    n1 = 1.0 / math.sqrt(1.0 / 8.0 + 1e-6)                    # row 1: mean square 1/8
+    np.testing.assert_allclose(v, [[n0, -n0], [n1, 0.0]], rtol=0, atol=1e-14)
+
+
+def test_final_layer_modulation_closed_form():
+    # c = (1, 0, ...) so SiLU(c) = (SiLU(1), 0, ...); W_fmod's first column
+    # = (shift; scale) / SiLU(1) with shift = 0.5 and scale = 2 everywhere.
+    # v = (rms(x)(1 + 2) + 0.5) W_out^T = 3 n + 0.5.  A dropped (1 + scale)
+    # gives 2 n + 0.5, swapped chunks 1.5 n + 2, a missing RMS 3 x + 0.5.
+    pk = _final_pack()
+    H = 8
+    x = np.array([[2.0, -2.0] * 4, [4.0] * 8])
+    c = np.zeros((1, H))
+    c[0, 0] = 1.0
+    w_fmod = np.zeros((2 * H, H))
+    w_fmod[:H, 0] = 0.5 / SILU1
+    w_fmod[H:, 0] = 2.0 / SILU1
+    w_out = _selector(2, H, [0, 1])
+    v = K.final_layer(x, c, w_fmod, w_out, pk)
+    n0 = 2.0 / math.sqrt(4.0 + 1e-6)
+    n1 = 4.0 / math.sqrt(16.0 + 1e-6)
+    np.testing.assert_allclose(v, [[3 * n0 + 0.5, -3 * n0 + 0.5], [3 * n1 + 0.5, 3 * n1 + 0.5]],
+                               rtol=0, atol=1e-13)
+
+
+def test_final_layer_uses_each_samples_modulation():
+    # two samples with different c: each target row takes its own sample's
+    # (shift, scale); sample 1's c is 0, so SiLU(c) = 0 and v is the plain norm
+    pk = P.pack([(1, 1, 1, 0), (1, 1, 1, 0)])
+    H = 8
+    x = np.array([[2.0, -2.0] * 4, [2.0, -2.0] * 4])
+    c = np.zeros((2, H))
+    c[0, 0] = 1.0
+    w_fmod = np.zeros((2 * H, H))
+    w_fmod[:H, 0] = 0.5 / SILU1
+    w_fmod[H:, 0] = 2.0 / SILU1
+    v = K.final_layer(x, c, w_fmod, _selector(1, H, [0]), pk)
+    n0 = 2.0 / math.sqrt(4.0 + 1e-6)
+    np.testing.assert_allclose(v[:, 0], [3 * n0 + 0.5, n0], rtol=0, atol=1e-13)
