@@ -21,6 +21,14 @@ Readings:
   R20  guided velocity v_u + g (v_c - v_u); cond and uncond share z_t and t.
   R25  in an editing pack only target rows are noised and scored; source rows
        carry the clean source latent.
+  R26  the negative-aware loss of the post-training stage (blog close-reading,
+       2.2(4), the Diffusion-NFT objective): per sample a reward r_b in [0, 1]
+       weighs the squared error of a positive-policy velocity v+ against
+       the target velocity and 1 - r_b weighs that of a negative-policy
+       velocity v-.  The target velocity is the base objective's z - eps on
+       the sample's target rows (same straight path); v+ and v- are inputs
+       (the pages do not say how the two policies are formed); the
+       normalisation is R17's.
 """
 
 import numpy as np
@@ -62,6 +70,26 @@ def loss(v, z, eps, pk):
     for b in range(pk["B"]):
         r0, r1 = pk["cu_tgt"][b], pk["cu_tgt"][b + 1]
         sse[b] = np.sum(diff[r0:r1] ** 2)
+    per_elem = sse / (pk["tgt_len"].astype(np.float64) * C)
+    return sse, float(np.mean(per_elem)) if pk["B"] else 0.0
+
+
+def nft_loss(v_pos, v_neg, z, eps, r, pk):
+    """Negative-aware flow-matching loss (R26).  v_pos, v_neg [n_tgt, C] in
+    target-row order; r [B] rewards in [0, 1].
+
+    SSE_b = r_b ||v+ - (z - eps)||^2 + (1 - r_b) ||v- - (z - eps)||^2 over the
+    target rows of sample b; returns (sse [B], mean_b SSE_b / (tgt_len_b C)).
+    """
+    target = velocity_target(z, eps, pk)
+    dp = np.asarray(v_pos, np.float64) - target
+    dn = np.asarray(v_neg, np.float64) - target
+    r = np.asarray(r, np.float64)
+    C = target.shape[1]
+    sse = np.zeros(pk["B"])
+    for b in range(pk["B"]):
+        r0, r1 = pk["cu_tgt"][b], pk["cu_tgt"][b + 1]
+        sse[b] = r[b] * np.sum(dp[r0:r1] ** 2) + (1.0 - r[b]) * np.sum(dn[r0:r1] ** 2)
     per_elem = sse / (pk["tgt_len"].astype(np.float64) * C)
     return sse, float(np.mean(per_elem)) if pk["B"] else 0.0
 

@@ -1,6 +1,7 @@
 """Pins for the oracle's rectified-flow wrapper: closed forms and exactness."""
 
 import numpy as np
+import pytest
 
 from oracle import block as K
 from oracle import flow as F
@@ -158,3 +159,93 @@ def test_timestep_embedding_closed_forms():
     np.testing.assert_allclose(e[:, 0], np.cos(1000 * t), atol=1e-14)
     np.testing.assert_allclose(np.arctan2(e[:, 128 + 127], e[:, 127]),
                                1000 * t * 10000 ** (-127 / 128), atol=1e-12)
+
+
+# ------------------------------------------------- negative-aware loss (R26)
+
+def test_nft_loss_hand_value():
+    # one sample, one 1x1 target row, C = 2: v+ - (z - eps) = (1, 0) and
+    # v- - (z - eps) = (0, 2), so SSE = r * 1 + (1 - r) * 4 and the loss is
+    # SSE / (1 * 2)
+    pk = P.pack([(1, 1, 1, 0)])
+    z, eps = np.array([[0.5, 0.5]]), np.array([[0.25, 0.5]])          # z - eps = (0.25, 0)
+    vp, vn = np.array([[1.25, 0.0]]), np.array([[0.25, 2.0]])
+    for r in (0.0, 0.3, 1.0):
+        sse, loss = F.nft_loss(vp, vn, z, eps, np.array([r]), pk)
+        assert sse[0] == pytest.approx(r + 4.0 * (1 - r), abs=1e-15)
+        assert loss == pytest.approx((r + 4.0 * (1 - r)) / 2.0, abs=1e-15)
+
+
+def test_nft_loss_reduces_to_the_base_loss_at_r_0_and_1():
+    pk = _pk()
+    r = np.random.default_rng(21)
+    z, eps = r.standard_normal((2, pk["cu_img"][-1], 8))
+    vp, vn = r.standard_normal((2, pk["cu_tgt"][-1], 8))
+    base_p, base_n = F.loss(vp, z, eps, pk), F.loss(vn, z, eps, pk)
+    one = F.nft_loss(vp, vn, z, eps, np.ones(3), pk)
+    zero = F.nft_loss(vp, vn, z, eps, np.zeros(3), pk)
+    np.testing.assert_array_equal(one[0], base_p[0])
+    np.testing.assert_array_equal(zero[0], base_n[0])
+    # mixed rewards pick per sample; v+ = v- makes r irrelevant
+    mix = F.nft_loss(vp, vn, z, eps, np.array([1.0, 0.0, 1.0]), pk)[0]
+    np.testing.assert_array_equal(mix, [base_p[0][0], base_n[0][1], base_p[0][2]])
+    same = F.nft_loss(vp, vp, z, eps, np.array([0.2, 0.9, 0.5]), pk)
+    np.testing.assert_allclose(same[0], base_p[0], rtol=1e-14)
+
+
+def test_nft_loss_brute_force_and_source_rows_ignored():
+    pk = _pk()
+    r = np.random.default_rng(22)
+    C = 3
+    z, eps = r.standard_normal((2, pk["cu_img"][-1], C))
+    vp, vn = r.standard_normal((2, pk["cu_tgt"][-1], C))
+    rw = np.array([0.25, 0.6, 0.9])
+    want = np.zeros(3)
+    for b in range(3):
+        i0, t0 = pk["cu_img"][b], pk["cu_tgt"][b]
+        for i in range(pk["tgt_len"][b]):
+            for ch in range(C):
+                tgt = z[i0 + i, ch] - eps[i0 + i, ch]
+                want[b] += rw[b] * (vp[t0 + i, ch] - tgt) ** 2 + (1 - rw[b]) * (vn[t0 + i, ch] - tgt) ** 2
+    sse, loss = F.nft_loss(vp, vn, z, eps, rw, pk)
+    np.testing.assert_allclose(sse, want, rtol=1e-13)
+    assert loss == pytest.approx(np.mean(want / (pk["tgt_len"] * C)), rel=1e-13)
+    eps2 = eps.copy()
+    eps2[np.setdiff1d(np.arange(len(z)), pk["tgt_rows"])] += 50.0   # source rows of the edit sample
+    np.testing.assert_array_equal(F.nft_loss(vp, vn, z, eps2, rw, pk)[0], sse)
+
+
+# --------------------------------------------------- the sampler's step loop
+
+def test_sampler_loop_hand_unrolled(monkeypatch):
+    # Replace the network by a stub that records what it is called with and
+    # returns a constant velocity per branch: a for the cond sample (first in
+    # the pack), b for the uncond sample.  The guided velocity is then
+    # b + g (a - b) at every step and the four steps, whose lengths sum to 1,
+    # land on z_0 = eps + b + g (a - b).  The stub also checks that step i
+    # runs at t = schedule[i], on z_t = the current latent for both samples.
+    h, w, C, g = 2, 3, 4, 4.0
+    n = h * w
+    r = np.random.default_rng(23)
+    eps = r.standard_normal((n, C))
+    tau_c, tau_u = r.standard_normal((2, 5, 8))
+    a, b = r.standard_normal((2, C))
+    calls = []
+
+    def stub(zt, tau, t, W, pk, heads):
+        calls.append((np.array(zt), np.array(t), pk["B"]))
+        np.testing.assert_array_equal(tau, np.concatenate([tau_c, tau_u]))
+        return np.concatenate([np.tile(a, (n, 1)), np.tile(b, (n, 1))])
+
+    monkeypatch.setattr(F, "velocity_model", stub)
+    z, vs = F.sample_packed_cfg(eps, tau_c, tau_u, {}, (h, w), 1, g)
+    vhat = b + g * (a - b)
+    np.testing.assert_allclose(z, eps + vhat, rtol=0, atol=1e-14)
+    assert [float(c[1][0]) for c in calls] == [1.0, 0.75, 0.5, 0.25]
+    assert all(c[2] == 2 and c[1][0] == c[1][1] for c in calls)
+    for i, (zt, _, _) in enumerate(calls):          # z_1 = eps, then one quarter step of vhat each
+        want = eps + 0.25 * i * vhat
+        np.testing.assert_allclose(zt[:n], want, atol=1e-14)
+        np.testing.assert_allclose(zt[n:], want, atol=1e-14)
+    for v in vs:
+        np.testing.assert_allclose(v, np.tile(vhat, (n, 1)), atol=1e-15)
