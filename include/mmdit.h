@@ -125,7 +125,10 @@ mmdit_status mmdit_pack_plan(const mmdit_sample* samples /* host [n] */, int32_t
 mmdit_status mmdit_pack(const mmdit_sample* samples /* host [n] */, int32_t n, mmdit_pack_t* io,
                         mmdit_stream stream);
 
-/* Gather per-sample tensors into a packed buffer.  src[b] (host array of
+/* Gather per-sample tensors into a packed buffer ([hyper] 方法: each
+ * sample's latent grid is flattened into a variable-length token sequence
+ * and the samples are concatenated into one packed sequence; [blog] 2.2(2):
+ * addressed by cumulative offsets).  src[b] (host array of
  * device pointers) is sample b's [rows_b, width] tensor, where rows_b is the
  * sample's image rows (which = 0), text rows (which = 1) or target rows
  * (which = 2); dst is the packed [n_rows, width] buffer.  width % 8 == 0. */
@@ -136,10 +139,16 @@ mmdit_status mmdit_pack_gather(const mmdit_pack_t* pack, int32_t which,
 /* ------------------------------------------------------------ model dims */
 
 /* Supported: head_dim in {64, 128}; hidden = heads*head_dim; hidden, mlp,
- * c_lat, d_txt multiples of 64; t_dim a multiple of 16; eps > 0.  RoPE bands
- * (frame, row, col) are (head_dim/4, 3*head_dim/8, 3*head_dim/8). */
+ * c_lat, d_txt multiples of 64; t_dim a multiple of 16; eps > 0.
+ * rope_dims: widths of the RoPE bands of the (frame, row, col) axes inside
+ * each head ([hyper] 方法 and [blog] 2.2(2): 2D RoPE per sample, a frame axis
+ * for editing), in that order from dimension 0; each even (0 allowed: that
+ * axis is not rotated) and summing to head_dim, else MMDIT_E_UNSUPPORTED.
+ * Pair j of a band of width w turns by pos * rope_theta^(-2j/w).  The
+ * workloads here use (head_dim/4, 3*head_dim/8, 3*head_dim/8). */
 typedef struct {
   int32_t hidden, heads, head_dim, mlp, c_lat, d_txt, t_dim;
+  int32_t rope_dims[3];
   float rope_theta, eps;
   mmdit_dtype dtype;
 } mmdit_dims;
@@ -185,7 +194,11 @@ mmdit_status mmdit_cond(const mmdit_dims* dims, const void* w_t1, const void* w_
 mmdit_status mmdit_modulation(const mmdit_dims* dims, const void* w, int32_t chunks, int32_t B,
                               const void* c, float* mod, mmdit_stream stream);
 
-/* Token embedding: x_img = zt W_in^T (zt [n_img, c_lat], W_in [H, c_lat]) and
+/* Token embedding ([blog] 2.2(2): the 128-channel latent is flattened into
+ * visual tokens and the frozen text encoder supplies the condition tau; the
+ * pages give no input projection, so the reading taken is one bias-free
+ * linear map per modality into the hidden width):
+ * x_img = zt W_in^T (zt [n_img, c_lat], W_in [H, c_lat]) and
  * x_txt = tau W_txt^T (tau [n_txt, d_txt], W_txt [H, d_txt]). */
 mmdit_status mmdit_embed(const mmdit_dims* dims, const void* w_in, const void* w_txt,
                          const mmdit_pack_t* pack, const void* zt, const void* tau, void* x_img,
@@ -361,7 +374,8 @@ typedef enum {
 
 /* Dense linear Y [M, N] = A [M, K] W^T, W [N, K], float32 accumulation, with
  * the fused epilogue.  For MMDIT_EPI_GATED_RES, gate is float32 with row
- * stride gate_stride and seg [M] int32.  a_silu != 0 applies SiLU to A. */
+ * stride gate_stride (>= N, a multiple of 4, else MMDIT_E_INVALID /
+ * MMDIT_E_UNSUPPORTED) and seg [M] int32.  a_silu != 0 applies SiLU to A. */
 mmdit_status mmdit_linear(mmdit_dtype dtype, int64_t M, int32_t N, int32_t K, const void* A,
                           const void* W, void* Y, int32_t epilogue, const float* gate,
                           int64_t gate_stride, const int32_t* seg, int32_t a_silu,
@@ -397,6 +411,21 @@ mmdit_status rf_make_xt(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, 
 mmdit_status rf_loss(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* v,
                      const void* z, const void* eps, float* sse, float* loss, void* ws,
                      size_t ws_bytes, mmdit_stream stream);
+
+/* Negative-aware flow-matching loss of the post-training stage ([blog]
+ * 2.2(4), the Diffusion-NFT objective: a per-sample reward r in [0, 1]
+ * weighs the squared error of a positive-policy velocity, 1 - r that of a
+ * negative-policy velocity, both against the target velocity):
+ *   sse[b] = r[b] ||v_pos - (z - eps)||^2 + (1 - r[b]) ||v_neg - (z - eps)||^2
+ * over sample b's target rows, loss[0] = mean_b sse[b] / (tgt_len_b * C).
+ * The target velocity is the base objective's z - eps (same straight path);
+ * how v_pos and v_neg are formed from the model is the caller's (the pages
+ * do not define it).  v_pos, v_neg [n_tgt, C] and z, eps [n_img, C] in dtype;
+ * r [B] float32 device.  Same workspace, reduction order and errors as
+ * rf_loss; r[b] = 1 for every b gives rf_loss(v_pos) bit for bit. */
+mmdit_status rf_nft_loss(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* v_pos,
+                         const void* v_neg, const void* z, const void* eps, const float* r, float* sse,
+                         float* loss, void* ws, size_t ws_bytes, mmdit_stream stream);
 
 /* Packed-CFG combine + Euler step ([hyper] 实验 and [blog] 2.2(3): cond and
  * uncond in one packed forward; [blog] 5: integrate the velocity ODE from

@@ -99,20 +99,26 @@ def rope_bands(head_dim):
     return (head_dim // 4, 3 * head_dim // 8, 3 * head_dim // 8)
 
 
-def rope_angles(pos, head_dim, theta=THETA):
-    """Angle of every rotation pair [n, head_dim/2] for positions pos [n, 3] (R7)."""
+def rope_angles(pos, head_dim, theta=THETA, bands=None):
+    """Angle of every rotation pair [n, head_dim/2] for positions pos [n, 3] (R7).
+
+    bands: the (frame, row, col) band widths, default R7's.
+    """
     pos = np.asarray(pos, np.float64).reshape(-1, 3)
+    bands = rope_bands(head_dim) if bands is None else tuple(bands)
+    if sum(bands) != head_dim or any(b % 2 for b in bands):
+        raise ValueError("band widths must be even and sum to head_dim")
     cols = []
-    for axis, width in enumerate(rope_bands(head_dim)):
+    for axis, width in enumerate(bands):
         for j in range(width // 2):
             cols.append(pos[:, axis] * theta ** (-2.0 * j / width))
     return np.stack(cols, axis=1)
 
 
-def apply_rope(x, pos, theta=THETA):
+def apply_rope(x, pos, theta=THETA, bands=None):
     """Rotate pairs (2j, 2j+1) of every head of x [n, heads, d] (R7)."""
     x = np.asarray(x, np.float64)
-    ang = rope_angles(pos, x.shape[-1], theta)[:, None, :]      # [n, 1, d/2]
+    ang = rope_angles(pos, x.shape[-1], theta, bands)[:, None, :]      # [n, 1, d/2]
     xe, xo = x[..., 0::2], x[..., 1::2]
     out = np.empty_like(x)
     out[..., 0::2] = xe * np.cos(ang) - xo * np.sin(ang)

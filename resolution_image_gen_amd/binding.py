@@ -14,7 +14,7 @@ __all__ = [
     "MmditError", "Pack", "Dims", "lib_path", "pack_plan", "pack", "pack_gather",
     "workspace_size", "workspace_layout", "cond", "modulation", "embed", "block_fwd",
     "rms_modulate", "qk_norm_rope", "attention", "linear", "final", "rf_make_xt",
-    "rf_loss", "rf_euler_step", "rf_pack_latent", "EPI_STORE", "EPI_STORE_F32", "EPI_GELU",
+    "rf_loss", "rf_nft_loss", "rf_euler_step", "rf_pack_latent", "EPI_STORE", "EPI_STORE_F32", "EPI_GELU",
     "EPI_GATED_RES", "MAX_SAMPLES",
 ]
 
@@ -50,8 +50,8 @@ class _PackT(ctypes.Structure):
 
 class _DimsT(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("heads", _i32), ("head_dim", _i32), ("mlp", _i32),
-                ("c_lat", _i32), ("d_txt", _i32), ("t_dim", _i32), ("rope_theta", _f32),
-                ("eps", _f32), ("dtype", _i32)]
+                ("c_lat", _i32), ("d_txt", _i32), ("t_dim", _i32), ("rope_dims", _i32 * 3),
+                ("rope_theta", _f32), ("eps", _f32), ("dtype", _i32)]
 
 
 class _StreamW(ctypes.Structure):
@@ -115,6 +115,7 @@ def _load():
         "mmdit_final_mod": (_i32, [D, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_make_xt": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "rf_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "rf_nft_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_euler_step": (_i32, [P, _i32, _i32, _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _vp]),
         "rf_pack_latent": (_i32, [P, _i32, _i32, _vp, _i32, _i32, _vp, _vp]),
         "mmdit_timing_enable": (_i32, [_i32]),
@@ -160,7 +161,7 @@ class Dims:
         self.d = d
         self.dtype = dtype
         self.c = _DimsT(d.hidden, d.heads, d.head_dim, d.mlp, d.c_lat, d.d_txt, d.t_dim,
-                        d.rope_theta, d.eps, BF16 if dtype == "bf16" else F32)
+                        (_i32 * 3)(*d.bands), d.rope_theta, d.eps, BF16 if dtype == "bf16" else F32)
 
     @property
     def torch_dtype(self):
@@ -412,6 +413,11 @@ def rf_make_xt(pk, z, eps, t, zt, stream=None):
 def rf_loss(pk, v, z, eps, sse, loss, ws, stream=None):
     _ck(_lib.rf_loss(pk.ref, _dt(v), v.shape[-1], _p(v), _p(z), _p(eps), _p(sse), _p(loss), _p(ws),
                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rf_nft_loss(pk, v_pos, v_neg, z, eps, r, sse, loss, ws, stream=None):
+    _ck(_lib.rf_nft_loss(pk.ref, _dt(v_pos), v_pos.shape[-1], _p(v_pos), _p(v_neg), _p(z), _p(eps), _p(r),
+                         _p(sse), _p(loss), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rf_euler_step(pk, v, cond_b, uncond_b, guidance, t_cur, t_next, z, zt_next=None, stream=None):

@@ -18,6 +18,12 @@ class Dims:
     t_dim: int = 256
     rope_theta: float = 10000.0
     eps: float = 1e-6
+    rope_dims: tuple = None          # (frame, row, col) band widths; None: (d/4, 3d/8, 3d/8)
+
+    @property
+    def bands(self):
+        d = self.head_dim
+        return tuple(self.rope_dims) if self.rope_dims is not None else (d // 4, 3 * d // 8, 3 * d // 8)
 
 
 @dataclass(frozen=True)

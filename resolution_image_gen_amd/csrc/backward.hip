@@ -674,8 +674,8 @@ mmdit_status norm_bwd2_impl(mmdit_dtype dt, int32_t H, float eps, const NormBwdS
 
 int64_t qk_bwd_blocks(int64_t n_rows) { return cdiv(n_rows, kQkRows); }
 
-mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkBwdSpec* p,
-                          int n, hipStream_t s) {
+mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_t* widths, float theta, float eps,
+                          const QkBwdSpec* p, int n, hipStream_t s) {
   QkBwdBatch bt;
   memset(&bt, 0, sizeof(bt));
   bt.heads = heads;
@@ -694,7 +694,6 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta,
   }
   bt.split = blocks[0];
   RopeTabB tab;
-  const int widths[3] = {D / 4, 3 * D / 8, 3 * D / 8};
   int pr = 0;
   for (int ax = 0; ax < 3; ++ax)
     for (int j = 0; j < widths[ax] / 2; ++j, ++pr) {

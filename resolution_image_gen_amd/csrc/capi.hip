@@ -88,11 +88,12 @@ mmdit_status pack_impl(const mmdit_sample*, int32_t, mmdit_pack_t*, hipStream_t)
 mmdit_status gather_impl(const mmdit_pack_t*, int32_t, const void* const*, int32_t, mmdit_dtype, void*, hipStream_t);
 mmdit_status make_xt_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const float*, void*, hipStream_t);
 mmdit_status loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, void*, size_t, hipStream_t);
+mmdit_status nft_loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, const void*, const float*, float*, float*, void*, size_t, hipStream_t);
 mmdit_status loss_grad_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, void*, hipStream_t);
 mmdit_status euler_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, int32_t, int32_t, float, float, float, float*, void*, hipStream_t);
 mmdit_status pack_latent_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const float*, int32_t, int32_t, void*, hipStream_t);
 mmdit_status rms_modulate_impl(mmdit_dtype, int64_t, int32_t, const void*, const int32_t*, const int32_t*, const float*, int64_t, int64_t, int64_t, void*, float, hipStream_t);
-mmdit_status qk_norm_rope_impl(mmdit_dtype, int64_t, int32_t, int32_t, void*, const int32_t*, const float*, const float*, float, float, hipStream_t);
+mmdit_status qk_norm_rope_impl(mmdit_dtype, int64_t, int32_t, int32_t, const int32_t*, void*, const int32_t*, const float*, const float*, float, float, hipStream_t);
 mmdit_status temb_impl(mmdit_dtype, int32_t, int32_t, const float*, void*, hipStream_t);
 mmdit_status attention_impl(mmdit_dtype, const mmdit_pack_t*, int32_t, int32_t, const void*, const void*, void*, void*, void*, size_t, hipStream_t, float* lse = nullptr);
 int64_t attention_vt_elems(const mmdit_pack_t*, int32_t);
@@ -121,6 +122,12 @@ mmdit_status check_dims(const mmdit_dims* d, const char* who) {
       d->d_txt % 64 || d->t_dim % 16 || d->hidden > 8192) {
     set_error("%s: unsupported dims (head_dim in {64,128}; hidden, mlp, c_lat, d_txt multiples of 64, "
               "hidden <= 8192; t_dim multiple of 16)", who);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  const int32_t* rd = d->rope_dims;
+  if (rd[0] < 0 || rd[1] < 0 || rd[2] < 0 || (rd[0] | rd[1] | rd[2]) & 1 || rd[0] + rd[1] + rd[2] != d->head_dim) {
+    set_error("%s: rope_dims (%d, %d, %d) must be even and sum to head_dim=%d", who, rd[0], rd[1], rd[2],
+              d->head_dim);
     return MMDIT_E_UNSUPPORTED;
   }
   return MMDIT_OK;
@@ -423,7 +430,7 @@ mmdit_status mmdit_qk_norm_rope(const mmdit_dims* d, int64_t n_rows, void* qkv, 
   MMDIT_TRY(need(qkv, who, "qkv"));
   MMDIT_TRY(need(g_q, who, "g_q"));
   MMDIT_TRY(need(g_k, who, "g_k"));
-  return qk_norm_rope_impl(d->dtype, n_rows, d->heads, d->head_dim, qkv, pos, g_q, g_k, d->rope_theta, d->eps,
+  return qk_norm_rope_impl(d->dtype, n_rows, d->heads, d->head_dim, d->rope_dims, qkv, pos, g_q, g_k, d->rope_theta, d->eps,
                            (hipStream_t)stream);
 }
 
@@ -475,6 +482,11 @@ mmdit_status mmdit_linear(mmdit_dtype dt, int64_t M, int32_t N, int32_t K, const
     if (gate_stride < N) {
       set_error("%s: gate_stride %lld < N %d", who, (long long)gate_stride, N);
       return MMDIT_E_INVALID;
+    }
+    // the epilogues read the gate as 16-byte vectors at gate + seg * gate_stride + n
+    if (gate_stride % 4) {
+      set_error("%s: gate_stride %lld is not a multiple of 4 floats", who, (long long)gate_stride);
+      return MMDIT_E_UNSUPPORTED;
     }
   }
   LinearArgs a = mk(M, N, K, A, W, Y, epilogue);
@@ -614,7 +626,7 @@ mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, con
   // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
   {
     QkArgs q[2] = {{qkv, pk->pos_img, w->img.g_q, w->img.g_k, ni}, {qkv_t, nullptr, w->txt.g_q, w->txt.g_k, nt}};
-    MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_theta, d->eps, q, 2, s));
+    MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_dims, d->rope_theta, d->eps, q, 2, s));
   }
   // o = block-diagonal joint attention
   MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s,
@@ -1053,7 +1065,7 @@ mmdit_status block_bwd_impl(const mmdit_dims* d, const mmdit_block_w* w, const m
                        g->img.g_q, g->img.g_k, ni},
                       {rows(Lb.dqkv, 1, 3 * H), srows(S.qk_raw, 1, 2 * H), nullptr, w->txt.g_q, w->txt.g_k,
                        gp + qk_bwd_blocks(ni) * 2 * D, g->txt.g_q, g->txt.g_k, nt}};
-    MMDIT_TRY(qk_bwd2_impl(dt, d->heads, D, d->rope_theta, d->eps, q, 2, s));
+    MMDIT_TRY(qk_bwd2_impl(dt, d->heads, D, d->rope_dims, d->rope_theta, d->eps, q, 2, s));
   }
   // QKV projection: dW_qkv = dqkv^T h1, dh1 = dqkv W_qkv
   {
@@ -1452,6 +1464,12 @@ mmdit_status rf_make_xt(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const
 mmdit_status rf_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
                      const void* eps, float* sse, float* loss, void* ws, size_t ws_bytes, mmdit_stream stream) {
   return loss_impl(pk, dt, C, v, z, eps, sse, loss, ws, ws_bytes, (hipStream_t)stream);
+}
+
+mmdit_status rf_nft_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v_pos, const void* v_neg,
+                         const void* z, const void* eps, const float* r, float* sse, float* loss, void* ws,
+                         size_t ws_bytes, mmdit_stream stream) {
+  return nft_loss_impl(pk, dt, C, v_pos, v_neg, z, eps, r, sse, loss, ws, ws_bytes, (hipStream_t)stream);
 }
 
 mmdit_status rf_euler_step(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, int32_t cond_b,

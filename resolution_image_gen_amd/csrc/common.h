@@ -158,8 +158,9 @@ struct QkArgs {
   const float* g_k;
   int64_t n_rows;
 };
-mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkArgs* a,
-                                int n, hipStream_t s);
+// widths: the RoPE band widths (frame, row, col), even, summing to D.
+mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_t* widths, float theta,
+                                float eps, const QkArgs* a, int n, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // [n, C] (row stride ldx) -> [C, npad] with zero columns n..npad; op 0 copy,
@@ -231,8 +232,8 @@ struct QkBwdSpec {
   int64_t n;
 };
 int64_t qk_bwd_blocks(int64_t n_rows);
-mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps, const QkBwdSpec* p,
-                          int n, hipStream_t s);
+mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_t* widths, float theta, float eps,
+                          const QkBwdSpec* p, int n, hipStream_t s);
 
 // dW_mod = d_mod^T SiLU(c) per stream ([6H, H] float32) and
 // dc += (d_mod W_mod) * SiLU'(c) summed over both streams.

@@ -74,6 +74,43 @@ __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
   }
 }
 
+// Per-target-row value of the negative-aware loss (blog close-reading,
+// 2.2(4), the Diffusion-NFT objective): r_b ||v+ - (z - eps)||^2 +
+// (1 - r_b) ||v- - (z - eps)||^2 over the row, r_b the reward of the row's
+// sample.  The same lane layout and summation order as row_sse_kernel, so
+// r_b = 1 gives exactly row_sse_kernel's value for v = v+.
+template <typename T>
+__global__ void row_nft_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ vp, const T* __restrict__ vn,
+                               const T* __restrict__ z, const T* __restrict__ eps, const float* __restrict__ r,
+                               const int32_t* __restrict__ seg, const int32_t* __restrict__ tgt_row,
+                               float* __restrict__ row_val) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int64_t rstep = ((int64_t)gridDim.x * blockDim.x) >> 4;
+  for (int64_t row = row0; row < n_tgt; row += rstep) {
+    float ap = 0.f, an = 0.f;
+    const int64_t src = tgt_row[row];
+    for (int c8 = lane16; c8 < (C >> 3); c8 += 16) {
+      float pv[8], nv[8], zv[8], ev[8];
+      Vec8<T>::load(vp + row * C + c8 * 8, pv);
+      Vec8<T>::load(vn + row * C + c8 * 8, nv);
+      Vec8<T>::load(z + src * C + c8 * 8, zv);
+      Vec8<T>::load(eps + src * C + c8 * 8, ev);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float tg = zv[i] - ev[i];
+        const float dp = pv[i] - tg, dn = nv[i] - tg;
+        ap += dp * dp;
+        an += dn * dn;
+      }
+    }
+    ap = group_sum(ap, 16);
+    an = group_sum(an, 16);
+    const float rb = r[seg[src]];
+    if (lane16 == 0) row_val[row] = rb * ap + (1.0f - rb) * an;
+  }
+}
+
 // dL/dv of the loss mean_b SSE_b / (tgt_len_b C): 2 (v - (z - eps)) / (B tgt_len_b C)
 // on every target row (one thread per 8 channels).
 template <typename T>
@@ -283,6 +320,42 @@ mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const 
   }
   MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse,
                      sse, loss);
+  return launch_check("loss_finalize_kernel", s);
+}
+
+mmdit_status nft_loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* vp, const void* vn,
+                           const void* z, const void* eps, const float* r, float* sse, float* loss, void* ws,
+                           size_t ws_bytes, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_nft_loss"));
+  MMDIT_TRY(check_c(C, "rf_nft_loss"));
+  if (!sse && pk->B > 0) {
+    set_error("rf_nft_loss: sse is NULL");
+    return MMDIT_E_INVALID;
+  }
+  if (!loss || (pk->n_tgt > 0 && (!vp || !vn || !z || !eps || !r || !pk->tgt_row || !pk->seg_img))) {
+    set_error("rf_nft_loss: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  if (!ws || ws_bytes < (size_t)pk->n_tgt * 4 + 4) {
+    set_error("rf_nft_loss: workspace needs %zu bytes, got %zu", (size_t)pk->n_tgt * 4 + 4, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  if (((uintptr_t)ws & 15) != 0) {
+    set_error("rf_nft_loss: workspace is not 16-byte aligned");
+    return MMDIT_E_UNSUPPORTED;
+  }
+  float* row_val = static_cast<float*>(ws);
+  if (pk->n_tgt > 0) {
+    int g = grid_for(pk->n_tgt * 16, 256);
+    if (dt == MMDIT_BF16)
+      MMDIT_LAUNCH(row_nft_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, (const bf16*)vp, (const bf16*)vn,
+                   (const bf16*)z, (const bf16*)eps, r, pk->seg_img, pk->tgt_row, row_val);
+    else
+      MMDIT_LAUNCH(row_nft_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, (const float*)vp,
+                   (const float*)vn, (const float*)z, (const float*)eps, r, pk->seg_img, pk->tgt_row, row_val);
+    MMDIT_TRY(launch_check("row_nft_kernel", s));
+  }
+  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_val, sse, loss);
   return launch_check("loss_finalize_kernel", s);
 }
 

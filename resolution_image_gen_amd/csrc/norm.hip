@@ -268,8 +268,8 @@ mmdit_status rms_modulate_impl(mmdit_dtype dt, int64_t n, int32_t H, const void*
   return rms_modulate2_impl(dt, H, eps, &a, 1, s);
 }
 
-mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float theta, float eps,
-                                const QkArgs* a, int n, hipStream_t s) {
+mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_t* widths, float theta,
+                                float eps, const QkArgs* a, int n, hipStream_t s) {
   if (D != 64 && D != 128) {
     set_error("qk_norm_rope: head_dim=%d unsupported (64 or 128)", D);
     return MMDIT_E_UNSUPPORTED;
@@ -290,9 +290,9 @@ mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float 
   bt.split = bt.p[0].n_rows;
   bt.heads = heads;
   bt.eps = eps;
-  // bands (frame, row, col) = (D/4, 3D/8, 3D/8) dims = (D/8, 3D/16, 3D/16) pairs
+  // per rotation pair: its axis and frequency; bands (frame, row, col) of the
+  // given widths from dimension 0
   RopeTab tab;
-  const int widths[3] = {D / 4, 3 * D / 8, 3 * D / 8};
   int p = 0;
   for (int ax = 0; ax < 3; ++ax)
     for (int j = 0; j < widths[ax] / 2; ++j, ++p) {
@@ -307,11 +307,11 @@ mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, float 
   return dt == MMDIT_BF16 ? launch_qk<bf16>(bt, total, D, tab, s) : launch_qk<float>(bt, total, D, tab, s);
 }
 
-mmdit_status qk_norm_rope_impl(mmdit_dtype dt, int64_t n, int32_t heads, int32_t D, void* qkv,
-                               const int32_t* pos, const float* gq, const float* gk, float theta,
+mmdit_status qk_norm_rope_impl(mmdit_dtype dt, int64_t n, int32_t heads, int32_t D, const int32_t* widths,
+                               void* qkv, const int32_t* pos, const float* gq, const float* gk, float theta,
                                float eps, hipStream_t s) {
   QkArgs a = {qkv, pos, gq, gk, n};
-  return qk_norm_rope2_impl(dt, heads, D, theta, eps, &a, 1, s);
+  return qk_norm_rope2_impl(dt, heads, D, widths, theta, eps, &a, 1, s);
 }
 
 mmdit_status temb_impl(mmdit_dtype dt, int32_t B, int32_t t_dim, const float* t, void* emb,

@@ -64,6 +64,19 @@ def _run_block(B, d, dtype, samples, nb, x_img, x_txt, c):
     return dims, pk, xi, xt, ws
 
 
+def _delta_tol(tol, dtype, x_out, delta):
+    """Bound for the branch delta x_out - x_in of a block: the bar, plus the
+    storage rounding of the residual stream.  The block stores x twice in the
+    model dtype (after the attention branch and after the MLP branch), each a
+    correctly rounded fused x + gate * branch, so the delta carries up to two
+    half-ulps of |x| (unit roundoff 2^-9 in bf16, 2^-24 in float32) that no
+    arithmetic can remove; relative to max|delta| that is
+    2 u max|x_out| / max|delta|, large when the branches are small against x
+    (N(0, 0.02) weights), negligible for the stress recipe."""
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    return tol + 2 * u * float(np.max(np.abs(x_out))) / float(np.max(np.abs(delta)))
+
+
 def _ws_view(ws, off, rows, cols, dtype):
     es = 4 if dtype == "f32" else 2
     t = ws[off:off + rows * cols * es].view(_tdt(dtype))
@@ -99,12 +112,13 @@ def test_block_fwd_vs_oracle(B, case):
     ni, nt = ref["cu_img"][-1], ref["cu_txt"][-1]
     got_i = to_np(xi)
     assert_close("x_out_img", got_i, want["x_out_img"], tol)
-    assert_close("delta_img (x_out - x_in)", got_i - x_img, want["x_out_img"] - x_img, tol if recipe == "stress"
-                 else 5 * tol)
+    dref = want["x_out_img"] - x_img
+    assert_close("delta_img (x_out - x_in)", got_i - x_img, dref, _delta_tol(tol, dtype, want["x_out_img"], dref))
     if nt:
         got_t = to_np(xt)[:nt]
         assert_close("x_out_txt", got_t, want["x_out_txt"], tol)
-        assert_close("delta_txt", got_t - x_txt, want["x_out_txt"] - x_txt, tol if recipe == "stress" else 5 * tol)
+        dref = want["x_out_txt"] - x_txt
+        assert_close("delta_txt", got_t - x_txt, dref, _delta_tol(tol, dtype, want["x_out_txt"], dref))
     # intermediates kept in the workspace
     L = B.workspace_layout(dims, pk)
     N = ni + nt
@@ -119,7 +133,9 @@ def test_block_fwd_vs_oracle(B, case):
         assert_close(f"q_{s}", qkv[r0:r1, :H], want[f"q_{s}"].reshape(n, H), tol)
         assert_close(f"k_{s}", qkv[r0:r1, H:2 * H], want[f"k_{s}"].reshape(n, H), tol)
         assert_close(f"v_{s}", qkv[r0:r1, 2 * H:], want[f"v_{s}"].reshape(n, H), tol)
-        assert_close(f"o_{s}", o[r0:r1], want[f"o_{s}"].reshape(n, H), tol)
+        # attention output: normwise, and row-wise per (token, head)
+        assert_close(f"o_{s}", o[r0:r1].reshape(n * d.heads, d.head_dim),
+                     want[f"o_{s}"].reshape(n * d.heads, d.head_dim), tol, rows=True)
         assert_close(f"h2_{s}", h2[r0:r1], want[f"h2_{s}"], tol)
         assert_close(f"u_{s}", u[r0:r1], want[f"u_{s}"], tol)
     mod_i = ws[L["mod_img"]:L["mod_img"] + len(samples) * 6 * H * 4].view(torch.float32).cpu().numpy()
@@ -215,9 +231,9 @@ def test_block_full_size_sampled_rows(B, name):
         i0, t0 = ref["cu_img"][b], ref["cu_txt"][b]
         assert_close(f"x_out_img[b={b}]", got_i[i0 + irows], want["x_out_img"], TOL[dtype])
         assert_close(f"delta_img[b={b}]", got_i[i0 + irows] - x_img[i0 + irows],
-                     want["x_out_img"] - x_img[i0 + irows], TOL[dtype])
+                     want["x_out_img"] - x_img[i0 + irows], TOL[dtype], rows=True)
         assert_close(f"delta_txt[b={b}]", got_t[t0 + trows] - x_txt[t0 + trows],
-                     want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype])
+                     want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype], rows=True)
 
 
 def test_block_last_round_split_ragged_tail():
@@ -245,9 +261,9 @@ def test_block_last_round_split_ragged_tail():
         want = OB.block_forward_rows(x_img, x_txt, c, nbf, ref, d.heads, b, irows, trows)
         i0, t0 = ref["cu_img"][b], ref["cu_txt"][b]
         assert_close(f"delta_img[b={b}]", got_i[i0 + irows] - x_img[i0 + irows],
-                     want["x_out_img"] - x_img[i0 + irows], TOL[dtype])
+                     want["x_out_img"] - x_img[i0 + irows], TOL[dtype], rows=True)
         assert_close(f"delta_txt[b={b}]", got_t[t0 + trows] - x_txt[t0 + trows],
-                     want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype])
+                     want["x_out_txt"] - x_txt[t0 + trows], TOL[dtype], rows=True)
 
 
 def test_block_sample_order_invariant_with_last_round_split():

@@ -93,6 +93,35 @@ def test_qk_norm_rope(B, case):
         assert np.array_equal(got[:, 2 * H:], qkv[:, 2 * H:].astype(np.float64)), "v must pass through"
 
 
+@pytest.mark.parametrize("bands", [(0, 64, 64), (64, 32, 32), (128, 0, 0)])
+def test_qk_norm_rope_other_bands(B, bands):
+    """Band widths other than the default split (frame, row, col) =
+    (32, 48, 48): the rotation table follows mmdit_dims.rope_dims."""
+    import dataclasses
+
+    from resolution_image_gen_amd import configs as CF
+
+    d = dataclasses.replace(CF.B4, rope_dims=bands)
+    samples = [(5, 7, 2, 3), (16, 9, 1, 4)]
+    ref = oracle_pack(samples)
+    dims = B.Dims(d, "f32")
+    pk = B.pack(samples)
+    H, D, heads = d.hidden, d.head_dim, d.heads
+    n = ref["cu_img"][-1]
+    qkv = S.normal((n, 3 * H), 1.0, "f32", "k3b", str(bands), "qkv")
+    gq = 1 + 0.1 * S.normal((D,), 1.0, "f32", "k3b", str(bands), "gq")
+    gk = np.ones(D, np.float32)
+    t = _dev(qkv, "f32")
+    B.qk_norm_rope(dims, t, pk.t["pos_img"], torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda())
+    q = OB.apply_rope(OB.rms_norm(qkv[:, :H].reshape(n, heads, D).astype(np.float64)) * gq, ref["pos_img"],
+                      bands=bands)
+    k = OB.apply_rope(OB.rms_norm(qkv[:, H:2 * H].reshape(n, heads, D).astype(np.float64)) * gk, ref["pos_img"],
+                      bands=bands)
+    got = to_np(t)
+    assert_close(f"q[{bands}]", got[:, :H], q.reshape(n, H), 1e-5)
+    assert_close(f"k[{bands}]", got[:, H:2 * H], k.reshape(n, H), 1e-5)
+
+
 @pytest.mark.parametrize("case", list(CASES))
 def test_attention(B, case):
     d, dtype, samples = CASES[case]

@@ -152,6 +152,42 @@ def test_rf_loss(B, dtype, name):
         assert torch.all(sse == 0) and loss.item() == 0.0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged"])
+def test_rf_nft_loss(B, dtype, name):
+    """Negative-aware loss against the oracle's definition; rewards of 1 give
+    rf_loss(v_pos) bit for bit, rewards of 0 rf_loss(v_neg)."""
+    samples = SAMPLE_SETS[name]
+    C = 64
+    ref, z, eps, _ = _rf_inputs(samples, C, dtype, seed=2)
+    from resolution_image_gen_amd import synthetic as S
+
+    n_tgt = ref["cu_tgt"][-1]
+    vp = S.normal((n_tgt, C), 1.0, dtype, "nft", name, "v_pos")
+    vn = S.normal((n_tgt, C), 1.0, dtype, "nft", name, "v_neg")
+    r = S.uniform((len(samples),), "f32", "nft", name, "r")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    pk = B.pack(samples)
+    vpd, vnd, zd, ed = (torch.from_numpy(a).cuda().to(dt) for a in (vp, vn, z, eps))
+    rd = torch.from_numpy(r).cuda()
+    sse = torch.empty(pk.B, device="cuda")
+    loss = torch.empty(1, device="cuda")
+    ws = torch.empty(pk.n_tgt * 4 + 256, dtype=torch.uint8, device="cuda")
+    print(f"rf_nft_loss {name} {dtype}: {pk.B} samples, {pk.n_tgt} target rows", flush=True)
+    B.rf_nft_loss(pk, vpd, vnd, zd, ed, rd, sse, loss, ws)
+    want_sse, want_loss = OF.nft_loss(vp, vn, z, eps, r, ref)
+    assert_close(f"nft sse[{name},{dtype}]", to_np(sse), want_sse, 1e-5)
+    assert abs(loss.item() - want_loss) <= 1e-5 * abs(want_loss)
+    first = sse.clone()
+    B.rf_nft_loss(pk, vpd, vnd, zd, ed, rd, sse, loss, ws)
+    assert torch.equal(sse, first)                      # deterministic, bitwise
+    sse2, loss2 = torch.empty_like(sse), torch.empty_like(loss)
+    for rv, vd in ((1.0, vpd), (0.0, vnd)):
+        B.rf_nft_loss(pk, vpd, vnd, zd, ed, torch.full_like(rd, rv), sse, loss, ws)
+        B.rf_loss(pk, vd, zd, ed, sse2, loss2, ws)
+        assert torch.equal(sse, sse2) and torch.equal(loss, loss2), rv
+
+
 def test_rf_loss_past_the_launch_grid_cap(B):
     """More target rows (2 x 8,388,608 + 4,096 > 2^24) than one 16-lane group
     per row of the largest grid the host launches: the groups stride over the

@@ -51,7 +51,7 @@ int main(void) {
          sizeof(mmdit_dims), sizeof(mmdit_sample), sizeof(mmdit_block_w));
   F(mmdit_pack_t, n_img) F(mmdit_pack_t, cu_txt) F(mmdit_pack_t, tgt_row) F(mmdit_pack_t, h_cu_txt)
   F(mmdit_pack_t, h_cu_img) F(mmdit_pack_t, h_cu_tgt) F(mmdit_pack_t, h_frames)
-  F(mmdit_dims, rope_theta) F(mmdit_dims, dtype) F(mmdit_block_w, txt)
+  F(mmdit_dims, rope_dims) F(mmdit_dims, rope_theta) F(mmdit_dims, dtype) F(mmdit_block_w, txt)
   return 0;
 }
 """
@@ -71,6 +71,7 @@ def test_struct_layout_matches_binding(B):
     assert c["mmdit_block_w"] == ctypes.sizeof(B._BlockW)
     for f in ("n_img", "cu_txt", "tgt_row", "h_cu_txt", "h_cu_img", "h_cu_tgt", "h_frames"):
         assert c[f"mmdit_pack_t.{f}"] == getattr(B._PackT, f).offset, f
+    assert c["mmdit_dims.rope_dims"] == B._DimsT.rope_dims.offset
     assert c["mmdit_dims.rope_theta"] == B._DimsT.rope_theta.offset
     assert c["mmdit_dims.dtype"] == B._DimsT.dtype.offset
     assert c["mmdit_block_w.txt"] == B._BlockW.txt.offset
@@ -120,8 +121,10 @@ def _dims(B, **kw):
 
     d = dict(CF.B4.__dict__)
     d.update(kw)
+    D = d["head_dim"]
+    rope = d.get("rope", (D // 4, 3 * D // 8, 3 * D // 8))
     return B._DimsT(d["hidden"], d["heads"], d["head_dim"], d["mlp"], d["c_lat"], d["d_txt"], d["t_dim"],
-                    d["rope_theta"], d["eps"], 1)
+                    (ctypes.c_int32 * 3)(*rope), d["rope_theta"], d["eps"], 1)
 
 
 def test_validation_errors_before_launch(B):
@@ -166,10 +169,23 @@ def test_validation_errors_before_launch(B):
     # linear shape errors
     assert lib.mmdit_linear(1, -1, 64, 64, fake, fake, fake, 0, None, 0, None, 0, None) == -1
     assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, None, 0, None, 0, None) == -1
+    # gate rows are read as 16-byte vectors: the stride must be a multiple of 4 floats
+    assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, fake, 66, fake, 0, None) == -3
+    assert b"gate_stride" in lib.mmdit_last_error()
+    assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, fake, 60, fake, 0, None) == -1
     # pack: too many samples
     arr = (B._Sample * 300)(*[B._Sample(1, 1, 1, 0)] * 300)
     assert lib.mmdit_pack(arr, 300, ctypes.byref(B._PackT()), None) == -1
     assert lib.mmdit_workspace_size(ctypes.byref(_dims(B, head_dim=96, heads=32)), P) == 0
+    # RoPE bands: even widths summing to head_dim, anything else is rejected
+    for rope in ((32, 48, 50), (33, 47, 48), (-2, 66, 64), (32, 48, 46)):
+        bad = _dims(B, rope=rope)
+        assert lib.mmdit_qk_norm_rope(ctypes.byref(bad), 4, fake, fake, fake, fake, None) == -3, rope
+        assert b"rope_dims" in lib.mmdit_last_error()
+        assert lib.mmdit_block_fwd(ctypes.byref(bad), ctypes.byref(w), P, fake, fake, fake, fake, need, None) == -3
+        assert lib.mmdit_workspace_size(ctypes.byref(bad), P) == 0
+    for rope in ((0, 64, 64), (128, 0, 0), (64, 32, 32)):   # other even splits are computed
+        assert lib.mmdit_workspace_size(ctypes.byref(_dims(B, rope=rope)), P) > 0
 
 
 def test_training_calls_validate_before_launch(B):

@@ -423,3 +423,29 @@ def test_final_layer_uses_each_samples_modulation():
     v = K.final_layer(x, c, w_fmod, _selector(1, H, [0]), pk)
     n0 = 2.0 / math.sqrt(4.0 + 1e-6)
     np.testing.assert_allclose(v[:, 0], [3 * n0 + 0.5, n0], rtol=0, atol=1e-13)
+
+
+def test_rope_other_band_widths():
+    # a frame band of width 0 leaves the frame id unused (2D RoPE); the row
+    # band's pair 0 turns by the raw row id whatever the split
+    pos = np.array([[3, 5, 7]])
+    a = K.rope_angles(pos, 8, bands=(0, 4, 4))
+    np.testing.assert_allclose(a[0], [5, 5 * 100.0 ** -1, 7, 7 * 100.0 ** -1], rtol=1e-14)
+    b = K.rope_angles(pos, 8, bands=(2, 2, 4))
+    np.testing.assert_allclose(b[0], [3, 5, 7, 7 * 100.0 ** -1], rtol=1e-14)
+    with pytest.raises(ValueError):
+        K.rope_angles(pos, 8, bands=(2, 2, 2))
+    with pytest.raises(ValueError):
+        K.rope_angles(pos, 8, bands=(1, 3, 4))
+
+
+def test_row_wise_metric_catches_a_wrong_small_row():
+    from helpers import rel_err, rel_err_rows
+
+    r = np.random.default_rng(30)
+    ref = r.standard_normal((8, 16))
+    ref[3] *= 0.02                          # a small-magnitude row
+    got = ref.copy()
+    got[3] *= 1.5                           # 50% off on that row only
+    assert rel_err(got, ref) < 2e-2 < rel_err_rows(got, ref)
+    assert rel_err_rows(ref, ref) == 0.0
