@@ -412,6 +412,19 @@ mmdit_status rf_loss(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, con
                      const void* z, const void* eps, float* sse, float* loss, void* ws,
                      size_t ws_bytes, mmdit_stream stream);
 
+/* rf_loss for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels, arguments, result bits and
+ * errors as rf_loss, with the per-row sums in a scratch array that the
+ * library holds in device memory (16 MiB + 16 B per device, until the process
+ * ends) instead of ws.  At most 4,194,304 target rows (n_tgt), else
+ * MMDIT_E_UNSUPPORTED.  Allocates nothing (no hipMalloc / hipFree).  Every
+ * call on one device shares that device's scratch: calls that overlap on one
+ * GPU (concurrent streams or threads) race and must be serialised by the
+ * caller. */
+mmdit_status rf_loss_noalloc(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* v,
+                             const void* z, const void* eps, float* sse, float* loss, mmdit_stream stream);
+
 /* Negative-aware flow-matching loss of the post-training stage ([blog]
  * 2.2(4), the Diffusion-NFT objective: a per-sample reward r in [0, 1]
  * weighs the squared error of a positive-policy velocity, 1 - r that of a

@@ -14,7 +14,7 @@ __all__ = [
     "MmditError", "Pack", "Dims", "lib_path", "pack_plan", "pack", "pack_gather",
     "workspace_size", "workspace_layout", "cond", "modulation", "embed", "block_fwd",
     "rms_modulate", "qk_norm_rope", "attention", "linear", "final", "rf_make_xt",
-    "rf_loss", "rf_nft_loss", "rf_euler_step", "rf_pack_latent", "EPI_STORE", "EPI_STORE_F32", "EPI_GELU",
+    "rf_loss", "rf_loss_noalloc", "rf_nft_loss", "rf_euler_step", "rf_pack_latent", "EPI_STORE", "EPI_STORE_F32", "EPI_GELU",
     "EPI_GATED_RES", "MAX_SAMPLES",
 ]
 
@@ -115,6 +115,7 @@ def _load():
         "mmdit_final_mod": (_i32, [D, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_make_xt": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "rf_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "rf_loss_noalloc": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
         "rf_nft_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_euler_step": (_i32, [P, _i32, _i32, _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _vp]),
         "rf_pack_latent": (_i32, [P, _i32, _i32, _vp, _i32, _i32, _vp, _vp]),
@@ -413,6 +414,11 @@ def rf_make_xt(pk, z, eps, t, zt, stream=None):
 def rf_loss(pk, v, z, eps, sse, loss, ws, stream=None):
     _ck(_lib.rf_loss(pk.ref, _dt(v), v.shape[-1], _p(v), _p(z), _p(eps), _p(sse), _p(loss), _p(ws),
                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rf_loss_noalloc(pk, v, z, eps, sse, loss, stream=None):
+    _ck(_lib.rf_loss_noalloc(pk.ref, _dt(v), v.shape[-1], _p(v), _p(z), _p(eps), _p(sse), _p(loss),
+                             _stream(stream)))
 
 
 def rf_nft_loss(pk, v_pos, v_neg, z, eps, r, sse, loss, ws, stream=None):

@@ -88,6 +88,7 @@ mmdit_status pack_impl(const mmdit_sample*, int32_t, mmdit_pack_t*, hipStream_t)
 mmdit_status gather_impl(const mmdit_pack_t*, int32_t, const void* const*, int32_t, mmdit_dtype, void*, hipStream_t);
 mmdit_status make_xt_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const float*, void*, hipStream_t);
 mmdit_status loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, void*, size_t, hipStream_t);
+mmdit_status loss_noalloc_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, hipStream_t);
 mmdit_status nft_loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, const void*, const float*, float*, float*, void*, size_t, hipStream_t);
 mmdit_status loss_grad_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, void*, hipStream_t);
 mmdit_status euler_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, int32_t, int32_t, float, float, float, float*, void*, hipStream_t);
@@ -1464,6 +1465,11 @@ mmdit_status rf_make_xt(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const
 mmdit_status rf_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
                      const void* eps, float* sse, float* loss, void* ws, size_t ws_bytes, mmdit_stream stream) {
   return loss_impl(pk, dt, C, v, z, eps, sse, loss, ws, ws_bytes, (hipStream_t)stream);
+}
+
+mmdit_status rf_loss_noalloc(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                             const void* eps, float* sse, float* loss, mmdit_stream stream) {
+  return loss_noalloc_impl(pk, dt, C, v, z, eps, sse, loss, (hipStream_t)stream);
 }
 
 mmdit_status rf_nft_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v_pos, const void* v_neg,

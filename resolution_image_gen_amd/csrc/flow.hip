@@ -8,7 +8,16 @@
 // All are HBM-bound streaming kernels over [rows, C] with 16-byte accesses.
 #include "common.h"
 
+#include <mutex>
+
 namespace mmdit {
+
+// Scratch of rf_loss_noalloc: the per-row sums of up to kNoAllocMaxRows
+// target rows (16 MiB + 16 B of float32 per device, held until the process
+// ends).  In host code `scratch` only names the symbol: kernels receive the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;
+static __device__ __align__(256) float scratch[kNoAllocMaxRows + 4];
 
 namespace {
 
@@ -357,6 +366,50 @@ mmdit_status nft_loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, co
   }
   MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_val, sse, loss);
   return launch_check("loss_finalize_kernel", s);
+}
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];   // device address of `scratch` per device
+}  // namespace
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+static mmdit_status scratch_address(void** out, const char* who) {
+  int dev = -1;
+  MMDIT_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kScratchDevices) {
+    set_error("%s: device %d beyond the %d devices the scratch table holds", who, dev, kScratchDevices);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MMDIT_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) {
+      set_error("%s: hipGetSymbolAddress returned NULL for the scratch array", who);
+      return MMDIT_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MMDIT_OK;
+}
+
+mmdit_status loss_noalloc_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                               const void* eps, float* sse, float* loss, hipStream_t s) {
+  MMDIT_TRY(check_pack(pk, "rf_loss_noalloc"));
+  if (pk->n_tgt > kNoAllocMaxRows) {
+    set_error("rf_loss_noalloc: %lld target rows exceed the scratch limit of %lld rows (use rf_loss with a "
+              "workspace)", (long long)pk->n_tgt, (long long)kNoAllocMaxRows);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  MMDIT_TRY(scratch_address(&ws, "rf_loss_noalloc"));
+  // every row sum the reduction reads is written by this call first, so the
+  // previous call's contents need no clearing
+  return loss_impl(pk, dt, C, v, z, eps, sse, loss, ws, (size_t)(kNoAllocMaxRows + 4) * sizeof(float), s);
 }
 
 static mmdit_status check_target_sample(const mmdit_pack_t* pk, int32_t b, const char* who) {

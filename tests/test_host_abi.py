@@ -166,6 +166,10 @@ def test_validation_errors_before_launch(B):
     assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, fake, n_tgt * 4 + 3, None) == -4
     assert lib.rf_loss(P, 1, 128, fake, fake, fake, fake, fake, ctypes.c_void_p((1 << 20) + 4), 1 << 20, None) == -3
     assert lib.rf_make_xt(P, 1, 12, fake, fake, fake, fake, None) == -3        # C % 8
+    # the workspace-free loss keeps its per-row sums in a fixed scratch of 2^22 rows
+    big = ctypes.byref(_fake_pack(B, [(2048, 2048, 1, 0), (1, 1, 1, 0)]))
+    assert lib.rf_loss_noalloc(big, 1, 128, fake, fake, fake, fake, fake, None) == -3
+    assert b"scratch" in lib.mmdit_last_error()
     # linear shape errors
     assert lib.mmdit_linear(1, -1, 64, 64, fake, fake, fake, 0, None, 0, None, 0, None) == -1
     assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, None, 0, None, 0, None) == -1
