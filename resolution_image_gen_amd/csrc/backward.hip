@@ -352,10 +352,7 @@ __global__ void __launch_bounds__(512) norm_bwd_kernel(NormBwdBatch bt) {
 }
 
 // ------------------------------------------------------- QK-norm + RoPE bwd
-struct RopeTabB {
-  float inv_freq[64];
-  int32_t axis[64];
-};
+typedef RopeTable RopeTabB;
 struct QkBwdProb {
   void* dqkv;           // [n, 3H] in: dq', dk' (and dv); out: dq, dk in place
   const void* raw;      // [n, 2H] q, k before the norm
@@ -694,16 +691,7 @@ mmdit_status qk_bwd2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_
   }
   bt.split = blocks[0];
   RopeTabB tab;
-  int pr = 0;
-  for (int ax = 0; ax < 3; ++ax)
-    for (int j = 0; j < widths[ax] / 2; ++j, ++pr) {
-      tab.axis[pr] = ax;
-      tab.inv_freq[pr] = (float)pow((double)theta, -2.0 * j / (double)widths[ax]);
-    }
-  for (; pr < 64; ++pr) {
-    tab.axis[pr] = 0;
-    tab.inv_freq[pr] = 0.f;
-  }
+  rope_table(&tab, widths, theta);
   const int64_t total = blocks[0] + blocks[1];
   if (total > 0) {
     dim3 g((unsigned)total), b(256);

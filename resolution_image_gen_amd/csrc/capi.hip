@@ -176,7 +176,7 @@ mmdit_status need(const void* p, const char* who, const char* name) {
 }
 
 struct Layout {
-  size_t mod_img, mod_txt, h, qkv, o, u, vt, end;
+  size_t mod_img, mod_txt, h, qkv, o, u, vt, rope, end;
 };
 
 Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -192,6 +192,7 @@ Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   L.o = o;       o = align256(o + N * H * es);
   L.u = o;       o = align256(o + N * (size_t)d->mlp * es);
   L.vt = o;      o = align256(o + (size_t)attention_vt_elems(pk, d->hidden) * es);
+  L.rope = o;    o = align256(o + (size_t)pk->n_img * d->head_dim * 4);   // (cos, sin) per image row and pair
   L.end = o;
   return L;
 }
@@ -608,29 +609,39 @@ mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, con
                     {x_txt, nullptr, pk->seg_txt, mod_t, h_t, nt, 6 * H, 0, H}};
     MMDIT_TRY(rms_modulate2_impl(dt, H, d->eps, r, 2, s));
   }
-  // qkv = h W_qkv^T
+  // qkv = h W_qkv^T, then QK-RMSNorm + RoPE of q and k (image rows at their
+  // (frame, row, col), text rows at the origin) in the projection's epilogue;
+  // training also keeps q and k before their norm
   {
-    LinearArgs a[2] = {mk(ni, 3 * H, H, h, w->img.w_qkv, qkv, MMDIT_EPI_STORE),
-                       mk(nt, 3 * H, H, h_t, w->txt.w_qkv, qkv_t, MMDIT_EPI_STORE)};
+    QkEpilogue qe;
+    qe.heads = d->heads;
+    qe.D = d->head_dim;
+    qe.eps = d->eps;
+    qe.theta = d->rope_theta;
+    for (int i = 0; i < 3; ++i) qe.widths[i] = d->rope_dims[i];
+    rope_table(&qe.tab, d->rope_dims, d->rope_theta);
+    const int epi = sv ? kEpiQkRopeAux : kEpiQkRope;
+    float* rope_cs = reinterpret_cast<float*>(base + L.rope);
+    MMDIT_TRY(rope_cs_impl(pk->pos_img, ni, d->head_dim, qe.tab, rope_cs, s));
+    LinearArgs a[2] = {mk(ni, 3 * H, H, h, w->img.w_qkv, qkv, epi), mk(nt, 3 * H, H, h_t, w->txt.w_qkv, qkv_t, epi)};
+    a[0].pos = pk->pos_img;
+    a[0].rope_cs = rope_cs;
+    a[1].pos = nullptr;
+    a[1].rope_cs = nullptr;
+    a[0].g_q = w->img.g_q;
+    a[0].g_k = w->img.g_k;
+    a[1].g_q = w->txt.g_q;
+    a[1].g_k = w->txt.g_k;
+    a[0].qk = a[1].qk = &qe;
+    if (sv) {
+      a[0].aux = sv + S->qk_raw;
+      a[1].aux = sv + S->qk_raw + ni * 2 * (size_t)H * es;
+    }
     a[0].tag = "qkv_proj";
     MMDIT_TRY(linear(dt, a, 2, s));
   }
-  if (sv) {   // q and k before their norm
-    const size_t w2 = 2 * (size_t)H * es, w3 = 3 * (size_t)H * es;
-    if (ni > 0)
-      MMDIT_TRY(hip_check(hipMemcpy2DAsync(sv + S->qk_raw, w2, qkv, w3, w2, ni, hipMemcpyDeviceToDevice, s),
-                          "hipMemcpy2DAsync"));
-    if (nt > 0)
-      MMDIT_TRY(hip_check(hipMemcpy2DAsync(sv + S->qk_raw + ni * w2, w2, qkv_t, w3, w2, nt,
-                                           hipMemcpyDeviceToDevice, s), "hipMemcpy2DAsync"));
-  }
-  // QK-RMSNorm + RoPE (image rows at their (frame, row, col); text rows at the origin)
-  {
-    QkArgs q[2] = {{qkv, pk->pos_img, w->img.g_q, w->img.g_k, ni}, {qkv_t, nullptr, w->txt.g_q, w->txt.g_k, nt}};
-    MMDIT_TRY(qk_norm_rope2_impl(dt, d->heads, d->head_dim, d->rope_dims, d->rope_theta, d->eps, q, 2, s));
-  }
   // o = block-diagonal joint attention
-  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.end - L.vt, s,
+  MMDIT_TRY(attention_impl(dt, pk, d->heads, d->head_dim, qkv, qkv_t, o, o_t, base + L.vt, L.rope - L.vt, s,
                            sv ? reinterpret_cast<float*>(sv + S->lse) : nullptr));
   // x += gate1 * (o W_o^T)
   {

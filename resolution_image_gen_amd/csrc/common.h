@@ -110,9 +110,83 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   return 0.5f * (1.0f + erf_as(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
 }
 
+// QK-RMSNorm + RoPE of the 8 consecutive dimensions (4 rotation pairs) of a
+// head vector that one lane holds.  Shared by the QK kernel and the QKV
+// projection's epilogue, with every fused multiply-add written out, so the
+// two give the same bits.
+__device__ __forceinline__ float qk_sumsq8(const float* v) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf(v[e], v[e], s);
+  return s;
+}
+// Sum of a head's per-lane partial sums over its `lanes` (8 or 16)
+// neighbouring lanes, aligned: DPP steps within rows of 16 lanes (pair swap,
+// quad swap, half-row mirror, row mirror), one VALU add each.  Every lane of
+// the group ends with the same value (each step adds two equal-shaped
+// partial sums, and addition commutes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float qk_head_sum(float v, int lanes) {
+  v += dpp_f<0xB1>(v);                   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);                  // row_half_mirror
+  if (lanes > 8) v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+// 1 / sqrt(mean square + eps) from the head's sum of squares over D dims
+// (hardware reciprocal square root, 1 ulp).
+__device__ __forceinline__ float qk_inv_rms(float ss, float D, float eps) {
+  return __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+}
+// cos and sin of the 4 pairs' angles pos[axis[j]] * inv_freq[j].
+__device__ __forceinline__ void qk_sincos4(const int32_t* p3, const int* axis, const float* invf, float* cs,
+                                           float* sn) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sincosf((float)p3[axis[j]] * invf[j], &sn[j], &cs[j]);
+}
+// v <- rotate(v * r * g) (rot false: no rotation).
+__device__ __forceinline__ void qk_apply8(float* v, float r, const float* g, bool rot, const float* cs,
+                                          const float* sn) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (v[e] * r) * g[e];
+  if (rot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = v[2 * j], b = v[2 * j + 1];
+      v[2 * j] = fmaf(a, cs[j], -(b * sn[j]));
+      v[2 * j + 1] = fmaf(a, sn[j], b * cs[j]);
+    }
+  }
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ internal API
+// RoPE rotation table: per rotation pair of a head, its axis (0 frame, 1 row,
+// 2 col) and frequency theta^(-2j/w) for pair j of a band of width w; bands
+// (frame, row, col) of the given widths from dimension 0.
+struct RopeTable {
+  float inv_freq[64];
+  int32_t axis[64];
+};
+void rope_table(RopeTable* t, const int32_t* widths, float theta);
+// out [n][D / 2][2] float32: (cos, sin) of every rotation pair of every row
+// at positions pos [n][3], the values the QK kernel rotates by.
+mmdit_status rope_cs_impl(const int32_t* pos, int64_t n, int32_t D, const RopeTable& tab, float* out,
+                          hipStream_t s);
+
+// QK-RMSNorm + RoPE applied by the QKV projection's epilogue (shared by the
+// problems of a grouped launch).
+struct QkEpilogue {
+  RopeTable tab;
+  int32_t heads, D;
+  float eps, theta;
+  int32_t widths[3];
+};
+
 // Dense linear y = op(A) W^T: A [M, K] (row stride lda), W [N, K], fp32 accumulation.
 struct LinearArgs {
   int64_t M;
@@ -132,11 +206,25 @@ struct LinearArgs {
   float* partial;          // optional float32 workspace for split-K (single problem)
   int64_t partial_elems;
   void* aux;               // [M, N] dense, model dtype: second output or input of the epilogues below
+                           // ([M, 2 H] for kEpiQkRopeAux)
+  const int32_t* pos;      // kEpiQkRope*: [M][3] positions of the rows (NULL: text rows, no rotation)
+  const float* rope_cs;    // kEpiQkRope*: their (cos, sin) table from rope_cs_impl (NULL iff pos is NULL)
+  const float* g_q;        // kEpiQkRope*: QK-norm gains [D]
+  const float* g_k;
+  const QkEpilogue* qk;    // kEpiQkRope*: dims and rotation table
 };
 // Epilogues used inside the library only (the public ones are mmdit_epilogue):
 constexpr int kEpiGeluAux = 4;      // Y = GELU(acc) and aux = acc (the pre-activation kept for backward)
 constexpr int kEpiGatedResAux = 5;  // Y += gate[seg] * acc and aux = acc (the branch kept for backward)
 constexpr int kEpiGeluBwd = 6;      // Y = acc * GELU'(aux), aux the saved pre-activation
+// The QKV projection (Y [M, 3H] = [Q | K | V]) with QK-RMSNorm + RoPE of the q
+// and k heads applied to the bf16-rounded products, the same arithmetic as
+// the separate qk_norm_rope kernel on the stored Y (so the same bits); with
+// Aux the bf16 q and k before their norm also go to aux [M, 2H].  Where the
+// launch's tiles do not all take the 256x256 LDS epilogue, linear() runs the
+// plain projection and then that kernel instead.
+constexpr int kEpiQkRope = 7;
+constexpr int kEpiQkRopeAux = 8;
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
 
 // RMSNorm + adaLN modulate of up to two row sets in one launch.

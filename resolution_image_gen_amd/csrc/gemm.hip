@@ -28,11 +28,19 @@ struct GemmProb {
   void* Y;
   const float* gate;
   const int32_t* seg;
-  void* aux;            // [M, N] dense (kEpi*Aux outputs, kEpiGeluBwd input)
+  void* aux;            // [M, N] dense (kEpi*Aux outputs, kEpiGeluBwd input; [M, 2H] for kEpiQkRopeAux)
+  const float* rope_cs; // kEpiQkRope*: [M][D/2] (cos, sin) per row and rotation pair (NULL: no rotation)
+  const float* g_q;     // kEpiQkRope*: QK-norm gains [D]
+  const float* g_k;
   int64_t lda, ldy, gate_stride, M;
   int32_t N, K;
   int32_t tiles_n;
   int32_t tile_begin;
+};
+
+struct QkDims {
+  int32_t heads, D;
+  float eps;
 };
 
 struct GemmBatch {
@@ -46,6 +54,7 @@ struct GemmBatch {
   int64_t partial_elems;
   int32_t tail_begin;   // > 0: blocks from here on share the tiles tail_begin.. (last-round fill)
   int32_t tail_chunks;  // blocks (sub-tiles) per last-round tile: 2, 4 or 8
+  QkDims qk;            // kEpiQkRope*: heads, head dim, eps
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -70,6 +79,10 @@ __device__ __forceinline__ void epi_store(const GemmProb& P, int64_t m, int n, f
   } else if constexpr (EPI == kEpiGeluBwd) {
     const float x = to_f(static_cast<const T*>(P.aux)[m * P.N + n]);
     static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(acc * gelu_grad_f(x));
+  } else if constexpr (EPI == kEpiQkRope || EPI == kEpiQkRopeAux) {
+    // QK-RMSNorm + RoPE needs whole head rows: only the 256x256 LDS epilogue
+    // applies it, and linear() launches these epilogues on that tile alone
+    static_cast<T*>(P.Y)[m * P.ldy + n] = from_f<T>(acc);
   } else {
     T* y = static_cast<T*>(P.Y) + m * P.ldy + n;
     const float g = P.gate[(int64_t)P.seg[m] * P.gate_stride + n];
@@ -561,9 +574,20 @@ __device__ __forceinline__ void store_tile(const GemmProb& P, int64_t m0, int n0
 // so every global access (the output, and for the gated residual the x row
 // and the gate vector) is a 16- or 32-byte vector access instead of a 2- or
 // 4-byte one per element.  Same per-element arithmetic as epi_store.
+//
+// The QKV projection's epilogue (kEpiQkRope*) also normalises and rotates
+// the q and k heads here (hyper.ai 2607.19064 方法 and blog close-reading
+// 2.2(2): RoPE per sample with a frame axis for editing; 2.2(3): norm and
+// RoPE chains fused): a tile's 256 columns lie in one of Q, K, V and hold
+// 256 / D whole heads, and the 32 threads of a row take 8 consecutive
+// columns each, so a head's sum of squares is a reduction over D / 8
+// neighbouring lanes.  The arithmetic is the qk_norm_rope kernel's on the
+// bf16-rounded products (same lane-to-dimension map, reduction tree, gain
+// and rotation expressions), so the result has the same bits as the plain
+// projection followed by that kernel.
 template <int EPI>
 __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, int n0, const f32x16 (&acc)[4][4],
-                                               bf16* smem) {
+                                               bf16* smem, const QkDims& qk) {
   float* T = reinterpret_cast<float*>(smem);   // [128][256]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g = lane >> 5;
@@ -576,6 +600,21 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
   const int64_t ldy = P.ldy, M = P.M, gs = P.gate_stride;
   const int N = P.N;
   const int ch = tid & 31, r0 = tid >> 5, n = n0 + ch * 8;
+  // QK epilogue: per-thread gains, rotation-pair frequencies and axes
+  constexpr bool QK = EPI == kEpiQkRope || EPI == kEpiQkRopeAux;
+  bool rot_tile = false;
+  int32_t Hq = 0, Dh = 0;
+  float qk_eps = 0.f, gn[8];
+  const float* csp = nullptr;   // this thread's 4 pairs of row 0 in the (cos, sin) table
+  if constexpr (QK) {
+    Dh = qk.D;
+    Hq = qk.heads * Dh;
+    qk_eps = qk.eps;
+    rot_tile = n0 < 2 * Hq;
+    const int dcol = (ch * 8) & (Dh - 1);
+    if (P.rope_cs) csp = P.rope_cs + dcol;
+    Vec8<float>::load((n0 < Hq ? P.g_q : P.g_k) + dcol, gn);
+  }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
@@ -603,6 +642,24 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
         float* y = static_cast<float*>(Yp) + m * ldy + n;
         *reinterpret_cast<f32x4*>(y) = *reinterpret_cast<const f32x4*>(a);
         *reinterpret_cast<f32x4*>(y + 4) = *reinterpret_cast<const f32x4*>(a + 4);
+      } else if constexpr (QK) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (float)(bf16)a[k];   // the stored product
+        if (rot_tile) {
+          if constexpr (EPI == kEpiQkRopeAux) Vec8<bf16>::store(static_cast<bf16*>(auxp) + m * 2 * Hq + n, v);
+          const float ss = qk_head_sum(qk_sumsq8(v), Dh >> 3);
+          const float r = qk_inv_rms(ss, (float)Dh, qk_eps);
+          float cs[4], sn[4];
+          if (csp) {
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(csp + m * Dh);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(csp + m * Dh + 4);
+            cs[0] = c0[0], sn[0] = c0[1], cs[1] = c0[2], sn[1] = c0[3];
+            cs[2] = c1[0], sn[2] = c1[1], cs[3] = c1[2], sn[3] = c1[3];
+          }
+          qk_apply8(v, r, gn, csp != nullptr, cs, sn);
+        }
+        Vec8<bf16>::store(static_cast<bf16*>(Yp) + m * ldy + n, v);
       } else {
         bf16* y = static_cast<bf16*>(Yp) + m * ldy + n;
         float o[8];
@@ -715,7 +772,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2) {
     // whole K, explicitly pipelined 4-wave mainloop (no split-K on this shape)
     mma_tile_pipe(P, m0, n0, smem, acc);
-    store_tile_lds<EPI>(P, m0, n0, acc, smem);
+    store_tile_lds<EPI>(P, m0, n0, acc, smem, bt.qk);
     return;
   }
   // this block's k steps (all of K unless split-K)
@@ -856,8 +913,16 @@ bool want_tailsplit(int64_t t256, bool n256, int& nb) {
   return t256 >= nb && tail > 0 && tail * 2 <= nb;
 }
 
-template <int EPI, bool SILU>
-mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
+// Tile configuration of an MFMA launch (a function of the shapes, the CU count
+// and the MMDIT_GEMM_* overrides only): cfg as in launch_mfma's switch, and
+// whether the last round is filled by sub-tiles (tail_ok: the epilogue allows it).
+struct MfmaPlan {
+  int cfg;
+  bool tail;
+  int nb;
+};
+
+MfmaPlan mfma_plan(const GemmBatch& bt, bool tail_ok) {
   bool n256 = true, n128 = true;
   int64_t t256 = 0;
   int kmax = 0;
@@ -882,12 +947,24 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
     else if (!n128) cfg = 0;
     else if (n256 && (2 * t256 > 3 * cu_count() || kmax <= 256 ||
                       (t256 * 10 >= cu_count() * 7 && t256 <= cu_count())))
-      cfg = big_tile_cfg(EPI);
+      cfg = big_tile_cfg(0);
     else cfg = 1;
   }
+  MfmaPlan pl;
+  pl.nb = 0;
+  pl.tail = tail_ok && tile_override() < 0 && want_tailsplit(t256, n256, pl.nb);
+  if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
+  if (cfg >= 1 && !n128) cfg = 0;
+  pl.cfg = cfg;
+  return pl;
+}
+
+template <int EPI, bool SILU>
+mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
+  const MfmaPlan pl = mfma_plan(bt, !SILU && EPI != MMDIT_EPI_STORE_F32);
+  int cfg = pl.cfg;
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
-    int nb = 0;
-    if (tile_override() < 0 && want_tailsplit(t256, n256, nb)) {
+    if (pl.tail) {
       int tiles = 0;
       for (int i = 0; i < bt.nprob; ++i) {
         bt.p[i].tiles_n = bt.p[i].N / 256;
@@ -896,12 +973,10 @@ mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
       }
       const bool w4 = big_tile_cfg(EPI) == 4;
       if (EPI == MMDIT_EPI_GATED_RES && bt.site == 1)
-        return w4 ? launch_tailsplit<EPI, 1, 2>(bt, tiles, nb, s) : launch_tailsplit<EPI, 1, 4>(bt, tiles, nb, s);
-      return w4 ? launch_tailsplit<EPI, 0, 2>(bt, tiles, nb, s) : launch_tailsplit<EPI, 0, 4>(bt, tiles, nb, s);
+        return w4 ? launch_tailsplit<EPI, 1, 2>(bt, tiles, pl.nb, s) : launch_tailsplit<EPI, 1, 4>(bt, tiles, pl.nb, s);
+      return w4 ? launch_tailsplit<EPI, 0, 2>(bt, tiles, pl.nb, s) : launch_tailsplit<EPI, 0, 4>(bt, tiles, pl.nb, s);
     }
   }
-  if ((cfg == 3 || cfg == 4) && !n256) cfg = 2;
-  if (cfg >= 1 && !n128) cfg = 0;
   if constexpr (EPI == MMDIT_EPI_GATED_RES && !SILU) {
     if (bt.site == 1) switch (cfg) {
       case 6: return launch_mfma_cfg<32, 128, 1, 4, EPI, SILU, 1>(bt, s);
@@ -994,6 +1069,48 @@ bool force_simt() {
   return v == 1;
 }
 
+// The QKV projection with QK-RMSNorm + RoPE: fused into the 256x256 tile's
+// LDS epilogue when every tile of the launch takes it, otherwise the plain
+// projection followed by the separate kernel (and, with Aux, a copy of the
+// q, k columns before the norm); the two give the same bits.
+mmdit_status linear_qk(mmdit_dtype dt, Path path, GemmBatch& bt, const LinearArgs* pa, int nprob, int epi,
+                       hipStream_t s) {
+  const QkEpilogue& q = *pa[0].qk;
+  bt.qk.heads = q.heads;
+  bt.qk.D = q.D;
+  bt.qk.eps = q.eps;
+  const int32_t H = q.heads * q.D;
+  bool fuse = dt == MMDIT_BF16 && path == Path::MFMA && H % 256 == 0 && (q.D == 64 || q.D == 128);
+  for (int i = 0; i < bt.nprob; ++i) fuse = fuse && bt.p[i].N == 3 * H && bt.p[i].ldy == 3 * H;
+  if (fuse) {
+    const MfmaPlan pl = mfma_plan(bt, true);
+    fuse = !pl.tail && pl.cfg == 4;
+  }
+  if (fuse) {
+    if (epi == kEpiQkRopeAux) return launch_mfma_cfg<256, 256, 2, 2, kEpiQkRopeAux, false>(bt, s);
+    return launch_mfma_cfg<256, 256, 2, 2, kEpiQkRope, false>(bt, s);
+  }
+  MMDIT_TRY((dispatch<MMDIT_EPI_STORE, false>(dt, path, bt, s)));
+  const size_t es = dt == MMDIT_BF16 ? 2 : 4;
+  QkArgs qa[2];
+  int k = 0;
+  for (int i = 0; i < nprob; ++i) {
+    const LinearArgs& a = pa[i];
+    if (a.M == 0) continue;
+    if (epi == kEpiQkRopeAux)
+      MMDIT_TRY(hip_check(hipMemcpy2DAsync(a.aux, 2 * (size_t)H * es, a.Y, (size_t)a.ldy * es, 2 * (size_t)H * es,
+                                           (size_t)a.M, hipMemcpyDeviceToDevice, s),
+                          "hipMemcpy2DAsync"));
+    qa[k].qkv = a.Y;
+    qa[k].pos = a.pos;
+    qa[k].g_q = a.g_q;
+    qa[k].g_k = a.g_k;
+    qa[k].n_rows = a.M;
+    ++k;
+  }
+  return qk_norm_rope2_impl(dt, q.heads, q.D, q.widths, q.theta, q.eps, qa, k, s);
+}
+
 }  // namespace
 
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t s) {
@@ -1019,8 +1136,10 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     }
     if (a.M == 0) continue;
     const bool gated = epi == MMDIT_EPI_GATED_RES || epi == kEpiGatedResAux;
-    const bool with_aux = epi == kEpiGeluAux || epi == kEpiGatedResAux || epi == kEpiGeluBwd;
-    if (!a.A || !a.W || !a.Y || (gated && (!a.gate || !a.seg)) || (with_aux && !a.aux)) {
+    const bool with_aux = epi == kEpiGeluAux || epi == kEpiGatedResAux || epi == kEpiGeluBwd || epi == kEpiQkRopeAux;
+    const bool qk = epi == kEpiQkRope || epi == kEpiQkRopeAux;
+    if (!a.A || !a.W || !a.Y || (gated && (!a.gate || !a.seg)) || (with_aux && !a.aux) ||
+        (qk && (!a.qk || !a.g_q || !a.g_k || (a.pos != nullptr) != (a.rope_cs != nullptr)))) {
       set_error("linear: NULL pointer");
       return MMDIT_E_INVALID;
     }
@@ -1031,6 +1150,9 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     p.gate = a.gate;
     p.seg = a.seg;
     p.aux = a.aux;
+    p.rope_cs = a.rope_cs;
+    p.g_q = a.g_q;
+    p.g_k = a.g_k;
     p.lda = a.lda;
     p.ldy = a.ldy;
     p.gate_stride = a.gate_stride;
@@ -1052,6 +1174,13 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
 
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
+  if (epi == kEpiQkRope || epi == kEpiQkRopeAux) {
+    if (silu) {
+      set_error("linear: the QK epilogue takes no SiLU on A");
+      return MMDIT_E_INVALID;
+    }
+    return linear_qk(dt, path, bt, pa, nprob, epi, s);
+  }
   switch (epi * 2 + (silu ? 1 : 0)) {
     case MMDIT_EPI_STORE * 2: return dispatch<MMDIT_EPI_STORE, false>(dt, path, bt, s);
     case MMDIT_EPI_STORE * 2 + 1: return dispatch<MMDIT_EPI_STORE, true>(dt, path, bt, s);

@@ -136,10 +136,7 @@ mmdit_status launch_rms(RmsBatch& bt, int64_t total, hipStream_t s) {
 // ------------------------------------------------------ QK-RMSNorm + RoPE
 // Lane layout: D/8 lanes per head vector, 8 consecutive dims (4 rotation
 // pairs) per lane, 64/(D/8) head vectors per wave step; q heads then k heads.
-struct RopeTab {
-  float inv_freq[64];  // per rotation pair: theta^(-2j/width of its band)
-  int32_t axis[64];    // 0 frame, 1 row, 2 col
-};
+typedef RopeTable RopeTab;
 
 struct QkProb {
   void* qkv;
@@ -171,12 +168,14 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkBatch bt, RopeTab t
   float cs[4], sn[4];
   if (pos) {
     const int32_t p3[3] = {pos[3 * row], pos[3 * row + 1], pos[3 * row + 2]};
+    int ax[4];
+    float invf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int pr = sub * 4 + j;
-      const float ang = (float)p3[tab.axis[pr]] * tab.inv_freq[pr];
-      sincosf(ang, &sn[j], &cs[j]);
+      ax[j] = tab.axis[sub * 4 + j];
+      invf[j] = tab.inv_freq[sub * 4 + j];
     }
+    qk_sincos4(p3, ax, invf, cs, sn);
   }
   float gq[8], gk[8];
   Vec8<float>::load(P.g_q + sub * 8, gq);
@@ -186,23 +185,36 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkBatch bt, RopeTab t
   for (int hv = hv0; hv < 2 * heads; hv += HPS) {
     float v[8];
     Vec8<T>::load(base + hv * D, v);
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-    ss = group_sum(ss, LPH);
-    const float r = 1.0f / sqrtf(ss / (float)D + bt.eps);
-    const float* g = hv < heads ? gq : gk;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * r * g[e];
-    if (pos) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = v[2 * j], b = v[2 * j + 1];
-        v[2 * j] = a * cs[j] - b * sn[j];
-        v[2 * j + 1] = a * sn[j] + b * cs[j];
-      }
-    }
+    const float ss = qk_head_sum(qk_sumsq8(v), LPH);
+    const float r = qk_inv_rms(ss, (float)D, bt.eps);
+    qk_apply8(v, r, hv < heads ? gq : gk, pos != nullptr, cs, sn);
     Vec8<T>::store(base + hv * D, v);
+  }
+}
+
+// cos and sin of every rotation pair of every row: out[row][pair] = (cos,
+// sin) of pos[row][axis(pair)] * inv_freq(pair), float32, D / 2 pairs per
+// row, computed exactly as the QK kernel computes them (qk_sincos4), so a
+// consumer of the table rotates with the same values.  One thread per 4 pairs.
+__global__ void __launch_bounds__(256) rope_cs_kernel(const int32_t* __restrict__ pos, int64_t n, int32_t D,
+                                                      RopeTab tab, float* __restrict__ out) {
+  const int32_t qpr = D >> 3;   // 4-pair groups per row
+  const int64_t total = n * qpr;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = u / qpr;
+    const int sub = (int)(u - row * qpr);
+    const int32_t p3[3] = {pos[3 * row], pos[3 * row + 1], pos[3 * row + 2]};
+    int ax[4];
+    float invf[4], cs[4], sn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ax[j] = tab.axis[sub * 4 + j];
+      invf[j] = tab.inv_freq[sub * 4 + j];
+    }
+    qk_sincos4(p3, ax, invf, cs, sn);
+    float* o = out + row * D + sub * 8;
+    *reinterpret_cast<f32x4*>(o) = f32x4{cs[0], sn[0], cs[1], sn[1]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{cs[2], sn[2], cs[3], sn[3]};
   }
 }
 
@@ -268,6 +280,28 @@ mmdit_status rms_modulate_impl(mmdit_dtype dt, int64_t n, int32_t H, const void*
   return rms_modulate2_impl(dt, H, eps, &a, 1, s);
 }
 
+mmdit_status rope_cs_impl(const int32_t* pos, int64_t n, int32_t D, const RopeTable& tab, float* out,
+                          hipStream_t s) {
+  if (n == 0) return MMDIT_OK;
+  int64_t g = cdiv(n * (D >> 3), 256);
+  if (g > 1 << 16) g = 1 << 16;
+  MMDIT_LAUNCH(rope_cs_kernel, dim3((unsigned)g), dim3(256), 0, s, pos, n, D, tab, out);
+  return launch_check("rope_cs_kernel", s);
+}
+
+void rope_table(RopeTable* t, const int32_t* widths, float theta) {
+  int p = 0;
+  for (int ax = 0; ax < 3; ++ax)
+    for (int j = 0; j < widths[ax] / 2 && p < 64; ++j, ++p) {
+      t->axis[p] = ax;
+      t->inv_freq[p] = (float)pow((double)theta, -2.0 * j / (double)widths[ax]);
+    }
+  for (; p < 64; ++p) {
+    t->axis[p] = 0;
+    t->inv_freq[p] = 0.f;
+  }
+}
+
 mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const int32_t* widths, float theta,
                                 float eps, const QkArgs* a, int n, hipStream_t s) {
   if (D != 64 && D != 128) {
@@ -290,19 +324,8 @@ mmdit_status qk_norm_rope2_impl(mmdit_dtype dt, int32_t heads, int32_t D, const 
   bt.split = bt.p[0].n_rows;
   bt.heads = heads;
   bt.eps = eps;
-  // per rotation pair: its axis and frequency; bands (frame, row, col) of the
-  // given widths from dimension 0
   RopeTab tab;
-  int p = 0;
-  for (int ax = 0; ax < 3; ++ax)
-    for (int j = 0; j < widths[ax] / 2; ++j, ++p) {
-      tab.axis[p] = ax;
-      tab.inv_freq[p] = (float)pow((double)theta, -2.0 * j / (double)widths[ax]);
-    }
-  for (; p < 64; ++p) {
-    tab.axis[p] = 0;
-    tab.inv_freq[p] = 0.f;
-  }
+  rope_table(&tab, widths, theta);
   const int64_t total = bt.p[0].n_rows + (k > 1 ? bt.p[1].n_rows : 0);
   return dt == MMDIT_BF16 ? launch_qk<bf16>(bt, total, D, tab, s) : launch_qk<float>(bt, total, D, tab, s);
 }

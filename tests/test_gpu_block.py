@@ -290,3 +290,61 @@ def test_block_sample_order_invariant_with_last_round_split():
     assert torch.equal(torch.cat([a[cu_i[p]:cu_i[p + 1]] for p in perm]), b), "image rows differ after permuting"
     a, b = xt1.cpu(), xt2.cpu()
     assert torch.equal(torch.cat([a[cu_t[p]:cu_t[p + 1]] for p in perm]), b[:cu_t[-1]]), "text rows differ"
+
+
+def test_fused_qkv_epilogue_same_bits_as_separate_kernel(B):
+    """At the 1024^2 packed-CFG shape (cond + uncond, 64x64 grid + 256 text
+    each: 1,224 QKV tiles of 256x256, no last-round split on 256 CUs) the QKV
+    projection applies QK-RMSNorm + RoPE in its LDS epilogue.  It must give
+    the same bits as the plain projection followed by the separate QK kernel,
+    recomputed here from the block's own pre-attention norm; the training
+    forward's copy of q and k before their norm must equal the plain
+    projection's."""
+    import ctypes  # noqa: F401
+
+    d, dtype = CF.B4, "bf16"
+    samples = [(64, 64, 1, 256), (64, 64, 1, 256)]
+    print("fused QKV epilogue at 2 x (64x64 + 256)", flush=True)
+    ref, nb, x_img, x_txt, c = _inputs(d, dtype, samples, "qkfuse", "stress")
+    dims, pk, xi, xt, ws = _run_block(B, d, dtype, samples, nb, x_img, x_txt, c)
+    H = d.hidden
+    ni, nt = int(ref["cu_img"][-1]), int(ref["cu_txt"][-1])
+    L = B.workspace_layout(dims, pk)
+    nbs = len(samples)
+    wb = _dev_block(nb, dtype)
+    fused = _ws_view(ws, L["qkv"], ni + nt, 3 * H, dtype).clone()
+    raws = {}
+    for s, r0, n, x, seg, pos in (("img", 0, ni, x_img, pk.t["seg_img"], pk.t["pos_img"]),
+                                  ("txt", ni, nt, x_txt, pk.t["seg_txt"], None)):
+        mod = ws[L["mod_" + s]:L["mod_" + s] + nbs * 6 * H * 4].view(torch.float32).view(nbs, 6 * H)
+        h1 = torch.empty(n, H, dtype=torch.bfloat16, device="cuda")
+        B.rms_modulate(dims, _dev(x, dtype), seg, mod, 0, H, h1)
+        plain = torch.empty(n, 3 * H, dtype=torch.bfloat16, device="cuda")
+        B.linear(h1, wb[s]["w_qkv"], plain, B.EPI_STORE)
+        raws[s] = plain[:, :2 * H].clone()
+        B.qk_norm_rope(dims, plain, pos, wb[s]["g_q"], wb[s]["g_k"])
+        torch.cuda.synchronize()
+        got = fused[r0:r0 + n]
+        diff = (got.float() - plain.float()).abs().max().item()
+        print(f"  {s}: max |fused - separate| = {diff:.3e}", flush=True)
+        assert torch.equal(got, plain), s
+    # training forward: same normalised q, k, v and the raw q, k kept
+    saved = torch.empty(B.block_saved_size(dims, pk), dtype=torch.uint8, device="cuda")
+    xi2, xt2 = _dev(x_img, dtype), _dev(x_txt, dtype)
+    B.block_fwd_train(dims, wb, pk, _dev(c, dtype), xi2, xt2, saved, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xi2, xi) and torch.equal(xt2, xt)
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    # saved layout: mod_img, mod_txt [B, 6H] f32; x_in, h1 [N, H]; qkv [N, 3H]; qk_raw [N, 2H] (bf16)
+    N = ni + nt
+    off = a256(a256(nbs * 6 * H * 4) + nbs * 6 * H * 4)
+    off = a256(off + N * H * 2)                    # x_in
+    off = a256(off + N * H * 2)                    # h1
+    qkv_s = saved[off:off + N * 3 * H * 2].view(torch.bfloat16).view(N, 3 * H)
+    off = a256(off + N * 3 * H * 2)
+    raw_s = saved[off:off + N * 2 * H * 2].view(torch.bfloat16).view(N, 2 * H)
+    assert torch.equal(qkv_s, fused)
+    assert torch.equal(raw_s[:ni], raws["img"]) and torch.equal(raw_s[ni:], raws["txt"])
