@@ -179,13 +179,29 @@ def cpu_baseline(wl, W, inputs, n_samples, min_seconds=10.0):
                       f"(noise, cond, embed, block, final, loss), float64 numpy, {runs} runs, {dt:.1f} s"}
 
 
+# Further launches that finish a tagged kernel's work (the MLP down
+# projection's split last round: the k parts of its remaining tiles, then the
+# fixup that sums them and applies the epilogue); their time counts toward
+# the tagged kernel's launches.
+FIXUP_OF = {"mlp_down_gated": ("mlp_down_sk", "mlp_down_fixup")}
+
+
+def _total_ms(kernels, tag):
+    ms, cnt = kernels[tag]
+    for fx in FIXUP_OF.get(tag, ()):
+        if fx in kernels:
+            ms += kernels[fx][0]
+    return ms, cnt
+
+
 def _roofline(kernels, work):
     """Roofline object of the dominant kernel: the tagged kernel with the
-    largest total time among those with a known algorithmic work; achieved =
-    work per launch / average launch time."""
-    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k][0])
+    largest total time (its fixup launches included) among those with a
+    known algorithmic work; achieved = work per launch / average launch time."""
+    dom = max((k for k in kernels if k in work), key=lambda k: _total_ms(kernels, k)[0])
     kind, per_launch = work[dom]
-    avg_ms = kernels[dom][0] / kernels[dom][1]
+    tot, cnt = _total_ms(kernels, dom)
+    avg_ms = tot / cnt
     if kind == "mfma":
         achieved = per_launch / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -209,7 +225,7 @@ def _kernel_lines(kernels, work, per, unit):
         row = {f"us_per_{unit}": round(ms / per * 1e3, 1), "launches": round(cnt / per, 2)}
         if k in work:
             kd, wk = work[k]
-            s = ms / cnt * 1e-3
+            s = _total_ms(kernels, k)[0] / cnt * 1e-3
             row["TFLOP/s" if kd == "mfma" else "GB/s"] = round(wk / s / (1e12 if kd == "mfma" else 1e9), 1)
         out[k] = row
     return out
@@ -312,7 +328,10 @@ def bench_sampler_extras(W, steps, warmup):
     sm2 = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
     ms2, _ = _timed_graph(sm2, steps, warmup)
     assert torch.isfinite(sm.z).all()
-    assert torch.equal(sm.z, sm2.z), "packed and two-pass CFG samplers disagree"
+    # the packed pack's MLP down takes a stream-K last round that the one-sample
+    # forwards do not, so the two agree to rounding, not bit for bit
+    diff = ((sm.z - sm2.z).abs().max() / sm2.z.abs().max()).item()
+    assert diff <= 2e-2, f"packed and two-pass CFG samplers disagree ({diff:.3e})"
     sm20 = R.Sampler(wl, W, eps, tau_c, tau_u, schedule=[1.0 - i / 20 for i in range(21)])
     ms20, _ = _timed_graph(sm20, 1, 1)
     assert torch.isfinite(sm20.z).all()
@@ -324,14 +343,17 @@ def bench_sampler_extras(W, steps, warmup):
     se2 = R.Sampler(ewl, W, eps, tau_c, tau_u, src=src, two_pass=True)
     ms_e2, _ = _timed_graph(se2, steps, warmup)
     assert torch.isfinite(se.z).all()
-    assert torch.equal(se.z, se2.z), "packed and two-pass CFG edit samplers disagree"
+    ediff = ((se.z - se2.z).abs().max() / se2.z.abs().max()).item()
+    assert ediff <= 2e-2, f"packed and two-pass CFG edit samplers disagree ({ediff:.3e})"
     eblk = block_flops(d, se.samples)[0] * ewl.depth * (len(ewl.schedule) - 1)
     return {"ms_per_4step_pack": round(ms, 2), "two_pass_ms_per_4step_pack": round(ms2, 2),
-            "packed_speedup_vs_two_pass": round(ms2 / ms, 3), "ms_per_20step_pack": round(ms20, 2),
+            "packed_speedup_vs_two_pass": round(ms2 / ms, 3), "packed_vs_two_pass_max_rel_diff": diff,
+            "ms_per_20step_pack": round(ms20, 2),
             "edit": {"workload": f"{ewl.name}: {ewl.note}", "ms_per_4step_pack": round(ms_e, 2),
                      "block_tflops": round(eblk / (ms_e * 1e-3) / 1e12, 1),
                      "two_pass_ms_per_4step_pack": round(ms_e2, 2),
-                     "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3)}}
+                     "packed_speedup_vs_two_pass": round(ms_e2 / ms_e, 3),
+                     "packed_vs_two_pass_max_rel_diff": ediff}}
 
 
 def _threads():

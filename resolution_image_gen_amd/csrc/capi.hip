@@ -176,7 +176,7 @@ mmdit_status need(const void* p, const char* who, const char* name) {
 }
 
 struct Layout {
-  size_t mod_img, mod_txt, h, qkv, o, u, vt, rope, end;
+  size_t mod_img, mod_txt, h, qkv, o, u, vt, rope, sk, end;
 };
 
 Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
@@ -193,6 +193,11 @@ Layout block_layout(const mmdit_dims* d, const mmdit_pack_t* pk) {
   L.u = o;       o = align256(o + N * (size_t)d->mlp * es);
   L.vt = o;      o = align256(o + (size_t)attention_vt_elems(pk, d->hidden) * es);
   L.rope = o;    o = align256(o + (size_t)pk->n_img * d->head_dim * 4);   // (cos, sin) per image row and pair
+  // partial tiles of the MLP down projection's stream-K last round (bf16 MFMA path only)
+  L.sk = o;
+  if (d->dtype == MMDIT_BF16)
+    o = align256(o + gemm_sk_partial_bytes(pk->n_img > 0 ? pk->n_img : pk->n_txt,
+                                           pk->n_img > 0 ? pk->n_txt : 0, d->hidden, d->mlp));
   L.end = o;
   return L;
 }
@@ -693,6 +698,8 @@ mmdit_status block_forward_impl(const mmdit_dims* d, const mmdit_block_w* w, con
     a[1].seg = pk->seg_txt;
     a[0].tag = "mlp_down_gated";
     a[0].site = 1;
+    a[0].partial = reinterpret_cast<float*>(base + L.sk);
+    a[0].partial_elems = (int64_t)((L.end - L.sk) / sizeof(float));
     if (sv) {
       a[0].aux = sv + S->dmlp;
       a[1].aux = sv + S->dmlp + ni * H * es;

@@ -226,6 +226,10 @@ constexpr int kEpiGeluBwd = 6;      // Y = acc * GELU'(aux), aux the saved pre-a
 constexpr int kEpiQkRope = 7;
 constexpr int kEpiQkRopeAux = 8;
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* probs, int nprob, hipStream_t s);
+// Bytes of float32 partial tiles the MLP down projection (site 1) needs for
+// its stream-K last round over problems of m0 and m1 rows (N columns, depth
+// K) on the current device; 0 when that launch takes no stream-K round.
+size_t gemm_sk_partial_bytes(int64_t m0, int64_t m1, int32_t N, int32_t K);
 
 // RMSNorm + adaLN modulate of up to two row sets in one launch.
 struct RmsArgs {

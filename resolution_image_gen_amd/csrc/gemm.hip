@@ -55,6 +55,11 @@ struct GemmBatch {
   int32_t tail_begin;   // > 0: blocks from here on share the tiles tail_begin.. (last-round fill)
   int32_t tail_chunks;  // blocks (sub-tiles) per last-round tile: 2, 4 or 8
   QkDims qk;            // kEpiQkRope*: heads, head dim, eps
+  // split last round (gemm_sk_part_kernel): tiles sk_full.. are cut along k
+  // into sk_S parts of sk_P 64-deep steps whose float32 partial tiles
+  // gemm_sk_fixup_kernel sums in k order
+  int32_t sk_full, sk_tail, sk_S, sk_P;
+  float* sk_partial;    // [sk_tail][sk_S][256][256]
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -462,18 +467,19 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// acc += A[m0:m0+256, :] W[n0:n0+256, :]^T over the whole K (K % 64 == 0).
-// 256 threads; smem holds two stages of both operands (128 KB).  Ends with a
-// barrier, so the caller may reuse the LDS right away.
+// acc += A[m0:m0+256, k] W[n0:n0+256, k]^T over the 64-deep k steps
+// kt0 .. kt0+nkt (all of K when nkt < 0; K % 64 == 0).  256 threads; smem
+// holds two stages of both operands (128 KB).  Ends with a barrier, so the
+// caller may reuse the LDS right away.
 __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int n0, bf16* smem,
-                                              f32x16 (&acc)[4][4]) {
+                                              f32x16 (&acc)[4][4], int kt0 = 0, int nkt = -1) {
   constexpr int BM = 256, BK = 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int rr = lane >> 3, pp = lane & 7;
   const int row0 = wave * 8 + rr;
-  const bf16* atile = static_cast<const bf16*>(P.A) + m0 * P.lda;
-  const bf16* btile = static_cast<const bf16*>(P.W) + (int64_t)n0 * P.K;
+  const bf16* atile = static_cast<const bf16*>(P.A) + m0 * P.lda + (int64_t)kt0 * BK;
+  const bf16* btile = static_cast<const bf16*>(P.W) + (int64_t)n0 * P.K + (int64_t)kt0 * BK;
   // per-lane byte offsets of the 8 one-KB blocks this wave fills per operand
   // and stage (rows past M load row M-1; never stored)
   uint32_t offa[8], offb[8];
@@ -494,7 +500,7 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
     boff[kk] = 2 * BM * BK * 2 + rb * 128 + (((kk * 2 + g) ^ swz8(rb)) << 4);
   }
   bf16x8 fa[2][4], fb[2][4];
-  const int KT = P.K / BK;
+  const int KT = nkt < 0 ? P.K / BK : nkt;
   auto issue = [&](int k) {
     const int s2 = k & 1;
     const char* ab = reinterpret_cast<const char*>(atile + k * BK);
@@ -782,6 +788,88 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
                                   bt.splitk > 1 ? bt.partial + (int64_t)blockIdx.y * P.M * P.N : nullptr);
 }
 
+// Split last round of the 256x256 pipelined tile.  When the tiles fill a
+// few rounds of the CUs and leave the last one more than half full, the full
+// rounds run as whole tiles (gemm_mfma_kernel over the first sk_full tiles)
+// and each remaining tile is cut along k into sk_S equal parts of sk_P
+// 64-deep steps, one block per part (gemm_sk_part_kernel): the last round
+// then takes ceil(tail * S / CUs) part-times instead of a whole tile time.
+// Parts are numbered part-major (part j of every remaining tile, then part
+// j + 1) and handed to the XCDs in contiguous runs, so the blocks running
+// together on an XCD read the same k range of neighbouring tiles and share
+// their operand blocks in L2.  Each part writes its float32 partial tile
+// (row-major [256][256], through the LDS epilogue); gemm_sk_fixup_kernel sums
+// a tile's parts in k order and applies the epilogue.  The split depends on
+// the launch's shape only, so results are bitwise reproducible; a row in a
+// split tile rounds its k sum at the part boundaries, so its bits differ from
+// the same row in a whole tile (within float32 rounding).
+template <int SITE>
+__global__ void __launch_bounds__(256) gemm_sk_part_kernel(GemmBatch bt) {
+  extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+  const int u = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+  const int t = u % bt.sk_tail, j = u / bt.sk_tail;
+  const int KT = bt.p[0].K / 64;
+  const int k0 = j * bt.sk_P;
+  const int nk = min(bt.sk_P, KT - k0);
+  int tile = bt.sk_full + t;
+  const GemmProb& P = pick(bt, tile);
+  int tm, tn;
+  grouped_tile(tile, (int)cdiv_d(P.M, 256), P.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256;
+  const int n0 = tn * 256;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+  mma_tile_pipe(P, m0, n0, smem, acc, k0, nk);
+  // the part's float32 tile, row-major [256][256]
+  GemmProb Q;
+  memset(&Q, 0, sizeof(Q));
+  Q.Y = bt.sk_partial + ((int64_t)t * bt.sk_S + j) * 256 * 256;
+  Q.ldy = 256;
+  Q.M = 256;
+  Q.N = 256;
+  QkDims none = {0, 0, 0.f};
+  store_tile_lds<MMDIT_EPI_STORE_F32>(Q, 0, 0, acc, smem, none);
+}
+
+// Sum of a split tile's parts in k order, then the gated-residual epilogue
+// (x += gate[seg] * sum, and with Aux the sum kept in aux), 8 columns per
+// thread with vector accesses.
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_sk_fixup_kernel(GemmBatch bt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8-column chunk of a split tile
+  const int t = (int)(e >> 13);                                // 256 rows x 32 chunks per tile
+  if (t >= bt.sk_tail) return;
+  const int r = (int)((e >> 5) & 255), c = (int)(e & 31) * 8;
+  int tile = bt.sk_full + t;
+  const GemmProb& P = pick(bt, tile);
+  int tm, tn;
+  grouped_tile(tile, (int)cdiv_d(P.M, 256), P.tiles_n, tm, tn);
+  const int64_t m = (int64_t)tm * 256 + r;
+  if (m >= P.M) return;
+  const int n = tn * 256 + c;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* src = bt.sk_partial + (int64_t)t * bt.sk_S * 65536 + r * 256 + c;
+  for (int j = 0; j < bt.sk_S; ++j) {
+    float v[8];
+    Vec8<float>::load(src + (int64_t)j * 65536, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] += v[k];
+  }
+  bf16* y = static_cast<bf16*>(P.Y) + m * P.ldy + n;
+  float xv[8], gv[8], o[8];
+  Vec8<bf16>::load(y, xv);
+  Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + n, gv);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
+  if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
+  Vec8<bf16>::store(y, o);
+}
+
 // Sums the split-K partials in a fixed order and applies the epilogue.
 template <int EPI>
 __global__ void splitk_reduce_kernel(GemmBatch bt) {
@@ -870,6 +958,90 @@ bool tailsplit_enabled() {
     v = e ? atoi(e) : 1;
   }
   return v != 0;
+}
+
+// env MMDIT_STREAMK=0 turns the stream-K last round off
+bool streamk_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_STREAMK");
+    v = e ? atoi(e) : 1;
+  }
+  return v != 0;
+}
+
+// Split-last-round plan of a launch of 256x256 tiles over problems of M[i]
+// rows, N columns and depth K: the whole rounds of the CUs, then the rest of
+// the tiles cut along k into S parts.  Taken for long K (>= 64 k steps) when
+// at least one round is full and the last one more than half (a last round
+// at most half full takes the sub-tile split instead), with the S in 2..4
+// that gives the fewest part-rounds per tile time, ceil(tail S / CUs) / S,
+// if that saves at least a fifth of the last round.
+struct SkPlan {
+  int full, tail, S, P;
+  size_t bytes;
+};
+
+bool sk_plan(const int64_t* M, int nprob, int N, int K, SkPlan& pl) {
+  const int nb = cu_count();
+  if (!streamk_enabled() || nb <= 0 || N % 256 || K % 64 || K / 64 < 64 || tile_override() >= 0 ||
+      big_tile_cfg(0) != 4)
+    return false;
+  int64_t T = 0;
+  for (int i = 0; i < nprob; ++i) T += cdiv(M[i], 256) * (N / 256);
+  const int64_t full = (T / nb) * nb, tail = T - full;
+  if (full < nb || tail * 2 <= nb) return false;
+  int best = 1;
+  double cost = 1.0;
+  for (int S = 2; S <= 4; ++S) {
+    const double c = (double)cdiv(tail * S, nb) / S;
+    if (c < cost - 1e-9) {
+      cost = c;
+      best = S;
+    }
+  }
+  if (best == 1 || cost > 0.8) return false;
+  const int KT = K / 64;
+  pl.full = (int)full;
+  pl.tail = (int)tail;
+  pl.S = best;
+  pl.P = (int)cdiv(KT, best);
+  pl.bytes = (size_t)tail * best * 256 * 256 * sizeof(float);
+  return true;
+}
+
+template <int EPI, int SITE>
+mmdit_status launch_sk(GemmBatch& bt, const SkPlan& pl, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    bt.p[i].tiles_n = bt.p[i].N / 256;
+    bt.p[i].tile_begin = tiles;
+    tiles += (int)(cdiv(bt.p[i].M, 256) * bt.p[i].tiles_n);
+  }
+  bt.sk_full = pl.full;
+  bt.sk_tail = pl.tail;
+  bt.sk_S = pl.S;
+  bt.sk_P = pl.P;
+  bt.sk_partial = bt.partial;
+  const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16) + 1024;
+  auto whole = gemm_mfma_kernel<256, 256, 2, 2, EPI, false, SITE>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)whole, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                        "hipFuncSetAttribute(gemm_mfma_kernel)"));
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)gemm_sk_part_kernel<SITE>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                        "hipFuncSetAttribute(gemm_sk_part_kernel)"));
+    attr_set = true;
+  }
+  const bool down = bt.tag && strcmp(bt.tag, "mlp_down_gated") == 0;
+  // whole tiles of the full rounds (the launch covers tiles 0 .. full-1)
+  MMDIT_LAUNCH(whole, dim3(pl.full), dim3(256), lds, s, bt);
+  MMDIT_TRY(launch_check(bt.tag ? bt.tag : "gemm_mfma_kernel<256,256,2,2,sk>", s));
+  MMDIT_LAUNCH(gemm_sk_part_kernel<SITE>, dim3(pl.tail * pl.S), dim3(256), lds, s, bt);
+  MMDIT_TRY(launch_check(down ? "mlp_down_sk" : "gemm_sk_part_kernel", s));
+  MMDIT_LAUNCH(gemm_sk_fixup_kernel<EPI>, dim3(pl.tail * 32), dim3(256), 0, s, bt);
+  return launch_check(down ? "mlp_down_fixup" : "gemm_sk_fixup_kernel", s);
 }
 
 // Last-round fill: when the 256x256 tiles leave the last round of CUs at
@@ -961,6 +1133,20 @@ MfmaPlan mfma_plan(const GemmBatch& bt, bool tail_ok) {
 
 template <int EPI, bool SILU>
 mmdit_status launch_mfma(GemmBatch& bt, hipStream_t s) {
+  if constexpr (!SILU && (EPI == MMDIT_EPI_GATED_RES || EPI == kEpiGatedResAux)) {
+    // the MLP down projection: stream-K last round where it pays and the
+    // caller gave the partial-tile workspace
+    bool same = true;
+    int64_t M[2];
+    for (int i = 0; i < bt.nprob; ++i) {
+      M[i] = bt.p[i].M;
+      same = same && bt.p[i].N == bt.p[0].N && bt.p[i].K == bt.p[0].K;
+    }
+    SkPlan sk;
+    if (bt.site == 1 && same && bt.partial && sk_plan(M, bt.nprob, bt.p[0].N, bt.p[0].K, sk) &&
+        (size_t)bt.partial_elems * sizeof(float) >= sk.bytes)
+      return launch_sk<EPI, 1>(bt, sk, s);
+  }
   const MfmaPlan pl = mfma_plan(bt, !SILU && EPI != MMDIT_EPI_STORE_F32);
   int cfg = pl.cfg;
   if constexpr (!SILU && EPI != MMDIT_EPI_STORE_F32) {
@@ -1112,6 +1298,14 @@ mmdit_status linear_qk(mmdit_dtype dt, Path path, GemmBatch& bt, const LinearArg
 }
 
 }  // namespace
+
+size_t gemm_sk_partial_bytes(int64_t m0, int64_t m1, int32_t N, int32_t K) {
+  const int64_t M[2] = {m0, m1};
+  const int np = m1 > 0 ? 2 : 1;
+  SkPlan pl;
+  if (m0 <= 0 || !sk_plan(M, np, N, K, pl)) return 0;
+  return pl.bytes;
+}
 
 mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t s) {
   if (nprob < 1 || nprob > 2) {

@@ -37,6 +37,9 @@ CASES = {
     # gated-residual + aux (out / down projections, 1.125 rounds) epilogues and
     # the backward's GELU' epilogue (dU of the down projection, 4.5 rounds)
     "pack256_b4": (CF.B4, "bf16", [(16, 16, 1, 128)] * 16),
+    # the 1024^2 packed-CFG pack: the MLP down projection's stream-K last round
+    # with the training forward's aux epilogue
+    "sampler_b4": (CF.B4, "bf16", [(64, 64, 1, 256)] * 2),
 }
 
 
@@ -93,7 +96,7 @@ def B():
     return binding
 
 
-@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("case", [c for c in CASES if c != "sampler_b4"])
 def test_block_backward_vs_oracle(B, case):
     d, dtype, samples, ref, nb, x_img, x_txt, c, dy_img, dy_txt = _setup(case)
     print(f"block backward {case}", flush=True)
@@ -117,7 +120,7 @@ def test_block_backward_vs_oracle(B, case):
                          rows=ROW_TOL_WGRAD_BF16 if dtype == "bf16" else True)
 
 
-@pytest.mark.parametrize("case", ["tiny_f32_edit", "small_bf16", "pack256_b4"])
+@pytest.mark.parametrize("case", ["tiny_f32_edit", "small_bf16", "pack256_b4", "sampler_b4"])
 def test_training_forward_matches_inference_forward_and_is_deterministic(B, case):
     d, dtype, samples, ref, nb, x_img, x_txt, c, dy_img, dy_txt = _setup(case)
     print(f"train forward / determinism {case}", flush=True)

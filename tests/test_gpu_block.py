@@ -209,10 +209,14 @@ def test_block_deterministic_and_sample_order_invariant(B):
     assert torch.equal(torch.cat([a[cu_t[p]:cu_t[p + 1]] for p in perm]), b[:cu_t[-1]]), "text rows differ"
 
 
-@pytest.mark.parametrize("name", ["native1024_bf16", "edit2048_bf16"])
+@pytest.mark.parametrize("name", ["native1024_bf16", "edit2048_bf16", "sampler1024_cfg_bf16"])
 def test_block_full_size_sampled_rows(B, name):
     """Full-size packs in the launch configuration of the benchmark; the oracle
-    recomputes sampled rows of two samples from the block inputs."""
+    recomputes sampled rows of two samples from the block inputs.  At the
+    1024^2 packed-CFG pack (408 MLP-down tiles: one full round of 256 CUs and
+    a last round 59% full) the MLP down projection takes the stream-K last
+    round: the second sample's image rows and all text rows lie in split
+    tiles."""
     wl = CF.WORKLOADS[name]
     d, dtype, samples = wl.dims, wl.dtype, list(wl.samples)
     print(f"full-size {name}", flush=True)
