@@ -268,6 +268,15 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
+// A wave-uniform pointer held in scalar registers, so that base + 32-bit lane
+// offset addresses a direct load without 64-bit vector arithmetic per load.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 // acc[TM][TN] += A[m0:m0+BM, K-steps kt0 .. kt0+nkt) W[n0:n0+BN, ...]^T for one
 // tile.  Operands go global -> LDS directly (global_load_lds_dwordx4: one wave
 // instruction fills 1 KB), NS-stage ring with one barrier per BK-deep step.
@@ -437,21 +446,35 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
     __builtin_amdgcn_sched_barrier(0);
     read_slice(st ^ 1, 0, 0);
     if constexpr (LOAD2) {
-      // stage kt + 2 into the buffer every wave has just finished (stage kt)
-      const char* ab = reinterpret_cast<const char*>(atile + (kt + 2) * BK);
-      const char* bb = reinterpret_cast<const char*>(btile + (kt + 2) * BK);
+      // stage kt + 2 into the buffer every wave has just finished (stage kt),
+      // then the touch of stage kt + 3 (past the last stage it repeats the
+      // last one): the 18 direct loads go between the 12 remaining MFMAs of
+      // the slice, two after each of the first eight, one after each of the
+      // next two, each fenced so the compiler keeps them there (grouped, they
+      // held the matrix cores idle for the whole burst); bases in scalar
+      // registers, lane offsets 32-bit
+      const char* ab = uniform_ptr(atile + (kt + 2) * BK);
+      const char* bb = uniform_ptr(btile + (kt + 2) * BK);
+      const int kt3 = kt + 3 < KT ? kt + 3 : KT - 1;
+      const char* ta = uniform_ptr(atile + kt3 * BK);
+      const char* tb = uniform_ptr(btile + kt3 * BK);
+      bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        load_lds16(ab + offa[i], smem + st * BM * BK + (wave + i * 4) * 512);
-        load_lds16(bb + offb[i], smem + 2 * BM * BK + st * BM * BK + (wave + i * 4) * 512);
+      for (int q = 0; q < 12; ++q) {
+        const int i = 1 + q / 4, j = q % 4;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < 8) {
+          load_lds16(ab + offa[q], smem + st * BM * BK + (wave + q * 4) * 512);
+          load_lds16(bb + offb[q], smem + 2 * BM * BK + st * BM * BK + (wave + q * 4) * 512);
+        } else if (q == 8) {
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(ta + pfa), (lds_ptr_t)junk, 4, 0, 0);
+        } else if (q == 9) {
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(tb + pfb), (lds_ptr_t)junk, 4, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 3 < KT) {
-        bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + (kt + 3) * BK) + pfa),
-                                         (lds_ptr_t)junk, 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + (kt + 3) * BK) + pfb),
-                                         (lds_ptr_t)junk, 4, 0, 0);
-      }
+      return;
     }
   }
   mma_rows(1, 1, 4);
@@ -478,8 +501,10 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
   const int wm = wave >> 1, wn = wave & 1;
   const int rr = lane >> 3, pp = lane & 7;
   const int row0 = wave * 8 + rr;
-  const bf16* atile = static_cast<const bf16*>(P.A) + m0 * P.lda + (int64_t)kt0 * BK;
-  const bf16* btile = static_cast<const bf16*>(P.W) + (int64_t)n0 * P.K + (int64_t)kt0 * BK;
+  const bf16* atile =
+      reinterpret_cast<const bf16*>(uniform_ptr(static_cast<const bf16*>(P.A) + m0 * P.lda + (int64_t)kt0 * BK));
+  const bf16* btile =
+      reinterpret_cast<const bf16*>(uniform_ptr(static_cast<const bf16*>(P.W) + (int64_t)n0 * P.K + (int64_t)kt0 * BK));
   // per-lane byte offsets of the 8 one-KB blocks this wave fills per operand
   // and stage (rows past M load row M-1; never stored)
   uint32_t offa[8], offb[8];
