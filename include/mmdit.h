@@ -375,7 +375,9 @@ typedef enum {
 /* Dense linear Y [M, N] = A [M, K] W^T, W [N, K], float32 accumulation, with
  * the fused epilogue.  For MMDIT_EPI_GATED_RES, gate is float32 with row
  * stride gate_stride (>= N, a multiple of 4, else MMDIT_E_INVALID /
- * MMDIT_E_UNSUPPORTED) and seg [M] int32.  a_silu != 0 applies SiLU to A. */
+ * MMDIT_E_UNSUPPORTED) and seg [M] int32.  a_silu != 0 applies SiLU to A.
+ * K (the row stride of A and W) must stay below 2^22 (the tiles address
+ * their operands with 32-bit offsets), else MMDIT_E_UNSUPPORTED. */
 mmdit_status mmdit_linear(mmdit_dtype dtype, int64_t M, int32_t N, int32_t K, const void* A,
                           const void* W, void* Y, int32_t epilogue, const float* gate,
                           int64_t gate_stride, const int32_t* seg, int32_t a_silu,

@@ -268,6 +268,21 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
+// Raw buffer resource over a wave-uniform base (no range clamp: the callers'
+// offsets stay below 2^32, which linear() checks through lda, K < 2^22).
+// Direct-to-LDS loads through it take a 32-bit lane offset and a scalar
+// offset, so no 64-bit address arithmetic per load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+template <int BYTES>
+__device__ __forceinline__ void buf_lds(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte loads");
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
 // A wave-uniform pointer held in scalar registers, so that base + 32-bit lane
 // offset addresses a direct load without 64-bit vector arithmetic per load.
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
@@ -391,7 +406,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 // segment of stage kt + 3 (into a scratch strip past the stages) so that its
 // loads find the rows in L2.
 template <bool NEXT, bool LOAD2>
-__device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, const uint32_t (&offa)[8],
+__device__ __forceinline__ void pipe_step(rsrc_t ra, rsrc_t rb, const uint32_t (&offa)[8],
                                           const uint32_t (&offb)[8], int kt, int KT, uint32_t pfa, uint32_t pfb,
                                           bf16* smem, const lds_char* lsm,
                                           const uint32_t (&aoff)[4], const uint32_t (&boff)[4],
@@ -451,13 +466,12 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
       // last one): the 18 direct loads go between the 12 remaining MFMAs of
       // the slice, two after each of the first eight, one after each of the
       // next two, each fenced so the compiler keeps them there (grouped, they
-      // held the matrix cores idle for the whole burst); bases in scalar
-      // registers, lane offsets 32-bit
-      const char* ab = uniform_ptr(atile + (kt + 2) * BK);
-      const char* bb = uniform_ptr(btile + (kt + 2) * BK);
+      // held the matrix cores idle for the whole burst); buffer loads: the
+      // tile's base in a scalar resource, the lane offset 32-bit, the k
+      // offset scalar
+      const uint32_t ks = (uint32_t)(kt + 2) * BK * 2;
       const int kt3 = kt + 3 < KT ? kt + 3 : KT - 1;
-      const char* ta = uniform_ptr(atile + kt3 * BK);
-      const char* tb = uniform_ptr(btile + kt3 * BK);
+      const uint32_t ks3 = (uint32_t)kt3 * BK * 2;
       bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
 #pragma unroll
       for (int q = 0; q < 12; ++q) {
@@ -465,12 +479,12 @@ __device__ __forceinline__ void pipe_step(const bf16* atile, const bf16* btile, 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (q < 8) {
-          load_lds16(ab + offa[q], smem + st * BM * BK + (wave + q * 4) * 512);
-          load_lds16(bb + offb[q], smem + 2 * BM * BK + st * BM * BK + (wave + q * 4) * 512);
+          buf_lds<16>(ra, offa[q], ks, smem + st * BM * BK + (wave + q * 4) * 512);
+          buf_lds<16>(rb, offb[q], ks, smem + 2 * BM * BK + st * BM * BK + (wave + q * 4) * 512);
         } else if (q == 8) {
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(ta + pfa), (lds_ptr_t)junk, 4, 0, 0);
+          buf_lds<4>(ra, pfa, ks3, junk);
         } else if (q == 9) {
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(tb + pfb), (lds_ptr_t)junk, 4, 0, 0);
+          buf_lds<4>(rb, pfb, ks3, junk);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -526,14 +540,14 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
   }
   bf16x8 fa[2][4], fb[2][4];
   const int KT = nkt < 0 ? P.K / BK : nkt;
+  const rsrc_t rsa = make_rsrc(atile), rsb = make_rsrc(btile);
   auto issue = [&](int k) {
     const int s2 = k & 1;
-    const char* ab = reinterpret_cast<const char*>(atile + k * BK);
-    const char* bb = reinterpret_cast<const char*>(btile + k * BK);
+    const uint32_t ks = (uint32_t)k * BK * 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      load_lds16(ab + offa[i], smem + s2 * BM * BK + (wave + i * 4) * 512);
-      load_lds16(bb + offb[i], smem + 2 * BM * BK + s2 * BM * BK + (wave + i * 4) * 512);
+      buf_lds<16>(rsa, offa[i], ks, smem + s2 * BM * BK + (wave + i * 4) * 512);
+      buf_lds<16>(rsb, offb[i], ks, smem + 2 * BM * BK + s2 * BM * BK + (wave + i * 4) * 512);
     }
   };
   // per-lane row of the L2 touches: A rows (wave 64 + lane), B rows likewise
@@ -546,10 +560,8 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
   if (KT > 1) issue(1);
   if (KT > 2) {
     bf16* junk = smem + 2 * 2 * BM * BK + wave * 128;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(atile + 2 * BK) + pfa), (lds_ptr_t)junk,
-                                     4, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(reinterpret_cast<const char*>(btile + 2 * BK) + pfb), (lds_ptr_t)junk,
-                                     4, 0, 0);
+    buf_lds<4>(rsa, pfa, 2 * BK * 2, junk);
+    buf_lds<4>(rsb, pfb, 2 * BK * 2, junk);
     __builtin_amdgcn_s_waitcnt(0x4F72);   // vmcnt(18): stage 0 landed
   } else if (KT == 2) {
     __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
@@ -565,12 +577,12 @@ __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int
     fa[0][i] = *reinterpret_cast<const lds_bf16x8*>(lsm + aoff[(i & 1) ? 2 : 0] + i * 4096);
   int kt = 0;
   for (; kt + 2 < KT; ++kt)
-    pipe_step<true, true>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+    pipe_step<true, true>(rsa, rsb, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
   if (KT >= 2) {
-    pipe_step<true, false>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+    pipe_step<true, false>(rsa, rsb, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
     ++kt;
   }
-  pipe_step<false, false>(atile, btile, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
+  pipe_step<false, false>(rsa, rsb, offa, offb, kt, KT, pfa, pfb, smem, lsm, aoff, boff, fa, fb, acc);
   __syncthreads();
 }
 
@@ -741,7 +753,6 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
     const int full = bt.tail_begin > 0 ? bt.tail_begin : (int)gridDim.x;
     tile = bt.xcd_remap ? xcd_tile(blockIdx.x, full) : (int)blockIdx.x;
   }
-  const int gtile = tile;
   const GemmProb& P = pick(bt, tile);
   int tm, tn;
   grouped_tile(tile, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
@@ -1347,6 +1358,10 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
     if (a.epilogue != epi || a.a_silu != silu) {
       set_error("linear: grouped problems must share the epilogue");
       return MMDIT_E_INVALID;
+    }
+    if (a.lda >= (1 << 22) || a.K >= (1 << 22)) {
+      set_error("linear: lda=%lld K=%d: both must stay below 2^22 (32-bit tile offsets)", (long long)a.lda, a.K);
+      return MMDIT_E_UNSUPPORTED;
     }
     if (a.M < 0 || a.N <= 0 || a.K <= 0 || a.lda < a.K || a.ldy < a.N) {
       set_error("linear: bad shape M=%lld N=%d K=%d lda=%lld ldy=%lld", (long long)a.M, a.N, a.K,

@@ -177,6 +177,9 @@ def test_validation_errors_before_launch(B):
     assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, fake, 66, fake, 0, None) == -3
     assert b"gate_stride" in lib.mmdit_last_error()
     assert lib.mmdit_linear(1, 64, 64, 64, fake, fake, fake, 3, fake, 60, fake, 0, None) == -1
+    # K at 2^22: the 32-bit tile offsets cannot address it
+    assert lib.mmdit_linear(1, 64, 64, 1 << 22, fake, fake, fake, 0, None, 0, None, 0, None) == -3
+    assert b"2^22" in lib.mmdit_last_error()
     # pack: too many samples
     arr = (B._Sample * 300)(*[B._Sample(1, 1, 1, 0)] * 300)
     assert lib.mmdit_pack(arr, 300, ctypes.byref(B._PackT()), None) == -1
