@@ -202,6 +202,17 @@ __device__ __forceinline__ int vsw(int d) { return (d >> 1) & 7; }
 // consecutive keys, so the matching V^T operand is one 16-byte LDS read.
 __device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// max and sum of a lane's value with that of lane l ^ 32 (v_permlane32_swap:
+// the two outputs hold, in every lane, its own value and the other half's)
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // NW waves of 32 queries per block.  Every query takes the same keys in the
 // same tile order whatever NW is, so the output does not depend on it.  Eight
 // waves share each K / V^T tile between twice the queries (half the tile
@@ -326,25 +337,30 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
     __builtin_amdgcn_sched_barrier(0);
     // register v of tile kt holds key kv0 + 32 kt + 16 (v / 8) + 8 g + v % 8;
     // only the last tile of a sample has keys past its end to mask
-    float mx = -INFINITY;
-    if (kv0 + BKV <= L) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
-    } else {
+    if (kv0 + BKV > L) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int32_t key = kv0 + kt * 32 + 16 * (v >> 3) + 8 * g + (v & 7);
           if (key >= L) sc[kt][v] = -INFINITY;
-          mx = fmaxf(mx, sc[kt][v]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // softmax in the log2 domain: p = 2^(s * log2(e)/sqrt(d) - m)
-    const float mn = fmaxf(m, mx * a.scale_log2);
+    // row maximum: four independent chains, then the other half's lanes
+    // (the same query's other keys) through a lane-half swap
+    float mq[4] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3]};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = kt == 0 ? 4 : 0; v < 16; ++v) mq[v & 3] = fmaxf(mq[v & 3], sc[kt][v]);
+    const float mx = half_swap_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+    // softmax in the log2 domain: p = 2^(s * log2(e)/sqrt(d) - m).  The
+    // reference m moves only when the tile's maximum exceeds it by more than
+    // 8 (p <= 256 otherwise, exact in float32 and in the bf16 operand's
+    // exponent range), so the rescale of O and the sum is rare after the
+    // first tiles; m is the same for both lanes of a query.
+    const float cand = mx * a.scale_log2;
+    const float mn = cand > m + 8.0f ? cand : m;
     const float corr = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
 #pragma unroll
@@ -384,7 +400,7 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = half_swap_sum(lsum);
   if (a.lse && jq < L && g == 0) a.lse[(int64_t)head * a.njp + pstart + jq] = m + log2f(lsum);
   if (jq < L) {
     bf16* o = out_row<bf16>(a, jq, Tb, t0, i0) + head * D;
