@@ -13,12 +13,16 @@
 // transposed, S^T = K Q^T, so each lane owns one query: its row maximum and
 // sum are lane-local (one cross-half exchange), and the probabilities feed
 // O^T = V^T P^T straight from registers; V is transposed while it is staged.
+// Software-pipelined by one tile: the softmax of tile i (vector ALU) runs
+// while the scores of tile i + 1 issue on the matrix cores.
 // attn_simt_kernel (float32, or any head_dim): 64 queries per block, four
 // lanes per query, per-key online softmax.
 #include "common.h"
 
 #include <math.h>
 #include <string.h>
+
+#include <type_traits>
 
 namespace mmdit {
 
@@ -151,12 +155,6 @@ __global__ void __launch_bounds__(256) attn_simt_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------- MFMA
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
-}
 
 // V^T[head][d][padded joint token] (bf16) from the v columns of the QKV
 // buffers; tokens past the end of a sample are written as zeros.
@@ -226,7 +224,6 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
   constexpr int KROWS = 512 / D;         // K rows per 1-KB block
   constexpr int KB = BKV / KROWS / NW;   // K blocks per wave per tile
   constexpr int VB = D / 8 / NW;         // V^T blocks (8 rows) per wave per tile
-  constexpr int STAGE = 2 * BKV * D;     // bf16 elements per stage (K then V^T)
   static_assert(KB >= 1 && VB >= 1, "tile split");
   extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
 
@@ -252,13 +249,16 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
     for (int s = 0; s < QS; ++s) qf[s] = bf16x8{};
   }
 
-  // per-lane sources of the 1-KB blocks this wave fills
+  // per-lane sources of the 1-KB blocks this wave fills.  V^T: byte offsets
+  // from the buffer's start (below 2^32: checked on the host), the tile's key
+  // offset scalar.
   const int kr = lane / (D / 8), kp = lane % (D / 8);     // row in block, chunk position
-  const bf16* vsrc[VB];
+  const rsrc_t rvt = make_rsrc(vt);
+  uint32_t voff[VB];
 #pragma unroll
   for (int i = 0; i < VB; ++i) {
     const int d = (wave + NW * i) * 8 + (lane >> 3);
-    vsrc[i] = vt + ((int64_t)head * D + d) * njp + pstart + (((lane & 7) ^ vsw(d)) << 3);
+    voff[i] = (uint32_t)((((int64_t)head * D + d) * njp + pstart + (((lane & 7) ^ vsw(d)) << 3)) * 2);
   }
   // K row of joint key j: text row t0 + j for j < Tb, image row i0 + j - Tb
   // after it; both bases are offset so that base + j * 3H addresses key j
@@ -267,21 +267,38 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
   const uint32_t rowb = 3u * (uint32_t)a.H * 2u;
   const char* ktxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.qkv_txt) + (int64_t)t0 * 3 * a.H + a.H + head * D);
   const char* kimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.qkv_img) + ((int64_t)i0 - Tb) * 3 * a.H + a.H + head * D);
+  const rsrc_t rtxt = make_rsrc(uniform_ptr(ktxt)), rimg = make_rsrc(uniform_ptr(kimg));
   const int wu = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t kswc[KB];
+  uint32_t kswc[KB], koff[KB];
 #pragma unroll
-  for (int i = 0; i < KB; ++i) kswc[i] = ((kp ^ ksw<D>((wave + NW * i) * KROWS + kr)) << 4);
-  auto issue = [&](int32_t kv0, int st) {
-    bf16* ks = smem + st * STAGE;
-    bf16* vs = ks + BKV * D;
+  for (int i = 0; i < KB; ++i) {
+    kswc[i] = ((kp ^ ksw<D>((wave + NW * i) * KROWS + kr)) << 4);
+    koff[i] = (uint32_t)((wu + NW * i) * KROWS + kr) * rowb + kswc[i];
+  }
+  // K tiles in two stages at smem + s BKV D, V^T tiles in two stages after
+  // them.  A whole K tile inside the text or inside the image rows loads
+  // through one segment's resource with the tile's offset scalar; a tile that
+  // straddles the two or runs past L (keys past L load key L - 1 and are
+  // masked in the scores) takes per-lane addresses.
+  auto issue_k = [&](int32_t kv0, int st) {
+    bf16* ks = smem + st * BKV * D;
+    if (kv0 + BKV <= L && (kv0 + BKV <= Tb || kv0 >= Tb)) {
+      const rsrc_t r = kv0 < Tb ? rtxt : rimg;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int blk = wu + NW * i;
-      const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);   // keys past L are masked in the scores
-      load_lds16((key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]), ks + blk * 512);
+      for (int i = 0; i < KB; ++i) buf_lds16(r, koff[i], (uint32_t)kv0 * rowb, ks + (wu + NW * i) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int blk = wu + NW * i;
+        const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);
+        load_lds16((key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]), ks + blk * 512);
+      }
     }
+  };
+  auto issue_v = [&](int32_t kv0, int st) {
+    bf16* vs = smem + (2 + st) * BKV * D;
 #pragma unroll
-    for (int i = 0; i < VB; ++i) load_lds16(vsrc[i] + kv0, vs + (wu + NW * i) * 512);
+    for (int i = 0; i < VB; ++i) buf_lds16(rvt, voff[i], (uint32_t)kv0 * 2, vs + (wu + NW * i) * 512);
   };
 
   f32x16 oacc[DT];
@@ -292,51 +309,48 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
   float m = -INFINITY, lsum = 0.f;
 
   const int ntile = (L + BKV - 1) / BKV;
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   const int prow = (l32 & 16) | kperm(l32 & 15);
-  for (int it = 0; it < ntile; ++it) {
-    const int st = it & 1;
-    const int32_t kv0 = it * BKV;
-    if (it + 1 < ntile) issue(kv0 + BKV, st ^ 1);
-    const bf16* ks = smem + st * STAGE;
-    const bf16* vs = ks + BKV * D;
-    // S^T for the two 32-key halves, their k steps interleaved (independent
-    // accumulators back to back) and the K fragments read two steps ahead
-    f32x16 sc[2];
+  const int r0 = prow, r1 = 32 + prow;
+  auto kfrag = [&](const bf16* ks, int r, int s) {
+    return *reinterpret_cast<const bf16x8*>(ks + r * D + (((s * 2 + g) ^ ksw<D>(r)) << 3));
+  };
+  // S^T of the 64 keys in K stage kst, the two 32-key halves' k steps
+  // interleaved (independent accumulators back to back), the K fragments read
+  // two steps ahead
+  auto scores = [&](int kst, f32x16 (&sc)[2]) {
+    const bf16* ks = smem + kst * BKV * D;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
-    const int r0 = prow, r1 = 32 + prow;
-    auto kfrag = [&](int r, int s) {
-      return *reinterpret_cast<const bf16x8*>(ks + r * D + (((s * 2 + g) ^ ksw<D>(r)) << 3));
-    };
     bf16x8 kf[3][2];
-    __builtin_amdgcn_sched_barrier(0);
-    kf[0][0] = kfrag(r0, 0);
-    kf[0][1] = kfrag(r1, 0);
-    kf[1][0] = kfrag(r0, 1);
-    kf[1][1] = kfrag(r1, 1);
+    kf[0][0] = kfrag(ks, r0, 0);
+    kf[0][1] = kfrag(ks, r1, 0);
+    kf[1][0] = kfrag(ks, r0, 1);
+    kf[1][1] = kfrag(ks, r1, 1);
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       if (s + 2 < QS) {
-        kf[(s + 2) % 3][0] = kfrag(r0, s + 2);
-        kf[(s + 2) % 3][1] = kfrag(r1, s + 2);
+        kf[(s + 2) % 3][0] = kfrag(ks, r0, s + 2);
+        kf[(s + 2) % 3][1] = kfrag(ks, r1, s + 2);
       }
       sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3][0], qf[s], sc[0], 0, 0, 0);
       sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3][1], qf[s], sc[1], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read: steps 0, 1
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      if (s + 2 < QS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // register v of tile kt holds key kv0 + 32 kt + 16 (v / 8) + 8 g + v % 8;
-    // only the last tile of a sample has keys past its end to mask
+  };
+
+  // One 64-key tile it, whose scores sc were computed by the previous step:
+  // the loads of K tile it + 2 and V^T tile it + 1 issue first (their stages
+  // were freed by the last barrier); then the softmax of tile it (vector ALU)
+  // runs while the scores of tile it + 1 (NEXT) go into sn on the matrix
+  // cores; then O^T += V^T P^T for tile it.  Register v of score tile kt holds
+  // key kv0 + 32 kt + 16 (v / 8) + 8 g + v % 8.
+  auto tile = [&](int it, f32x16 (&sc)[2], f32x16 (&sn)[2], auto next_c) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int st = it & 1;
+    const int32_t kv0 = it * BKV;
+    if (NEXT) issue_v(kv0 + BKV, st ^ 1);
+    if (it + 2 < ntile) issue_k(kv0 + 2 * BKV, st);
     if (kv0 + BKV > L) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -346,8 +360,10 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
           if (key >= L) sc[kt][v] = -INFINITY;
         }
     }
-    // row maximum: four independent chains, then the other half's lanes
-    // (the same query's other keys) through a lane-half swap
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) scores(st ^ 1, sn);
+    // row maximum: four independent chains, then the other half's lanes (the
+    // same query's other keys) through a lane-half swap
     float mq[4] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3]};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -367,38 +383,81 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, const
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kt][v] = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], a.scale_log2, -mn));
+    // P as the bf16 operand of the PV product, four 16-key steps; the row sum
+    // takes the same bf16-rounded P, two at a time (v_dot2 against (1, 1)), so
+    // the normaliser matches the weights
+    bf16x8 pf[4];
+    float ps = 0.f;
+    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pf[ks2][u] = (bf16)sc[ks2 >> 1][8 * (ks2 & 1) + u];
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 0, 1), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 2, 3), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 4, 5), one2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 6, 7), one2, ps, false);
+    }
+    if constexpr (NEXT) {
+      // the scores' K reads and MFMAs with the softmax's vector work between them
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        if (s + 2 < QS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (__any(corr != 1.0f)) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[t][v] *= corr;
     }
-    // O^T[d][query] += V^T[d][keys] P^T[keys][query]; step ks covers keys
-    // 16 ks .. 16 ks + 15, this lane's 8 of them being 16 ks + 8 g + 0..7.
-    // The row sum takes the same bf16-rounded P as the product, two at a
-    // time (v_dot2 against (1, 1)), so the normaliser matches the weights.
-    float ps = 0.f;
-    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+    // O^T[d][query] += V^T[d][keys] P^T[keys][query]; step ks2 covers keys
+    // 16 ks2 .. 16 ks2 + 15, this lane's 8 of them being 16 ks2 + 8 g + 0..7
+    const bf16* vs = smem + (2 + st) * BKV * D;
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2) {
-      bf16x8 pf;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pf[u] = (bf16)sc[ks2 >> 1][8 * (ks2 & 1) + u];
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, ps, false);
       const int c = 2 * ks2 + g;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const int d = t * 32 + l32;
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + d * BKV + ((c ^ vsw(d)) << 3));
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks2], oacc[t], 0, 0, 0);
       }
     }
     lsum = lsum * corr + ps;
+    // V^T tile it + 1 and K tile it + 2 have landed for every wave
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  // K tiles 0 and 1 and V^T tile 0, the scores of tile 0, then a barrier so
+  // that K stage 0 may be refilled
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (ntile > 1) issue_k(BKV, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(0, sa);
+  __syncthreads();
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  int it = 0;
+  for (; it + 2 < ntile; it += 2) {
+    tile(it, sa, sb, yes{});
+    tile(it + 1, sb, sa, yes{});
+  }
+  if (ntile - it == 2) {
+    tile(it, sa, sb, yes{});
+    tile(it + 1, sb, sa, no{});
+  } else {
+    tile(it, sa, sb, no{});
   }
   lsum = half_swap_sum(lsum);
   if (a.lse && jq < L && g == 0) a.lse[(int64_t)head * a.njp + pstart + jq] = m + log2f(lsum);
@@ -1073,8 +1132,10 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
       set_error("mmdit_attention: workspace needs %zu bytes, got %zu", (size_t)vt_elems * 2, ws_bytes);
       return MMDIT_E_WORKSPACE;
     }
-    if (vt_elems / a.H > INT32_MAX || (double)pk->max_joint * 3.0 * a.H * 2.0 >= 2147483648.0) {
-      set_error("mmdit_attention: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31)");
+    if (vt_elems / a.H > INT32_MAX || (double)pk->max_joint * 3.0 * a.H * 2.0 >= 2147483648.0 ||
+        (double)vt_elems * 2.0 >= 4294967296.0) {
+      set_error("mmdit_attention: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31, "
+                "the V^T staging < 2^32 bytes)");
       return MMDIT_E_UNSUPPORTED;
     }
     const int32_t njp = (int32_t)(vt_elems / a.H);
@@ -1092,7 +1153,7 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
     a.nq = (int32_t)cdiv(pk->max_joint, 32 * nw);
     a.nB = pk->B;
     dim3 grid((unsigned)(8 * cdiv((int64_t)a.nq * heads * pk->B, 8)));
-    const size_t lds = 2 * 2 * 64 * D * sizeof(bf16);
+    const size_t lds = (2 + 2) * 64 * D * sizeof(bf16);   // two K stages, two V^T stages
     const void* fn = D == 128 ? (nw == 8 ? (const void*)attn_mfma_kernel<128, 8> : (const void*)attn_mfma_kernel<128, 4>)
                               : (nw == 8 ? (const void*)attn_mfma_kernel<64, 8> : (const void*)attn_mfma_kernel<64, 4>);
     static bool attr[4] = {false, false, false, false};

@@ -346,4 +346,41 @@ mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t 
                                 const float* lse, const void* do_img, const void* do_txt, void* dqkv_img,
                                 void* dqkv_txt, void* ws, size_t ws_bytes, hipStream_t s);
 
+// Direct global -> LDS loads: each lane's 16 bytes land at lds_block + 16 *
+// lane (the LDS address of the wave instruction is wave-uniform).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
+}
+
+// Raw buffer resource over a wave-uniform base (no range clamp: every caller
+// keeps its offsets below 2^32 and checks that on the host).
+// Direct-to-LDS loads through it take a 32-bit lane offset and a scalar
+// offset, so no 64-bit address arithmetic per load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+template <int BYTES>
+__device__ __forceinline__ void buf_lds(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte loads");
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+// A wave-uniform pointer held in scalar registers, so that base + 32-bit lane
+// offset addresses a direct load without 64-bit vector arithmetic per load.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void buf_lds16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  buf_lds<16>(r, voff, soff, lds);
+}
+
 }  // namespace mmdit

@@ -236,9 +236,6 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(GemmBatch bt) {
 // 8 chunks of 16 B; chunk c of row r sits at position c ^ swz8(r), which the
 // loads realise by choosing each lane's global chunk, so the 16-B fragment
 // reads of the MFMA operands are free of bank conflicts.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -264,33 +261,6 @@ __device__ __forceinline__ void grouped_tile(int tile, int tiles_m, int tiles_n,
   tn = r / gsize;
 }
 
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_block) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_block, 16, 0, 0);
-}
-
-// Raw buffer resource over a wave-uniform base (no range clamp: the callers'
-// offsets stay below 2^32, which linear() checks through lda, K < 2^22).
-// Direct-to-LDS loads through it take a 32-bit lane offset and a scalar
-// offset, so no 64-bit address arithmetic per load.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
-}
-template <int BYTES>
-__device__ __forceinline__ void buf_lds(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte loads");
-  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
-}
-
-// A wave-uniform pointer held in scalar registers, so that base + 32-bit lane
-// offset addresses a direct load without 64-bit vector arithmetic per load.
-__device__ __forceinline__ const char* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
-}
 
 // acc[TM][TN] += A[m0:m0+BM, K-steps kt0 .. kt0+nkt) W[n0:n0+BN, ...]^T for one
 // tile.  Operands go global -> LDS directly (global_load_lds_dwordx4: one wave
