@@ -405,6 +405,28 @@ mmdit_status mmdit_final_mod(const mmdit_dims* dims, const void* w_out, const mm
 mmdit_status rf_make_xt(const mmdit_pack_t* pack, mmdit_dtype dtype, int32_t C, const void* z,
                         const void* eps, const float* t, void* zt, mmdit_stream stream);
 
+/* The embedding with the noising folded into it (the stack-level fusion of
+ * [blog] 2.2(3) and [hyper] 方法): x_txt = tau W_txt^T as in mmdit_embed and
+ * x_img = z_t W_in^T with z_t the rf_make_xt noising of z, eps (t [B] float32)
+ * formed while the GEMM stages its A operand; zt [n_img, C] receives z_t (the
+ * embedding backward reads it).  Bit for bit rf_make_xt then mmdit_embed
+ * (bfloat16 with C % 64 == 0 and H % 128 == 0 fuse; otherwise the two run in
+ * sequence).  NULL pointers -> MMDIT_E_INVALID. */
+mmdit_status rf_embed(const mmdit_dims* dims, const void* w_in, const void* w_txt, const mmdit_pack_t* pack,
+                      const void* z, const void* eps, const float* t, const void* tau, void* x_img,
+                      void* x_txt, void* zt, mmdit_stream stream);
+
+/* The final layer after its modulation and the flow-matching loss in one call
+ * ([blog] 2.2(2) and 2.2(3)): v as mmdit_final_mod (modf float32 [B][2H]),
+ * then sse and loss as rf_loss, the per-row sums of squared residuals taken
+ * inside the final GEMM's split-K reduction (when the product runs split-K;
+ * otherwise by the loss's row-sum kernel).  Bit for bit mmdit_final_mod then
+ * rf_loss.  ws: mmdit_workspace_size bytes (the final layer's workspace
+ * followed by the row sums); too small -> MMDIT_E_WORKSPACE. */
+mmdit_status rf_final_loss(const mmdit_dims* dims, const void* w_out, const mmdit_pack_t* pack,
+                           const float* modf, const void* x_img, const void* z, const void* eps, void* v,
+                           float* sse, float* loss, void* ws, size_t ws_bytes, mmdit_stream stream);
+
 /* Flow-matching loss ([hyper] 方法 objective; [blog] 2.2(2), target latent
  * only): sse[b] = sum over sample b's target rows of (v - (z - eps))^2 and
  * loss[0] = mean_b sse[b] / (tgt_len_b * C), float32.  v [n_tgt, C]; z, eps

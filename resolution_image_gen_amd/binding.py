@@ -13,7 +13,7 @@ import os
 __all__ = [
     "MmditError", "Pack", "Dims", "lib_path", "pack_plan", "pack", "pack_gather",
     "workspace_size", "workspace_layout", "cond", "modulation", "embed", "block_fwd",
-    "rms_modulate", "qk_norm_rope", "attention", "linear", "final", "rf_make_xt",
+    "rms_modulate", "qk_norm_rope", "attention", "linear", "final", "rf_make_xt", "rf_embed", "rf_final_loss",
     "rf_loss", "rf_loss_noalloc", "rf_nft_loss", "rf_euler_step", "rf_pack_latent", "EPI_STORE", "EPI_STORE_F32", "EPI_GELU",
     "EPI_GATED_RES", "MAX_SAMPLES",
 ]
@@ -114,6 +114,8 @@ def _load():
         "mmdit_final": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "mmdit_final_mod": (_i32, [D, _vp, P, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_make_xt": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+        "rf_embed": (_i32, [D, _vp, _vp, P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "rf_final_loss": (_i32, [D, _vp, P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "rf_loss_noalloc": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
         "rf_nft_loss": (_i32, [P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -405,6 +407,16 @@ def final_mod(dims, w_out, pk, modf, x_img, v, ws, stream=None):
     """final with its adaLN vectors from modulation(w_fmod, 2, c)."""
     _ck(_lib.mmdit_final_mod(ctypes.byref(dims.c), _p(w_out), pk.ref, _p(modf), _p(x_img), _p(v),
                              _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rf_embed(dims, w_in, w_txt, pk, z, eps, t, tau, x_img, x_txt, zt, stream=None):
+    _ck(_lib.rf_embed(ctypes.byref(dims.c), _p(w_in), _p(w_txt), pk.ref, _p(z), _p(eps), _p(t), _p(tau),
+                      _p(x_img), _p(x_txt), _p(zt), _stream(stream)))
+
+
+def rf_final_loss(dims, w_out, pk, modf, x_img, z, eps, v, sse, loss, ws, stream=None):
+    _ck(_lib.rf_final_loss(ctypes.byref(dims.c), _p(w_out), pk.ref, _p(modf), _p(x_img), _p(z), _p(eps), _p(v),
+                           _p(sse), _p(loss), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rf_make_xt(pk, z, eps, t, zt, stream=None):

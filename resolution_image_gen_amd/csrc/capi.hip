@@ -88,6 +88,8 @@ mmdit_status pack_impl(const mmdit_sample*, int32_t, mmdit_pack_t*, hipStream_t)
 mmdit_status gather_impl(const mmdit_pack_t*, int32_t, const void* const*, int32_t, mmdit_dtype, void*, hipStream_t);
 mmdit_status make_xt_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const float*, void*, hipStream_t);
 mmdit_status loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, void*, size_t, hipStream_t);
+mmdit_status row_sse_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, hipStream_t);
+mmdit_status loss_finalize_impl(const mmdit_pack_t*, int32_t, const float*, float*, float*, hipStream_t);
 mmdit_status loss_noalloc_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, float*, float*, hipStream_t);
 mmdit_status nft_loss_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, const void*, const float*, float*, float*, void*, size_t, hipStream_t);
 mmdit_status loss_grad_impl(const mmdit_pack_t*, mmdit_dtype, int32_t, const void*, const void*, const void*, void*, hipStream_t);
@@ -301,8 +303,8 @@ size_t mmdit_workspace_size(const mmdit_dims* d, const mmdit_pack_t* pk) {
   if (check_dims(d, "mmdit_workspace_size") != MMDIT_OK || check_pack(pk, "mmdit_workspace_size") != MMDIT_OK)
     return 0;
   size_t w = block_layout(d, pk).end;
-  size_t f = final_ws(d, pk);
   size_t l = align256((size_t)pk->n_tgt * 4 + 4);
+  size_t f = final_ws(d, pk) + l;   // rf_final_loss: the final layer's and the row sums
   size_t c = align256((size_t)pk->B * (d->t_dim + d->hidden) * esize(d->dtype) + 256);
   if (f > w) w = f;
   if (l > w) w = l;
@@ -1415,7 +1417,8 @@ namespace {
 // Final layer after its modulation: h = rms(x)(1 + scale_f) + shift_f on the
 // target rows, v = h W_out^T.  modf float32 [B][2H] (shift, scale).
 mmdit_status final_rest_impl(const mmdit_dims* d, const void* w_out, const mmdit_pack_t* pk, const float* modf,
-                             const void* x_img, void* v, void* ws, hipStream_t s) {
+                             const void* x_img, void* v, void* ws, hipStream_t s, const void* sse_z = nullptr,
+                             const void* sse_e = nullptr, float* row_sse = nullptr, int32_t* sse_done = nullptr) {
   const int32_t H = d->hidden;
   void* hf = static_cast<char*>(ws) + align256((size_t)pk->B * 2 * H * 4);
   MMDIT_TRY(rms_modulate_impl(d->dtype, pk->n_tgt, H, x_img, pk->tgt_row, pk->seg_img, modf, 2 * H, 0, H, hf,
@@ -1424,6 +1427,13 @@ mmdit_status final_rest_impl(const mmdit_dims* d, const void* w_out, const mmdit
   b.tag = "final_out";
   b.partial = reinterpret_cast<float*>(static_cast<char*>(hf) + align256((size_t)pk->n_tgt * H * esize(d->dtype)));
   b.partial_elems = (int64_t)8 * pk->n_tgt * d->c_lat;
+  if (row_sse) {
+    b.sse_z = sse_z;
+    b.sse_e = sse_e;
+    b.sse_row = pk->tgt_row;
+    b.row_sse = row_sse;
+    b.sse_done = sse_done;
+  }
   return linear(d->dtype, &b, 1, s);
 }
 
@@ -1478,6 +1488,69 @@ mmdit_status mmdit_final_mod(const mmdit_dims* d, const void* w_out, const mmdit
 mmdit_status rf_make_xt(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* z, const void* eps,
                         const float* t, void* zt, mmdit_stream stream) {
   return make_xt_impl(pk, dt, C, z, eps, t, zt, (hipStream_t)stream);
+}
+
+mmdit_status rf_embed(const mmdit_dims* d, const void* w_in, const void* w_txt, const mmdit_pack_t* pk,
+                      const void* z, const void* eps, const float* t, const void* tau, void* x_img, void* x_txt,
+                      void* zt, mmdit_stream stream) {
+  const char* who = "rf_embed";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  hipStream_t s = (hipStream_t)stream;
+  if (pk->n_txt > 0) {
+    MMDIT_TRY(need(w_txt, who, "w_txt"));
+    MMDIT_TRY(need(tau, who, "tau"));
+    MMDIT_TRY(need(x_txt, who, "x_txt"));
+    LinearArgs a = mk(pk->n_txt, d->hidden, d->d_txt, tau, w_txt, x_txt, MMDIT_EPI_STORE);
+    a.tag = "embed_txt";
+    MMDIT_TRY(linear(d->dtype, &a, 1, s));
+  }
+  if (pk->n_img == 0) return MMDIT_OK;
+  MMDIT_TRY(need(w_in, who, "w_in"));
+  MMDIT_TRY(need(z, who, "z"));
+  MMDIT_TRY(need(eps, who, "eps"));
+  MMDIT_TRY(need(t, who, "t"));
+  MMDIT_TRY(need(x_img, who, "x_img"));
+  MMDIT_TRY(need(zt, who, "zt"));
+  if (d->dtype == MMDIT_BF16 && d->c_lat % 64 == 0 && d->hidden % 128 == 0) {
+    // the noising in the A staging of the embedding GEMM (which also writes zt)
+    LinearArgs a = mk(pk->n_img, d->hidden, d->c_lat, z, w_in, x_img, MMDIT_EPI_STORE);
+    a.tag = "embed_img_xt";
+    XtArgs x = {eps, t, pk->seg_img, pk->pos_img, zt};
+    return linear_xt(a, x, s);
+  }
+  MMDIT_TRY(make_xt_impl(pk, d->dtype, d->c_lat, z, eps, t, zt, s));
+  LinearArgs a = mk(pk->n_img, d->hidden, d->c_lat, zt, w_in, x_img, MMDIT_EPI_STORE);
+  a.tag = "embed_img";
+  return linear(d->dtype, &a, 1, s);
+}
+
+mmdit_status rf_final_loss(const mmdit_dims* d, const void* w_out, const mmdit_pack_t* pk, const float* modf,
+                           const void* x_img, const void* z, const void* eps, void* v, float* sse, float* loss,
+                           void* ws, size_t ws_bytes, mmdit_stream stream) {
+  const char* who = "rf_final_loss";
+  MMDIT_TRY(check_dims(d, who));
+  MMDIT_TRY(check_pack(pk, who));
+  MMDIT_TRY(need(loss, who, "loss"));
+  if (pk->B > 0) MMDIT_TRY(need(sse, who, "sse"));
+  const size_t fb = final_ws(d, pk), lb = align256((size_t)pk->n_tgt * 4 + 4);
+  if (!ws || ws_bytes < fb + lb) {
+    set_error("%s: workspace needs %zu bytes, got %zu", who, fb + lb, ws_bytes);
+    return MMDIT_E_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  float* row_sse = reinterpret_cast<float*>(static_cast<char*>(ws) + fb);
+  if (pk->n_tgt > 0) {
+    MMDIT_TRY(check_final_args(d, w_out, pk, x_img, v, ws, ws_bytes, who));
+    MMDIT_TRY(need(modf, who, "modf"));
+    MMDIT_TRY(need(z, who, "z"));
+    MMDIT_TRY(need(eps, who, "eps"));
+    // the row sums ride in the final GEMM's split-K reduction when it has one
+    int32_t done = 0;
+    MMDIT_TRY(final_rest_impl(d, w_out, pk, modf, x_img, v, ws, s, z, eps, row_sse, &done));
+    if (!done) MMDIT_TRY(row_sse_impl(pk, d->dtype, d->c_lat, v, z, eps, row_sse, s));
+  }
+  return loss_finalize_impl(pk, d->c_lat, row_sse, sse, loss, s);
 }
 
 mmdit_status rf_loss(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,

@@ -103,6 +103,16 @@ __device__ __forceinline__ float erf_as(float x) {
       t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
   return copysignf(1.0f - poly * __expf(-ax * ax), x);
 }
+// Rectified-flow noising of one element, z_t = (1 - t) z + t eps, with its
+// multiply-add written out: the noising kernel and the image embedding's
+// fused A staging give the same bits.
+__device__ __forceinline__ float rf_xt(float z, float e, float t) { return fmaf(t, e, (1.0f - t) * z); }
+// One squared residual of the flow-matching loss added to a sum, written out
+// (the loss kernels and the final layer's fused row sums give the same bits).
+__device__ __forceinline__ float rf_sq_acc(float v, float z, float e, float acc) {
+  const float d = v - (z - e);
+  return fmaf(d, d, acc);
+}
 // GELU in its erf form, 0.5 x (1 + erf(x / sqrt 2)).
 __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 // Its derivative Phi(x) + x phi(x), with the same erf.
@@ -212,7 +222,27 @@ struct LinearArgs {
   const float* g_q;        // kEpiQkRope*: QK-norm gains [D]
   const float* g_k;
   const QkEpilogue* qk;    // kEpiQkRope*: dims and rotation table
+  // MMDIT_EPI_STORE, bf16: when the product runs split-K, its reduction also
+  // writes row_sse[r] = sum_c (Y[r][c] - (z - eps)[sse_row[r]][c])^2 (z, eps
+  // [rows, N] model dtype) and sets *sse_done = 1; otherwise *sse_done stays.
+  const void* sse_z;
+  const void* sse_e;
+  const int32_t* sse_row;
+  float* row_sse;
+  int32_t* sse_done;
 };
+// The noising of the image embedding's A operand (linear_xt): A holds z and
+// eps [M, K] the noise; row m is noised with t[seg[m]] when pos[3 m] == 0 (a
+// frame-0, i.e. target, row) and taken as z otherwise; zt [M, K] (optional)
+// receives the bf16 z_t.
+struct XtArgs {
+  const void* eps;
+  const float* t;
+  const int32_t* seg;
+  const int32_t* pos;
+  void* zt;
+};
+mmdit_status linear_xt(const LinearArgs& a, const XtArgs& x, hipStream_t s);
 // Epilogues used inside the library only (the public ones are mmdit_epilogue):
 constexpr int kEpiGeluAux = 4;      // Y = GELU(acc) and aux = acc (the pre-activation kept for backward)
 constexpr int kEpiGatedResAux = 5;  // Y += gate[seg] * acc and aux = acc (the branch kept for backward)

@@ -47,7 +47,7 @@ __global__ void make_xt_kernel(int64_t n_img, int32_t C, const T* __restrict__ z
       float ev[8];
       Vec8<T>::load(eps + off, ev);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) zv[i] = (1.0f - tb) * zv[i] + tb * ev[i];
+      for (int i = 0; i < 8; ++i) zv[i] = rf_xt(zv[i], ev[i], tb);
     }
     Vec8<T>::store(zt + off, zv);
   }
@@ -73,10 +73,7 @@ __global__ void row_sse_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
       Vec8<T>::load(z + src * C + c8 * 8, zv);
       Vec8<T>::load(eps + src * C + c8 * 8, ev);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float d = vv[i] - (zv[i] - ev[i]);
-        acc += d * d;
-      }
+      for (int i = 0; i < 8; ++i) acc = rf_sq_acc(vv[i], zv[i], ev[i], acc);
     }
     acc = group_sum(acc, 16);
     if (lane16 == 0) row_sse[row] = acc;
@@ -107,10 +104,8 @@ __global__ void row_nft_kernel(int64_t n_tgt, int32_t C, const T* __restrict__ v
       Vec8<T>::load(eps + src * C + c8 * 8, ev);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float tg = zv[i] - ev[i];
-        const float dp = pv[i] - tg, dn = nv[i] - tg;
-        ap += dp * dp;
-        an += dn * dn;
+        ap = rf_sq_acc(pv[i], zv[i], ev[i], ap);
+        an = rf_sq_acc(nv[i], zv[i], ev[i], an);
       }
     }
     ap = group_sum(ap, 16);
@@ -295,6 +290,25 @@ mmdit_status loss_grad_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, c
   return launch_check("loss_grad_kernel", s);
 }
 
+mmdit_status row_sse_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v, const void* z,
+                          const void* eps, float* row_sse, hipStream_t s) {
+  if (pk->n_tgt == 0) return MMDIT_OK;
+  const int g = grid_for(pk->n_tgt * 16, 256);
+  if (dt == MMDIT_BF16)
+    MMDIT_LAUNCH(row_sse_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, (const bf16*)v, (const bf16*)z,
+                 (const bf16*)eps, pk->tgt_row, row_sse);
+  else
+    MMDIT_LAUNCH(row_sse_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_tgt, C, (const float*)v, (const float*)z,
+                 (const float*)eps, pk->tgt_row, row_sse);
+  return launch_check("row_sse_kernel", s);
+}
+
+mmdit_status loss_finalize_impl(const mmdit_pack_t* pk, int32_t C, const float* row_sse, float* sse, float* loss,
+                                hipStream_t s) {
+  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse, sse, loss);
+  return launch_check("loss_finalize_kernel", s);
+}
+
 mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v,
                        const void* z, const void* eps, float* sse, float* loss, void* ws,
                        size_t ws_bytes, hipStream_t s) {
@@ -317,19 +331,8 @@ mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const 
     return MMDIT_E_UNSUPPORTED;
   }
   float* row_sse = static_cast<float*>(ws);
-  if (pk->n_tgt > 0) {
-    int g = grid_for(pk->n_tgt * 16, 256);
-    if (dt == MMDIT_BF16)
-      MMDIT_LAUNCH(row_sse_kernel<bf16>, dim3(g), dim3(256), 0, s, pk->n_tgt, C,
-                         (const bf16*)v, (const bf16*)z, (const bf16*)eps, pk->tgt_row, row_sse);
-    else
-      MMDIT_LAUNCH(row_sse_kernel<float>, dim3(g), dim3(256), 0, s, pk->n_tgt, C,
-                         (const float*)v, (const float*)z, (const float*)eps, pk->tgt_row, row_sse);
-    MMDIT_TRY(launch_check("row_sse_kernel", s));
-  }
-  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse,
-                     sse, loss);
-  return launch_check("loss_finalize_kernel", s);
+  MMDIT_TRY(row_sse_impl(pk, dt, C, v, z, eps, row_sse, s));
+  return loss_finalize_impl(pk, C, row_sse, sse, loss, s);
 }
 
 mmdit_status nft_loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* vp, const void* vn,

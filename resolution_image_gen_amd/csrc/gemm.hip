@@ -32,6 +32,11 @@ struct GemmProb {
   const float* rope_cs; // kEpiQkRope*: [M][D/2] (cos, sin) per row and rotation pair (NULL: no rotation)
   const float* g_q;     // kEpiQkRope*: QK-norm gains [D]
   const float* g_k;
+  const bf16* xt_e;     // noised A staging (SITE 2): eps, per-sample t, per-row sample and position, z_t copy
+  const float* xt_t;
+  const int32_t* xt_seg;
+  const int32_t* xt_pos;
+  bf16* xt_zt;
   int64_t lda, ldy, gate_stride, M;
   int32_t N, K;
   int32_t tiles_n;
@@ -60,6 +65,13 @@ struct GemmBatch {
   // gemm_sk_fixup_kernel sums in k order
   int32_t sk_full, sk_tail, sk_S, sk_P;
   float* sk_partial;    // [sk_tail][sk_S][256][256]
+  // split-K reduction of a bf16 store that also sums the flow-matching
+  // squared residuals of each row (row_sse non-NULL)
+  const bf16* sse_z;
+  const bf16* sse_e;
+  const int32_t* sse_row;
+  float* row_sse;
+  int32_t* sse_done;
 };
 
 __device__ __forceinline__ const GemmProb& pick(const GemmBatch& bt, int& tile) {
@@ -266,7 +278,12 @@ __device__ __forceinline__ void grouped_tile(int tile, int tiles_m, int tiles_n,
 // tile.  Operands go global -> LDS directly (global_load_lds_dwordx4: one wave
 // instruction fills 1 KB), NS-stage ring with one barrier per BK-deep step.
 // Ends with a barrier, so the caller may reuse the LDS right away.
-template <int BM, int BN, int WM, int WN, bool SILU, int BK, int NS>
+//
+// XT: A is z and a second tile of the noise eps is staged beside it (after
+// the W stages); each A fragment is z_t = (1 - t) z + t eps of its row (t =
+// its sample's t on frame-0 rows, else 0), rounded to bf16, and the first
+// column tile's wn == 0 waves also store it to xt_zt.
+template <int BM, int BN, int WM, int WN, bool SILU, int BK, int NS, bool XT = false>
 __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, int kt0, int nkt, bf16* smem,
                                          f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
   constexpr int NW = WM * WN;
@@ -275,10 +292,11 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
   constexpr int RPB = 64 / CPR;          // rows per 1-KB block (one wave instruction)
   constexpr int ABLK = BM / RPB, BBLK = BN / RPB;
   static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile / wave mismatch");
-  constexpr int LPS = ABLK / NW + BBLK / NW;   // direct loads per stage per wave
+  constexpr int LPS = (XT ? 2 : 1) * (ABLK / NW) + BBLK / NW;   // direct loads per stage per wave
   static_assert(NS <= 4 && 2 * LPS < 64, "vmcnt range");
   bf16* As = smem;                    // [NS][BM*BK]
   bf16* Bs = smem + NS * BM * BK;     // [NS][BN*BK]
+  bf16* Es = Bs + NS * BN * BK;       // XT: [NS][BM*BK]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const bf16* A = static_cast<const bf16*>(P.A);
@@ -289,6 +307,7 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
   // the block, LDS chunk position p = lane % CPR holds global chunk p ^ swz(row)
   const int rr = lane / CPR, pp = lane % CPR;
   const bf16* asrc[ABLK / NW];
+  const bf16* esrc[ABLK / NW];
   const bf16* bsrc[BBLK / NW];
 #pragma unroll
   for (int i = 0; i < ABLK / NW; ++i) {
@@ -296,6 +315,7 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
     int64_t m = m0 + row;
     if (m >= P.M) m = P.M - 1;        // rows past M load a valid row; never stored
     asrc[i] = A + m * P.lda + ((pp ^ swz(row)) << 3);
+    if constexpr (XT) esrc[i] = P.xt_e + m * P.lda + ((pp ^ swz(row)) << 3);
   }
 #pragma unroll
   for (int i = 0; i < BBLK / NW; ++i) {
@@ -307,6 +327,11 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
 #pragma unroll
     for (int i = 0; i < ABLK / NW; ++i)
       load_lds16(asrc[i] + ke, As + st * BM * BK + (wave + i * NW) * 512);
+    if constexpr (XT) {
+#pragma unroll
+      for (int i = 0; i < ABLK / NW; ++i)
+        load_lds16(esrc[i] + ke, Es + st * BM * BK + (wave + i * NW) * 512);
+    }
 #pragma unroll
     for (int i = 0; i < BBLK / NW; ++i)
       load_lds16(bsrc[i] + ke, Bs + st * BN * BK + (wave + i * NW) * 512);
@@ -324,6 +349,16 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
   wait_stages(min(NS - 1, nkt) - 1);
   __syncthreads();
   const int l32 = lane & 31, g = lane >> 5;
+  // XT: each fragment row's t, and whether this wave stores z_t
+  float tx[TM];
+  if constexpr (XT) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm * TM * 32 + i * 32 + l32;
+      tx[i] = (m < P.M && P.xt_pos[3 * m] == 0) ? P.xt_t[P.xt_seg[m]] : 0.0f;
+    }
+  }
+  const bool zt_out = XT && P.xt_zt != nullptr && n0 == 0 && wn == 0;
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + NS - 1 < nkt) issue(kt + NS - 1);
     const bf16* as = As + (kt % NS) * BM * BK;
@@ -337,6 +372,14 @@ __device__ __forceinline__ void mma_tile(const GemmProb& P, int64_t m0, int n0, 
         const int r = wm * TM * 32 + i * 32 + l32;
         af[i] = *reinterpret_cast<const bf16x8*>(as + r * BK + ((ch ^ swz(r)) << 3));
         if (SILU) af[i] = silu8(af[i]);
+        if constexpr (XT) {
+          const bf16* es = Es + (kt % NS) * BM * BK;
+          const bf16x8 ef = *reinterpret_cast<const bf16x8*>(es + r * BK + ((ch ^ swz(r)) << 3));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) af[i][e] = (bf16)rf_xt((float)af[i][e], (float)ef[e], tx[i]);
+          if (zt_out && m0 + r < P.M)
+            *reinterpret_cast<bf16x8*>(P.xt_zt + (m0 + r) * P.lda + (int64_t)(kt0 + kt) * BK + ch * 8) = af[i];
+        }
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -708,8 +751,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
   }
 }
 
-// SITE only separates the MLP down projection's instantiation from the output
-// projection's (same epilogue) so profiles can tell the two apart.
+// SITE 1 only separates the MLP down projection's instantiation from the
+// output projection's (same epilogue) so profiles can tell the two apart;
+// SITE 2 is the image embedding with the noising in its A staging (XT).
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -781,7 +825,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       return;
     }
   }
-  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2) {
+  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2 && SITE != 2) {
     // whole K, explicitly pipelined 4-wave mainloop (no split-K on this shape)
     mma_tile_pipe(P, m0, n0, smem, acc);
     store_tile_lds<EPI>(P, m0, n0, acc, smem, bt.qk);
@@ -789,7 +833,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   }
   // this block's k steps (all of K unless split-K)
   const int KT = P.K / BK / bt.splitk;
-  mma_tile<BM, BN, WM, WN, SILU, BK, NS>(P, m0, n0, blockIdx.y * KT, KT, smem, acc);
+  mma_tile<BM, BN, WM, WN, SILU, BK, NS, SITE == 2>(P, m0, n0, blockIdx.y * KT, KT, smem, acc);
   store_tile<BM, BN, WM, WN, EPI>(P, m0, n0, acc,
                                   bt.splitk > 1 ? bt.partial + (int64_t)blockIdx.y * P.M * P.N : nullptr);
 }
@@ -888,6 +932,41 @@ __global__ void splitk_reduce_kernel(GemmBatch bt) {
   }
 }
 
+// Split-K reduction of a bf16 store whose rows are also the flow-matching
+// velocity: 16 lanes per row, 8 columns per lane step, the partials summed in
+// split order (as splitk_reduce_kernel), Y stored, and the row's squared
+// residuals against z - eps summed in the same lane layout and order as the
+// loss's own row-sum kernel (so the same bits).
+__global__ void splitk_reduce_sse_kernel(GemmBatch bt) {
+  const GemmProb& P = bt.p[0];
+  const int64_t total = P.M * P.N;
+  const int C = P.N;
+  const int lane16 = threadIdx.x & 15;
+  const int64_t row0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int64_t rstep = ((int64_t)gridDim.x * blockDim.x) >> 4;
+  bf16* Y = static_cast<bf16*>(P.Y);
+  for (int64_t row = row0; row < P.M; row += rstep) {
+    float acc = 0.f;
+    const int64_t src = bt.sse_row[row];
+    for (int c8 = lane16; c8 < (C >> 3); c8 += 16) {
+      float o[8], zv[8], ev[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = 0.f;
+        for (int sp = 0; sp < bt.splitk; ++sp) a += bt.partial[sp * total + row * C + c8 * 8 + i];
+        o[i] = (float)(bf16)a;
+      }
+      Vec8<bf16>::store(Y + row * P.ldy + c8 * 8, o);
+      Vec8<bf16>::load(bt.sse_z + src * C + c8 * 8, zv);
+      Vec8<bf16>::load(bt.sse_e + src * C + c8 * 8, ev);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = rf_sq_acc(o[i], zv[i], ev[i], acc);
+    }
+    acc = group_sum(acc, 16);
+    if (lane16 == 0) bt.row_sse[row] = acc;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
 mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   int tiles = 0;
@@ -899,7 +978,7 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   if (tiles == 0) return MMDIT_OK;
   // the 4-wave pipelined 256x256 tile also keeps a 1 KB strip for its L2 touches
   constexpr bool pipe = BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2;
-  const size_t lds = (size_t)NS * (BM + BN) * BK * sizeof(bf16) + (pipe ? 1024 : 0);
+  const size_t lds = (size_t)NS * (BM + BN + (SITE == 2 ? BM : 0)) * BK * sizeof(bf16) + (pipe ? 1024 : 0);
   auto kern = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -912,9 +991,17 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   static char name[80];
   if (!name[0])
     snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s,bk%d,s%d>", BM, BN, WM, WN, EPI,
-             SILU ? ",silu" : "", SITE ? ",down" : "", BK, NS);
+             SILU ? ",silu" : "", SITE == 1 ? ",down" : SITE == 2 ? ",xt" : "", BK, NS);
   MMDIT_TRY(launch_check(bt.tag ? bt.tag : name, s));
   if (bt.splitk > 1) {
+    if (EPI == MMDIT_EPI_STORE && bt.row_sse && bt.p[0].N % 8 == 0) {
+      const int64_t nb = cdiv(bt.p[0].M * 16, 256);
+      const int blocks = (int)(nb < 4096 ? nb : 4096);
+      MMDIT_LAUNCH(splitk_reduce_sse_kernel, dim3(blocks), dim3(256), 0, s, bt);
+      MMDIT_TRY(launch_check("splitk_reduce_sse_kernel", s));
+      *bt.sse_done = 1;
+      return MMDIT_OK;
+    }
     const int64_t total = bt.p[0].M * bt.p[0].N;
     const int64_t nb = cdiv(total, 256);
     const int blocks = (int)(nb < 4096 ? nb : 4096);
@@ -1375,6 +1462,17 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
   bt.partial_elems = pa[0].partial_elems;
   bt.tail_begin = 0;
   bt.tail_chunks = 1;
+  if (pa[0].row_sse && dt == MMDIT_BF16 && epi == MMDIT_EPI_STORE && nprob == 1) {
+    if (!pa[0].sse_z || !pa[0].sse_e || !pa[0].sse_row || !pa[0].sse_done) {
+      set_error("linear: NULL pointer (row sums)");
+      return MMDIT_E_INVALID;
+    }
+    bt.sse_z = static_cast<const bf16*>(pa[0].sse_z);
+    bt.sse_e = static_cast<const bf16*>(pa[0].sse_e);
+    bt.sse_row = pa[0].sse_row;
+    bt.row_sse = pa[0].row_sse;
+    bt.sse_done = pa[0].sse_done;
+  }
 
   if (n == 0) return MMDIT_OK;
   Path path = force_simt() ? Path::SIMT : skinny ? Path::SKINNY : mfma ? Path::MFMA : Path::SIMT;
@@ -1399,6 +1497,41 @@ mmdit_status linear(mmdit_dtype dt, const LinearArgs* pa, int nprob, hipStream_t
       set_error("linear: unsupported epilogue %d (a_silu=%d)", epi, silu);
       return MMDIT_E_UNSUPPORTED;
   }
+}
+
+mmdit_status linear_xt(const LinearArgs& a, const XtArgs& x, hipStream_t s) {
+  if (a.M < 0 || a.N <= 0 || a.K <= 0 || a.K % 64 || a.N % 128 || a.lda != a.K || a.ldy < a.N ||
+      a.K >= (1 << 22) || a.epilogue != MMDIT_EPI_STORE || a.a_silu) {
+    set_error("linear_xt: unsupported shape M=%lld N=%d K=%d", (long long)a.M, a.N, a.K);
+    return MMDIT_E_UNSUPPORTED;
+  }
+  if (a.M == 0) return MMDIT_OK;
+  if (!a.A || !a.W || !a.Y || !x.eps || !x.t || !x.seg || !x.pos) {
+    set_error("linear_xt: NULL pointer");
+    return MMDIT_E_INVALID;
+  }
+  GemmBatch bt;
+  memset(&bt, 0, sizeof(bt));
+  GemmProb& p = bt.p[0];
+  p.A = a.A;
+  p.W = a.W;
+  p.Y = a.Y;
+  p.xt_e = static_cast<const bf16*>(x.eps);
+  p.xt_t = x.t;
+  p.xt_seg = x.seg;
+  p.xt_pos = x.pos;
+  p.xt_zt = static_cast<bf16*>(x.zt);
+  p.lda = a.lda;
+  p.ldy = a.ldy;
+  p.M = a.M;
+  p.N = a.N;
+  p.K = a.K;
+  bt.nprob = 1;
+  bt.tag = a.tag;
+  bt.xcd_remap = 1;
+  bt.splitk = 1;
+  bt.tail_chunks = 1;
+  return launch_mfma_cfg<128, 128, 2, 2, MMDIT_EPI_STORE, false, 2>(bt, s);
 }
 
 }  // namespace mmdit

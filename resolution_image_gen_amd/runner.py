@@ -135,12 +135,18 @@ class _SideMods:
         B.modulation(dm, W.wrap["w_fmod"], 2, c, self.modf, side)
         self.ev_modf.record(side)
 
-    def blocks_and_final(self, W, dm, pk, x_img, x_txt, ws, v, main):
+    def blocks_and_final(self, W, dm, pk, x_img, x_txt, ws, v, main, loss=None):
+        """Every block, then the final layer; with loss = (z, eps, sse, loss)
+        the final layer and the RF loss in one call (rf_final_loss)."""
         for i, bw in enumerate(W.bw):
             main.wait_event(self.ev_mod[i])
             B.block_fwd_mod(dm, bw, pk, self.mods[i], x_img, x_txt, ws, main)
         main.wait_event(self.ev_modf)
-        B.final_mod(dm, W.wrap["w_out"], pk, self.modf, x_img, v, ws, main)
+        if loss is None:
+            B.final_mod(dm, W.wrap["w_out"], pk, self.modf, x_img, v, ws, main)
+        else:
+            z, eps, sse, lo = loss
+            B.rf_final_loss(dm, W.wrap["w_out"], pk, self.modf, x_img, z, eps, v, sse, lo, ws, main)
 
 
 class TrainForward:
@@ -196,10 +202,12 @@ class TrainForward:
         B.pack_gather(pk, 0, self.z_s, self.z, main)
         B.pack_gather(pk, 0, self.eps_s, self.eps, main)
         B.pack_gather(pk, 1, self.tau_s, self.tau, main)
-        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, main)
-        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, main)
-        self.side.blocks_and_final(W, dm, pk, self.x_img, self.x_txt, self.ws, self.v, main)
-        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, main)
+        # noising folded into the image embedding, the loss's row sums into
+        # the final layer
+        B.rf_embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.z, self.eps, self.t, self.tau, self.x_img,
+                   self.x_txt, self.zt, main)
+        self.side.blocks_and_final(W, dm, pk, self.x_img, self.x_txt, self.ws, self.v, main,
+                                   loss=(self.z, self.eps, self.sse, self.loss))
 
     def capture(self):
         """Record one whole training forward (every launch) as a HIP graph."""
@@ -247,6 +255,7 @@ class TrainStep(TrainForward):
         self.dx_img = torch.empty(max(pk.n_img, 1), d.hidden, **e)
         self.dx_txt = torch.empty(max(pk.n_txt, 1), d.hidden, **e)
         self.dc = torch.empty(max(pk.B, 1), d.hidden, **f32)
+        self.modf = torch.empty(max(pk.B, 1), 2 * d.hidden, **f32)
         self.grads = {"wrap": {k: torch.empty(tuple(W.wrap[k].shape), **f32) for k in WRAP_KEYS},
                       "blocks": [{s: {k: torch.empty(tuple(blk[s][k].shape), **f32) for k in B.GRAD_KEYS}
                                   for s in ("img", "txt")} for blk in W.blocks]}
@@ -262,13 +271,14 @@ class TrainStep(TrainForward):
         B.pack_gather(pk, 0, self.z_s, self.z, stream)
         B.pack_gather(pk, 0, self.eps_s, self.eps, stream)
         B.pack_gather(pk, 1, self.tau_s, self.tau, stream)
-        B.rf_make_xt(pk, self.z, self.eps, self.t, self.zt, stream)
         B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], self.t, self.c, self.ws, stream)
-        B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt, stream)
+        B.rf_embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.z, self.eps, self.t, self.tau, self.x_img,
+                   self.x_txt, self.zt, stream)
         for bw, sv in zip(W.bw, self.saved):
             B.block_fwd_train(dm, bw, pk, self.c, self.x_img, self.x_txt, sv, self.ws, stream)
-        B.final(dm, W.wrap["w_fmod"], W.wrap["w_out"], pk, self.c, self.x_img, self.v, self.ws, stream)
-        B.rf_loss(pk, self.v, self.z, self.eps, self.sse, self.loss, self.ws, stream)
+        B.modulation(dm, W.wrap["w_fmod"], 2, self.c, self.modf, stream)
+        B.rf_final_loss(dm, W.wrap["w_out"], pk, self.modf, self.x_img, self.z, self.eps, self.v, self.sse,
+                        self.loss, self.ws, stream)
         # backward
         g = self.grads["wrap"]
         self.dc.zero_()

@@ -226,3 +226,65 @@ def test_sampler_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(sm.z, eager), f"replay {i} differs"
         del junk
+
+
+_SMALL_BF16 = CF.Dims(hidden=512, heads=4, head_dim=128, mlp=2048, c_lat=64, d_txt=512)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "pack256_bf16", "edit_small_bf16"])
+def test_fused_rf_entries_same_bits(name):
+    """rf_embed equals rf_make_xt then mmdit_embed, and rf_final_loss equals
+    mmdit_final_mod then rf_loss, bit for bit.  The bf16 packs take the fused
+    kernels (the noising in the image embedding's A staging; the loss's row
+    sums in the final GEMM's split-K reduction), f32 runs the two in sequence;
+    the edit pack has clean source rows (frame 1) next to the noised targets."""
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import runner as R
+
+    if name == "edit_small_bf16":
+        wl = CF.Workload(name, _SMALL_BF16, "bf16", ((12, 10, 2, 24), (5, 7, 2, 3), (8, 8, 1, 16)),
+                         img_budget=10 ** 6)
+    else:
+        wl = CF.WORKLOADS[name]
+    print(f"fused rf entries {name}", flush=True)
+    W = R.Weights(wl)
+    inp = R.training_inputs(wl)
+    tf = R.TrainForward(wl, W, inp)
+    tf.run()
+    torch.cuda.synchronize()
+    pk, dm = tf.pk, tf.dims
+    fused = wl.dtype == "bf16"
+    # embedding
+    zt1, x1, xt1 = torch.empty_like(tf.zt), torch.empty_like(tf.x_img), torch.empty_like(tf.x_txt)
+    zt2, x2, xt2 = torch.empty_like(tf.zt), torch.empty_like(tf.x_img), torch.empty_like(tf.x_txt)
+    B.timing_enable(True)
+    B.rf_embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, tf.z, tf.eps, tf.t, tf.tau, x1, xt1, zt1)
+    rep = B.timing_report()
+    B.timing_enable(False)
+    B.rf_make_xt(pk, tf.z, tf.eps, tf.t, zt2)
+    B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, zt2, tf.tau, x2, xt2)
+    torch.cuda.synchronize()
+    n_img, n_txt = pk.n_img, pk.n_txt
+    assert torch.equal(zt1[:n_img], zt2[:n_img])
+    assert torch.equal(x1[:n_img], x2[:n_img])
+    assert torch.equal(xt1[:n_txt], xt2[:n_txt])
+    assert ("embed_img_xt" in rep and "make_xt_kernel" not in rep) == fused, sorted(rep)
+    # final layer + loss on the blocks' output
+    v1, v2 = torch.empty_like(tf.v), torch.empty_like(tf.v)
+    s1, s2 = torch.empty_like(tf.sse), torch.empty_like(tf.sse)
+    l1, l2 = torch.empty_like(tf.loss), torch.empty_like(tf.loss)
+    B.timing_enable(True)
+    B.rf_final_loss(dm, W.wrap["w_out"], pk, tf.side.modf, tf.x_img, tf.z, tf.eps, v1, s1, l1, tf.ws)
+    rep = B.timing_report()
+    B.timing_enable(False)
+    B.final_mod(dm, W.wrap["w_out"], pk, tf.side.modf, tf.x_img, v2, tf.ws)
+    B.rf_loss(pk, v2, tf.z, tf.eps, s2, l2, tf.ws)
+    torch.cuda.synchronize()
+    n_tgt = pk.n_tgt
+    assert torch.equal(v1[:n_tgt], v2[:n_tgt])
+    assert torch.equal(s1[:pk.B], s2[:pk.B])
+    assert torch.equal(l1, l2)
+    if name == "pack256_bf16":
+        assert "splitk_reduce_sse_kernel" in rep and "row_sse_kernel" not in rep, sorted(rep)
+    # the training forward (which calls both) matched its own unfused parts
+    assert torch.equal(tf.v[:n_tgt], v2[:n_tgt]) and torch.equal(tf.loss, l2)
