@@ -328,10 +328,15 @@ def bench_sampler_extras(W, steps, warmup):
     sm2 = R.Sampler(wl, W, eps, tau_c, tau_u, two_pass=True)
     ms2, _ = _timed_graph(sm2, steps, warmup)
     assert torch.isfinite(sm.z).all()
-    # the packed pack's MLP down takes a stream-K last round that the one-sample
-    # forwards do not, so the two agree to rounding, not bit for bit
+    # the packed pack's GEMMs split their last rounds differently from the
+    # one-sample forwards' (MLP down's k-parts, the sub-tiles), so the two
+    # agree to rounding, not bit for bit: held to the bound the sampler's
+    # parity test uses against the oracle, (|1 - g| + g) x 2e-2 (the CFG
+    # combine amplifies a branch's error by up to |1 - g| + g)
+    g = wl.guidance
+    bound = (abs(1.0 - g) + g) * 2e-2
     diff = ((sm.z - sm2.z).abs().max() / sm2.z.abs().max()).item()
-    assert diff <= 2e-2, f"packed and two-pass CFG samplers disagree ({diff:.3e})"
+    assert diff <= bound, f"packed and two-pass CFG samplers disagree ({diff:.3e} > {bound:.3e})"
     sm20 = R.Sampler(wl, W, eps, tau_c, tau_u, schedule=[1.0 - i / 20 for i in range(21)])
     ms20, _ = _timed_graph(sm20, 1, 1)
     assert torch.isfinite(sm20.z).all()
@@ -344,10 +349,11 @@ def bench_sampler_extras(W, steps, warmup):
     ms_e2, _ = _timed_graph(se2, steps, warmup)
     assert torch.isfinite(se.z).all()
     ediff = ((se.z - se2.z).abs().max() / se2.z.abs().max()).item()
-    assert ediff <= 2e-2, f"packed and two-pass CFG edit samplers disagree ({ediff:.3e})"
+    assert ediff <= bound, f"packed and two-pass CFG edit samplers disagree ({ediff:.3e} > {bound:.3e})"
     eblk = block_flops(d, se.samples)[0] * ewl.depth * (len(ewl.schedule) - 1)
     return {"ms_per_4step_pack": round(ms, 2), "two_pass_ms_per_4step_pack": round(ms2, 2),
             "packed_speedup_vs_two_pass": round(ms2 / ms, 3), "packed_vs_two_pass_max_rel_diff": diff,
+            "packed_vs_two_pass_bound": bound,
             "ms_per_20step_pack": round(ms20, 2),
             "edit": {"workload": f"{ewl.name}: {ewl.note}", "ms_per_4step_pack": round(ms_e, 2),
                      "block_tflops": round(eblk / (ms_e * 1e-3) / 1e12, 1),
