@@ -3,6 +3,8 @@ and the packed-CFG Euler sampler.  Marshalling and buffer ownership only:
 every arithmetic step is a libmmdit kernel launch on the given stream.
 """
 
+import os
+
 import numpy as np
 import torch
 
@@ -100,6 +102,10 @@ def training_inputs(wl, samples=None):
 # beside the embeddings; the backward's weight gradients beside its input
 # gradients).  False puts every launch on the caller's stream.
 OVERLAP = True
+# The packed sampler computes every step's adaLN vectors in one pass over the
+# weights when they fit one weight-streaming product; MMDIT_SAMPLER_ALL_STEPS=0
+# computes them per step (the same bits).
+ALL_STEP_VECTORS = os.environ.get("MMDIT_SAMPLER_ALL_STEPS", "1") != "0"
 
 
 class _SideMods:
@@ -110,13 +116,21 @@ class _SideMods:
     vectors right before block i.  Same kernels, so the same bits as the
     single-stream calls.  Default-priority stream; events without timing."""
 
-    def __init__(self, W, n_samples, device):
+    def __init__(self, W, n_samples, device, steps=0):
         H, dt = W.dims.c.hidden, W.dims.torch_dtype
         es = 2 if dt == torch.bfloat16 else 4
         nb = len(W.bw)
+        self.n_samples = n_samples
         self.mods = torch.empty(nb, 2, n_samples, 6 * H, dtype=torch.float32, device=device)
         self.modf = torch.empty(n_samples, 2 * H, dtype=torch.float32, device=device)
         self.ws = torch.empty(n_samples * (W.dims.c.t_dim + H) * es + 1024, dtype=torch.uint8, device=device)
+        if steps:   # launch_steps: every step's vectors at once
+            rows = steps * n_samples
+            self.c_all = torch.empty(rows, H, dtype=dt, device=device)
+            self.ws_all = torch.empty(rows * (W.dims.c.t_dim + H) * es + 1024, dtype=torch.uint8, device=device)
+            self.mods_all = torch.empty(2, rows, 6 * H, dtype=torch.float32, device=device)
+            self.modf_all = torch.empty(rows, 2 * H, dtype=torch.float32, device=device)
+            self.mods_steps = torch.empty(steps, nb, 2, n_samples, 6 * H, dtype=torch.float32, device=device)
         self.stream = torch.cuda.Stream(device=device)
         self.ev_start = torch.cuda.Event()
         self.ev_mod = [torch.cuda.Event() for _ in range(nb)]
@@ -134,6 +148,42 @@ class _SideMods:
             self.ev_mod[i].record(side)
         B.modulation(dm, W.wrap["w_fmod"], 2, c, self.modf, side)
         self.ev_modf.record(side)
+
+    def launch_steps(self, W, dm, t_all, main, overlap=True):
+        """The vectors of every step of a sampler pack in one pass over the
+        weights: cond and every block's and the final layer's vectors for all
+        S steps' rows at once (t_all [S * B], step-major; S * B <= 16, the
+        rows the weight-streaming GEMV takes in one product, each row's
+        arithmetic the same as alone), then each block's [2][S][B][6H] copied
+        into per-step [2][B][6H] slots (mods_steps[k][i]); one event per
+        block as in launch."""
+        side = self.stream if overlap else main
+        S = t_all.shape[0] // self.n_samples
+        self.ev_start.record(main)
+        side.wait_event(self.ev_start)
+        c_all = self.c_all[:S * self.n_samples]
+        B.cond(dm, W.wrap["w_t1"], W.wrap["w_t2"], t_all, c_all, self.ws_all, side)
+        B.modulation(dm, W.wrap["w_fmod"], 2, c_all, self.modf_all[:S * self.n_samples], side)
+        H6 = self.mods.shape[-1]
+        for i, bw in enumerate(W.bw):
+            m = self.mods_all[:, :S * self.n_samples]
+            B.block_modulation(dm, bw, c_all, m, side)
+            with torch.cuda.stream(side):
+                self.mods_steps[:S, i].copy_(m.view(2, S, self.n_samples, H6).permute(1, 0, 2, 3))
+            self.ev_mod[i].record(side)
+        self.ev_modf.record(side)
+
+    def blocks_and_final_step(self, W, dm, pk, k, x_img, x_txt, ws, v, main):
+        """Step k's blocks and final layer with the vectors of launch_steps
+        (each block waits for its own vectors only on the first step)."""
+        for i, bw in enumerate(W.bw):
+            if k == 0:
+                main.wait_event(self.ev_mod[i])
+            B.block_fwd_mod(dm, bw, pk, self.mods_steps[k, i], x_img, x_txt, ws, main)
+        if k == 0:
+            main.wait_event(self.ev_modf)
+        nb = self.n_samples
+        B.final_mod(dm, W.wrap["w_out"], pk, self.modf_all[k * nb:(k + 1) * nb], x_img, v, ws, main)
 
     def blocks_and_final(self, W, dm, pk, x_img, x_txt, ws, v, main, loss=None):
         """Every block, then the final layer; with loss = (z, eps, sse, loss)
@@ -336,7 +386,12 @@ class Sampler:
         # an edit sample's image rows at z_1 = eps: [eps; source], both in dtype
         self.img_rows = None if src is None else torch.cat([_dev(eps, dt, device), _dev(src, dt, device)])
         self.two_pass = two_pass
-        self.side = _SideMods(W, 2, device)
+        nsteps = len(self.schedule) - 1
+        # every step's adaLN vectors in one pass over the weights when the
+        # steps' rows fit one weight-streaming product (4 steps x 2 samples)
+        self.all_steps = ALL_STEP_VECTORS and not two_pass and 2 * nsteps <= 16
+        self.side = _SideMods(W, 2, device, steps=nsteps if self.all_steps else 0)
+        self.t_all = self.tsched.reshape(-1).contiguous()
         self.overlap = OVERLAP
         if two_pass:   # one-sample packs; the two-sample workspace covers each
             self.pk_one = [B.pack(self.samples[:1], device), B.pack(self.samples[1:], device)]
@@ -379,11 +434,17 @@ class Sampler:
         if self.img_rows is not None:         # source rows of both samples (targets too, as eps)
             B.pack_gather(pk, 0, [self.img_rows, self.img_rows], self.zt, stream)
         B.rf_pack_latent(pk, self.z, 0, 1, self.zt, stream)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if self.all_steps:
+            self.side.launch_steps(W, dm, self.t_all, main, self.overlap)
         for i in range(len(self.schedule) - 1):
             if self.two_pass:
                 self._two_pass_forward(i, stream)
+            elif self.all_steps:
+                B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt,
+                        main)
+                self.side.blocks_and_final_step(W, dm, pk, i, self.x_img, self.x_txt, self.ws, self.v, main)
             else:
-                main = stream if stream is not None else torch.cuda.current_stream()
                 self.side.launch(W, dm, self.tsched[i], self.c, main, self.overlap)
                 B.embed(dm, W.wrap["w_in"], W.wrap["w_txt"], pk, self.zt, self.tau, self.x_img, self.x_txt,
                         main)

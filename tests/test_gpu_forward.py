@@ -288,3 +288,26 @@ def test_fused_rf_entries_same_bits(name):
         assert "splitk_reduce_sse_kernel" in rep and "row_sse_kernel" not in rep, sorted(rep)
     # the training forward (which calls both) matched its own unfused parts
     assert torch.equal(tf.v[:n_tgt], v2[:n_tgt]) and torch.equal(tf.loss, l2)
+
+
+def test_sampler_all_steps_vectors_same_bits():
+    """The packed sampler computes every step's adaLN vectors in one pass over
+    the weights (4 steps x 2 samples = 8 rows of the weight-streaming GEMV);
+    the result equals the per-step vectors' bit for bit."""
+    from resolution_image_gen_amd import runner as R
+
+    wl = _small_sampler_wl("bf16", depth=2)
+    W = R.Weights(wl, recipe="stress")
+    h, w = wl.samples[0][:2]
+    eps = S.normal((h * w, wl.dims.c_lat), 1.0, "bf16", wl.name, "eps3")
+    tau_c = S.text(24, wl.dims.d_txt, "bf16", wl.name, "tau_c3")
+    tau_u = S.text(20, wl.dims.d_txt, "bf16", wl.name, "tau_u3")
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    assert sm.all_steps
+    sm.run()
+    torch.cuda.synchronize()
+    z_all = sm.z.clone()
+    sm.all_steps = False
+    sm.run()
+    torch.cuda.synchronize()
+    assert torch.equal(sm.z, z_all), (sm.z - z_all).abs().max()
