@@ -168,8 +168,8 @@ typedef struct {
   mmdit_stream_w img, txt;
 } mmdit_block_w;
 
-/* Workspace bytes needed by mmdit_block_fwd, mmdit_final and rf_loss for
- * this pack (0 on invalid arguments). */
+/* Workspace bytes needed by mmdit_block_fwd, mmdit_final, rf_loss and
+ * rf_final_loss for this pack (0 on invalid arguments). */
 size_t mmdit_workspace_size(const mmdit_dims* dims, const mmdit_pack_t* pack);
 
 /* Byte offsets of the block's intermediates inside the workspace after
