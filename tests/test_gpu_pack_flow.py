@@ -307,7 +307,13 @@ def test_empty_pack_calls_are_no_ops(B):
     v = torch.full((1, C), 7.0, **f)
     w_f, w_o = torch.zeros(2 * H, H, **f), torch.zeros(C, H, **f)
     B.final(dims, w_f, w_o, pk, c, x_img, v, ws)
+    w_in, w_txt = torch.zeros(H, C, **f), torch.zeros(H, d.d_txt, **f)
+    tau = torch.full((1, d.d_txt), 7.0, **f)
+    B.rf_embed(dims, w_in, w_txt, pk, z, eps, t, tau, x_img, x_txt, zt)
+    modf = torch.full((1, 2 * H), 7.0, **f)
+    loss2 = torch.full((1,), 7.0, **f)
+    B.rf_final_loss(dims, w_o, pk, modf, x_img, z, eps, v, sse, loss2, ws)
     torch.cuda.synchronize()
-    assert loss.item() == 0.0
+    assert loss.item() == 0.0 and loss2.item() == 0.0
     for a in (zt, sse, x_img, x_txt, v):
         assert torch.all(a == 7.0)
