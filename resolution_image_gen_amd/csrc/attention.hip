@@ -20,6 +20,7 @@
 #include "common.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <type_traits>
@@ -1146,10 +1147,11 @@ mmdit_status attention_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t head
     else
       MMDIT_LAUNCH(v_transpose_kernel<64>, tgrid, dim3(256), 0, s, a, vt, njp);
     MMDIT_TRY(launch_check("v_transpose_kernel", s));
-    // 8-wave blocks (256 queries) once a sample is long enough (measured: 3%
-    // faster at 33k tokens per sample, 3.5% slower at 8.4k, 19% slower at
-    // 384), else 4-wave blocks
-    const int nw = pk->max_joint >= 16384 ? 8 : 4;
+    // 4-wave blocks (128 queries): with the pipelined loop as fast as the
+    // 8-wave ones at 33k tokens per sample and 4-9% faster at 4k-8k;
+    // MMDIT_ATTN_WAVES=8 selects 256-query blocks (the same bits)
+    const char* we = getenv("MMDIT_ATTN_WAVES");
+    const int nw = (we && atoi(we) == 8) ? 8 : 4;
     a.nq = (int32_t)cdiv(pk->max_joint, 32 * nw);
     a.nB = pk->B;
     dim3 grid((unsigned)(8 * cdiv((int64_t)a.nq * heads * pk->B, 8)));

@@ -37,7 +37,7 @@ CASES = {
     "long_bf16_d128": (CF.B4, "bf16", [(48, 50, 1, 37), (40, 52, 1, 100), (3, 5, 1, 7)]),
     "long_bf16_d64": (CF.Dims(hidden=512, heads=8, head_dim=64, mlp=2048, c_lat=64, d_txt=512), "bf16",
                       [(50, 44, 1, 19), (21, 30, 2, 33)]),
-    # a sample past 16384 joint tokens: attention takes 256-query blocks of 8 waves
+    # a sample past 16384 joint tokens (also run with 256-query blocks of 8 waves)
     "long16k_bf16_d128": (CF.Dims(hidden=256, heads=2, head_dim=128, mlp=1024, c_lat=64, d_txt=256), "bf16",
                           [(128, 130, 1, 210), (7, 9, 1, 30)]),
     "long16k_bf16_d64": (CF.Dims(hidden=256, heads=4, head_dim=64, mlp=1024, c_lat=64, d_txt=256), "bf16",
@@ -123,7 +123,7 @@ def test_qk_norm_rope_other_bands(B, bands):
 
 
 @pytest.mark.parametrize("case", list(CASES))
-def test_attention(B, case):
+def test_attention(B, case, monkeypatch):
     d, dtype, samples = CASES[case]
     ref = oracle_pack(samples)
     dims = B.Dims(d, dtype)
@@ -149,6 +149,15 @@ def test_attention(B, case):
     assert_close(f"o_img[{case}]", to_np(oi), want_i.reshape(ni, H), tol)
     if nt:
         assert_close(f"o_txt[{case}]", to_np(ot)[:nt], want_t.reshape(nt, H), tol)
+    if dtype == "bf16" and case.startswith("long"):
+        # every query takes the same keys in the same order whatever the block
+        # shape: 8-wave blocks give the same bits
+        oi8, ot8 = torch.empty_like(oi), torch.empty_like(ot)
+        monkeypatch.setenv("MMDIT_ATTN_WAVES", "8")
+        B.attention(dims, pk, _dev(qi, dtype), _dev(qt, dtype), oi8, ot8)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("MMDIT_ATTN_WAVES")
+        assert torch.equal(oi8, oi) and torch.equal(ot8[:nt], ot[:nt])
 
 
 LINEAR_CASES = [
