@@ -793,26 +793,42 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a, cons
   const char* ktxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_txt) + (int64_t)t0 * 3 * a.f.H + a.f.H + head * D);
   const char* kimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.f.qkv_img) + ((int64_t)i0 - Tb) * 3 * a.f.H + a.f.H + head * D);
   const int wu = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t kswc[RB];
-  const bf16* tsrc[RB];
+  // whole tiles inside the text or the image rows load through one segment's
+  // buffer resource (the tile offset scalar, 32-bit lane offsets; the K^T
+  // buffer likewise, below 2^32 bytes: checked on the host); a straddling or
+  // ragged tile takes per-lane addresses
+  const rsrc_t rtxt = make_rsrc(uniform_ptr(ktxt)), rimg = make_rsrc(uniform_ptr(kimg)), rkt = make_rsrc(kt);
+  uint32_t kswc[RB], koff[RB], toff[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     kswc[i] = ((kp ^ ksw<D>((wave + 4 * i) * KROWS + kr)) << 4);
+    koff[i] = (uint32_t)((wu + 4 * i) * KROWS + kr) * rowb + kswc[i];
     const int d = (wave + 4 * i) * 16 + (lane >> 2);
-    tsrc[i] = kt + ((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3);
+    toff[i] = (uint32_t)((((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3)) * 2);
   }
   auto issue = [&](int32_t kv0, int st) {
     bf16* ks = smem + st * STAGE;
     bf16* vs = ks + TILE;
     bf16* ts = vs + TILE;
+    if (kv0 + BK <= L && (kv0 + BK <= Tb || kv0 >= Tb)) {
+      const rsrc_t r = kv0 < Tb ? rtxt : rimg;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int blk = wu + 4 * i;
-      const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);   // keys past L are masked
-      const char* kb = (key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]);
-      load_lds16(kb, ks + blk * 512);
-      load_lds16(kb + a.f.H * 2, vs + blk * 512);
-      load_lds16(tsrc[i] + kv0, ts + blk * 512);
+      for (int i = 0; i < RB; ++i) {
+        const int blk = wu + 4 * i;
+        buf_lds16(r, koff[i], (uint32_t)kv0 * rowb, ks + blk * 512);
+        buf_lds16(r, koff[i] + (uint32_t)a.f.H * 2u, (uint32_t)kv0 * rowb, vs + blk * 512);
+        buf_lds16(rkt, toff[i], (uint32_t)kv0 * 2, ts + blk * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int blk = wu + 4 * i;
+        const int32_t key = min(kv0 + blk * KROWS + kr, L - 1);   // keys past L are masked
+        const char* kb = (key < Tb ? ktxt : kimg) + ((uint32_t)key * rowb + kswc[i]);
+        load_lds16(kb, ks + blk * 512);
+        load_lds16(kb + a.f.H * 2, vs + blk * 512);
+        buf_lds16(rkt, toff[i], (uint32_t)kv0 * 2, ts + blk * 512);
+      }
     }
   };
 
@@ -930,15 +946,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
   const char* gtxt = reinterpret_cast<const char*>(static_cast<const bf16*>(a.do_txt) + (int64_t)t0 * a.f.H + head * D);
   const char* gimg = reinterpret_cast<const char*>(static_cast<const bf16*>(a.do_img) + ((int64_t)i0 - Tb) * a.f.H + head * D);
   const int wu = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t kswc[RB];
-  int64_t toff[RB];
+  const bf16* tsrc = DK ? qt : gt;   // the transposed operand: Q^T (dK) or dO^T (dV)
+  // whole query tiles inside the text or the image rows load through buffer
+  // resources with the tile offset scalar (as in attn_bwd_dq_kernel)
+  const rsrc_t rqt = make_rsrc(uniform_ptr(qtxt)), rqi = make_rsrc(uniform_ptr(qimg));
+  const rsrc_t rgt = make_rsrc(uniform_ptr(gtxt)), rgi = make_rsrc(uniform_ptr(gimg)), rts = make_rsrc(tsrc);
+  uint32_t kswc[RB], qoff[RB], goff[RB], toff[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     kswc[i] = ((kp ^ ksw<D>((wave + 4 * i) * KROWS + kr)) << 4);
+    qoff[i] = (uint32_t)((wu + 4 * i) * KROWS + kr) * rowq + kswc[i];
+    goff[i] = (uint32_t)((wu + 4 * i) * KROWS + kr) * rowg + kswc[i];
     const int d = (wave + 4 * i) * 16 + (lane >> 2);
-    toff[i] = ((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3);
+    toff[i] = (uint32_t)((((int64_t)head * D + d) * a.f.njp + pstart + (((lane & 3) ^ tsw(d)) << 3)) * 2);
   }
-  const bf16* tsrc = DK ? qt : gt;   // the transposed operand: Q^T (dK) or dO^T (dV)
   const float* lse_g = a.f.lse + (int64_t)head * a.f.njp + pstart;
   const float* ds_g = a.dsum + (int64_t)head * a.f.njp + pstart;
   auto issue = [&](int32_t q0, int st) {
@@ -946,13 +967,26 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a, co
     bf16* gs = qs + TILE;                  // dO (dK only)
     bf16* ts = qs + (NT - 1) * TILE;       // the transposed tile
     float* lf = reinterpret_cast<float*>(qs + NT * TILE);
+    if (q0 + BQ <= L && (q0 + BQ <= Tb || q0 >= Tb)) {
+      const bool txt = q0 < Tb;
+      const rsrc_t rq = txt ? rqt : rqi;
+      const rsrc_t rg = txt ? rgt : rgi;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int blk = wu + 4 * i;
-      const int32_t q = min(q0 + blk * KROWS + kr, L - 1);   // queries past L are masked
-      load_lds16((q < Tb ? qtxt : qimg) + ((uint32_t)q * rowq + kswc[i]), qs + blk * 512);
-      if constexpr (DK) load_lds16((q < Tb ? gtxt : gimg) + ((uint32_t)q * rowg + kswc[i]), gs + blk * 512);
-      load_lds16(tsrc + toff[i] + q0, ts + blk * 512);
+      for (int i = 0; i < RB; ++i) {
+        const int blk = wu + 4 * i;
+        buf_lds16(rq, qoff[i], (uint32_t)q0 * rowq, qs + blk * 512);
+        if constexpr (DK) buf_lds16(rg, goff[i], (uint32_t)q0 * rowg, gs + blk * 512);
+        buf_lds16(rts, toff[i], (uint32_t)q0 * 2, ts + blk * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int blk = wu + 4 * i;
+        const int32_t q = min(q0 + blk * KROWS + kr, L - 1);   // queries past L are masked
+        load_lds16((q < Tb ? qtxt : qimg) + ((uint32_t)q * rowq + kswc[i]), qs + blk * 512);
+        if constexpr (DK) load_lds16((q < Tb ? gtxt : gimg) + ((uint32_t)q * rowg + kswc[i]), gs + blk * 512);
+        buf_lds16(rts, toff[i], (uint32_t)q0 * 2, ts + blk * 512);
+      }
     }
     // lse (and D) of the tile's 32 queries by direct loads too: a plain load
     // into registers would make the LDS store wait for every load in flight,
@@ -1220,8 +1254,9 @@ mmdit_status attention_bwd_impl(mmdit_dtype dt, const mmdit_pack_t* pk, int32_t 
   const size_t njp_h = (size_t)(attention_vt_elems(pk, heads * D) / D);
   a.dsum = static_cast<float*>(ws);
   if (dt == MMDIT_BF16) {
-    if ((double)pk->max_joint * 3.0 * a.f.H * 2.0 >= 2147483648.0) {
-      set_error("attention backward: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31)");
+    if ((double)pk->max_joint * 3.0 * a.f.H * 2.0 >= 2147483648.0 || (double)njp_h * D * 2.0 >= 4294967296.0) {
+      set_error("attention backward: sample too long (joint length x 3 x hidden x 2 bytes must be < 2^31, "
+                "each transposed operand < 2^32 bytes)");
       return MMDIT_E_UNSUPPORTED;
     }
     bf16* qt = reinterpret_cast<bf16*>(static_cast<char*>(ws) + ((njp_h * sizeof(float) + 255) & ~(size_t)255));
