@@ -91,18 +91,6 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 // x sigmoid(x) with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
 // IEEE division (a ten-instruction sequence); 1 + exp(-x) >= 1 is never denormal.
 __device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-// t = 1 / (1 + p x), for x >= 0 (odd for x < 0); absolute error <= 1.5e-7.
-// About a dozen instructions, against the several-branch library erff; t
-// takes the hardware reciprocal (1 ulp; its argument is >= 1).
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
-  const float poly =
-      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  return copysignf(1.0f - poly * __expf(-ax * ax), x);
-}
 // Rectified-flow noising of one element, z_t = (1 - t) z + t eps, with its
 // multiply-add written out: the noising kernel and the image embedding's
 // fused A staging give the same bits.
@@ -113,11 +101,32 @@ __device__ __forceinline__ float rf_sq_acc(float v, float z, float e, float acc)
   const float d = v - (z - e);
   return fmaf(d, d, acc);
 }
-// GELU in its erf form, 0.5 x (1 + erf(x / sqrt 2)).
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
-// Its derivative Phi(x) + x phi(x), with the same erf.
+// GELU in its erf form, 0.5 x (1 + erf(x / sqrt 2)), with erf by Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26: for z >= 0,
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z),
+// absolute error <= 1.5e-7.  With z = |x| / sqrt 2, 0.5 erfc(z) = Q e where
+// Q = t (b1 + t (b2 + ...)), b = a / 2, and e = exp(-x^2 / 2), so
+// Phi(x) = 1 - Q e for x >= 0 and Q e below, and
+//   GELU(x) = x Phi(x) = max(x, 0) - |x| Q e
+// (0.5 x + 0.5 |x| absorbs the sign): no 1 + erf cancellation in the negative
+// tail.  The derivative Phi(x) + x phi(x), phi(x) = e / sqrt(2 pi), reuses e:
+// one hardware reciprocal (1 ulp; its argument is >= 1) and one exponential.
+__device__ __forceinline__ void gelu_qe(float x, float& q, float& e) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(ax, 0.3275911f * 0.70710678118654752f, 1.0f));
+  q = t * (0.127414796f + t * (-0.142248368f + t * (0.7107068705f + t * (-0.7265760135f + t * 0.5307027145f))));
+  e = __builtin_amdgcn_exp2f(x * (x * -0.72134752044448170f));   // exp(-x^2 / 2)
+}
+__device__ __forceinline__ float gelu_f(float x) {
+  float q, e;
+  gelu_qe(x, q, e);
+  return fmaf(-fabsf(x) * q, e, fmaxf(x, 0.0f));
+}
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  return 0.5f * (1.0f + erf_as(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+  float q, e;
+  gelu_qe(x, q, e);
+  const float qe = q * e;
+  return fmaf(x * 0.39894228040143268f, e, x >= 0.0f ? 1.0f - qe : qe);
 }
 
 // QK-RMSNorm + RoPE of the 8 consecutive dimensions (4 rotation pairs) of a
