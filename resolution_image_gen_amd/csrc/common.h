@@ -76,6 +76,15 @@ template <> struct Vec8<float> {
   }
 };
 
+// Workgroup barrier ordering LDS accesses only: the fences are limited to the
+// local address space, so global loads in flight stay in flight across it
+// (a plain __syncthreads waits for every outstanding global access too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // --------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

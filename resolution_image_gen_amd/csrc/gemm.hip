@@ -671,9 +671,12 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
     if (P.rope_cs) csp = P.rope_cs + dcol;
     Vec8<float>::load((n0 < Hq ? P.g_q : P.g_k) + dcol, gn);
   }
+  constexpr bool GATED = EPI == MMDIT_EPI_GATED_RES || EPI == kEpiGatedResAux;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    __syncthreads();
+    const int64_t mb = m0 + half * 128 + r0;
+    const int nrow = (int)min<int64_t>(16, (M - mb + 7) >> 3);   // rows of this thread that exist (may be <= 0)
+    lds_barrier();
     if (wm == half) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -685,9 +688,27 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
             T[r * 256 + wn * 128 + j * 32 + l32] = acc[i][j][v];
           }
     }
-    __syncthreads();
+    lds_barrier();
+    // gated residual: all of the thread's residual rows and their samples
+    // are read at once (one memory latency instead of one per few rows), the
+    // gate vector once when those rows belong to one sample
+    bf16x8 xr[GATED ? 16 : 1];
+    int32_t sg[GATED ? 16 : 1];
+    float g0[8];
+    int32_t s0 = 0;
+    if constexpr (GATED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < nrow) {
+          xr[i] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(Yp) + (mb + 8 * i) * ldy + n);
+          sg[i] = segp[mb + 8 * i];
+        }
+      if (nrow > 0) {
+        s0 = sg[0];
+        Vec8<float>::load(gatep + (int64_t)s0 * gs + n, g0);
+      }
+    }
     // thread tid takes columns n..n+7 of rows r0, r0 + 8, ..., r0 + 120
-    const int64_t mb = m0 + half * 128 + r0;
     auto chunk = [&](int i) {
       const int64_t m = mb + 8 * i;
       const float* t = T + (r0 + 8 * i) * 256 + ch * 8;
@@ -733,8 +754,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
           for (int k = 0; k < 8; ++k) o[k] = a[k] * gelu_grad_f(xv[k]);
         } else {
           float xv[8], gv[8];
-          Vec8<bf16>::load(y, xv);
-          Vec8<float>::load(gatep + (int64_t)segp[m] * gs + n, gv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xv[k] = (float)xr[i][k];
+          if (sg[i] == s0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) gv[k] = g0[k];
+          } else {
+            Vec8<float>::load(gatep + (int64_t)sg[i] * gs + n, gv);
+          }
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
           if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(auxp) + m * N + n, a);
@@ -742,11 +769,13 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
         Vec8<bf16>::store(y, o);
       }
     };
-    if (mb + 120 < M) {   // all 16 rows of this thread exist
-#pragma unroll 4
+    if (nrow == 16) {   // all 16 rows of this thread exist
+#pragma unroll GATED ? 16 : 4
       for (int i = 0; i < 16; ++i) chunk(i);
     } else {
-      for (int i = 0; i < 16 && mb + 8 * i < M; ++i) chunk(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < nrow) chunk(i);
     }
   }
 }
@@ -902,18 +931,23 @@ __global__ void __launch_bounds__(256) gemm_sk_fixup_kernel(GemmBatch bt) {
   const int64_t m = (int64_t)tm * 256 + r;
   if (m >= P.M) return;
   const int n = tn * 256 + c;
+  // the residual row and its sample first, so their loads are in flight with the parts'
+  bf16* y = static_cast<bf16*>(P.Y) + m * P.ldy + n;
+  const bf16x8 xr = *reinterpret_cast<const bf16x8*>(y);
+  const int32_t sgm = P.seg[m];
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* src = bt.sk_partial + (int64_t)t * bt.sk_S * 65536 + r * 256 + c;
+#pragma unroll 4
   for (int j = 0; j < bt.sk_S; ++j) {
     float v[8];
     Vec8<float>::load(src + (int64_t)j * 65536, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) a[k] += v[k];
   }
-  bf16* y = static_cast<bf16*>(P.Y) + m * P.ldy + n;
   float xv[8], gv[8], o[8];
-  Vec8<bf16>::load(y, xv);
-  Vec8<float>::load(P.gate + (int64_t)P.seg[m] * P.gate_stride + n, gv);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) xv[k] = (float)xr[k];
+  Vec8<float>::load(P.gate + (int64_t)sgm * P.gate_stride + n, gv);
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = xv[k] + gv[k] * a[k];
   if constexpr (EPI == kEpiGatedResAux) Vec8<bf16>::store(static_cast<bf16*>(P.aux) + m * P.N + n, a);
