@@ -689,11 +689,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
           }
     }
     lds_barrier();
-    // gated residual: all of the thread's residual rows and their samples
-    // are read at once (one memory latency instead of one per few rows), the
-    // gate vector once when those rows belong to one sample
-    bf16x8 xr[GATED ? 16 : 1];
+    // The row operands of the epilogue are read for all of the thread's rows
+    // at once (one memory latency instead of one per few rows): the gated
+    // residual's x rows and samples (the gate vector once when those rows
+    // belong to one sample), the GELU backward's saved pre-activations, the
+    // RoPE rows' (cos, sin) pairs.
+    bf16x8 xr[GATED || EPI == kEpiGeluBwd ? 16 : 1];
     int32_t sg[GATED ? 16 : 1];
+    f32x4 cq[QK ? 16 : 1][2];
     float g0[8];
     int32_t s0 = 0;
     if constexpr (GATED) {
@@ -706,6 +709,19 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
       if (nrow > 0) {
         s0 = sg[0];
         Vec8<float>::load(gatep + (int64_t)s0 * gs + n, g0);
+      }
+    } else if constexpr (EPI == kEpiGeluBwd) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < nrow) xr[i] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(auxp) + (mb + 8 * i) * N + n);
+    } else if constexpr (QK) {
+      if (rot_tile && csp) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i < nrow) {
+            cq[i][0] = *reinterpret_cast<const f32x4*>(csp + (mb + 8 * i) * Dh);
+            cq[i][1] = *reinterpret_cast<const f32x4*>(csp + (mb + 8 * i) * Dh + 4);
+          }
       }
     }
     // thread tid takes columns n..n+7 of rows r0, r0 + 8, ..., r0 + 120
@@ -729,8 +745,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
           const float r = qk_inv_rms(ss, (float)Dh, qk_eps);
           float cs[4], sn[4];
           if (csp) {
-            const f32x4 c0 = *reinterpret_cast<const f32x4*>(csp + m * Dh);
-            const f32x4 c1 = *reinterpret_cast<const f32x4*>(csp + m * Dh + 4);
+            const f32x4 c0 = cq[i][0], c1 = cq[i][1];
             cs[0] = c0[0], sn[0] = c0[1], cs[1] = c0[2], sn[1] = c0[3];
             cs[2] = c1[0], sn[2] = c1[1], cs[3] = c1[2], sn[3] = c1[3];
           }
@@ -749,7 +764,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
           if constexpr (EPI == kEpiGeluAux) Vec8<bf16>::store(static_cast<bf16*>(auxp) + m * N + n, a);
         } else if constexpr (EPI == kEpiGeluBwd) {
           float xv[8];
-          Vec8<bf16>::load(static_cast<const bf16*>(auxp) + m * N + n, xv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xv[k] = (float)xr[i][k];
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = a[k] * gelu_grad_f(xv[k]);
         } else {
@@ -770,7 +786,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
       }
     };
     if (nrow == 16) {   // all 16 rows of this thread exist
-#pragma unroll GATED ? 16 : 4
+#pragma unroll GATED || QK || EPI == kEpiGeluBwd ? 16 : 4
       for (int i = 0; i < 16; ++i) chunk(i);
     } else {
 #pragma unroll
