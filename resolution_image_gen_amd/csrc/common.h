@@ -129,7 +129,8 @@ __device__ __forceinline__ void gelu_qe(float x, float& q, float& e) {
 __device__ __forceinline__ float gelu_f(float x) {
   float q, e;
   gelu_qe(x, q, e);
-  return fmaf(-fabsf(x) * q, e, fmaxf(x, 0.0f));
+  // max(x, 0) as a clamp to [0, FLT_MAX]: one v_med3 (fmaxf would first quiet x)
+  return fmaf(-fabsf(x) * q, e, __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f));
 }
 __device__ __forceinline__ float gelu_grad_f(float x) {
   float q, e;
