@@ -18,6 +18,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifndef MMDIT_PERSIST_DEFAULT
+#define MMDIT_PERSIST_DEFAULT 1
+#endif
+
 namespace mmdit {
 
 namespace {
@@ -59,6 +63,11 @@ struct GemmBatch {
   int64_t partial_elems;
   int32_t tail_begin;   // > 0: blocks from here on share the tiles tail_begin.. (last-round fill)
   int32_t tail_chunks;  // blocks (sub-tiles) per last-round tile: 2, 4 or 8
+  // > 0: the whole 256x256 tiles of the pipelined 4-wave shape are run by
+  // `persist` blocks (one per CU), block b taking tiles b, b + persist, ...
+  // of the XCD-renumbered order; last-round sub-tile blocks follow them
+  int32_t persist;
+  int32_t ntiles;       // whole tiles of the launch (persistent form)
   QkDims qk;            // kEpiQkRope*: heads, head dim, eps
   // split last round (gemm_sk_part_kernel): tiles sk_full.. are cut along k
   // into sk_S parts of sk_P 64-deep steps whose float32 partial tiles
@@ -522,9 +531,10 @@ __device__ __forceinline__ void pipe_step(rsrc_t ra, rsrc_t rb, const uint32_t (
 // holds two stages of both operands (128 KB).  Ends with a barrier, so the
 // caller may reuse the LDS right away.
 __device__ __forceinline__ void mma_tile_pipe(const GemmProb& P, int64_t m0, int n0, bf16* smem,
-                                              f32x16 (&acc)[4][4], int kt0 = 0, int nkt = -1) {
+                                              f32x16 (&acc)[4][4], int kt0 = 0, int nkt = -1, int tid_in = -1) {
   constexpr int BM = 256, BK = 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = tid_in >= 0 ? tid_in : (int)threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int rr = lane >> 3, pp = lane & 7;
   const int row0 = wave * 8 + rr;
@@ -643,9 +653,9 @@ __device__ __forceinline__ void store_tile(const GemmProb& P, int64_t m0, int n0
 // projection followed by that kernel.
 template <int EPI>
 __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, int n0, const f32x16 (&acc)[4][4],
-                                               bf16* smem, const QkDims& qk) {
+                                               bf16* smem, const QkDims& qk, int tid_in = -1) {
   float* T = reinterpret_cast<float*>(smem);   // [128][256]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tid_in >= 0 ? tid_in : (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g = lane >> 5;
   // the problem's fields in registers once (the compiler would otherwise
   // reload them after every store, which it cannot prove does not alias them)
@@ -803,14 +813,51 @@ template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int 
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
+  constexpr bool PIPE = BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2 && SITE != 2;
+  int hw = blockIdx.x;
+  if constexpr (PIPE) {
+    if (bt.persist > 0) {
+      // persistent blocks: the virtual block ids hw, hw + persist, ... (the
+      // same XCD as hw, persist being a multiple of 8), each a whole tile in
+      // the order of the one-block-per-tile grid, so every tile takes the
+      // same arithmetic as there
+      const int full = bt.tail_begin > 0 ? bt.tail_begin : bt.ntiles;
+      if (hw < bt.persist) {
+        for (int vid = hw; vid < full; vid += bt.persist) {
+          // the previous tile's epilogue has read its last LDS staging
+          if (vid != hw) lds_barrier();
+          int t = bt.xcd_remap ? xcd_tile(vid, full) : vid;
+          const GemmProb& P = pick(bt, t);
+          int tm, tn;
+          grouped_tile(t, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
+          f32x16 acc[4][4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+          // the thread index through an opaque move each tile, so that the
+          // per-thread offsets are recomputed per tile instead of held live
+          // across the loop (hoisted, they spill)
+          int tid = threadIdx.x;
+          asm volatile("" : "+v"(tid));
+          mma_tile_pipe(P, (int64_t)tm * BM, tn * BN, smem, acc, 0, -1, tid);
+          store_tile_lds<EPI>(P, (int64_t)tm * BM, tn * BN, acc, smem, bt.qk, tid);
+        }
+        return;
+      }
+      hw = hw - bt.persist + bt.tail_begin;   // the last-round sub-tile blocks
+    }
+  }
   int tile, chunk = -1;
-  if (bt.tail_begin > 0 && (int)blockIdx.x >= bt.tail_begin) {
-    const int u = blockIdx.x - bt.tail_begin;
+  if (bt.tail_begin > 0 && hw >= bt.tail_begin) {
+    const int u = hw - bt.tail_begin;
     tile = bt.tail_begin + u / bt.tail_chunks;
     chunk = u % bt.tail_chunks;
   } else {
     const int full = bt.tail_begin > 0 ? bt.tail_begin : (int)gridDim.x;
-    tile = bt.xcd_remap ? xcd_tile(blockIdx.x, full) : (int)blockIdx.x;
+    tile = bt.xcd_remap ? xcd_tile(hw, full) : hw;
   }
   const GemmProb& P = pick(bt, tile);
   int tm, tn;
@@ -870,7 +917,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
       return;
     }
   }
-  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2 && SITE != 2) {
+  if constexpr (PIPE) {
     // whole K, explicitly pipelined 4-wave mainloop (no split-K on this shape)
     mma_tile_pipe(P, m0, n0, smem, acc);
     store_tile_lds<EPI>(P, m0, n0, acc, smem, bt.qk);
@@ -1017,6 +1064,8 @@ __global__ void splitk_reduce_sse_kernel(GemmBatch bt) {
   }
 }
 
+int persist_blocks(int whole_tiles);
+
 template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
 mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
   int tiles = 0;
@@ -1037,7 +1086,15 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  MMDIT_LAUNCH(kern, dim3(tiles, bt.splitk), dim3(WM * WN * 64), lds, s, bt);
+  unsigned grid = (unsigned)tiles;
+  if constexpr (pipe && SITE != 2) {
+    if (bt.splitk <= 1 && bt.tail_begin == 0) {
+      bt.persist = persist_blocks(tiles);
+      bt.ntiles = tiles;
+      if (bt.persist > 0) grid = (unsigned)bt.persist;
+    }
+  }
+  MMDIT_LAUNCH(kern, dim3(grid, bt.splitk), dim3(WM * WN * 64), lds, s, bt);
   static char name[80];
   if (!name[0])
     snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s,bk%d,s%d>", BM, BN, WM, WN, EPI,
@@ -1079,6 +1136,20 @@ int cu_count() {
       n = -1;
   }
   return n;
+}
+
+// Persistent blocks for the whole tiles of the pipelined 256x256 shape: one
+// block per CU (a multiple of 8, so each keeps its XCD) when the whole tiles
+// fill at least two rounds; env MMDIT_GEMM_PERSIST=0 turns it off.
+int persist_blocks(int whole_tiles) {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MMDIT_GEMM_PERSIST");
+    v = e ? atoi(e) : MMDIT_PERSIST_DEFAULT;
+  }
+  const int nb = cu_count() & ~7;
+  if (v == 0 || nb <= 0 || whole_tiles < 2 * nb) return 0;
+  return nb;
 }
 
 // The 256x256 tile: 4 = 4 waves with the pipelined mainloop (default; it
@@ -1179,7 +1250,10 @@ mmdit_status launch_sk(GemmBatch& bt, const SkPlan& pl, hipStream_t s) {
   }
   const bool down = bt.tag && strcmp(bt.tag, "mlp_down_gated") == 0;
   // whole tiles of the full rounds (the launch covers tiles 0 .. full-1)
-  MMDIT_LAUNCH(whole, dim3(pl.full), dim3(256), lds, s, bt);
+  bt.persist = persist_blocks(pl.full);
+  bt.ntiles = pl.full;
+  MMDIT_LAUNCH(whole, dim3(bt.persist > 0 ? bt.persist : pl.full), dim3(256), lds, s, bt);
+  bt.persist = 0;
   MMDIT_TRY(launch_check(bt.tag ? bt.tag : "gemm_mfma_kernel<256,256,2,2,sk>", s));
   MMDIT_LAUNCH(gemm_sk_part_kernel<SITE>, dim3(pl.tail * pl.S), dim3(256), lds, s, bt);
   MMDIT_TRY(launch_check(down ? "mlp_down_sk" : "gemm_sk_part_kernel", s));
@@ -1213,7 +1287,13 @@ mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(2 * WN * 64), lds, s, bt);
+  unsigned grid = (unsigned)(bt.tail_begin + tail * S);
+  if constexpr (WN == 2) {
+    bt.persist = persist_blocks(bt.tail_begin);
+    bt.ntiles = tiles;
+    if (bt.persist > 0) grid = (unsigned)(bt.persist + tail * S);
+  }
+  MMDIT_LAUNCH(kern, dim3(grid), dim3(2 * WN * 64), lds, s, bt);
   static char name[80];
   if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,%d,epi%d%s,tailsplit>", WN, EPI, SITE ? ",down" : "");
   return launch_check(bt.tag ? bt.tag : name, s);
