@@ -17,7 +17,8 @@ dominant kernel.  The CPU oracle runs one block-step of the same pack.
 
 Extra keys: the 256^2-stage training forward (16 x (16x16 grid + 128 text)
 tokens, one block + RF loss) as `train_forward_256`, the rectified-flow
-kernels' bandwidth as `rf_kernels`; optional legs behind flags (two-pass
+kernels' bandwidth as `rf_kernels`, the RMSNorm + modulate chain against a
+plain copy of its bytes as `chains_vs_copy`; optional legs behind flags (two-pass
 CFG, 20-step and editing samplers, the 50k-token training step).
 
 Prints ONE JSON line.
@@ -415,6 +416,58 @@ def cpu_baseline_sampler(head, min_seconds=10.0):
             "extrapolation": f"x{nblk} block-steps ({wl.depth} blocks x {len(wl.schedule) - 1} steps)"}
 
 
+def bench_chain_vs_copy(reps=10):
+    """The RMSNorm + modulate chain against a plain device copy of the same
+    bytes (torch's copy_, the practical ceiling of a read-once write-once
+    pass): batches of 16 back-to-back launches between two events on their
+    stream (one launch queued before the first event, so the host's launch
+    cost stays hidden behind the GPU's work), chain and copy batches
+    interleaved, median per launch; at the 1024^2 packed-CFG pack's 8,704
+    rows and the 1024^2 native pack's 17,280 rows of hidden 3,072 (bf16; two
+    samples' modulation vectors)."""
+    import statistics
+
+    import torch
+
+    from resolution_image_gen_amd import binding as B
+    from resolution_image_gen_amd import configs as CF
+
+    d = CF.B4
+    H = d.hidden
+    dims = B.Dims(d, "bf16")
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    for rows in (8704, 17280):
+        x = torch.randn(rows, H, generator=gen, device="cuda").to(torch.bfloat16)
+        y, yc = torch.empty_like(x), torch.empty_like(x)
+        seg = torch.zeros(rows, dtype=torch.int32, device="cuda")
+        seg[rows // 2:] = 1
+        mod = torch.randn(2, 6 * H, generator=gen, device="cuda")
+        fns = {"chain": lambda: B.rms_modulate(dims, x, seg, mod, 0, H, y), "copy": lambda: yc.copy_(x)}
+        ts = {k: [] for k in fns}
+        for _ in range(3):
+            for f in fns.values():
+                f()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            for k, f in fns.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                f()
+                e0.record()
+                for _ in range(16):
+                    f()
+                e1.record()
+                e1.synchronize()
+                ts[k].append(e0.elapsed_time(e1) * 1e3 / 16)
+        nb = 2.0 * rows * H * 2
+        uc, up = statistics.median(ts["chain"]), statistics.median(ts["copy"])
+        res[f"rms_modulate {rows}x{H}"] = {
+            "us": round(uc, 2), "GB/s": round(nb / uc / 1e3, 1), "frac_hbm": round(nb / uc / 1e3 / 8000.0, 3),
+            "copy_us": round(up, 2), "copy_GB/s": round(nb / up / 1e3, 1), "of_copy": round(up / uc, 3)}
+        del x, y, yc
+    return res
+
+
 def bench_rf_kernels(reps=20):
     """Kernel-duration bandwidth of the rectified-flow kernels (noising, loss,
     CFG combine + Euler) at their own pack shapes, where they are launch-bound,
@@ -713,6 +766,7 @@ def main():
         res, _ = bench_train_forward("pack256_bf16", 20, 5)
         out["train_forward_256"] = res
         out["rf_kernels"] = bench_rf_kernels()
+        out["chains_vs_copy"] = bench_chain_vs_copy()
         torch.cuda.empty_cache()
     if args.train_steps > 0:
         out["train_step"] = bench_train_step(args.train_steps, 1, args.train_depth)
