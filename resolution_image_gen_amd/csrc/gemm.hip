@@ -806,49 +806,57 @@ __device__ __forceinline__ void store_tile_lds(const GemmProb& P, int64_t m0, in
   }
 }
 
+// Whole 256x256 tiles of a persistent launch: block hw runs the virtual
+// block ids hw, hw + persist, ... below `full` (the same XCD as hw, persist
+// being a multiple of 8), each a whole tile in the order of the
+// one-block-per-tile grid, so every tile takes the same arithmetic as there.
+// (Written out in each kernel: behind a shared function taking the launch's
+// argument block by reference, the compiler copied that block to scratch.)
+#define MMDIT_PERSIST_TILES(hw_, full_)                                           \
+  do {                                                                          \
+    const int phw = (hw_), pfull = (full_);                                         \
+    for (int vid = phw; vid < pfull; vid += bt.persist) {                         \
+      /* the previous tile's epilogue has read its last LDS staging */          \
+      if (vid != phw) lds_barrier();                                             \
+      int t = bt.xcd_remap ? xcd_tile(vid, pfull) : vid;                         \
+      const GemmProb& P = pick(bt, t);                                          \
+      int tm, tn;                                                               \
+      grouped_tile(t, (int)cdiv_d(P.M, 256), P.tiles_n, tm, tn);                \
+      f32x16 acc[4][4];                                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                             \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                           \
+          _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;    \
+      /* the thread index through an opaque move each tile, so that the       \
+         per-thread offsets are recomputed per tile instead of held live      \
+         across the loop (hoisted, they spill) */                             \
+      int tid = threadIdx.x;                                                    \
+      asm volatile("" : "+v"(tid));                                             \
+      mma_tile_pipe(P, (int64_t)tm * 256, tn * 256, smem, acc, 0, -1, tid);     \
+      store_tile_lds<EPI>(P, (int64_t)tm * 256, tn * 256, acc, smem, bt.qk, tid); \
+    }                                                                           \
+  } while (0)
+
 // SITE 1 only separates the MLP down projection's instantiation from the
 // output projection's (same epilogue) so profiles can tell the two apart;
 // SITE 2 is the image embedding with the noising in its A staging (XT).
-template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2>
+// PERSIST: the launch's first bt.persist blocks walk the whole tiles
+// (MMDIT_PERSIST_TILES), any blocks after them take the last-round sub-tiles;
+// a separate instantiation, so the one-block-per-tile kernels keep their own
+// register allocation.
+template <int BM, int BN, int WM, int WN, int EPI, bool SILU, int SITE = 0, int BK = 64, int NS = 2,
+          bool PERSIST = false>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   extern __shared__ __attribute__((aligned(1024))) bf16 smem[];
   constexpr bool PIPE = BM == 256 && BN == 256 && WM == 2 && WN == 2 && !SILU && BK == 64 && NS == 2 && SITE != 2;
   int hw = blockIdx.x;
-  if constexpr (PIPE) {
-    if (bt.persist > 0) {
-      // persistent blocks: the virtual block ids hw, hw + persist, ... (the
-      // same XCD as hw, persist being a multiple of 8), each a whole tile in
-      // the order of the one-block-per-tile grid, so every tile takes the
-      // same arithmetic as there
-      const int full = bt.tail_begin > 0 ? bt.tail_begin : bt.ntiles;
-      if (hw < bt.persist) {
-        for (int vid = hw; vid < full; vid += bt.persist) {
-          // the previous tile's epilogue has read its last LDS staging
-          if (vid != hw) lds_barrier();
-          int t = bt.xcd_remap ? xcd_tile(vid, full) : vid;
-          const GemmProb& P = pick(bt, t);
-          int tm, tn;
-          grouped_tile(t, (int)cdiv_d(P.M, BM), P.tiles_n, tm, tn);
-          f32x16 acc[4][4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-          // the thread index through an opaque move each tile, so that the
-          // per-thread offsets are recomputed per tile instead of held live
-          // across the loop (hoisted, they spill)
-          int tid = threadIdx.x;
-          asm volatile("" : "+v"(tid));
-          mma_tile_pipe(P, (int64_t)tm * BM, tn * BN, smem, acc, 0, -1, tid);
-          store_tile_lds<EPI>(P, (int64_t)tm * BM, tn * BN, acc, smem, bt.qk, tid);
-        }
-        return;
-      }
-      hw = hw - bt.persist + bt.tail_begin;   // the last-round sub-tile blocks
+  if constexpr (PIPE && PERSIST) {
+    // persistent blocks first, then the last-round sub-tile blocks
+    if (hw < bt.persist) {
+      MMDIT_PERSIST_TILES(hw, bt.tail_begin > 0 ? bt.tail_begin : bt.ntiles);
+      return;
     }
+    hw = hw - bt.persist + bt.tail_begin;
   }
   int tile, chunk = -1;
   if (bt.tail_begin > 0 && hw >= bt.tail_begin) {
@@ -1086,15 +1094,27 @@ mmdit_status launch_mfma_cfg(GemmBatch& bt, hipStream_t s) {
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  unsigned grid = (unsigned)tiles;
+  bool persistent = false;
   if constexpr (pipe && SITE != 2) {
     if (bt.splitk <= 1 && bt.tail_begin == 0) {
       bt.persist = persist_blocks(tiles);
       bt.ntiles = tiles;
-      if (bt.persist > 0) grid = (unsigned)bt.persist;
+      persistent = bt.persist > 0;
     }
   }
-  MMDIT_LAUNCH(kern, dim3(grid, bt.splitk), dim3(WM * WN * 64), lds, s, bt);
+  if constexpr (pipe && SITE != 2) {
+    if (persistent) {
+      auto pk = gemm_mfma_kernel<BM, BN, WM, WN, EPI, SILU, SITE, BK, NS, true>;
+      static bool pattr = false;
+      if (!pattr) {
+        MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                            "hipFuncSetAttribute(gemm_mfma_kernel)"));
+        pattr = true;
+      }
+      MMDIT_LAUNCH(pk, dim3(bt.persist), dim3(256), lds, s, bt);
+    }
+  }
+  if (!persistent) MMDIT_LAUNCH(kern, dim3(tiles, bt.splitk), dim3(WM * WN * 64), lds, s, bt);
   static char name[80];
   if (!name[0])
     snprintf(name, sizeof(name), "gemm_mfma_kernel<%d,%d,%d,%d,epi%d%s%s,bk%d,s%d>", BM, BN, WM, WN, EPI,
@@ -1252,7 +1272,18 @@ mmdit_status launch_sk(GemmBatch& bt, const SkPlan& pl, hipStream_t s) {
   // whole tiles of the full rounds (the launch covers tiles 0 .. full-1)
   bt.persist = persist_blocks(pl.full);
   bt.ntiles = pl.full;
-  MMDIT_LAUNCH(whole, dim3(bt.persist > 0 ? bt.persist : pl.full), dim3(256), lds, s, bt);
+  if (bt.persist > 0) {
+    auto pk = gemm_mfma_kernel<256, 256, 2, 2, EPI, false, SITE, 64, 2, true>;
+    static bool pattr = false;
+    if (!pattr) {
+      MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                          "hipFuncSetAttribute(gemm_mfma_kernel)"));
+      pattr = true;
+    }
+    MMDIT_LAUNCH(pk, dim3(bt.persist), dim3(256), lds, s, bt);
+  } else {
+    MMDIT_LAUNCH(whole, dim3(pl.full), dim3(256), lds, s, bt);
+  }
   bt.persist = 0;
   MMDIT_TRY(launch_check(bt.tag ? bt.tag : "gemm_mfma_kernel<256,256,2,2,sk>", s));
   MMDIT_LAUNCH(gemm_sk_part_kernel<SITE>, dim3(pl.tail * pl.S), dim3(256), lds, s, bt);
@@ -1281,19 +1312,23 @@ mmdit_status launch_tailsplit(GemmBatch& bt, int tiles, int nb, hipStream_t s) {
   bt.tail_chunks = S;
   const size_t lds = 2 * (256 + 256) * 64 * sizeof(bf16) + (WN == 2 ? 1024 : 0);
   auto kern = gemm_mfma_kernel<256, 256, 2, WN, EPI, false, SITE>;
+  auto kernp = gemm_mfma_kernel<256, 256, 2, WN, EPI, false, SITE, 64, 2, true>;
   static bool attr_set = false;
   if (!attr_set) {
     MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
                         "hipFuncSetAttribute(gemm_mfma_kernel)"));
+    MMDIT_TRY(hip_check(hipFuncSetAttribute((const void*)kernp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                        "hipFuncSetAttribute(gemm_mfma_kernel)"));
     attr_set = true;
   }
-  unsigned grid = (unsigned)(bt.tail_begin + tail * S);
-  if constexpr (WN == 2) {
+  if (WN == 2) {
     bt.persist = persist_blocks(bt.tail_begin);
     bt.ntiles = tiles;
-    if (bt.persist > 0) grid = (unsigned)(bt.persist + tail * S);
   }
-  MMDIT_LAUNCH(kern, dim3(grid), dim3(2 * WN * 64), lds, s, bt);
+  if (bt.persist > 0)
+    MMDIT_LAUNCH(kernp, dim3(bt.persist + tail * S), dim3(2 * WN * 64), lds, s, bt);
+  else
+    MMDIT_LAUNCH(kern, dim3(bt.tail_begin + tail * S), dim3(2 * WN * 64), lds, s, bt);
   static char name[80];
   if (!name[0]) snprintf(name, sizeof(name), "gemm_mfma_kernel<256,256,2,%d,epi%d%s,tailsplit>", WN, EPI, SITE ? ",down" : "");
   return launch_check(bt.tag ? bt.tag : name, s);
