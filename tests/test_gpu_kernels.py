@@ -167,7 +167,10 @@ LINEAR_CASES = [
     ("f32", 5, 1536, 256, 1, True),
     ("bf16", 1000, 384, 256, 0, False),       # MFMA 128x128, ragged M
     ("bf16", 4096, 4096, 128, 0, False),      # MFMA 256x128
-    ("bf16", 4000, 8192, 128, 2, False),      # MFMA 256x256, ragged M, GELU
+    ("bf16", 4000, 8192, 128, 2, False),      # MFMA 256x256, ragged M, GELU (two rounds: persistent blocks)
+    ("bf16", 4500, 8192, 128, 2, False),      # persistent blocks + last-round sub-tiles in one launch, GELU
+    ("bf16", 4500, 8192, 192, 3, False),      # persistent blocks, gated residual, ragged M
+    ("bf16", 4096, 8192, 256, 0, False),      # persistent blocks, plain store
     ("bf16", 300, 512, 128, 1, True),         # MFMA with SiLU on A (M > 16), float32 out
     ("bf16", 515, 320, 192, 2, False),        # MFMA 128x64 (N % 128 != 0), GELU
     ("bf16", 700, 256, 512, 3, False),        # gated residual
@@ -202,6 +205,24 @@ def test_linear(B, dtype, M, N, K, epi, silu):
         return
     tol = TOL[dtype] if (dtype == "bf16") else 1e-5
     assert_close(f"linear {key}", to_np(Y), y, tol)
+
+
+@pytest.mark.parametrize("epi", [0, 2])
+def test_linear_rows_independent_of_launch(B, epi):
+    """The 1024^2 packed-CFG pack's MLP up shape (8,704 x 12,288 x 3,072: a
+    persistent launch with last-round sub-tiles) gives every row the bits the
+    same row gets in a launch of 256 rows (one round, other tiles): each
+    element takes the same k order in every tile shape."""
+    M, N, K = 8704, 12288, 3072
+    g = torch.Generator(device="cuda").manual_seed(7)
+    A = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn(N, K, generator=g, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    B.linear(A, W, Y, epilogue=epi)
+    for r0 in (0, 4224, M - 256):
+        Ys = torch.empty(256, N, device="cuda", dtype=torch.bfloat16)
+        B.linear(A[r0:r0 + 256].contiguous(), W, Ys, epilogue=epi)
+        assert torch.equal(Ys, Y[r0:r0 + 256]), f"rows {r0}..{r0 + 255} differ"
 
 
 @pytest.mark.parametrize("case", ["tiny_f32", "pack256_bf16"])
