@@ -124,6 +124,52 @@ def test_sampler_vs_oracle(dtype, schedule, edit):
         np.testing.assert_array_equal(zt[3 * n:], src)
 
 
+def test_sampler_vs_oracle_headline_width():
+    """The 4-step packed-CFG sampler at its own width and pack (hidden 3,072,
+    24 x 128 heads, MLP 12,288, latent 128; cond + uncond each a 64 x 64 grid
+    + 256 text tokens, 8,704 tokens; guidance 4; bf16), cut to one block and
+    the schedule's first two steps (1 -> 0.75 -> 0.5) so the float64 oracle
+    finishes in seconds: both branches' step-0 velocities at the bar, the
+    guided velocities and the latent after two steps at the guidance bound."""
+    import time
+
+    from resolution_image_gen_amd import runner as R
+
+    sched = (1.0, 0.75, 0.5)
+    wl = CF.Workload("sampler1024_cfg_bf16_2step", CF.B4, "bf16", ((64, 64, 1, 256), (64, 64, 1, 256)),
+                     img_budget=8192, depth=1, steps=2, guidance=4.0, schedule=sched)
+    t0 = time.time()
+    W = R.Weights(wl, recipe="stress")
+    h, w = 64, 64
+    n = h * w
+    eps = S.normal((n, wl.dims.c_lat), 1.0, "bf16", wl.name, "eps")
+    tau_c = S.text(256, wl.dims.d_txt, "bf16", wl.name, "tau_c")
+    tau_u = S.text(256, wl.dims.d_txt, "bf16", wl.name, "tau_u")
+    vs = []
+    sm = R.Sampler(wl, W, eps, tau_c, tau_u)
+    sm.run(on_step=lambda i, st: vs.append(to_np(st.v)))
+    torch.cuda.synchronize()
+    print(f"headline-width sampler on the GPU after {time.time() - t0:.1f} s", flush=True)
+    Wd = {k: np.asarray(v, np.float64) for k, v in W.np_wrap.items()}
+    Wd["blocks"] = [f64_block(nb) for nb in W.np_blocks]
+    g = wl.guidance
+    pk = oracle_pack([(h, w, 1, 256), (h, w, 1, 256)])
+    v0 = OF.velocity_model(np.concatenate([eps, eps]), np.concatenate([tau_c, tau_u]), np.ones(2), Wd, pk,
+                           wl.dims.heads)
+    tol = TOL["bf16"]
+    assert_close("v_cond step 0", vs[0][:n], v0[:n], tol)
+    assert_close("v_uncond step 0", vs[0][n:], v0[n:], tol)
+    z_ref, vhat_ref = OF.sample_packed_cfg(eps, tau_c, tau_u, Wd, (h, w), wl.dims.heads, g, sched)
+    print(f"oracle done after {time.time() - t0:.1f} s", flush=True)
+    assert len(vs) == len(vhat_ref) == 2
+    vmax = np.max(np.abs(v0))
+    for i, v in enumerate(vs):
+        bound = (abs(1 - g) + g) * tol * vmax / np.max(np.abs(vhat_ref[i]))
+        assert_close(f"vhat step {i}", OF.cfg_combine(v[:n], v[n:], g), vhat_ref[i], bound)
+    zb = (abs(1 - g) + g) * tol * vmax / np.max(np.abs(z_ref))
+    assert_close("z after two steps", to_np(sm.z), z_ref, zb)
+
+
 def test_packed_cfg_equals_two_pass_on_gpu():
     """Packing cond + uncond in one forward reproduces two separate forwards."""
     from resolution_image_gen_amd import binding as B
