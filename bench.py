@@ -16,7 +16,9 @@ on its stream: it gives the per-kernel table and the roofline of the
 dominant kernel.  The CPU oracle runs one block-step of the same pack.
 
 Extra keys: the 256^2-stage training forward (16 x (16x16 grid + 128 text)
-tokens, one block + RF loss) as `train_forward_256`, the rectified-flow
+tokens, one block + RF loss) as `train_forward_256`, the same for the 1024^2
+native-resolution pack, the 2048^2 edit pair and the tiny float32 pack
+(`native1024_bf16`, `edit2048_bf16`, `tiny_f32`), the rectified-flow
 kernels' bandwidth as `rf_kernels`, the RMSNorm + modulate chain against a
 plain copy of its bytes as `chains_vs_copy`; optional legs behind flags (two-pass
 CFG, 20-step and editing samplers, the 50k-token training step).
@@ -594,11 +596,13 @@ def bench_train_step(steps, warmup, depth):
             "loss": round(ts.loss.item(), 6), "roofline": roof, "kernels_us_per_block": table}
 
 
-def bench_train_forward(name, steps, warmup, graph=True):
+def bench_train_forward(name, steps, warmup, graph=True, weights=None):
     """One training forward per step (pack ids, gathers, RF noising, cond,
     embed, the blocks, final layer, RF loss) over workload `name`: eager ms
     per step over `steps` steps, the same step replayed from a HIP graph, and
-    one more pass of `steps` steps on one stream with every launch timed."""
+    one more pass of `steps` steps on one stream with every launch timed.
+    `weights`: device weights of another workload with the same widths, dtype
+    and depth to reuse (timing does not depend on their values)."""
     import torch
 
     from resolution_image_gen_amd import binding as B
@@ -606,7 +610,7 @@ def bench_train_forward(name, steps, warmup, graph=True):
     from resolution_image_gen_amd import runner as R
 
     wl = CF.WORKLOADS[name]
-    W = R.Weights(wl)
+    W = weights if weights is not None else R.Weights(wl)
     inputs = R.training_inputs(wl)
     tf = R.TrainForward(wl, W, inputs)
     stream = torch.cuda.current_stream()
@@ -655,7 +659,17 @@ def bench_train_forward(name, steps, warmup, graph=True):
            "block_tflop_per_step": round(blk / 1e12, 4), "roofline": roof,
            "kernels_us_per_step": {k: v["us_per_step"]
                                    for k, v in _kernel_lines(kernels, work, steps, "step").items()}}
-    return out, (wl, _NumpyWeights(W), inputs)
+    return out, (wl, _NumpyWeights(W), inputs, W)
+
+
+def _compact(res):
+    """The headline figures of a bench_train_forward result (no per-kernel table)."""
+    keep = ("workload", "ms_per_step", "graph_ms_per_step", "tokens_per_s", "tflops", "pct_bf16_peak",
+            "block_tflop_per_step")
+    out = {k: res[k] for k in keep}
+    r = res["roofline"]
+    out["roofline"] = {k: r.get(k) for k in ("bound", "kernel", "avg_launch_us", "achieved", "peak", "unit", "frac")}
+    return out
 
 
 def main():
@@ -712,7 +726,7 @@ def main():
               "data": "synthetic: seeded N(0,1) latents, noise and text features; random-init N(0,0.02) weights"}
 
     if args.workload:   # one training-forward workload alone
-        res, (wl, Wn, inputs) = bench_train_forward(args.workload, args.steps, args.warmup)
+        res, (wl, Wn, inputs, _) = bench_train_forward(args.workload, args.steps, args.warmup)
         n_tokens = sum(f * h * w + t for h, w, f, t in wl.samples)
         out = {"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", **common,
                "ms_per_step": res["ms_per_step"], "dtype": wl.dtype,
@@ -763,8 +777,17 @@ def main():
     del W, head
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        res, _ = bench_train_forward("pack256_bf16", 20, 5)
+        res, (_, _, _, W0) = bench_train_forward("pack256_bf16", 20, 5)
         out["train_forward_256"] = res
+        # the other one-block configurations at their own packs (same widths:
+        # the 256^2 stage's weights are reused), and the tiny float32 pack
+        out["native1024_bf16"] = _compact(bench_train_forward("native1024_bf16", 10, 3, weights=W0)[0])
+        out["edit2048_bf16"] = _compact(bench_train_forward("edit2048_bf16", 5, 2, weights=W0)[0])
+        del W0
+        tiny = _compact(bench_train_forward("tiny_f32", 20, 5)[0])
+        # float32 (the plain per-element kernels): no bf16 roofline applies
+        out["tiny_f32"] = {k: tiny[k] for k in ("workload", "ms_per_step", "graph_ms_per_step", "tokens_per_s")}
+        torch.cuda.empty_cache()
         out["rf_kernels"] = bench_rf_kernels()
         out["chains_vs_copy"] = bench_chain_vs_copy()
         torch.cuda.empty_cache()
