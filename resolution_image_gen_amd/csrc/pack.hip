@@ -76,19 +76,18 @@ struct GatherChunk {
   const uint8_t* src[kChunk];
 };
 
-// Copies 16-byte units; row_bytes % 16 == 0.
-__global__ void gather_kernel(GatherChunk ck, int32_t row_bytes, uint8_t* dst) {
-  const int32_t upr = row_bytes >> 4;
-  const int64_t n_units = (int64_t)(ck.dst0[ck.nb] - ck.dst0[0]) * upr;
+// Copies 16-byte units; row_bytes % 16 == 0.  A sample's rows are contiguous
+// in its source and in the packed buffer, so each sample is one flat copy:
+// blockIdx.y picks the sample (a uniform index into the argument block), the
+// x blocks stride over its units (no per-unit search or division).
+__global__ void __launch_bounds__(256) gather_kernel(GatherChunk ck, int32_t row_bytes, uint8_t* dst) {
+  const int b = blockIdx.y;
+  const int64_t n_units = (int64_t)(ck.dst0[b + 1] - ck.dst0[b]) * (row_bytes >> 4);
+  const u32x4* s = reinterpret_cast<const u32x4*>(ck.src[b]);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)ck.dst0[b] * row_bytes);
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    int32_t row = ck.dst0[0] + (int32_t)(u / upr);
-    int32_t cu = (int32_t)(u % upr);
-    int b = find_sample(ck.dst0, ck.nb, row);
-    const u32x4* s = reinterpret_cast<const u32x4*>(ck.src[b] + (int64_t)(row - ck.dst0[b]) * row_bytes) + cu;
-    u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)row * row_bytes) + cu;
-    *d = *s;
-  }
+       u += (int64_t)gridDim.x * blockDim.x)
+    d[u] = s[u];
 }
 
 int grid_for(int64_t work, int threads) {
@@ -225,10 +224,15 @@ mmdit_status gather_impl(const mmdit_pack_t* pk, int32_t which, const void* cons
       }
       ck.src[i] = static_cast<const uint8_t*>(src[b0 + i]);
     }
-    int64_t units = (int64_t)(ck.dst0[ck.nb] - ck.dst0[0]) * (row_bytes / 16);
+    int64_t units = 0;   // the largest sample's 16-byte units
+    for (int i = 0; i < ck.nb; ++i) {
+      const int64_t u = (int64_t)(ck.dst0[i + 1] - ck.dst0[i]) * (row_bytes / 16);
+      units = u > units ? u : units;
+    }
     if (units == 0) continue;
-    MMDIT_LAUNCH(gather_kernel, dim3(grid_for(units, 256)), dim3(256), 0, stream, ck,
-                       row_bytes, static_cast<uint8_t*>(dst));
+    const int gx = grid_for(units, 256) < 1024 ? grid_for(units, 256) : 1024;
+    MMDIT_LAUNCH(gather_kernel, dim3(gx, ck.nb), dim3(256), 0, stream, ck, row_bytes,
+                 static_cast<uint8_t*>(dst));
     MMDIT_TRY(launch_check("gather_kernel", stream));
   }
   return MMDIT_OK;
