@@ -475,7 +475,8 @@ def bench_rf_kernels(reps=20):
     CFG combine + Euler) at their own pack shapes, where they are launch-bound,
     and at a 64 M-element shape, where they reach steady state.  Bytes are
     algorithmic: noising reads z and eps and writes z_t (3 x 2 B per element);
-    the loss reads v, z and eps of every target element (3 x 2 B); the Euler
+    the loss reads v, z and eps of every target element (3 x 2 B), the
+    negative-aware loss v+, v-, z and eps (4 x 2 B); the Euler
     step reads v_c, v_u (2 x 2 B) and the float32 z, writes z and the next
     bf16 input of both CFG samples (4 + 4 + 2 x 2 B)."""
     import torch
@@ -514,7 +515,12 @@ def bench_rf_kernels(reps=20):
         res[f"noise {name}"] = {"elements": n * C, "us": round(us, 2), "GB/s": round(6.0 * n * C / us / 1e3, 1)}
         us = timed(lambda: B.rf_loss(pk, v, z, eps, sse, loss, ws), ["row_sse_kernel", "loss_finalize_kernel"])
         res[f"loss {name}"] = {"elements": nt * C, "us": round(us, 2), "GB/s": round(6.0 * nt * C / us / 1e3, 1)}
-        del z, eps, zt, v
+        # negative-aware loss: reads v+, v-, z and eps of every target element (4 x 2 B)
+        vn = rnd(nt, C)
+        r = torch.rand(pk.B, generator=gen, device="cuda")
+        us = timed(lambda: B.rf_nft_loss(pk, v, vn, z, eps, r, sse, loss, ws), ["row_nft_kernel", "loss_finalize_kernel"])
+        res[f"nft loss {name}"] = {"elements": nt * C, "us": round(us, 2), "GB/s": round(8.0 * nt * C / us / 1e3, 1)}
+        del z, eps, zt, v, vn
     euler_shapes = {"1024^2 CFG pack": [(64, 64, 1, 256)] * 2, "64M elements": [(512, 1024, 1, 0)] * 2}
     for name, samples in euler_shapes.items():
         pk = B.pack(list(samples))
