@@ -513,12 +513,12 @@ def bench_rf_kernels(reps=20):
         ws = torch.empty(nt * 4 + 4, dtype=torch.uint8, device="cuda")
         us = timed(lambda: B.rf_make_xt(pk, z, eps, t, zt), ["make_xt_kernel"])
         res[f"noise {name}"] = {"elements": n * C, "us": round(us, 2), "GB/s": round(6.0 * n * C / us / 1e3, 1)}
-        us = timed(lambda: B.rf_loss(pk, v, z, eps, sse, loss, ws), ["row_sse_kernel", "loss_finalize_kernel"])
+        us = timed(lambda: B.rf_loss(pk, v, z, eps, sse, loss, ws), ["row_sse_kernel", "loss_finalize_kernel", "loss_sample_sums_kernel", "loss_mean_kernel"])
         res[f"loss {name}"] = {"elements": nt * C, "us": round(us, 2), "GB/s": round(6.0 * nt * C / us / 1e3, 1)}
         # negative-aware loss: reads v+, v-, z and eps of every target element (4 x 2 B)
         vn = rnd(nt, C)
         r = torch.rand(pk.B, generator=gen, device="cuda")
-        us = timed(lambda: B.rf_nft_loss(pk, v, vn, z, eps, r, sse, loss, ws), ["row_nft_kernel", "loss_finalize_kernel"])
+        us = timed(lambda: B.rf_nft_loss(pk, v, vn, z, eps, r, sse, loss, ws), ["row_nft_kernel", "loss_finalize_kernel", "loss_sample_sums_kernel", "loss_mean_kernel"])
         res[f"nft loss {name}"] = {"elements": nt * C, "us": round(us, 2), "GB/s": round(8.0 * nt * C / us / 1e3, 1)}
         del z, eps, zt, v, vn
     euler_shapes = {"1024^2 CFG pack": [(64, 64, 1, 256)] * 2, "64M elements": [(512, 1024, 1, 0)] * 2}

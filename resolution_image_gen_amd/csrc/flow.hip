@@ -140,6 +140,9 @@ __global__ void loss_grad_kernel(int64_t n_tgt, int32_t C, int32_t B, const T* _
   }
 }
 
+// Target rows from which the loss's per-sample sums take one block per sample.
+constexpr int64_t kLossBlocksRows = 131072;
+
 // One block of 16 waves.  Wave w takes samples w, w + 16, ...: its lanes sum
 // the sample's rows r0 + lane, r0 + lane + 64, ... and the wave reduces them
 // (a fixed order that depends only on the sample's rows, so the result is
@@ -190,6 +193,55 @@ __global__ void __launch_bounds__(1024) loss_finalize_kernel(int32_t B, int32_t 
       total += sh[b] / ((float)(cu_tgt[b + 1] - cu_tgt[b]) * (float)C);
     loss[0] = B > 0 ? total / (float)B : 0.f;
   }
+}
+
+// For large packs (from kLossBlocksRows target rows) the per-sample sums
+// instead take one block of 256 threads per sample (blockIdx.x), so the
+// reduction spreads over the CUs (one wave per sample reads a few hundred
+// GB/s at most).  The
+// 16-byte-aligned middle of the sample's rows is read as float4, thread t
+// taking j = t, t + 256, ... with four loads in flight (four accumulators,
+// summed in a fixed tree); the up to 3 + 3 rows outside it go to threads
+// 0..5; each wave reduces its threads, then thread 0 adds the four waves in
+// order.  The order depends only on the sample's rows, so the result is
+// deterministic and independent of the other samples.
+__global__ void __launch_bounds__(256) loss_sample_sums_kernel(const int32_t* __restrict__ cu_tgt,
+                                                               const float* __restrict__ row_val,
+                                                               float* __restrict__ sse) {
+  __shared__ float wsum[4];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t r0 = cu_tgt[b], r1 = cu_tgt[b + 1];
+  const int32_t a0 = min((r0 + 3) & ~3, r1), a1 = max(r1 & ~3, a0);
+  const f32x4* mid = reinterpret_cast<const f32x4*>(row_val + a0);
+  const int32_t nv = (a1 - a0) >> 2;
+  f32x4 s4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s4[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int32_t j = t;
+  for (; j + 3 * 256 < nv; j += 4 * 256) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s4[k] += mid[j + k * 256];
+  }
+  for (int k = 0; j < nv; j += 256, ++k) s4[k] += mid[j];
+  s4[0] += s4[2];
+  s4[1] += s4[3];
+  s4[0] += s4[1];
+  float acc = (s4[0][0] + s4[0][1]) + (s4[0][2] + s4[0][3]);
+  if (t < 3 && r0 + t < a0) acc += row_val[r0 + t];
+  if (t >= 3 && t < 6 && a1 + t - 3 < r1) acc += row_val[a1 + t - 3];
+  acc = wave_sum(acc);
+  if (lane == 0) wsum[wave] = acc;
+  __syncthreads();
+  if (t == 0) sse[b] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// The mean loss over the samples, in sample order: one thread.
+__global__ void loss_mean_kernel(int32_t B, int32_t C, const int32_t* __restrict__ cu_tgt,
+                                 const float* __restrict__ sse, float* __restrict__ loss) {
+  if (threadIdx.x != 0) return;
+  float total = 0.f;
+  for (int b = 0; b < B; ++b) total += sse[b] / ((float)(cu_tgt[b + 1] - cu_tgt[b]) * (float)C);
+  loss[0] = B > 0 ? total / (float)B : 0.f;
 }
 
 // z (float32 [n, C]) += dt * (v_u + g (v_c - v_u)); optionally writes z into two target row ranges.
@@ -305,8 +357,18 @@ mmdit_status row_sse_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, con
 
 mmdit_status loss_finalize_impl(const mmdit_pack_t* pk, int32_t C, const float* row_sse, float* sse, float* loss,
                                 hipStream_t s) {
-  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse, sse, loss);
-  return launch_check("loss_finalize_kernel", s);
+  // a function of the pack's size only, so every call on a pack takes the
+  // same reduction order
+  if (pk->n_tgt < kLossBlocksRows) {
+    MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_sse, sse, loss);
+    return launch_check("loss_finalize_kernel", s);
+  }
+  if (pk->B > 0) {
+    MMDIT_LAUNCH(loss_sample_sums_kernel, dim3((unsigned)pk->B), dim3(256), 0, s, pk->cu_tgt, row_sse, sse);
+    MMDIT_TRY(launch_check("loss_sample_sums_kernel", s));
+  }
+  MMDIT_LAUNCH(loss_mean_kernel, dim3(1), dim3(64), 0, s, pk->B, C, pk->cu_tgt, sse, loss);
+  return launch_check("loss_mean_kernel", s);
 }
 
 mmdit_status loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, const void* v,
@@ -367,8 +429,7 @@ mmdit_status nft_loss_impl(const mmdit_pack_t* pk, mmdit_dtype dt, int32_t C, co
                    (const float*)vn, (const float*)z, (const float*)eps, r, pk->seg_img, pk->tgt_row, row_val);
     MMDIT_TRY(launch_check("row_nft_kernel", s));
   }
-  MMDIT_LAUNCH(loss_finalize_kernel, dim3(1), dim3(1024), 0, s, pk->B, C, pk->cu_tgt, row_val, sse, loss);
-  return launch_check("loss_finalize_kernel", s);
+  return loss_finalize_impl(pk, C, row_val, sse, loss, s);
 }
 
 namespace {

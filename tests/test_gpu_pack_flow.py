@@ -20,6 +20,9 @@ SAMPLE_SETS = {
     "max_samples": [(1 + i % 4, 1 + i % 3, 1 + i % 2, i % 6) for i in range(256)],
     # long samples whose target rows start and end off 4-row boundaries
     "long_ragged": [(3, 5, 1, 0), (127, 129, 1, 0), (1, 7, 2, 3), (64, 65, 1, 0)],
+    # past 131,072 target rows (the loss's per-sample sums take one block per
+    # sample), sample boundaries off 4-row boundaries
+    "large_ragged": [(257, 259, 1, 0), (3, 5, 1, 0), (255, 255, 1, 0)],
 }
 
 
@@ -118,7 +121,7 @@ def test_make_xt(B, dtype, name):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged"])
+@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged", "large_ragged"])
 def test_rf_loss(B, dtype, name):
     samples = SAMPLE_SETS[name]
     C = 64
@@ -153,7 +156,7 @@ def test_rf_loss(B, dtype, name):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged"])
+@pytest.mark.parametrize("name", ["ragged", "pack256", "edit2048", "many", "long_ragged", "large_ragged"])
 def test_rf_nft_loss(B, dtype, name):
     """Negative-aware loss against the oracle's definition; rewards of 1 give
     rf_loss(v_pos) bit for bit, rewards of 0 rf_loss(v_neg)."""
